@@ -1,0 +1,33 @@
+"""The seeded input generator: deterministic, right shapes, dtypes and laws."""
+
+import numpy as np
+import torch
+
+from sample_gradient_clipping_amd.inputs import linear_inputs, sample_scales, theta_init
+
+
+def test_linear_inputs_deterministic_and_shaped():
+    A, G = linear_inputs(3, 16, 8, 12, "bf16", "llama_logu", seed=5)
+    A2, G2 = linear_inputs(3, 16, 8, 12, "bf16", "llama_logu", seed=5)
+    assert A.dtype == torch.bfloat16 and A.shape == (3, 16, 8) and G.shape == (3, 16, 12)
+    assert torch.equal(A, A2) and torch.equal(G, G2)
+    A3, _ = linear_inputs(3, 16, 8, 12, "bf16", "llama_logu", seed=6)
+    assert not torch.equal(A, A3)
+
+
+def test_recipe_laws():
+    A, G = linear_inputs(4, 256, 64, 64, "f32", "llama_logu", seed=1)
+    s = sample_scales(4, "llama_logu", 1)
+    assert np.all((s >= 0.1) & (s <= 10))
+    g = G.double().numpy()
+    for i in range(4):
+        assert abs(g[i].std() / (0.01 * s[i]) - 1) < 0.02
+    assert abs(A.double().std().item() - 1) < 0.02
+    s1 = sample_scales(4, "unit_u0.1_3", 1)
+    assert np.all((s1 >= 0.1) & (s1 <= 3))
+
+
+def test_theta_init():
+    assert torch.count_nonzero(theta_init(4, 5, 1, zero=True)) == 0
+    t = theta_init(64, 64, 1)
+    assert abs(t.std().item() - 0.02) < 0.002
