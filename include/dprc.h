@@ -1,0 +1,167 @@
+/*
+ * dprc.h - C ABI of the DP-SGD-with-randomized-clipping hot path on MI355X.
+ *
+ * The library (libdprc.so, hand-written HIP kernels for gfx950) runs steps 3-5
+ * of the algorithm in the randomized-clipping summary, "技術的サマリー：ランダム化
+ * クリッピングを備えた LLM 向け効率的な DP-SGD", section アルゴリズム的フロー:
+ *   3. per-sample squared-norm estimation of each linear layer's gradient
+ *      (dp_norm_est: Hutch, Hutch++, and the exact ghost / FGC baselines),
+ *   4. per-sample clip factors c_i = min(1, C / sqrt(n_i)),
+ *   5. the clipped sum of per-sample gradients (dp_clip_aggregate), then
+ *      Gaussian noise and the SGD update (dp_noise_update),
+ * with the clip / noise / update formulas of the glossary page
+ * "DP-SGD（差分プライバシー確率的勾配降下法）とは？", section DP-SGDのアルゴリズム,
+ * steps 3-5.
+ *
+ * Notation (the pages'): B samples of T tokens; a linear layer of shape (p, d)
+ * has per-sample activations A_i (T x d) and output gradients G_i (T x p); its
+ * per-sample weight gradient is G_i^T A_i (p x d) and
+ * ||A_i^T G_i||_F^2 = tr(G_i^T A_i A_i^T G_i) (section 中核メカニズム).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are caller-owned DEVICE memory, dense row-major, and 16-byte
+ *    aligned (A, G, S, theta, workspace) or 4-byte aligned (n_sq, c_out,
+ *    status).  The library never allocates, frees, prints or synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    runs asynchronously.  A DP_OK return means "validated and enqueued".
+ *  - Arguments are validated on the host before anything is enqueued; on an
+ *    error nothing is enqueued and no output is touched.  DP_ERR_HIP means a
+ *    launch failed (hipGetLastError); outputs are then undefined.
+ *  - Calls are thread-safe (no mutable global state).  Concurrent calls that
+ *    share a workspace or an output buffer race, as any stream work would.
+ *  - Results are deterministic: no floating-point atomics; the same inputs and
+ *    seeds give the same bits on the same device.
+ */
+#ifndef DPRC_H
+#define DPRC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DPRC_ABI_VERSION 1
+
+typedef void *dp_stream_t; /* a hipStream_t */
+
+typedef enum {
+  DP_OK = 0,
+  DP_ERR_INVALID_ARG = 1, /* bad size, pointer, alignment or parameter */
+  DP_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. dtype/method combination) */
+  DP_ERR_WORKSPACE = 3,   /* ws_bytes smaller than the matching *_workspace() query */
+  DP_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} dp_status_t;
+
+typedef enum { DP_F32 = 0, DP_BF16 = 1 } dp_dtype_t; /* A and G share one dtype */
+
+typedef enum {
+  DP_NORM_HUTCH = 0,   /* Hutchinson, k Gaussian probes (section 中核メカニズム, item 1) */
+  DP_NORM_HUTCHPP = 1, /* Hutch++: QR head + Hutchinson tail (item 2) */
+  DP_NORM_GHOST = 2,   /* exact, T x T Gram products (ghost clipping, baseline) */
+  DP_NORM_FGC = 3      /* exact, materialised d x p per-sample gradient (baseline) */
+} dp_norm_method_t;
+
+/* dp_norm_est flags */
+#define DP_ACCUMULATE 1u   /* n_sq[i] += estimate (sum over layers) instead of n_sq[i] = estimate */
+#define DP_PROBE_SHARED 2u /* one probe matrix for the whole batch (the sample-0 stream) */
+
+/* dp_clip_aggregate status bits (ORed into *status) */
+#define DP_STATUS_NONFINITE_NORM 1u /* some n_sq[i] was NaN/Inf: its c_i was set to 0 */
+
+int dp_abi_version(void);
+const char *dp_status_string(dp_status_t s);
+
+/*
+ * Bytes of workspace dp_norm_est needs for these arguments (0 if none), or
+ * (size_t)-1 if the arguments are invalid.
+ */
+size_t dp_norm_est_workspace(int method, int dtype, int B, int T, int d, int p, int k);
+
+/*
+ * Per-sample squared gradient norm of one linear layer, n_i ~ ||A_i^T G_i||_F^2.
+ *
+ *  method  dp_norm_method_t.  HUTCH: n_i = ||A_i^T (G_i P_i)||_F^2 / k with
+ *          P_i (p x k) i.i.d. N(0,1) (section 中核メカニズム, item 1; the 1/k
+ *          makes it unbiased).  HUTCHPP: s = k/3 sketch columns, Q = orth(O S),
+ *          n_i = ||A^T G Q||^2 + ||A^T G (I - Q Q^T) W||^2 / r with r = k - 2s
+ *          (item 2).  GHOST: <A_i A_i^T, G_i G_i^T>_F.  FGC: ||A_i^T G_i||_F^2
+ *          with A_i^T G_i materialised in the workspace.
+ *  dtype   DP_F32 or DP_BF16 for A and G (fp32 accumulation either way).
+ *  B, T    batch size (>= 0) and tokens per sample (>= 0); B = 0 is a no-op,
+ *          T = 0 gives n_i = 0.
+ *  d, p    layer input / output widths (>= 1).
+ *  k       probes: HUTCH 1 <= k <= p; HUTCHPP 3 <= k <= p; ignored for exact methods.
+ *  A       [B][T][d] device, dtype.      G  [B][T][p] device, dtype.
+ *  seed    64-bit Philox4x32-10 key of the probe stream.
+ *  layer   layer index (counter word), so layers draw independent probes.
+ *          Probe entry (row r, column j) of sample i is lane r mod 4 of the
+ *          counter (r / 4, j, i, layer).
+ *  flags   DP_ACCUMULATE | DP_PROBE_SHARED.
+ *  n_sq    [B] fp32 device output (or accumulator with DP_ACCUMULATE).
+ *  ws      device workspace of ws_bytes >= dp_norm_est_workspace(...).
+ */
+dp_status_t dp_norm_est(int method, int dtype, int B, int T, int d, int p, int k,
+                        const void *A, const void *G, uint64_t seed, uint32_t layer,
+                        uint32_t flags, float *n_sq, void *ws, size_t ws_bytes,
+                        dp_stream_t stream);
+
+/* Bytes of workspace dp_clip_aggregate needs, or (size_t)-1 if invalid. */
+size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p);
+
+/*
+ * Clip factors and the clipped sum of per-sample gradients of one layer.
+ *
+ *  c_i = 1 if n_sq[i] <= C^2 (0 and negative values included), C / sqrt(n_sq[i])
+ *  otherwise, 0 if n_sq[i] is not finite (the sample is dropped and
+ *  DP_STATUS_NONFINITE_NORM is ORed into *status); then
+ *      S[o][q] = sum_i c_i sum_t G_i[t][o] A_i[t][q]          (S = sum_i c_i G_i^T A_i)
+ *  which is the second backward pass on the loss rescaled by c_i (glossary
+ *  step 3-4 without the noise; summary step 4-5).
+ *
+ *  A [B][T][d], G [B][T][p] device (dtype); n_sq [B] fp32 device (squared norms
+ *  summed over all layers); C > 0 finite.
+ *  c_out   [B] fp32 device output, or NULL.
+ *  status  one uint32 device word the kernel ORs flags into (the caller clears
+ *          it), or NULL.
+ *  S       [p][d] fp32 device output (the (p, d) weight layout), overwritten.
+ *  ws      device workspace of ws_bytes >= dp_clip_aggregate_workspace(...).
+ */
+dp_status_t dp_clip_aggregate(int dtype, int B, int T, int d, int p, const void *A,
+                              const void *G, const float *n_sq, float C, float *c_out,
+                              uint32_t *status, float *S, void *ws, size_t ws_bytes,
+                              dp_stream_t stream);
+
+/*
+ * Noise and SGD update of one (p, d) fp32 parameter block, in place:
+ *      theta[e] <- theta[e] - (eta / B) * (S[e] + sigma * C * xi[e]),  xi ~ N(0, 1)
+ * (glossary, section DP-SGDのアルゴリズム, steps 4-5 with |B| = B).
+ *  xi[e] for the flat index e = o * d + q is lane e mod 4 of the Philox4x32-10
+ *  counter (low word of e/4, high word of e/4, 0xFFFFFFFF, layer) under key
+ *  `seed`, turned into normals by Box-Muller on 24-bit uniforms.
+ *  d, p >= 1; B >= 1; sigma >= 0 and C > 0 finite; eta finite.
+ *  theta, S: [p][d] fp32 device (theta in/out, S read-only; they must not overlap).
+ */
+dp_status_t dp_noise_update(int d, int p, float *theta, const float *S, float sigma,
+                            float C, float eta, int B, uint64_t seed, uint32_t layer,
+                            dp_stream_t stream);
+
+/* ---- test hooks: expose the random streams for bit-level parity checks ---- */
+
+/* out[4 n] = Philox4x32-10 words of the n counters ctr[4 n] (device arrays). */
+dp_status_t dp_philox_u32(uint64_t seed, const uint32_t *ctr, uint32_t *out, size_t n,
+                          dp_stream_t stream);
+
+/* Pt[j][r] (fp32 device, [k][p]) = entry (r, j) of the probe P of `sample` in `layer`. */
+dp_status_t dp_probe_fill(uint64_t seed, uint32_t layer, uint32_t sample, int p, int k,
+                          float *Pt, dp_stream_t stream);
+
+/* xi[e - offset] for e in [offset, offset + n): the noise normals (fp32 device). */
+dp_status_t dp_noise_fill(uint64_t seed, uint32_t layer, uint64_t offset, size_t n,
+                          float *xi, dp_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DPRC_H */

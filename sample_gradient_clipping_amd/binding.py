@@ -1,0 +1,201 @@
+"""ctypes binding of libdprc.so: the C ABI of include/dprc.h with the same names.
+
+Argument marshalling only.  Tensors are torch tensors on the GPU (torch is
+used for device memory and streams); every step of the computation runs in
+the library's HIP kernels.  Work is enqueued on torch's current stream.  If
+the library is missing, loading raises: there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+DP_OK, DP_ERR_INVALID_ARG, DP_ERR_UNSUPPORTED, DP_ERR_WORKSPACE, DP_ERR_HIP = range(5)
+DP_F32, DP_BF16 = 0, 1
+DP_NORM_HUTCH, DP_NORM_HUTCHPP, DP_NORM_GHOST, DP_NORM_FGC = range(4)
+DP_ACCUMULATE = 1
+DP_PROBE_SHARED = 2
+DP_STATUS_NONFINITE_NORM = 1
+METHODS = {"hutch": DP_NORM_HUTCH, "hutchpp": DP_NORM_HUTCHPP, "ghost": DP_NORM_GHOST,
+           "fgc": DP_NORM_FGC}
+_SIZE_INVALID = ctypes.c_size_t(-1).value
+
+
+class DprcError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {dp_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib_path():
+    return os.environ.get("DPRC_LIB", os.path.join(_PKG, "libdprc.so"))
+
+
+def load_library():
+    """Load libdprc.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m sample_gradient_clipping_amd.build`")
+    L = ctypes.CDLL(path)
+    c_int, c_u32, c_u64, c_sz, c_f, c_p = (ctypes.c_int, ctypes.c_uint32, ctypes.c_uint64,
+                                           ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p)
+    L.dp_abi_version.restype = c_int
+    L.dp_status_string.argtypes = [c_int]
+    L.dp_status_string.restype = ctypes.c_char_p
+    L.dp_norm_est_workspace.argtypes = [c_int] * 7
+    L.dp_norm_est_workspace.restype = c_sz
+    L.dp_norm_est.argtypes = [c_int] * 7 + [c_p, c_p, c_u64, c_u32, c_u32, c_p, c_p, c_sz, c_p]
+    L.dp_norm_est.restype = c_int
+    L.dp_clip_aggregate_workspace.argtypes = [c_int] * 5
+    L.dp_clip_aggregate_workspace.restype = c_sz
+    L.dp_clip_aggregate.argtypes = [c_int] * 5 + [c_p, c_p, c_p, c_f, c_p, c_p, c_p, c_p, c_sz, c_p]
+    L.dp_clip_aggregate.restype = c_int
+    L.dp_noise_update.argtypes = [c_int, c_int, c_p, c_p, c_f, c_f, c_f, c_int, c_u64, c_u32, c_p]
+    L.dp_noise_update.restype = c_int
+    L.dp_philox_u32.argtypes = [c_u64, c_p, c_p, c_sz, c_p]
+    L.dp_philox_u32.restype = c_int
+    L.dp_probe_fill.argtypes = [c_u64, c_u32, c_u32, c_int, c_int, c_p, c_p]
+    L.dp_probe_fill.restype = c_int
+    L.dp_noise_fill.argtypes = [c_u64, c_u32, c_u64, c_sz, c_p, c_p]
+    L.dp_noise_fill.restype = c_int
+    _lib = L
+    return L
+
+
+def dp_abi_version():
+    return load_library().dp_abi_version()
+
+
+def dp_status_string(status):
+    return load_library().dp_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != DP_OK:
+        raise DprcError(status, where)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return DP_F32
+    if t.dtype == torch.bfloat16:
+        return DP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _method_code(method):
+    return METHODS[method] if isinstance(method, str) else int(method)
+
+
+def _workspace(nbytes, device, ws):
+    if nbytes == _SIZE_INVALID:
+        return None
+    if ws is not None:
+        return ws
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def dp_norm_est_workspace(method, dtype, B, T, d, p, k):
+    """Workspace bytes, or None for invalid arguments."""
+    code = dtype if isinstance(dtype, int) else {"f32": DP_F32, "bf16": DP_BF16}[dtype]
+    n = load_library().dp_norm_est_workspace(_method_code(method), code, B, T, d, p, k)
+    return None if n == _SIZE_INVALID else n
+
+
+def dp_norm_est(method, A, G, k, seed, layer, n_sq, flags=0, ws=None, stream=None):
+    """n_sq[i] (=, or += with DP_ACCUMULATE) squared-norm estimate of sample i.
+
+    A [B][T][d], G [B][T][p]: contiguous device tensors, fp32 or bf16.
+    n_sq: fp32 [B] device tensor.  ``ws``: optional uint8 device workspace.
+    """
+    L = load_library()
+    B, T, d = A.shape
+    p = G.shape[2]
+    dt = _dtype_code(A)
+    m = _method_code(method)
+    k = int(k or 0)
+    nbytes = L.dp_norm_est_workspace(m, dt, B, T, d, p, k)
+    ws_t = _workspace(nbytes, A.device, ws)
+    st = L.dp_norm_est(m, dt, B, T, d, p, k, _ptr(A), _ptr(G), int(seed) & (2**64 - 1),
+                       int(layer), int(flags), _ptr(n_sq), _ptr(ws_t),
+                       0 if ws_t is None else ws_t.numel(), _stream(stream))
+    _check(st, "dp_norm_est")
+    return n_sq
+
+
+def dp_clip_aggregate_workspace(dtype, B, T, d, p):
+    code = dtype if isinstance(dtype, int) else {"f32": DP_F32, "bf16": DP_BF16}[dtype]
+    n = load_library().dp_clip_aggregate_workspace(code, B, T, d, p)
+    return None if n == _SIZE_INVALID else n
+
+
+def dp_clip_aggregate(A, G, n_sq, C, S, c_out=None, status=None, ws=None, stream=None):
+    """Clip factors from n_sq and S[o][q] = sum_i c_i sum_t G_i[t][o] A_i[t][q]."""
+    L = load_library()
+    B, T, d = A.shape
+    p = G.shape[2]
+    dt = _dtype_code(A)
+    nbytes = L.dp_clip_aggregate_workspace(dt, B, T, d, p)
+    ws_t = _workspace(nbytes, A.device, ws)
+    st = L.dp_clip_aggregate(dt, B, T, d, p, _ptr(A), _ptr(G), _ptr(n_sq), float(C), _ptr(c_out),
+                             _ptr(status), _ptr(S), _ptr(ws_t),
+                             0 if ws_t is None else ws_t.numel(), _stream(stream))
+    _check(st, "dp_clip_aggregate")
+    return S
+
+
+def dp_noise_update(theta, S, sigma, C, eta, B, seed, layer, stream=None):
+    """theta <- theta - (eta / B) (S + sigma C xi) in place; theta, S fp32 [p][d]."""
+    p, d = theta.shape
+    st = load_library().dp_noise_update(d, p, _ptr(theta), _ptr(S), float(sigma), float(C),
+                                        float(eta), int(B), int(seed) & (2**64 - 1), int(layer),
+                                        _stream(stream))
+    _check(st, "dp_noise_update")
+    return theta
+
+
+def dp_philox_u32(seed, ctr, out, stream=None):
+    """out[n][4] = Philox4x32-10 words of counters ctr[n][4] (uint32-valued int32 tensors)."""
+    n = ctr.numel() // 4
+    st = load_library().dp_philox_u32(int(seed) & (2**64 - 1), _ptr(ctr), _ptr(out), n,
+                                      _stream(stream))
+    _check(st, "dp_philox_u32")
+    return out
+
+
+def dp_probe_fill(seed, layer, sample, p, k, Pt, stream=None):
+    """Pt [k][p] fp32 = probe entries P[r][j] of (seed, layer, sample)."""
+    st = load_library().dp_probe_fill(int(seed) & (2**64 - 1), int(layer), int(sample), int(p),
+                                      int(k), _ptr(Pt), _stream(stream))
+    _check(st, "dp_probe_fill")
+    return Pt
+
+
+def dp_noise_fill(seed, layer, offset, xi, stream=None):
+    """xi[n] fp32 = noise normals of flat indices offset .. offset + n - 1."""
+    st = load_library().dp_noise_fill(int(seed) & (2**64 - 1), int(layer), int(offset),
+                                      xi.numel(), _ptr(xi), _stream(stream))
+    _check(st, "dp_noise_fill")
+    return xi

@@ -1,0 +1,446 @@
+// C ABI of libdprc (declared in include/dprc.h): host-side validation,
+// workspace layout and launch sequencing.  No allocation, no synchronisation,
+// no mutable global state; everything is enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "dprc.h"
+#include "internal.h"
+
+using namespace dprc;
+
+static_assert(DPRC_STATUS_NONFINITE == DP_STATUS_NONFINITE_NORM, "status bit mismatch");
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kInvalid = static_cast<size_t>(-1);
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carve-out of one workspace.
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int frob_chunks(int64_t elems) {
+  int64_t c = elems / 65536;
+  if (c < 1) c = 1;
+  if (c > 1024) c = 1024;
+  return static_cast<int>(c);
+}
+
+// ---- dp_norm_est planning ----
+struct NormPlan {
+  bool mfma = false;
+  int s = 0, r = 0, k3 = 0;  // Hutch++ split
+  int nsplit_d = 1, nsplit_p = 1, nchunk = 1, nparts = 0;
+  // offsets (bytes) into the workspace; unused ones stay 0
+  size_t pf = 0, pb = 0, y = 0, yb = 0, z = 0, zp = 0, z1b = 0, v = 0, xp = 0, x = 0, p3 = 0,
+         p3b = 0, m = 0, part = 0;
+  size_t total = 0;
+};
+
+bool valid_method(int m) { return m >= DP_NORM_HUTCH && m <= DP_NORM_FGC; }
+bool valid_dtype(int t) { return t == DP_F32 || t == DP_BF16; }
+
+bool norm_args_ok(int method, int dtype, int B, int T, int d, int p, int k) {
+  if (!valid_method(method) || !valid_dtype(dtype)) return false;
+  if (B < 0 || T < 0 || d < 1 || p < 1) return false;
+  if (static_cast<int64_t>(T) * (d > p ? d : p) > (static_cast<int64_t>(1) << 40)) return false;
+  if (method == DP_NORM_HUTCH && (k < 1 || k > p)) return false;
+  if (method == DP_NORM_HUTCHPP && (k < 3 || k > p || k / 3 > 32)) return false;
+  return true;
+}
+
+NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
+  NormPlan P;
+  Carver cv;
+  const size_t Bz = static_cast<size_t>(B);
+  const size_t f4 = 4, h2 = 2;
+  const bool bf = dtype == DP_BF16;
+  if (method == DP_NORM_HUTCH) {
+    P.mfma = bf && k <= kMfmaProbeCols && mfma_sketch_ok(T, p) && mfma_project_ok(T, d);
+    if (P.mfma) {
+      P.nsplit_d = mfma_project_splits(B, T, d);
+      P.pb = cv.take(Bz * kMfmaProbeCols * p * h2);
+      P.yb = cv.take(Bz * kMfmaProbeCols * T * h2);
+      P.zp = cv.take(Bz * P.nsplit_d * kMfmaProbeCols * d * f4);
+      P.nchunk = frob_chunks(static_cast<int64_t>(kMfmaProbeCols) * d);
+    } else {
+      P.pf = cv.take(Bz * k * p * f4);
+      P.y = cv.take(Bz * k * T * f4);
+      P.z = cv.take(Bz * k * d * f4);
+      P.nchunk = frob_chunks(static_cast<int64_t>(k) * d);
+    }
+  } else if (method == DP_NORM_HUTCHPP) {
+    P.s = k / 3;
+    P.r = k - 2 * P.s;
+    P.k3 = P.s + P.r;
+    P.mfma = bf && P.k3 <= kMfmaProbeCols && mfma_sketch_ok(T, p) && mfma_sketch_ok(T, d) &&
+             mfma_project_ok(T, d) && mfma_project_ok(T, p);
+    P.pf = cv.take(Bz * P.k3 * p * f4);
+    P.p3 = cv.take(Bz * P.k3 * p * f4);
+    if (P.mfma) {
+      P.nsplit_d = mfma_project_splits(B, T, d);
+      P.nsplit_p = mfma_project_splits(B, T, p);
+      P.pb = cv.take(Bz * kMfmaProbeCols * p * h2);
+      P.yb = cv.take(Bz * kMfmaProbeCols * T * h2);
+      P.zp = cv.take(Bz * P.nsplit_d * kMfmaProbeCols * d * f4);
+      P.z1b = cv.take(Bz * kMfmaProbeCols * d * h2);
+      P.xp = cv.take(Bz * P.nsplit_p * kMfmaProbeCols * p * f4);
+      P.x = cv.take(Bz * kMfmaProbeCols * p * f4);
+      P.p3b = cv.take(Bz * kMfmaProbeCols * p * h2);
+      P.nchunk = frob_chunks(static_cast<int64_t>(kMfmaProbeCols) * d);
+    } else {
+      P.y = cv.take(Bz * P.k3 * (T > 0 ? T : 1) * f4);
+      P.z = cv.take(Bz * P.k3 * d * f4);
+      P.v = cv.take(Bz * P.s * (T > 0 ? T : 1) * f4);
+      P.x = cv.take(Bz * P.s * p * f4);
+      P.nchunk = frob_chunks(static_cast<int64_t>(P.k3) * d);
+    }
+  } else if (method == DP_NORM_GHOST) {
+    P.nparts = ghost_generic_nparts(T);
+    P.nchunk = P.nparts;
+  } else {  // FGC
+    P.mfma = bf && mfma_gemm_ok(T, d, p);
+    P.m = cv.take(Bz * p * d * f4);
+    P.nchunk = frob_chunks(static_cast<int64_t>(p) * d);
+  }
+  const int nparts = method == DP_NORM_GHOST ? P.nparts : P.nchunk;
+  P.part = cv.take(Bz * (nparts > 0 ? nparts : 1) * sizeof(double));
+  P.total = cv.off;
+  return P;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + off);
+}
+
+#define DP_TRY(expr)                          \
+  do {                                        \
+    hipError_t e_ = (expr);                   \
+    if (e_ != hipSuccess) return DP_ERR_HIP;  \
+  } while (0)
+
+template <typename TIn>
+dp_status_t run_norm_generic_hutch(const NormPlan& P, int B, int T, int d, int p, int k,
+                                   const TIn* A, const TIn* G, uint64_t seed, uint32_t layer,
+                                   bool shared, bool accum, float* n_sq, void* ws, hipStream_t s) {
+  float* Pf = at<float>(ws, P.pf);
+  float* Y = at<float>(ws, P.y);
+  float* Z = at<float>(ws, P.z);
+  double* part = at<double>(ws, P.part);
+  const int nS = shared ? 1 : B;
+  const int64_t pbs = shared ? 0 : static_cast<int64_t>(k) * p;
+  DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, k, k, Pf, s));
+  DP_TRY(launch_sketch_generic<TIn>(G, B, T, p, Pf, pbs, k, Y, s));
+  DP_TRY(launch_project_generic<TIn>(A, B, T, d, Y, k, Z, s));
+  DP_TRY(launch_frob_partial(Z, B, 1, k, d, k, 1.0f / k, 0, 0.f, part, P.nchunk, s));
+  DP_TRY(launch_sum_parts(part, B, P.nchunk, n_sq, accum ? 1 : 0, s));
+  return DP_OK;
+}
+
+dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, int k,
+                                const bf16_t* A, const bf16_t* G, uint64_t seed, uint32_t layer,
+                                bool shared, bool accum, float* n_sq, void* ws, hipStream_t s) {
+  bf16_t* Pb = at<bf16_t>(ws, P.pb);
+  bf16_t* Yb = at<bf16_t>(ws, P.yb);
+  float* Zp = at<float>(ws, P.zp);
+  double* part = at<double>(ws, P.part);
+  const int nS = shared ? 1 : B;
+  const int64_t pbs = shared ? 0 : static_cast<int64_t>(kMfmaProbeCols) * p;
+  DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, k, kMfmaProbeCols, Pb, s));
+  DP_TRY(launch_sketch_mfma(G, B, T, p, Pb, pbs, Yb, s));
+  DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
+  DP_TRY(launch_frob_partial(Zp, B, P.nsplit_d, kMfmaProbeCols, d, k, 1.0f / k, 0, 0.f, part,
+                             P.nchunk, s));
+  DP_TRY(launch_sum_parts(part, B, P.nchunk, n_sq, accum ? 1 : 0, s));
+  return DP_OK;
+}
+
+template <typename TIn>
+dp_status_t run_norm_generic_hpp(const NormPlan& P, int B, int T, int d, int p, const TIn* A,
+                                 const TIn* G, uint64_t seed, uint32_t layer, bool shared,
+                                 bool accum, float* n_sq, void* ws, hipStream_t s) {
+  const int S_ = P.s, R_ = P.r, K3 = P.k3;
+  float* Pf = at<float>(ws, P.pf);
+  float* P3 = at<float>(ws, P.p3);
+  float* Y = at<float>(ws, P.y);
+  float* Z = at<float>(ws, P.z);
+  float* V = at<float>(ws, P.v);
+  float* X = at<float>(ws, P.x);
+  double* part = at<double>(ws, P.part);
+  const int nS = shared ? 1 : B;
+  const int64_t pbs = shared ? 0 : static_cast<int64_t>(K3) * p;
+  DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, K3, K3, Pf, s));
+  // pass 1: Z1 = A^T (G S)
+  DP_TRY(launch_sketch_generic<TIn>(G, B, T, p, Pf, pbs, S_, Y, s));
+  DP_TRY(launch_project_generic<TIn>(A, B, T, d, Y, S_, Z, s));
+  // pass 2: X = G^T (A Z1) = O S
+  DP_TRY(launch_sketch_generic<TIn>(A, B, T, d, Z, static_cast<int64_t>(S_) * d, S_, V, s));
+  DP_TRY(launch_project_generic<TIn>(G, B, T, p, V, S_, X, s));
+  // Q = orth(X), W' = (I - Q Q^T) W
+  DP_TRY(launch_hpp_orth(X, S_, Pf, pbs, K3, B, p, S_, R_, P3, s));
+  // pass 3: head + tail / r
+  DP_TRY(launch_sketch_generic<TIn>(G, B, T, p, P3, static_cast<int64_t>(K3) * p, K3, Y, s));
+  DP_TRY(launch_project_generic<TIn>(A, B, T, d, Y, K3, Z, s));
+  DP_TRY(launch_frob_partial(Z, B, 1, K3, d, S_, 1.0f, R_, 1.0f / R_, part, P.nchunk, s));
+  DP_TRY(launch_sum_parts(part, B, P.nchunk, n_sq, accum ? 1 : 0, s));
+  return DP_OK;
+}
+
+dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, const bf16_t* A,
+                              const bf16_t* G, uint64_t seed, uint32_t layer, bool shared,
+                              bool accum, float* n_sq, void* ws, hipStream_t s) {
+  const int S_ = P.s, R_ = P.r, K3 = P.k3;
+  float* Pf = at<float>(ws, P.pf);
+  float* P3 = at<float>(ws, P.p3);
+  bf16_t* Pb = at<bf16_t>(ws, P.pb);
+  bf16_t* Yb = at<bf16_t>(ws, P.yb);
+  float* Zp = at<float>(ws, P.zp);
+  bf16_t* Z1b = at<bf16_t>(ws, P.z1b);
+  float* Xp = at<float>(ws, P.xp);
+  float* X = at<float>(ws, P.x);
+  bf16_t* P3b = at<bf16_t>(ws, P.p3b);
+  double* part = at<double>(ws, P.part);
+  const int nS = shared ? 1 : B;
+  const int64_t pfs = shared ? 0 : static_cast<int64_t>(K3) * p;
+  const int64_t pbs = shared ? 0 : static_cast<int64_t>(kMfmaProbeCols) * p;
+  const int64_t pad_d = static_cast<int64_t>(kMfmaProbeCols) * d;
+  const int64_t pad_p = static_cast<int64_t>(kMfmaProbeCols) * p;
+  DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, K3, K3, Pf, s));
+  DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, S_, kMfmaProbeCols, Pb, s));
+  // pass 1: Z1 = A^T (G S)
+  DP_TRY(launch_sketch_mfma(G, B, T, p, Pb, pbs, Yb, s));
+  DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
+  DP_TRY(launch_sum_splits(Zp, B, P.nsplit_d, kMfmaProbeCols, d, nullptr, Z1b, s));
+  // pass 2: X = G^T (A Z1)
+  DP_TRY(launch_sketch_mfma(A, B, T, d, Z1b, pad_d, Yb, s));
+  DP_TRY(launch_project_mfma(G, B, T, p, Yb, P.nsplit_p, Xp, s));
+  DP_TRY(launch_sum_splits(Xp, B, P.nsplit_p, kMfmaProbeCols, p, X, nullptr, s));
+  // Q = orth(X), W' = (I - Q Q^T) W
+  DP_TRY(launch_hpp_orth(X, kMfmaProbeCols, Pf, pfs, K3, B, p, S_, R_, P3, s));
+  DP_TRY(launch_to_bf16_pad(P3, B, K3, kMfmaProbeCols, p, P3b, s));
+  // pass 3
+  DP_TRY(launch_sketch_mfma(G, B, T, p, P3b, pad_p, Yb, s));
+  DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
+  DP_TRY(launch_frob_partial(Zp, B, P.nsplit_d, kMfmaProbeCols, d, S_, 1.0f, R_, 1.0f / R_, part,
+                             P.nchunk, s));
+  DP_TRY(launch_sum_parts(part, B, P.nchunk, n_sq, accum ? 1 : 0, s));
+  return DP_OK;
+}
+
+template <typename TIn>
+dp_status_t run_norm_exact(int method, const NormPlan& P, int B, int T, int d, int p,
+                           const TIn* A, const TIn* G, bool accum, float* n_sq, void* ws,
+                           hipStream_t s) {
+  double* part = at<double>(ws, P.part);
+  if (method == DP_NORM_GHOST) {
+    int np = 0;
+    DP_TRY(launch_ghost_generic<TIn>(A, G, B, T, d, p, part, &np, s));
+    DP_TRY(launch_sum_parts(part, B, np, n_sq, accum ? 1 : 0, s));
+    return DP_OK;
+  }
+  float* M = at<float>(ws, P.m);
+  if constexpr (sizeof(TIn) == 2) {
+    if (P.mfma) {
+      DP_TRY(launch_fgc_mfma(A, G, B, T, d, p, M, s));
+    } else {
+      DP_TRY(launch_fgc_generic<TIn>(A, G, B, T, d, p, M, s));
+    }
+  } else {
+    DP_TRY(launch_fgc_generic<TIn>(A, G, B, T, d, p, M, s));
+  }
+  DP_TRY(launch_frob_partial(M, B, 1, p, d, p, 1.0f, 0, 0.f, part, P.nchunk, s));
+  DP_TRY(launch_sum_parts(part, B, P.nchunk, n_sq, accum ? 1 : 0, s));
+  return DP_OK;
+}
+
+// ---- dp_clip_aggregate planning ----
+struct AggPlan {
+  bool mfma = false;
+  int nsplit = 1;
+  size_t c = 0, order = 0, count = 0, part = 0, total = 0;
+};
+
+AggPlan plan_agg(int dtype, int B, int T, int d, int p) {
+  AggPlan P;
+  Carver cv;
+  const size_t Bz = static_cast<size_t>(B > 0 ? B : 1);
+  P.c = cv.take(Bz * 4);
+  P.order = cv.take(Bz * 4);
+  P.count = cv.take(4);
+  P.mfma = dtype == DP_BF16 && B > 0 && mfma_gemm_ok(T, d, p);
+  if (P.mfma) {
+    P.nsplit = mfma_gemm_splits(B, T, d, p);
+    if (P.nsplit > 1) P.part = cv.take(static_cast<size_t>(P.nsplit) * p * d * 4);
+  }
+  P.total = cv.off;
+  return P;
+}
+
+bool agg_args_ok(int dtype, int B, int T, int d, int p) {
+  return valid_dtype(dtype) && B >= 0 && T >= 0 && d >= 1 && p >= 1 &&
+         static_cast<int64_t>(T) * (d > p ? d : p) <= (static_cast<int64_t>(1) << 40);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dp_abi_version(void) { return DPRC_ABI_VERSION; }
+
+const char* dp_status_string(dp_status_t s) {
+  switch (s) {
+    case DP_OK: return "DP_OK";
+    case DP_ERR_INVALID_ARG: return "DP_ERR_INVALID_ARG: invalid size, pointer, alignment or parameter";
+    case DP_ERR_UNSUPPORTED: return "DP_ERR_UNSUPPORTED: combination not implemented";
+    case DP_ERR_WORKSPACE: return "DP_ERR_WORKSPACE: workspace smaller than the query";
+    case DP_ERR_HIP: return "DP_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown dp_status_t";
+}
+
+size_t dp_norm_est_workspace(int method, int dtype, int B, int T, int d, int p, int k) {
+  if (!norm_args_ok(method, dtype, B, T, d, p, k)) return kInvalid;
+  return plan_norm(method, dtype, B, T, d, p, k).total;
+}
+
+dp_status_t dp_norm_est(int method, int dtype, int B, int T, int d, int p, int k, const void* A,
+                        const void* G, uint64_t seed, uint32_t layer, uint32_t flags, float* n_sq,
+                        void* ws, size_t ws_bytes, dp_stream_t stream) {
+  if (!norm_args_ok(method, dtype, B, T, d, p, k)) return DP_ERR_INVALID_ARG;
+  if ((flags & ~(DP_ACCUMULATE | DP_PROBE_SHARED)) != 0) return DP_ERR_INVALID_ARG;
+  if (B == 0) return DP_OK;
+  if (n_sq == nullptr || !aligned(n_sq, 4)) return DP_ERR_INVALID_ARG;
+  if (T > 0 && (A == nullptr || G == nullptr || !aligned(A, 16) || !aligned(G, 16)))
+    return DP_ERR_INVALID_ARG;
+  const NormPlan P = plan_norm(method, dtype, B, T, d, p, k);
+  if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
+  if (P.total > 0 && (ws == nullptr || !aligned(ws, 16))) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool accum = (flags & DP_ACCUMULATE) != 0;
+  const bool shared = (flags & DP_PROBE_SHARED) != 0;
+  const bool bf = dtype == DP_BF16;
+  const bf16_t* Ab = static_cast<const bf16_t*>(A);
+  const bf16_t* Gb = static_cast<const bf16_t*>(G);
+  const float* Af = static_cast<const float*>(A);
+  const float* Gf = static_cast<const float*>(G);
+  switch (method) {
+    case DP_NORM_HUTCH:
+      if (P.mfma) return run_norm_mfma_hutch(P, B, T, d, p, k, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s);
+      return bf ? run_norm_generic_hutch<bf16_t>(P, B, T, d, p, k, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s)
+                : run_norm_generic_hutch<float>(P, B, T, d, p, k, Af, Gf, seed, layer, shared, accum, n_sq, ws, s);
+    case DP_NORM_HUTCHPP:
+      if (P.mfma) return run_norm_mfma_hpp(P, B, T, d, p, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s);
+      return bf ? run_norm_generic_hpp<bf16_t>(P, B, T, d, p, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s)
+                : run_norm_generic_hpp<float>(P, B, T, d, p, Af, Gf, seed, layer, shared, accum, n_sq, ws, s);
+    default:
+      return bf ? run_norm_exact<bf16_t>(method, P, B, T, d, p, Ab, Gb, accum, n_sq, ws, s)
+                : run_norm_exact<float>(method, P, B, T, d, p, Af, Gf, accum, n_sq, ws, s);
+  }
+}
+
+size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p) {
+  if (!agg_args_ok(dtype, B, T, d, p)) return kInvalid;
+  return plan_agg(dtype, B, T, d, p).total;
+}
+
+dp_status_t dp_clip_aggregate(int dtype, int B, int T, int d, int p, const void* A, const void* G,
+                              const float* n_sq, float C, float* c_out, uint32_t* status, float* S,
+                              void* ws, size_t ws_bytes, dp_stream_t stream) {
+  if (!agg_args_ok(dtype, B, T, d, p)) return DP_ERR_INVALID_ARG;
+  if (!(C > 0.f) || !std::isfinite(C)) return DP_ERR_INVALID_ARG;
+  if (S == nullptr || !aligned(S, 16)) return DP_ERR_INVALID_ARG;
+  if (B > 0 && (n_sq == nullptr || !aligned(n_sq, 4))) return DP_ERR_INVALID_ARG;
+  if (B > 0 && T > 0 && (A == nullptr || G == nullptr || !aligned(A, 16) || !aligned(G, 16)))
+    return DP_ERR_INVALID_ARG;
+  if ((c_out && !aligned(c_out, 4)) || (status && !aligned(status, 4))) return DP_ERR_INVALID_ARG;
+  const AggPlan P = plan_agg(dtype, B, T, d, p);
+  if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* c = at<float>(ws, P.c);
+  int* order = at<int>(ws, P.order);
+  int* count = at<int>(ws, P.count);
+  DP_TRY(launch_clip(n_sq, B, C, c, c_out, status, order, count, s));
+  if (P.mfma) {
+    const bf16_t* Ab = static_cast<const bf16_t*>(A);
+    const bf16_t* Gb = static_cast<const bf16_t*>(G);
+    if (P.nsplit == 1) {
+      DP_TRY(launch_aggregate_mfma(Ab, Gb, B, T, d, p, c, order, count, 1, S, s));
+    } else {
+      float* part = at<float>(ws, P.part);
+      DP_TRY(launch_aggregate_mfma(Ab, Gb, B, T, d, p, c, order, count, P.nsplit, part, s));
+      DP_TRY(launch_reduce_splits(part, P.nsplit, static_cast<int64_t>(p) * d, S, s));
+    }
+    return DP_OK;
+  }
+  if (dtype == DP_BF16) {
+    DP_TRY(launch_aggregate_generic<bf16_t>(static_cast<const bf16_t*>(A),
+                                            static_cast<const bf16_t*>(G), B, T, d, p, c, S, s));
+  } else {
+    DP_TRY(launch_aggregate_generic<float>(static_cast<const float*>(A),
+                                           static_cast<const float*>(G), B, T, d, p, c, S, s));
+  }
+  return DP_OK;
+}
+
+dp_status_t dp_noise_update(int d, int p, float* theta, const float* S, float sigma, float C,
+                            float eta, int B, uint64_t seed, uint32_t layer, dp_stream_t stream) {
+  if (d < 1 || p < 1 || B < 1) return DP_ERR_INVALID_ARG;
+  if (!(sigma >= 0.f) || !std::isfinite(sigma) || !(C > 0.f) || !std::isfinite(C) ||
+      !std::isfinite(eta))
+    return DP_ERR_INVALID_ARG;
+  if (theta == nullptr || S == nullptr || !aligned(theta, 16) || !aligned(S, 16))
+    return DP_ERR_INVALID_ARG;
+  const int64_t n = static_cast<int64_t>(p) * d;
+  const uintptr_t t0 = reinterpret_cast<uintptr_t>(theta), s0 = reinterpret_cast<uintptr_t>(S);
+  const uintptr_t bytes = static_cast<uintptr_t>(n) * 4;
+  if (t0 < s0 + bytes && s0 < t0 + bytes) return DP_ERR_INVALID_ARG;  // overlap
+  const float sigmaC = sigma * C;
+  const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
+  DP_TRY(launch_noise_update(theta, S, n, sigmaC, eta_over_B, seed, layer,
+                             static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
+dp_status_t dp_philox_u32(uint64_t seed, const uint32_t* ctr, uint32_t* out, size_t n,
+                          dp_stream_t stream) {
+  if (n == 0) return DP_OK;
+  if (ctr == nullptr || out == nullptr || !aligned(ctr, 4) || !aligned(out, 4))
+    return DP_ERR_INVALID_ARG;
+  DP_TRY(launch_philox_u32(seed, ctr, out, n, static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
+dp_status_t dp_probe_fill(uint64_t seed, uint32_t layer, uint32_t sample, int p, int k, float* Pt,
+                          dp_stream_t stream) {
+  if (p < 1 || k < 1 || Pt == nullptr || !aligned(Pt, 4)) return DP_ERR_INVALID_ARG;
+  DP_TRY(launch_probe_fill_f32(seed, layer, sample, 1, p, k, k, Pt,
+                               static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
+dp_status_t dp_noise_fill(uint64_t seed, uint32_t layer, uint64_t offset, size_t n, float* xi,
+                          dp_stream_t stream) {
+  if (n == 0) return DP_OK;
+  if (xi == nullptr || !aligned(xi, 4)) return DP_ERR_INVALID_ARG;
+  if (offset + n < offset) return DP_ERR_INVALID_ARG;
+  DP_TRY(launch_noise_fill(seed, layer, offset, n, xi, static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
+}  // extern "C"

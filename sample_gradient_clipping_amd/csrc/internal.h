@@ -1,0 +1,97 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Every launcher enqueues on `s` and returns hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dprc {
+
+typedef uint16_t bf16_t;
+
+// Status bit ORed by the clip kernel when some squared norm is not finite.
+#define DPRC_STATUS_NONFINITE 1u
+
+// ---- random streams (rng_kernels.hip) ----
+hipError_t launch_philox_u32(uint64_t seed, const uint32_t* ctr, uint32_t* out, size_t n,
+                             hipStream_t s);
+// Probe P^T of `nsamp` samples (sample index = sample0 + i): out[i][j][r] for
+// j < kpad, r < p; columns j >= kfill are zero.
+hipError_t launch_probe_fill_f32(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
+                                 int p, int kfill, int kpad, float* out, hipStream_t s);
+hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
+                                  int p, int kfill, int kpad, bf16_t* out, hipStream_t s);
+hipError_t launch_noise_fill(uint64_t seed, uint32_t layer, uint64_t offset, size_t n, float* xi,
+                             hipStream_t s);
+hipError_t launch_noise_update(float* theta, const float* S, int64_t n, float sigmaC,
+                               float eta_over_B, uint64_t seed, uint32_t layer, hipStream_t s);
+
+// ---- generic VALU kernels, any shape, fp32 math (generic_kernels.hip) ----
+// Y[b][j][t] = sum_r X[b][t][r] * P[b or 0][j][r]; P fp32 [.][kp][W].
+template <typename TIn>
+hipError_t launch_sketch_generic(const TIn* X, int B, int T, int W, const float* P,
+                                 int64_t p_bstride, int kp, float* Y, hipStream_t s);
+// Z[b][j][q] = sum_t X[b][t][q] * Y[b][j][t].
+template <typename TIn>
+hipError_t launch_project_generic(const TIn* X, int B, int T, int W, const float* Y, int kp,
+                                  float* Z, hipStream_t s);
+// part[b][chunk] = sum over (j, q) of w_j (sum_split Z[b][split][j][q])^2, with
+// w_j = w0 for j < n0, w1 for n0 <= j < n0 + n1, 0 otherwise.
+hipError_t launch_frob_partial(const float* Z, int B, int nsplit, int kp, int W, int n0, float w0,
+                               int n1, float w1, double* part, int nchunk, hipStream_t s);
+// n[b] = (accumulate ? n[b] : 0) + sum_c part[b][c].
+hipError_t launch_sum_parts(const double* part, int B, int nparts, float* n, int accumulate,
+                            hipStream_t s);
+// Z[b][j][q] = sum_split Zp[b][split][j][q] (fp32) and optionally a bf16 copy.
+hipError_t launch_sum_splits(const float* Zp, int B, int nsplit, int rows, int W, float* Z,
+                             bf16_t* Zb, hipStream_t s);
+template <typename TIn>
+hipError_t launch_ghost_generic(const TIn* A, const TIn* G, int B, int T, int d, int p,
+                                double* part, int* nparts_out, hipStream_t s);
+int ghost_generic_nparts(int T);
+template <typename TIn>
+hipError_t launch_fgc_generic(const TIn* A, const TIn* G, int B, int T, int d, int p, float* M,
+                              hipStream_t s);
+template <typename TIn>
+hipError_t launch_aggregate_generic(const TIn* A, const TIn* G, int B, int T, int d, int p,
+                                    const float* c, float* S, hipStream_t s);
+// c[i], optional c_out, status bit, and the active samples in ascending c order.
+hipError_t launch_clip(const float* n, int B, float C, float* c, float* c_out, uint32_t* status,
+                       int* order, int* count, hipStream_t s);
+// out[e] = sum_{sp < nsplit} part[sp][e].
+hipError_t launch_reduce_splits(const float* part, int nsplit, int64_t n, float* out, hipStream_t s);
+// Hutch++ probe for the last pass: rows 0..s-1 = orthonormal basis of the s
+// rows of X (CGS2), rows s..s+r-1 = W - Q Q^T W.  X [B][xrows][p] (rows 0..s-1
+// used), W rows s..s+r-1 of Pw [.][wrows][p].  out fp32 [B][s+r][p].
+hipError_t launch_hpp_orth(const float* X, int xrows, const float* Pw, int64_t pw_bstride,
+                           int wrows, int B, int p, int s_cols, int r_cols, float* out,
+                           hipStream_t s);
+// out[b][j][x] = bf16(in[b][j][x]) for j < rows_in, 0 for rows_in <= j < rows_out.
+hipError_t launch_to_bf16_pad(const float* in, int B, int rows_in, int rows_out, int W,
+                              bf16_t* out, hipStream_t s);
+
+// ---- MFMA kernels for bf16 inputs (mfma_hutch.hip, mfma_gemm.hip) ----
+constexpr int kMfmaProbeCols = 32;  // padded probe width of the MFMA Hutch path
+bool mfma_sketch_ok(int T, int W);
+bool mfma_project_ok(int T, int W);
+int mfma_project_splits(int B, int T, int W);
+// Y[b][j][t] (bf16, [B][32][T]) = sum_r X[b][t][r] P[b or 0][j][r], P bf16 [.][32][W].
+hipError_t launch_sketch_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* P,
+                              int64_t p_bstride, bf16_t* Y, hipStream_t s);
+// Zp[b][split][j][q] (fp32, j < 32) = sum_{t in split} X[b][t][q] Y[b][j][t].
+hipError_t launch_project_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* Y, int nsplit,
+                               float* Zp, hipStream_t s);
+
+bool mfma_gemm_ok(int T, int d, int p);
+int mfma_gemm_splits(int B, int T, int d, int p);
+// Clipped sum over the active samples order[0..*count) (ascending c):
+// part[split][o][q] = sum over the split's tokens of c G[t][o] A[t][q].
+hipError_t launch_aggregate_mfma(const bf16_t* A, const bf16_t* G, int B, int T, int d, int p,
+                                 const float* c, const int* order, const int* count, int nsplit,
+                                 float* part, hipStream_t s);
+// Per-sample materialised gradients M[b][o][q] = sum_t G_b[t][o] A_b[t][q] (FGC).
+hipError_t launch_fgc_mfma(const bf16_t* A, const bf16_t* G, int B, int T, int d, int p, float* M,
+                           hipStream_t s);
+
+}  // namespace dprc

@@ -1,0 +1,269 @@
+// MFMA (bf16 in, fp32 accumulate) kernels of the Hutchinson estimator on
+// gfx950 (the randomized-clipping summary, section 中核メカニズム, item 1):
+//   sketch   Y_i = G_i P_i      reduction along each token row (contiguous)
+//   project  Z_i = A_i^T Y_i    reduction along the tokens (strided rows)
+// Both stream their big operand from HBM exactly once with 16-byte loads and
+// feed v_mfma_f32_16x16x32_bf16 directly from registers.
+//
+// MFMA operand facts used (16x16x32 bf16, wave64): lane l supplies row l % 16
+// of A and column l % 16 of B, each with 8 bf16 of the contraction index; the
+// result D[4 (l / 16) + i][l % 16] sits in accumulator register i of lane l.
+// Which 8 contraction indices a lane group holds is free, as long as the A and
+// B operands agree; the kernels use that freedom to make every lane's 8 values
+// one contiguous 16-byte load.
+#include "common.h"
+#include "internal.h"
+
+namespace dprc {
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16(const bf16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// Sketch.  A workgroup (4 waves) owns 16*MB tokens of one sample; wave w
+// reduces the quarter r in [w W/4, (w+1) W/4) in steps of 64.  In a step, lane
+// (m = l % 16, g = l / 16) loads 32 contiguous bytes of token row m at offset
+// 16 g; contraction slot (h, g, e) is r = r0 + 16 g + 8 h + e for both the
+// token rows (A operand) and the probe rows P^T[j] (B operand).  The four
+// waves' partial Y tiles are summed in LDS in a fixed order and stored as bf16
+// Y^T[b][j][t].
+// ---------------------------------------------------------------------------
+constexpr int kSketchK = 64;
+
+template <int MB>
+__global__ void __launch_bounds__(256) k_sketch_mfma(const bf16_t* __restrict__ X, int T, int W,
+                                                     const bf16_t* __restrict__ P,
+                                                     int64_t p_bstride, bf16_t* __restrict__ Y) {
+  constexpr int TM = 16 * MB;
+  __shared__ float red[4][32][TM + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * TM;
+  const int Wq = W >> 2;
+  const int rbeg = wave * Wq + 16 * g;
+
+  const bf16_t* xr[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    xr[mb] = X + (static_cast<int64_t>(b) * T + t0 + mb * 16 + m) * W + rbeg;
+  const bf16_t* pr[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+    pr[nb] = P + b * p_bstride + static_cast<int64_t>(nb * 16 + m) * W + rbeg;
+
+  f32x4 acc[MB][2];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 xa[2][MB][2], pv[2][2][2];
+  auto load = [&](int buf, int r) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) xa[buf][mb][h] = ld16(xr[mb] + r + 8 * h);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) pv[buf][nb][h] = ld16(pr[nb] + r + 8 * h);
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma16(xa[buf][mb][h], pv[buf][nb][h], acc[mb][nb]);
+  };
+
+  const int niter = Wq / kSketchK;
+  load(0, 0);
+  for (int it = 0; it < niter; it += 2) {
+    if (it + 1 < niter) load(1, (it + 1) * kSketchK);
+    compute(0);
+    if (it + 1 < niter) {
+      if (it + 2 < niter) load(0, (it + 2) * kSketchK);
+      compute(1);
+    }
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][nb * 16 + m][mb * 16 + 4 * g + i] = acc[mb][nb][i];
+  __syncthreads();
+
+  // 32 x TM outputs, TM / 8 consecutive tokens per thread.
+  constexpr int PER = TM / 8;
+  const int j = threadIdx.x >> 3;
+  const int tc = (threadIdx.x & 7) * PER;
+  uint32_t packed[PER / 2];
+#pragma unroll
+  for (int u = 0; u < PER; u += 2) {
+    float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      v0 += red[w][j][tc + u];
+      v1 += red[w][j][tc + u + 1];
+    }
+    packed[u / 2] = pack_bf16x2(v0, v1);
+  }
+  bf16_t* dst = Y + (static_cast<int64_t>(b) * kMfmaProbeCols + j) * T + t0 + tc;
+  if constexpr (PER == 8) {
+    u32x4 v{packed[0], packed[1], packed[2], packed[3]};
+    *reinterpret_cast<u32x4*>(dst) = v;
+  } else {
+    uint2 v{packed[0], packed[1]};
+    *reinterpret_cast<uint2*>(dst) = v;
+  }
+}
+
+bool mfma_sketch_ok(int T, int W) { return T > 0 && T % 32 == 0 && W % (4 * kSketchK) == 0; }
+
+hipError_t launch_sketch_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* P,
+                              int64_t p_bstride, bf16_t* Y, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  if (!mfma_sketch_ok(T, W)) return hipErrorInvalidValue;
+  if (T % 64 == 0 && static_cast<int64_t>(B) * (T / 64) >= 512) {
+    hipLaunchKernelGGL(k_sketch_mfma<4>, dim3(T / 64, B), dim3(256), 0, s, X, T, W, P, p_bstride, Y);
+  } else {
+    hipLaunchKernelGGL(k_sketch_mfma<2>, dim3(T / 32, B), dim3(256), 0, s, X, T, W, P, p_bstride, Y);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Project.  A workgroup owns 128 columns q of one sample and one token split;
+// wave w takes a contiguous quarter of the split in steps of 32 tokens.  In a
+// step, lane (m, g) loads tokens t0 + 8 g + e (e = 0..7) of the 16-byte column
+// group q0 + 8 m; an in-register 8 x 8 transpose of those 16-bit values gives
+// the A operand of eight MFMA blocks, block c holding rows q = q0 + 8 m + c.
+// The B operand is Y^T[j][t0 + 8 g .. + 7], one 16-byte load.  Contraction
+// slot (g, e) is token t0 + 8 g + e for both operands.
+// ---------------------------------------------------------------------------
+constexpr int kProjQ = 128;
+constexpr int kProjK = 32;
+
+__device__ __forceinline__ u32x4 transpose_col(const u32x4 (&rows)[8], int c) {
+  u32x4 a;
+  const int w = c >> 1;
+  if ((c & 1) == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = (rows[2 * k][w] & 0xFFFFu) | (rows[2 * k + 1][w] << 16);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = (rows[2 * k][w] >> 16) | (rows[2 * k + 1][w] & 0xFFFF0000u);
+  }
+  return a;
+}
+
+__global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__ X, int T, int W,
+                                                      const bf16_t* __restrict__ Y,
+                                                      int split_tokens, int nsplit,
+                                                      float* __restrict__ Zp) {
+  __shared__ float red[4][32][kProjQ + 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int q0 = blockIdx.x * kProjQ;
+  const int split = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tw = split_tokens >> 2;
+  const int tbeg = split * split_tokens + wave * tw;
+
+  const bf16_t* xbase = X + (static_cast<int64_t>(b) * T + tbeg + 8 * g) * W + q0 + 8 * m;
+  const bf16_t* yb0 = Y + (static_cast<int64_t>(b) * kMfmaProbeCols + m) * T + tbeg + 8 * g;
+  const bf16_t* yb1 = yb0 + static_cast<int64_t>(16) * T;
+
+  f32x4 acc[8][2];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    acc[c][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  u32x4 rows[2][8], yv[2][2];
+  auto load = [&](int buf, int t) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rows[buf][e] = ld16(xbase + static_cast<int64_t>(t + e) * W);
+    yv[buf][0] = ld16(yb0 + t);
+    yv[buf][1] = ld16(yb1 + t);
+  };
+  auto compute = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const u32x4 a = transpose_col(rows[buf], c);
+      acc[c][0] = mfma16(a, yv[buf][0], acc[c][0]);
+      acc[c][1] = mfma16(a, yv[buf][1], acc[c][1]);
+    }
+  };
+
+  const int niter = tw / kProjK;
+  load(0, 0);
+  for (int it = 0; it < niter; it += 2) {
+    if (it + 1 < niter) load(1, (it + 1) * kProjK);
+    compute(0);
+    if (it + 1 < niter) {
+      if (it + 2 < niter) load(0, (it + 2) * kProjK);
+      compute(1);
+    }
+  }
+
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][nb * 16 + m][8 * (4 * g + i) + c] = acc[c][nb][i];
+  __syncthreads();
+
+  // 32 x 128 outputs: thread -> row j = tid / 8, 16 consecutive q.
+  const int j = threadIdx.x >> 3;
+  const int qc = (threadIdx.x & 7) * 16;
+  float* dst = Zp + ((static_cast<int64_t>(b) * nsplit + split) * kMfmaProbeCols + j) * W + q0 + qc;
+#pragma unroll
+  for (int u = 0; u < 16; u += 4) {
+    float4 v;
+    v.x = red[0][j][qc + u + 0] + red[1][j][qc + u + 0] + red[2][j][qc + u + 0] + red[3][j][qc + u + 0];
+    v.y = red[0][j][qc + u + 1] + red[1][j][qc + u + 1] + red[2][j][qc + u + 1] + red[3][j][qc + u + 1];
+    v.z = red[0][j][qc + u + 2] + red[1][j][qc + u + 2] + red[2][j][qc + u + 2] + red[3][j][qc + u + 2];
+    v.w = red[0][j][qc + u + 3] + red[1][j][qc + u + 3] + red[2][j][qc + u + 3] + red[3][j][qc + u + 3];
+    *reinterpret_cast<float4*>(dst + u) = v;
+  }
+}
+
+bool mfma_project_ok(int T, int W) { return T > 0 && T % (4 * kProjK) == 0 && W % kProjQ == 0; }
+
+// Token splits: about 1024 workgroups in all, each split a multiple of 128
+// tokens dividing T.
+int mfma_project_splits(int B, int T, int W) {
+  const int64_t base = static_cast<int64_t>(B) * (W / kProjQ);
+  int want = static_cast<int>((1024 + base - 1) / (base > 0 ? base : 1));
+  const int maxs = T / (4 * kProjK);
+  if (want > maxs) want = maxs;
+  if (want < 1) want = 1;
+  for (int s = want; s >= 1; --s)
+    if (T % (s * 4 * kProjK) == 0) return s;
+  return 1;
+}
+
+hipError_t launch_project_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* Y, int nsplit,
+                               float* Zp, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  if (!mfma_project_ok(T, W) || nsplit < 1 || T % (nsplit * 4 * kProjK) != 0)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_project_mfma, dim3(W / kProjQ, nsplit, B), dim3(256), 0, s, X, T, W, Y,
+                     T / nsplit, nsplit, Zp);
+  return hipGetLastError();
+}
+
+}  // namespace dprc

@@ -1,0 +1,161 @@
+// Random streams of the method on gfx950: Hutchinson probes and DP noise from
+// Philox4x32-10 + Box-Muller, and the fused noise-add + SGD update.
+//
+// Probe entry (row r, column j) of sample i in layer l is lane r mod 4 of the
+// counter (r / 4, j, i, l) under key `seed` (the randomized-clipping summary,
+// section 中核メカニズム, item 1: P has i.i.d. Gaussian entries).  The noise of
+// flat parameter index e is lane e mod 4 of (lo(e / 4), hi(e / 4), 0xFFFFFFFF, l)
+// (glossary page, section DP-SGDのアルゴリズム, step 4).
+#include "common.h"
+#include "internal.h"
+
+namespace dprc {
+
+__global__ void k_philox_u32(uint32_t k0, uint32_t k1, const uint32_t* __restrict__ ctr,
+                             uint32_t* __restrict__ out, size_t n) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  u32x4 c;
+  c.x = ctr[4 * i + 0];
+  c.y = ctr[4 * i + 1];
+  c.z = ctr[4 * i + 2];
+  c.w = ctr[4 * i + 3];
+  const u32x4 w = philox4x32_10(c, k0, k1);
+  out[4 * i + 0] = w.x;
+  out[4 * i + 1] = w.y;
+  out[4 * i + 2] = w.z;
+  out[4 * i + 3] = w.w;
+}
+
+hipError_t launch_philox_u32(uint64_t seed, const uint32_t* ctr, uint32_t* out, size_t n,
+                             hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+  hipLaunchKernelGGL(k_philox_u32, dim3(blocks), dim3(256), 0, s, static_cast<uint32_t>(seed),
+                     static_cast<uint32_t>(seed >> 32), ctr, out, n);
+  return hipGetLastError();
+}
+
+// One thread per (sample, column j, row group g): four rows 4g..4g+3 of column j.
+template <typename TOut>
+__global__ void k_probe_fill(uint32_t k0, uint32_t k1, uint32_t layer, uint32_t sample0, int p,
+                             int kfill, int kpad, TOut* __restrict__ out) {
+  const int ngroups = (p + 3) >> 2;
+  const int g = blockIdx.x * blockDim.x + threadIdx.x;
+  const int j = blockIdx.y;
+  const int i = blockIdx.z;
+  if (g >= ngroups) return;
+  float z[4] = {0.f, 0.f, 0.f, 0.f};
+  if (j < kfill) {
+    u32x4 c;
+    c.x = static_cast<uint32_t>(g);
+    c.y = static_cast<uint32_t>(j);
+    c.z = sample0 + static_cast<uint32_t>(i);
+    c.w = layer;
+    normals4(c, k0, k1, z);
+  }
+  TOut* row = out + (static_cast<int64_t>(i) * kpad + j) * p;
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {
+    const int r = 4 * g + l;
+    if (r < p) {
+      if constexpr (sizeof(TOut) == 4)
+        row[r] = z[l];
+      else
+        row[r] = f32_to_bf16(z[l]);
+    }
+  }
+}
+
+template <typename TOut>
+static hipError_t probe_fill(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp, int p,
+                             int kfill, int kpad, TOut* out, hipStream_t s) {
+  if (nsamp <= 0 || p <= 0 || kpad <= 0) return hipSuccess;
+  const int ngroups = (p + 3) >> 2;
+  dim3 grid((ngroups + 255) / 256, kpad, nsamp);
+  hipLaunchKernelGGL(k_probe_fill<TOut>, grid, dim3(256), 0, s, static_cast<uint32_t>(seed),
+                     static_cast<uint32_t>(seed >> 32), layer, sample0, p, kfill, kpad, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_fill_f32(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
+                                 int p, int kfill, int kpad, float* out, hipStream_t s) {
+  return probe_fill<float>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s);
+}
+
+hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
+                                  int p, int kfill, int kpad, bf16_t* out, hipStream_t s) {
+  return probe_fill<bf16_t>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s);
+}
+
+__device__ __forceinline__ u32x4 noise_counter(uint64_t grp, uint32_t layer) {
+  u32x4 c;
+  c.x = static_cast<uint32_t>(grp);
+  c.y = static_cast<uint32_t>(grp >> 32);
+  c.z = kNoiseC2;
+  c.w = layer;
+  return c;
+}
+
+// xi[e - offset] for e in [offset, offset + n); one thread per counter group.
+__global__ void k_noise_fill(uint32_t k0, uint32_t k1, uint32_t layer, uint64_t offset, size_t n,
+                             float* __restrict__ xi) {
+  const uint64_t g0 = offset >> 2;
+  const uint64_t g = g0 + static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const uint64_t end = offset + n;
+  if ((g << 2) >= end) return;
+  float z[4];
+  normals4(noise_counter(g, layer), k0, k1, z);
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {
+    const uint64_t e = (g << 2) + l;
+    if (e >= offset && e < end) xi[e - offset] = z[l];
+  }
+}
+
+hipError_t launch_noise_fill(uint64_t seed, uint32_t layer, uint64_t offset, size_t n, float* xi,
+                             hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const uint64_t groups = ((offset + n + 3) >> 2) - (offset >> 2);
+  hipLaunchKernelGGL(k_noise_fill, dim3(static_cast<unsigned>((groups + 255) / 256)), dim3(256), 0,
+                     s, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), layer,
+                     offset, n, xi);
+  return hipGetLastError();
+}
+
+// theta[e] -= eta_over_B * (S[e] + sigmaC * xi[e]) for four consecutive e per
+// thread (one Philox block); 16-byte vector accesses when the group is whole.
+__global__ void __launch_bounds__(256) k_noise_update(float* __restrict__ theta,
+                                                      const float* __restrict__ S, int64_t n,
+                                                      float sigmaC, float eta_over_B, uint32_t k0,
+                                                      uint32_t k1, uint32_t layer) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t e0 = g << 2;
+  if (e0 >= n) return;
+  float z[4];
+  normals4(noise_counter(static_cast<uint64_t>(g), layer), k0, k1, z);
+  if (e0 + 3 < n) {
+    float4 th = *reinterpret_cast<const float4*>(theta + e0);
+    const float4 sv = *reinterpret_cast<const float4*>(S + e0);
+    th.x -= eta_over_B * fmaf(sigmaC, z[0], sv.x);
+    th.y -= eta_over_B * fmaf(sigmaC, z[1], sv.y);
+    th.z -= eta_over_B * fmaf(sigmaC, z[2], sv.z);
+    th.w -= eta_over_B * fmaf(sigmaC, z[3], sv.w);
+    *reinterpret_cast<float4*>(theta + e0) = th;
+  } else {
+    for (int l = 0; l < 4 && e0 + l < n; ++l)
+      theta[e0 + l] -= eta_over_B * fmaf(sigmaC, z[l], S[e0 + l]);
+  }
+}
+
+hipError_t launch_noise_update(float* theta, const float* S, int64_t n, float sigmaC,
+                               float eta_over_B, uint64_t seed, uint32_t layer, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t groups = (n + 3) >> 2;
+  hipLaunchKernelGGL(k_noise_update, dim3(static_cast<unsigned>((groups + 255) / 256)), dim3(256),
+                     0, s, theta, S, n, sigmaC, eta_over_B, static_cast<uint32_t>(seed),
+                     static_cast<uint32_t>(seed >> 32), layer);
+  return hipGetLastError();
+}
+
+}  // namespace dprc

@@ -1,0 +1,132 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+function include/dprc.h declares, and rejects bad arguments before anything
+is enqueued (every case here returns before the first HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from sample_gradient_clipping_amd import binding as dp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dprc.h")
+
+FAKE = ctypes.c_void_p(0x100000)      # aligned, never dereferenced on these paths
+FAKE_MIS = ctypes.c_void_p(0x100004)  # 4-byte aligned, not 16
+NULL = ctypes.c_void_p(0)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dp.lib_path()):
+        pytest.fail("libdprc.so not built (run __graft_entry__.build())")
+    return dp.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dp_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared_functions()
+    assert "dp_norm_est" in names and "dp_clip_aggregate" in names and "dp_noise_update" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in dprc.h but not exported"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert dp.dp_abi_version() == 1
+    for s in range(5):
+        assert dp.dp_status_string(s).startswith("DP_")
+    assert "unknown" in dp.dp_status_string(99)
+
+
+def test_workspace_queries(lib):
+    assert dp.dp_norm_est_workspace("hutch", "bf16", 8, 4096, 2048, 2048, 32) > 0
+    assert dp.dp_norm_est_workspace("hutch", "f32", 4, 64, 64, 64, 8) > 0
+    assert dp.dp_norm_est_workspace("ghost", "f32", 4, 64, 64, 64, 0) > 0
+    # invalid: k > p, k < 3 for Hutch++, bad method/dtype, negative sizes
+    assert dp.dp_norm_est_workspace("hutch", "f32", 4, 64, 64, 64, 65) is None
+    assert dp.dp_norm_est_workspace("hutchpp", "f32", 4, 64, 64, 64, 2) is None
+    assert dp.load_library().dp_norm_est_workspace(9, 0, 1, 1, 1, 1, 1) == ctypes.c_size_t(-1).value
+    assert dp.load_library().dp_norm_est_workspace(0, 7, 1, 1, 1, 1, 1) == ctypes.c_size_t(-1).value
+    assert dp.dp_norm_est_workspace("hutch", "f32", -1, 64, 64, 64, 8) is None
+    assert dp.dp_norm_est_workspace("hutch", "f32", 4, 64, 0, 64, 8) is None
+    assert dp.dp_clip_aggregate_workspace("bf16", 8, 4096, 2048, 2048) > 0
+    assert dp.dp_clip_aggregate_workspace("f32", 4, 64, 0, 64) is None
+
+
+def _norm(lib, method=0, dtype=0, B=2, T=8, d=8, p=8, k=4, A=FAKE, G=FAKE, flags=0, n=FAKE,
+          ws=FAKE, ws_bytes=1 << 30):
+    return lib.dp_norm_est(method, dtype, B, T, d, p, k, A, G, 1, 0, flags, n, ws, ws_bytes, NULL)
+
+
+def test_norm_est_rejects_bad_arguments(lib):
+    E, W = dp.DP_ERR_INVALID_ARG, dp.DP_ERR_WORKSPACE
+    assert _norm(lib, method=7) == E
+    assert _norm(lib, dtype=3) == E
+    assert _norm(lib, k=0) == E
+    assert _norm(lib, k=9) == E            # k > p
+    assert _norm(lib, method=1, k=2) == E  # Hutch++ needs k >= 3
+    assert _norm(lib, d=0) == E
+    assert _norm(lib, B=-1) == E
+    assert _norm(lib, flags=8) == E
+    assert _norm(lib, A=NULL) == E
+    assert _norm(lib, G=FAKE_MIS) == E
+    assert _norm(lib, n=NULL) == E
+    assert _norm(lib, ws=NULL) == E
+    assert _norm(lib, ws_bytes=16) == W
+    assert _norm(lib, B=0) == dp.DP_OK    # empty batch: nothing to do
+
+
+def _agg(lib, dtype=0, B=2, T=8, d=8, p=8, A=FAKE, G=FAKE, n=FAKE, C=1.0, S=FAKE, ws=FAKE,
+         ws_bytes=1 << 30, c_out=NULL, status=NULL):
+    return lib.dp_clip_aggregate(dtype, B, T, d, p, A, G, n, C, c_out, status, S, ws, ws_bytes,
+                                 NULL)
+
+
+def test_clip_aggregate_rejects_bad_arguments(lib):
+    E = dp.DP_ERR_INVALID_ARG
+    assert _agg(lib, C=0.0) == E
+    assert _agg(lib, C=-1.0) == E
+    assert _agg(lib, C=float("inf")) == E
+    assert _agg(lib, C=float("nan")) == E
+    assert _agg(lib, S=NULL) == E
+    assert _agg(lib, S=FAKE_MIS) == E
+    assert _agg(lib, n=NULL) == E
+    assert _agg(lib, A=NULL) == E
+    assert _agg(lib, dtype=5) == E
+    assert _agg(lib, p=0) == E
+    assert _agg(lib, c_out=ctypes.c_void_p(0x100002)) == E
+    assert _agg(lib, ws_bytes=0) == dp.DP_ERR_WORKSPACE
+
+
+def test_noise_update_rejects_bad_arguments(lib):
+    E = dp.DP_ERR_INVALID_ARG
+    f = lambda **kw: lib.dp_noise_update(kw.get("d", 8), kw.get("p", 8), kw.get("th", FAKE),
+                                         kw.get("S", ctypes.c_void_p(0x200000)),
+                                         kw.get("sigma", 1.0), kw.get("C", 1.0),
+                                         kw.get("eta", 0.1), kw.get("B", 4), 1, 0, NULL)
+    assert f(B=0) == E
+    assert f(sigma=-1.0) == E
+    assert f(sigma=float("nan")) == E
+    assert f(C=0.0) == E
+    assert f(eta=float("inf")) == E
+    assert f(d=0) == E
+    assert f(th=NULL) == E
+    assert f(th=FAKE_MIS) == E
+    assert f(S=ctypes.c_void_p(0x100000 + 64)) == E  # overlaps theta
+
+
+def test_test_hooks_reject_bad_arguments(lib):
+    E = dp.DP_ERR_INVALID_ARG
+    assert lib.dp_philox_u32(1, NULL, FAKE, 4, NULL) == E
+    assert lib.dp_philox_u32(1, FAKE, FAKE, 0, NULL) == dp.DP_OK
+    assert lib.dp_probe_fill(1, 0, 0, 0, 4, FAKE, NULL) == E
+    assert lib.dp_probe_fill(1, 0, 0, 4, 4, NULL, NULL) == E
+    assert lib.dp_noise_fill(1, 0, 0, 4, NULL, NULL) == E
+    assert lib.dp_noise_fill(1, 0, 2**64 - 2, 4, FAKE, NULL) == E
