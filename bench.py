@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""DP-SGD-RC step throughput on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is the whole hot path over one batch: per-sample norm estimation of
+every linear layer (summed over layers), clip factors, the clipped-sum
+contraction and the fused noise + SGD update of every layer.  Inputs are
+synthetic, generated on the device before timing and already resident in
+HBM; several input copies are rotated so that the 256 MB last-level cache
+cannot serve one step's inputs from the previous step.
+
+Prints ONE JSON line: tokens/s of the timed steps, the roofline of the
+dominant kernel (duration from HIP events recorded by the library around
+that kernel, inside the timed steps), and the CPU oracle timed on a bounded
+sample of the same workload on this host.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DP-SGD-RC step tokens/sec (norm-est+clip+noisy agg); % HBM / MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg2_attn_proj")
+    ap.add_argument("--method", default=None, help="override the workload's estimator")
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_inputs(wl, copies, dev):
+    import torch
+    from sample_gradient_clipping_amd.inputs import linear_inputs, linear_inputs_device
+    out = []
+    for c in range(copies):
+        layers = []
+        for l in wl.layers:
+            seed = wl.data_seed + 7919 * c
+            if wl.tokens * (l.d + l.p) <= (1 << 22):
+                A, G = linear_inputs(wl.B, wl.T, l.d, l.p, wl.dtype, wl.recipe, seed, l.layer_id)
+                A, G = A.to(dev), G.to(dev)
+            else:
+                A, G = linear_inputs_device(wl.B, wl.T, l.d, l.p, wl.dtype, wl.recipe, seed,
+                                            l.layer_id, dev)
+            layers.append((A, G))
+        out.append(layers)
+    torch.cuda.synchronize()
+    return out
+
+
+def cpu_baseline(wl, method):
+    """The oracle (plain fp64 numpy) on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    from sample_gradient_clipping_amd.inputs import linear_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS default
+        cores = os.cpu_count() or 1
+    layers = wl.layers
+    scale_blocks = 1
+    if len(layers) > 7:  # a layer stack: time block 0, extrapolate to all blocks
+        scale_blocks = len(layers) // 7
+        layers = layers[:7]
+    Bs = 1 if wl.tokens * max(l.d + l.p for l in layers) > (1 << 27) else wl.B
+    if wl.name.startswith("cfg2"):
+        Bs = 2
+    data = []
+    for l in layers:
+        A, G = linear_inputs(Bs, wl.T, l.d, l.p, wl.dtype, wl.recipe, wl.data_seed, l.layer_id)
+        data.append((l.layer_id, A, G, np.zeros((l.p, l.d))))
+    t0 = time.perf_counter()
+    oracle.dp_step(data, method, wl.k, wl.C, wl.sigma, wl.eta, wl.method_seed, wl.noise_seed)
+    t = time.perf_counter() - t0
+    t_step = t * scale_blocks
+    sample = (f"{Bs} of {wl.B} samples x {wl.T} tokens, {len(layers)} of {len(wl.layers)} linear "
+              f"layers" + (f", time x{scale_blocks} (extrapolated to all blocks)"
+                           if scale_blocks > 1 else "")
+              + f"; full oracle step (norms, clip, aggregation, noise+update) in {t:.2f} s")
+    return {"value": Bs * wl.T / t_step, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle", "sample": sample}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (--gpus {args.gpus} requested): the hot path is "
+              "built and measured on one MI355X; multi-GPU sharding is a design note, not built.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sample_gradient_clipping_amd import binding as dp
+    from sample_gradient_clipping_amd import roofline as rf
+    from sample_gradient_clipping_amd.configs import workloads
+
+    wl = workloads()[args.workload]
+    method = args.method or wl.method
+    dev = torch.device("cuda:0")
+    dp.load_library()
+    E = rf.elem_size(wl.dtype)
+    per_copy = sum(wl.tokens * (l.d + l.p) * E for l in wl.layers)
+    copies = args.copies or max(1, min(4, math.ceil((768 << 20) / per_copy)))
+    log(f"[bench] workload {wl.name}: B={wl.B} T={wl.T} layers={len(wl.layers)} method={method} "
+        f"k={wl.k} inputs {per_copy / 2**30:.2f} GiB x {copies} copies")
+    inputs = make_inputs(wl, copies, dev)
+
+    L = len(wl.layers)
+    n = torch.zeros(wl.B, dtype=torch.float32, device=dev)
+    S = [torch.empty(l.p, l.d, dtype=torch.float32, device=dev) for l in wl.layers]
+    theta = [torch.zeros(l.p, l.d, dtype=torch.float32, device=dev) for l in wl.layers]
+    ws_n = max(dp.dp_norm_est_workspace(method, wl.dtype, wl.B, wl.T, l.d, l.p, wl.k)
+               for l in wl.layers)
+    ws_a = max(dp.dp_clip_aggregate_workspace(wl.dtype, wl.B, wl.T, l.d, l.p) for l in wl.layers)
+    ws_norm = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    ws_agg = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev)
+
+    K, W = args.steps, args.warmup
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
+          for _ in range(K)]
+    for s in ev:
+        for l in s:
+            for e in l:
+                e.record()
+    torch.cuda.synchronize()
+
+    def step(it, evs):
+        cp = inputs[it % copies]
+        for li, l in enumerate(wl.layers):
+            A, G = cp[li]
+            dp.dp_norm_est(method, A, G, wl.k, wl.method_seed + it, l.layer_id, n,
+                           flags=dp.DP_ACCUMULATE if li else 0, ws=ws_norm,
+                           events=None if evs is None else (evs[li][0], evs[li][1]))
+        for li, l in enumerate(wl.layers):
+            A, G = cp[li]
+            dp.dp_clip_aggregate(A, G, n, wl.C, S[li], ws=ws_agg,
+                                 events=None if evs is None else (evs[li][2], evs[li][3]))
+            dp.dp_noise_update(theta[li], S[li], wl.sigma, wl.C, wl.eta, wl.B,
+                               wl.noise_seed + it, l.layer_id,
+                               events=None if evs is None else (evs[li][4], evs[li][5]))
+
+    for it in range(W):
+        step(it, None)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for it in range(K):
+        step(W + it, ev[it])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / K
+    tokens_per_s = wl.tokens * K / (ms_total / 1e3)
+    log(f"[bench] {K} steps in {ms_total:.3f} ms (wall {wall * 1e3:.1f} ms): {ms_step:.4f} ms/step, "
+        f"{tokens_per_s / 1e6:.2f} M tokens/s")
+
+    # Per-kernel durations from the library's events, summed over the timed steps.
+    t_norm = t_agg = t_noise = 0.0
+    for it in range(K):
+        for li in range(L):
+            e = ev[it][li]
+            t_norm += e[0].elapsed_time(e[1])
+            t_agg += e[2].elapsed_time(e[3])
+            t_noise += e[4].elapsed_time(e[5])
+    launches = K * L
+    if method in ("hutch",):
+        b_norm = sum(rf.hutch_bytes(wl.B, wl.T, l.d, l.p, wl.dtype) for l in wl.layers)
+        f_norm = sum(rf.hutch_flops(wl.B, wl.T, l.d, l.p, wl.k) for l in wl.layers)
+    elif method == "hutchpp":
+        b_norm = sum(rf.hutchpp_bytes(wl.B, wl.T, l.d, l.p, wl.dtype) for l in wl.layers)
+        f_norm = sum(rf.hutchpp_flops(wl.B, wl.T, l.d, l.p, wl.k) for l in wl.layers)
+    elif method == "ghost":
+        b_norm = sum(rf.hutch_bytes(wl.B, wl.T, l.d, l.p, wl.dtype) for l in wl.layers)
+        f_norm = sum(rf.ghost_flops(wl.B, wl.T, l.d, l.p) for l in wl.layers)
+    else:
+        b_norm = sum(rf.fgc_bytes(wl.B, wl.T, l.d, l.p, wl.dtype) for l in wl.layers)
+        f_norm = sum(rf.gemm_flops(wl.B, wl.T, l.d, l.p) for l in wl.layers)
+    f_agg = sum(rf.gemm_flops(wl.B, wl.T, l.d, l.p) for l in wl.layers)
+    b_agg = sum(rf.aggregate_bytes(wl.B, wl.T, l.d, l.p, wl.dtype) for l in wl.layers)
+    b_noise = sum(rf.noise_bytes(l.d, l.p) for l in wl.layers)
+    # per step: algorithmic work of all layers / summed kernel time of one step
+    s_norm, s_agg, s_noise = t_norm / K / 1e3, t_agg / K / 1e3, t_noise / K / 1e3
+    kernels = {
+        "norm_est": {"name": f"{method} passes (per layer: sketch+projection)" if method == "hutch"
+                     else f"{method} main kernels", "ms_per_launch": t_norm / launches,
+                     "bound": "hbm" if method in ("hutch", "hutchpp") else "mfma",
+                     "GBps": b_norm / s_norm / 1e9, "TFLOPs": f_norm / s_norm / 1e12},
+        "aggregate": {"name": "clipped-sum contraction", "ms_per_launch": t_agg / launches,
+                      "bound": "mfma", "GBps": b_agg / s_agg / 1e9, "TFLOPs": f_agg / s_agg / 1e12},
+        "noise_update": {"name": "Philox noise + SGD update", "ms_per_launch": t_noise / launches,
+                         "bound": "hbm", "GBps": b_noise / s_noise / 1e9},
+    }
+    for kname, kv in kernels.items():
+        kv["frac"] = (kv["GBps"] / rf.PEAK_HBM_GBPS if kv["bound"] == "hbm"
+                      else kv["TFLOPs"] / rf.PEAK_BF16_TFLOPS)
+        kv["share_of_step"] = (kv["ms_per_launch"] * L) / ms_step
+    dom_name = max(kernels, key=lambda k_: kernels[k_]["share_of_step"])
+    dom = kernels[dom_name]
+    if dom["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": dom["GBps"], "peak": rf.PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": dom["GBps"] / rf.PEAK_HBM_GBPS, "traffic": None}
+    else:
+        roof = {"bound": "mfma", "achieved": dom["TFLOPs"], "peak": rf.PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": dom["TFLOPs"] / rf.PEAK_BF16_TFLOPS, "traffic": None}
+    roof["kernel"] = dom["name"]
+    for kname, kv in kernels.items():
+        log(f"[bench] {kname:13s} {kv['ms_per_launch'] * 1e3:9.2f} us/launch  "
+            f"{kv['GBps']:8.1f} GB/s  {kv.get('TFLOPs', 0):8.1f} TF/s  frac {kv['frac']:.3f}  "
+            f"share {kv['share_of_step']:.2f}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(wl, method)
+        log(f"[bench] cpu_baseline {cpu}")
+
+    line = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "layers": len(wl.layers),
+                   "shapes_dp": sorted({(l.d, l.p) for l in wl.layers}), "method": method,
+                   "k": wl.k, "C": wl.C, "sigma": wl.sigma, "eta": wl.eta,
+                   "input_copies": copies, "global_batch": wl.B, "seq_len": wl.T},
+        "roofline": roof,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

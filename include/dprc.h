@@ -147,6 +147,28 @@ dp_status_t dp_noise_update(int d, int p, float *theta, const float *S, float si
                             float C, float eta, int B, uint64_t seed, uint32_t layer,
                             dp_stream_t stream);
 
+/* ---- timed variants: the same calls, plus live kernel timing ----
+ * Identical to the call without "_timed", and additionally record the two
+ * hipEvent_t handles ev_begin / ev_end (either may be NULL) on `stream`
+ * immediately before the first and after the last launch of the call's main
+ * kernels: dp_norm_est - the streaming passes over A and G (Hutch: sketch and
+ * projection; Hutch++: all three passes with the QR between them; ghost: the
+ * Gram kernel; FGC: the materialising contraction); dp_clip_aggregate - the
+ * clipped-sum contraction (not the clip factors nor the split reduction);
+ * dp_noise_update - the noise + update kernel.  The caller owns the events.
+ */
+dp_status_t dp_norm_est_timed(int method, int dtype, int B, int T, int d, int p, int k,
+                              const void *A, const void *G, uint64_t seed, uint32_t layer,
+                              uint32_t flags, float *n_sq, void *ws, size_t ws_bytes,
+                              dp_stream_t stream, void *ev_begin, void *ev_end);
+dp_status_t dp_clip_aggregate_timed(int dtype, int B, int T, int d, int p, const void *A,
+                                    const void *G, const float *n_sq, float C, float *c_out,
+                                    uint32_t *status, float *S, void *ws, size_t ws_bytes,
+                                    dp_stream_t stream, void *ev_begin, void *ev_end);
+dp_status_t dp_noise_update_timed(int d, int p, float *theta, const float *S, float sigma,
+                                  float C, float eta, int B, uint64_t seed, uint32_t layer,
+                                  dp_stream_t stream, void *ev_begin, void *ev_end);
+
 /* ---- test hooks: expose the random streams for bit-level parity checks ---- */
 
 /* out[4 n] = Philox4x32-10 words of the n counters ctr[4 n] (device arrays). */

@@ -62,6 +62,12 @@ def load_library():
     L.dp_clip_aggregate.restype = c_int
     L.dp_noise_update.argtypes = [c_int, c_int, c_p, c_p, c_f, c_f, c_f, c_int, c_u64, c_u32, c_p]
     L.dp_noise_update.restype = c_int
+    L.dp_norm_est_timed.argtypes = L.dp_norm_est.argtypes + [c_p, c_p]
+    L.dp_norm_est_timed.restype = c_int
+    L.dp_clip_aggregate_timed.argtypes = L.dp_clip_aggregate.argtypes + [c_p, c_p]
+    L.dp_clip_aggregate_timed.restype = c_int
+    L.dp_noise_update_timed.argtypes = L.dp_noise_update.argtypes + [c_p, c_p]
+    L.dp_noise_update_timed.restype = c_int
     L.dp_philox_u32.argtypes = [c_u64, c_p, c_p, c_sz, c_p]
     L.dp_philox_u32.restype = c_int
     L.dp_probe_fill.argtypes = [c_u64, c_u32, c_u32, c_int, c_int, c_p, c_p]
@@ -97,6 +103,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _event(ev):
+    """Raw hipEvent_t of a torch.cuda.Event (recorded once so that it exists)."""
+    if ev is None:
+        return None
+    if ev.cuda_event == 0:
+        ev.record()
+    return ctypes.c_void_p(ev.cuda_event)
+
+
 def _dtype_code(t):
     if t.dtype == torch.float32:
         return DP_F32
@@ -124,11 +139,12 @@ def dp_norm_est_workspace(method, dtype, B, T, d, p, k):
     return None if n == _SIZE_INVALID else n
 
 
-def dp_norm_est(method, A, G, k, seed, layer, n_sq, flags=0, ws=None, stream=None):
+def dp_norm_est(method, A, G, k, seed, layer, n_sq, flags=0, ws=None, stream=None, events=None):
     """n_sq[i] (=, or += with DP_ACCUMULATE) squared-norm estimate of sample i.
 
     A [B][T][d], G [B][T][p]: contiguous device tensors, fp32 or bf16.
     n_sq: fp32 [B] device tensor.  ``ws``: optional uint8 device workspace.
+    ``events``: optional (begin, end) torch.cuda.Event pair -> dp_norm_est_timed.
     """
     L = load_library()
     B, T, d = A.shape
@@ -138,9 +154,13 @@ def dp_norm_est(method, A, G, k, seed, layer, n_sq, flags=0, ws=None, stream=Non
     k = int(k or 0)
     nbytes = L.dp_norm_est_workspace(m, dt, B, T, d, p, k)
     ws_t = _workspace(nbytes, A.device, ws)
-    st = L.dp_norm_est(m, dt, B, T, d, p, k, _ptr(A), _ptr(G), int(seed) & (2**64 - 1),
-                       int(layer), int(flags), _ptr(n_sq), _ptr(ws_t),
-                       0 if ws_t is None else ws_t.numel(), _stream(stream))
+    args = [m, dt, B, T, d, p, k, _ptr(A), _ptr(G), int(seed) & (2**64 - 1), int(layer),
+            int(flags), _ptr(n_sq), _ptr(ws_t), 0 if ws_t is None else ws_t.numel(),
+            _stream(stream)]
+    if events is None:
+        st = L.dp_norm_est(*args)
+    else:
+        st = L.dp_norm_est_timed(*args, _event(events[0]), _event(events[1]))
     _check(st, "dp_norm_est")
     return n_sq
 
@@ -151,7 +171,8 @@ def dp_clip_aggregate_workspace(dtype, B, T, d, p):
     return None if n == _SIZE_INVALID else n
 
 
-def dp_clip_aggregate(A, G, n_sq, C, S, c_out=None, status=None, ws=None, stream=None):
+def dp_clip_aggregate(A, G, n_sq, C, S, c_out=None, status=None, ws=None, stream=None,
+                      events=None):
     """Clip factors from n_sq and S[o][q] = sum_i c_i sum_t G_i[t][o] A_i[t][q]."""
     L = load_library()
     B, T, d = A.shape
@@ -159,19 +180,26 @@ def dp_clip_aggregate(A, G, n_sq, C, S, c_out=None, status=None, ws=None, stream
     dt = _dtype_code(A)
     nbytes = L.dp_clip_aggregate_workspace(dt, B, T, d, p)
     ws_t = _workspace(nbytes, A.device, ws)
-    st = L.dp_clip_aggregate(dt, B, T, d, p, _ptr(A), _ptr(G), _ptr(n_sq), float(C), _ptr(c_out),
-                             _ptr(status), _ptr(S), _ptr(ws_t),
-                             0 if ws_t is None else ws_t.numel(), _stream(stream))
+    args = [dt, B, T, d, p, _ptr(A), _ptr(G), _ptr(n_sq), float(C), _ptr(c_out), _ptr(status),
+            _ptr(S), _ptr(ws_t), 0 if ws_t is None else ws_t.numel(), _stream(stream)]
+    if events is None:
+        st = L.dp_clip_aggregate(*args)
+    else:
+        st = L.dp_clip_aggregate_timed(*args, _event(events[0]), _event(events[1]))
     _check(st, "dp_clip_aggregate")
     return S
 
 
-def dp_noise_update(theta, S, sigma, C, eta, B, seed, layer, stream=None):
+def dp_noise_update(theta, S, sigma, C, eta, B, seed, layer, stream=None, events=None):
     """theta <- theta - (eta / B) (S + sigma C xi) in place; theta, S fp32 [p][d]."""
     p, d = theta.shape
-    st = load_library().dp_noise_update(d, p, _ptr(theta), _ptr(S), float(sigma), float(C),
-                                        float(eta), int(B), int(seed) & (2**64 - 1), int(layer),
-                                        _stream(stream))
+    L = load_library()
+    args = [d, p, _ptr(theta), _ptr(S), float(sigma), float(C), float(eta), int(B),
+            int(seed) & (2**64 - 1), int(layer), _stream(stream)]
+    if events is None:
+        st = L.dp_noise_update(*args)
+    else:
+        st = L.dp_noise_update_timed(*args, _event(events[0]), _event(events[1]))
     _check(st, "dp_noise_update")
     return theta
 

@@ -33,8 +33,10 @@ struct Carver {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// One frob block per ~1K elements: enough blocks to stream the partials at
+// full bandwidth.
 int frob_chunks(int64_t elems) {
-  int64_t c = elems / 65536;
+  int64_t c = elems / 1024;
   if (c < 1) c = 1;
   if (c > 1024) c = 1024;
   return static_cast<int>(c);
@@ -128,6 +130,13 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<unsigned char*>(ws) + off);
 }
 
+// Optional timing events recorded around a call's main kernels (may be null).
+struct Marks {
+  hipEvent_t begin = nullptr, end = nullptr;
+  hipError_t open(hipStream_t s) const { return begin ? hipEventRecord(begin, s) : hipSuccess; }
+  hipError_t close(hipStream_t s) const { return end ? hipEventRecord(end, s) : hipSuccess; }
+};
+
 #define DP_TRY(expr)                          \
   do {                                        \
     hipError_t e_ = (expr);                   \
@@ -137,7 +146,8 @@ T* at(void* ws, size_t off) {
 template <typename TIn>
 dp_status_t run_norm_generic_hutch(const NormPlan& P, int B, int T, int d, int p, int k,
                                    const TIn* A, const TIn* G, uint64_t seed, uint32_t layer,
-                                   bool shared, bool accum, float* n_sq, void* ws, hipStream_t s) {
+                                   bool shared, bool accum, float* n_sq, void* ws, hipStream_t s,
+                                   const Marks& mk) {
   float* Pf = at<float>(ws, P.pf);
   float* Y = at<float>(ws, P.y);
   float* Z = at<float>(ws, P.z);
@@ -145,8 +155,10 @@ dp_status_t run_norm_generic_hutch(const NormPlan& P, int B, int T, int d, int p
   const int nS = shared ? 1 : B;
   const int64_t pbs = shared ? 0 : static_cast<int64_t>(k) * p;
   DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, k, k, Pf, s));
+  DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_generic<TIn>(G, B, T, p, Pf, pbs, k, Y, s));
   DP_TRY(launch_project_generic<TIn>(A, B, T, d, Y, k, Z, s));
+  DP_TRY(mk.close(s));
   DP_TRY(launch_frob_partial(Z, B, 1, k, d, k, 1.0f / k, 0, 0.f, part, P.nchunk, s));
   DP_TRY(launch_sum_parts(part, B, P.nchunk, n_sq, accum ? 1 : 0, s));
   return DP_OK;
@@ -154,7 +166,8 @@ dp_status_t run_norm_generic_hutch(const NormPlan& P, int B, int T, int d, int p
 
 dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, int k,
                                 const bf16_t* A, const bf16_t* G, uint64_t seed, uint32_t layer,
-                                bool shared, bool accum, float* n_sq, void* ws, hipStream_t s) {
+                                bool shared, bool accum, float* n_sq, void* ws, hipStream_t s,
+                                const Marks& mk) {
   bf16_t* Pb = at<bf16_t>(ws, P.pb);
   bf16_t* Yb = at<bf16_t>(ws, P.yb);
   float* Zp = at<float>(ws, P.zp);
@@ -162,8 +175,10 @@ dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, i
   const int nS = shared ? 1 : B;
   const int64_t pbs = shared ? 0 : static_cast<int64_t>(kMfmaProbeCols) * p;
   DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, k, kMfmaProbeCols, Pb, s));
+  DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_mfma(G, B, T, p, Pb, pbs, Yb, s));
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
+  DP_TRY(mk.close(s));
   DP_TRY(launch_frob_partial(Zp, B, P.nsplit_d, kMfmaProbeCols, d, k, 1.0f / k, 0, 0.f, part,
                              P.nchunk, s));
   DP_TRY(launch_sum_parts(part, B, P.nchunk, n_sq, accum ? 1 : 0, s));
@@ -173,7 +188,8 @@ dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, i
 template <typename TIn>
 dp_status_t run_norm_generic_hpp(const NormPlan& P, int B, int T, int d, int p, const TIn* A,
                                  const TIn* G, uint64_t seed, uint32_t layer, bool shared,
-                                 bool accum, float* n_sq, void* ws, hipStream_t s) {
+                                 bool accum, float* n_sq, void* ws, hipStream_t s,
+                                 const Marks& mk) {
   const int S_ = P.s, R_ = P.r, K3 = P.k3;
   float* Pf = at<float>(ws, P.pf);
   float* P3 = at<float>(ws, P.p3);
@@ -186,6 +202,7 @@ dp_status_t run_norm_generic_hpp(const NormPlan& P, int B, int T, int d, int p, 
   const int64_t pbs = shared ? 0 : static_cast<int64_t>(K3) * p;
   DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, K3, K3, Pf, s));
   // pass 1: Z1 = A^T (G S)
+  DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_generic<TIn>(G, B, T, p, Pf, pbs, S_, Y, s));
   DP_TRY(launch_project_generic<TIn>(A, B, T, d, Y, S_, Z, s));
   // pass 2: X = G^T (A Z1) = O S
@@ -196,6 +213,7 @@ dp_status_t run_norm_generic_hpp(const NormPlan& P, int B, int T, int d, int p, 
   // pass 3: head + tail / r
   DP_TRY(launch_sketch_generic<TIn>(G, B, T, p, P3, static_cast<int64_t>(K3) * p, K3, Y, s));
   DP_TRY(launch_project_generic<TIn>(A, B, T, d, Y, K3, Z, s));
+  DP_TRY(mk.close(s));
   DP_TRY(launch_frob_partial(Z, B, 1, K3, d, S_, 1.0f, R_, 1.0f / R_, part, P.nchunk, s));
   DP_TRY(launch_sum_parts(part, B, P.nchunk, n_sq, accum ? 1 : 0, s));
   return DP_OK;
@@ -203,7 +221,7 @@ dp_status_t run_norm_generic_hpp(const NormPlan& P, int B, int T, int d, int p, 
 
 dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, const bf16_t* A,
                               const bf16_t* G, uint64_t seed, uint32_t layer, bool shared,
-                              bool accum, float* n_sq, void* ws, hipStream_t s) {
+                              bool accum, float* n_sq, void* ws, hipStream_t s, const Marks& mk) {
   const int S_ = P.s, R_ = P.r, K3 = P.k3;
   float* Pf = at<float>(ws, P.pf);
   float* P3 = at<float>(ws, P.p3);
@@ -223,6 +241,7 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
   DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, K3, K3, Pf, s));
   DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, S_, kMfmaProbeCols, Pb, s));
   // pass 1: Z1 = A^T (G S)
+  DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_mfma(G, B, T, p, Pb, pbs, Yb, s));
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
   DP_TRY(launch_sum_splits(Zp, B, P.nsplit_d, kMfmaProbeCols, d, nullptr, Z1b, s));
@@ -236,6 +255,7 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
   // pass 3
   DP_TRY(launch_sketch_mfma(G, B, T, p, P3b, pad_p, Yb, s));
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
+  DP_TRY(mk.close(s));
   DP_TRY(launch_frob_partial(Zp, B, P.nsplit_d, kMfmaProbeCols, d, S_, 1.0f, R_, 1.0f / R_, part,
                              P.nchunk, s));
   DP_TRY(launch_sum_parts(part, B, P.nchunk, n_sq, accum ? 1 : 0, s));
@@ -245,15 +265,18 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
 template <typename TIn>
 dp_status_t run_norm_exact(int method, const NormPlan& P, int B, int T, int d, int p,
                            const TIn* A, const TIn* G, bool accum, float* n_sq, void* ws,
-                           hipStream_t s) {
+                           hipStream_t s, const Marks& mk) {
   double* part = at<double>(ws, P.part);
   if (method == DP_NORM_GHOST) {
     int np = 0;
+    DP_TRY(mk.open(s));
     DP_TRY(launch_ghost_generic<TIn>(A, G, B, T, d, p, part, &np, s));
+    DP_TRY(mk.close(s));
     DP_TRY(launch_sum_parts(part, B, np, n_sq, accum ? 1 : 0, s));
     return DP_OK;
   }
   float* M = at<float>(ws, P.m);
+  DP_TRY(mk.open(s));
   if constexpr (sizeof(TIn) == 2) {
     if (P.mfma) {
       DP_TRY(launch_fgc_mfma(A, G, B, T, d, p, M, s));
@@ -263,6 +286,7 @@ dp_status_t run_norm_exact(int method, const NormPlan& P, int B, int T, int d, i
   } else {
     DP_TRY(launch_fgc_generic<TIn>(A, G, B, T, d, p, M, s));
   }
+  DP_TRY(mk.close(s));
   DP_TRY(launch_frob_partial(M, B, 1, p, d, p, 1.0f, 0, 0.f, part, P.nchunk, s));
   DP_TRY(launch_sum_parts(part, B, P.nchunk, n_sq, accum ? 1 : 0, s));
   return DP_OK;
@@ -318,9 +342,10 @@ size_t dp_norm_est_workspace(int method, int dtype, int B, int T, int d, int p, 
   return plan_norm(method, dtype, B, T, d, p, k).total;
 }
 
-dp_status_t dp_norm_est(int method, int dtype, int B, int T, int d, int p, int k, const void* A,
-                        const void* G, uint64_t seed, uint32_t layer, uint32_t flags, float* n_sq,
-                        void* ws, size_t ws_bytes, dp_stream_t stream) {
+static dp_status_t norm_est_impl(int method, int dtype, int B, int T, int d, int p, int k,
+                                 const void* A, const void* G, uint64_t seed, uint32_t layer,
+                                 uint32_t flags, float* n_sq, void* ws, size_t ws_bytes,
+                                 dp_stream_t stream, const Marks& mk) {
   if (!norm_args_ok(method, dtype, B, T, d, p, k)) return DP_ERR_INVALID_ARG;
   if ((flags & ~(DP_ACCUMULATE | DP_PROBE_SHARED)) != 0) return DP_ERR_INVALID_ARG;
   if (B == 0) return DP_OK;
@@ -340,17 +365,33 @@ dp_status_t dp_norm_est(int method, int dtype, int B, int T, int d, int p, int k
   const float* Gf = static_cast<const float*>(G);
   switch (method) {
     case DP_NORM_HUTCH:
-      if (P.mfma) return run_norm_mfma_hutch(P, B, T, d, p, k, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s);
-      return bf ? run_norm_generic_hutch<bf16_t>(P, B, T, d, p, k, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s)
-                : run_norm_generic_hutch<float>(P, B, T, d, p, k, Af, Gf, seed, layer, shared, accum, n_sq, ws, s);
+      if (P.mfma) return run_norm_mfma_hutch(P, B, T, d, p, k, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s, mk);
+      return bf ? run_norm_generic_hutch<bf16_t>(P, B, T, d, p, k, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s, mk)
+                : run_norm_generic_hutch<float>(P, B, T, d, p, k, Af, Gf, seed, layer, shared, accum, n_sq, ws, s, mk);
     case DP_NORM_HUTCHPP:
-      if (P.mfma) return run_norm_mfma_hpp(P, B, T, d, p, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s);
-      return bf ? run_norm_generic_hpp<bf16_t>(P, B, T, d, p, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s)
-                : run_norm_generic_hpp<float>(P, B, T, d, p, Af, Gf, seed, layer, shared, accum, n_sq, ws, s);
+      if (P.mfma) return run_norm_mfma_hpp(P, B, T, d, p, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s, mk);
+      return bf ? run_norm_generic_hpp<bf16_t>(P, B, T, d, p, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s, mk)
+                : run_norm_generic_hpp<float>(P, B, T, d, p, Af, Gf, seed, layer, shared, accum, n_sq, ws, s, mk);
     default:
-      return bf ? run_norm_exact<bf16_t>(method, P, B, T, d, p, Ab, Gb, accum, n_sq, ws, s)
-                : run_norm_exact<float>(method, P, B, T, d, p, Af, Gf, accum, n_sq, ws, s);
+      return bf ? run_norm_exact<bf16_t>(method, P, B, T, d, p, Ab, Gb, accum, n_sq, ws, s, mk)
+                : run_norm_exact<float>(method, P, B, T, d, p, Af, Gf, accum, n_sq, ws, s, mk);
   }
+}
+
+dp_status_t dp_norm_est(int method, int dtype, int B, int T, int d, int p, int k, const void* A,
+                        const void* G, uint64_t seed, uint32_t layer, uint32_t flags, float* n_sq,
+                        void* ws, size_t ws_bytes, dp_stream_t stream) {
+  return norm_est_impl(method, dtype, B, T, d, p, k, A, G, seed, layer, flags, n_sq, ws, ws_bytes,
+                       stream, Marks{});
+}
+
+dp_status_t dp_norm_est_timed(int method, int dtype, int B, int T, int d, int p, int k,
+                              const void* A, const void* G, uint64_t seed, uint32_t layer,
+                              uint32_t flags, float* n_sq, void* ws, size_t ws_bytes,
+                              dp_stream_t stream, void* ev_begin, void* ev_end) {
+  return norm_est_impl(method, dtype, B, T, d, p, k, A, G, seed, layer, flags, n_sq, ws, ws_bytes,
+                       stream,
+                       Marks{static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)});
 }
 
 size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p) {
@@ -358,9 +399,10 @@ size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p) {
   return plan_agg(dtype, B, T, d, p).total;
 }
 
-dp_status_t dp_clip_aggregate(int dtype, int B, int T, int d, int p, const void* A, const void* G,
-                              const float* n_sq, float C, float* c_out, uint32_t* status, float* S,
-                              void* ws, size_t ws_bytes, dp_stream_t stream) {
+static dp_status_t clip_aggregate_impl(int dtype, int B, int T, int d, int p, const void* A,
+                                       const void* G, const float* n_sq, float C, float* c_out,
+                                       uint32_t* status, float* S, void* ws, size_t ws_bytes,
+                                       dp_stream_t stream, const Marks& mk) {
   if (!agg_args_ok(dtype, B, T, d, p)) return DP_ERR_INVALID_ARG;
   if (!(C > 0.f) || !std::isfinite(C)) return DP_ERR_INVALID_ARG;
   if (S == nullptr || !aligned(S, 16)) return DP_ERR_INVALID_ARG;
@@ -380,14 +422,19 @@ dp_status_t dp_clip_aggregate(int dtype, int B, int T, int d, int p, const void*
     const bf16_t* Ab = static_cast<const bf16_t*>(A);
     const bf16_t* Gb = static_cast<const bf16_t*>(G);
     if (P.nsplit == 1) {
+      DP_TRY(mk.open(s));
       DP_TRY(launch_aggregate_mfma(Ab, Gb, B, T, d, p, c, order, count, 1, S, s));
+      DP_TRY(mk.close(s));
     } else {
       float* part = at<float>(ws, P.part);
+      DP_TRY(mk.open(s));
       DP_TRY(launch_aggregate_mfma(Ab, Gb, B, T, d, p, c, order, count, P.nsplit, part, s));
+      DP_TRY(mk.close(s));
       DP_TRY(launch_reduce_splits(part, P.nsplit, static_cast<int64_t>(p) * d, S, s));
     }
     return DP_OK;
   }
+  DP_TRY(mk.open(s));
   if (dtype == DP_BF16) {
     DP_TRY(launch_aggregate_generic<bf16_t>(static_cast<const bf16_t*>(A),
                                             static_cast<const bf16_t*>(G), B, T, d, p, c, S, s));
@@ -395,11 +442,29 @@ dp_status_t dp_clip_aggregate(int dtype, int B, int T, int d, int p, const void*
     DP_TRY(launch_aggregate_generic<float>(static_cast<const float*>(A),
                                            static_cast<const float*>(G), B, T, d, p, c, S, s));
   }
+  DP_TRY(mk.close(s));
   return DP_OK;
 }
 
-dp_status_t dp_noise_update(int d, int p, float* theta, const float* S, float sigma, float C,
-                            float eta, int B, uint64_t seed, uint32_t layer, dp_stream_t stream) {
+dp_status_t dp_clip_aggregate(int dtype, int B, int T, int d, int p, const void* A, const void* G,
+                              const float* n_sq, float C, float* c_out, uint32_t* status, float* S,
+                              void* ws, size_t ws_bytes, dp_stream_t stream) {
+  return clip_aggregate_impl(dtype, B, T, d, p, A, G, n_sq, C, c_out, status, S, ws, ws_bytes,
+                             stream, Marks{});
+}
+
+dp_status_t dp_clip_aggregate_timed(int dtype, int B, int T, int d, int p, const void* A,
+                                    const void* G, const float* n_sq, float C, float* c_out,
+                                    uint32_t* status, float* S, void* ws, size_t ws_bytes,
+                                    dp_stream_t stream, void* ev_begin, void* ev_end) {
+  return clip_aggregate_impl(dtype, B, T, d, p, A, G, n_sq, C, c_out, status, S, ws, ws_bytes,
+                             stream,
+                             Marks{static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)});
+}
+
+static dp_status_t noise_update_impl(int d, int p, float* theta, const float* S, float sigma,
+                                     float C, float eta, int B, uint64_t seed, uint32_t layer,
+                                     dp_stream_t stream, const Marks& mk) {
   if (d < 1 || p < 1 || B < 1) return DP_ERR_INVALID_ARG;
   if (!(sigma >= 0.f) || !std::isfinite(sigma) || !(C > 0.f) || !std::isfinite(C) ||
       !std::isfinite(eta))
@@ -412,9 +477,23 @@ dp_status_t dp_noise_update(int d, int p, float* theta, const float* S, float si
   if (t0 < s0 + bytes && s0 < t0 + bytes) return DP_ERR_INVALID_ARG;  // overlap
   const float sigmaC = sigma * C;
   const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
-  DP_TRY(launch_noise_update(theta, S, n, sigmaC, eta_over_B, seed, layer,
-                             static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DP_TRY(mk.open(s));
+  DP_TRY(launch_noise_update(theta, S, n, sigmaC, eta_over_B, seed, layer, s));
+  DP_TRY(mk.close(s));
   return DP_OK;
+}
+
+dp_status_t dp_noise_update(int d, int p, float* theta, const float* S, float sigma, float C,
+                            float eta, int B, uint64_t seed, uint32_t layer, dp_stream_t stream) {
+  return noise_update_impl(d, p, theta, S, sigma, C, eta, B, seed, layer, stream, Marks{});
+}
+
+dp_status_t dp_noise_update_timed(int d, int p, float* theta, const float* S, float sigma, float C,
+                                  float eta, int B, uint64_t seed, uint32_t layer,
+                                  dp_stream_t stream, void* ev_begin, void* ev_end) {
+  return noise_update_impl(d, p, theta, S, sigma, C, eta, B, seed, layer, stream,
+                           Marks{static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)});
 }
 
 dp_status_t dp_philox_u32(uint64_t seed, const uint32_t* ctr, uint32_t* out, size_t n,

@@ -4,13 +4,29 @@
 //               DP-SGDのアルゴリズム, step 4; randomized-clipping summary,
 //               section アルゴリズム的フロー, step 5)
 //   fgc         M_i[o][q]            = sum_t G_i[t][o] A_i[t][q]   (FGC baseline)
-// M = o (p), N = q (d), K = tokens.  Both operands are stored token-major, so
-// the contraction index is the strided one: each 8 x 8 block of 16-bit values
-// is transposed in registers on its way into LDS, where every column then
-// holds its 64 tokens contiguously and MFMA operands are single 16-byte reads.
+// M = o (p), N = q (d), K = tokens.
 //
-// Workgroup tile 256 x 256, four waves of 128 x 128 (8 x 8 blocks of
-// v_mfma_f32_16x16x32_bf16), 32 tokens per stage, two LDS stages.
+// Data path.  Both operands are stored token-major, so the contraction index
+// is the strided one.  Tiles of 32 tokens go from HBM straight into LDS with
+// global_load_lds (no registers, no VALU), in their natural [token][column]
+// layout; the MFMA operands then come out of LDS with ds_read_b64_tr_b16,
+// which transposes 16-bit values inside each group of 16 lanes: output lane i,
+// slot j receives element (i mod 4) of the 8 bytes that lane 4 j + i / 4 of the
+// group addressed.  Pointing lane 4 j + q of group g at token row 8 g + 2 j + h,
+// columns c0 + 4 q .. + 3, gives lane i the four tokens 8 g + h + {0,2,4,6} of
+// column c0 + i -- the v_mfma_f32_16x16x32_bf16 operand layout (lane i: row or
+// column i % 16, lane group g: 8 contraction values), two reads (h = 0, 1) per
+// operand.  Which token sits in which contraction slot is immaterial as long
+// as both operands agree.  One 16-byte DMA instruction fills two consecutive
+// 512-byte rows; each such row pair is followed by 32 bytes of padding, so the
+// four rows read by a 16-lane group (four different pairs) start 8 banks apart.
+//
+// Pipeline.  Workgroup tile 256 x 256, eight waves of 128 (M) x 64 (N), four
+// LDS stages of 32 tokens.  Each stage lives in its own __shared__ array so
+// that the compiler can see the in-flight LDS DMA does not alias the stage
+// being read; the loop is unrolled over the four arrays.  Synchronisation is
+// an explicit vmcnt wait for this wave's loads of the stage plus a bare
+// s_barrier (no fence that would drain the loads of later stages).
 //
 // Per-sample clip factors without a second accumulator: the active samples are
 // visited in ascending c, and the accumulator holds sum_{seen} (c_seg / c_cur)
@@ -22,45 +38,74 @@
 namespace dprc {
 
 constexpr int kGM = 256, kGN = 256, kGK = 32;
-// LDS: each operand column (an M or N index) holds its 32 tokens (64 B) in a
-// row of 80 B; every 8 rows get 64 B more, so that the eight lanes of one LDS
-// cycle hit distinct banks for both the transposing writes and the MFMA reads.
-constexpr int kLdsRow = 80;
-__host__ __device__ constexpr int lds_row_off(int r) { return r * kLdsRow + (r >> 3) * 64; }
-constexpr int kLdsSide = lds_row_off(kGM);       // one operand tile (256 rows)
-constexpr int kLdsStage = 2 * kLdsSide;          // both operands
-constexpr int kLdsBytes = 2 * kLdsStage;         // two stages
+constexpr int kWaves = 8;
+constexpr int kRowBytes = 512;                  // 256 bf16
+constexpr int kPairBytes = 2 * kRowBytes + 32;  // two rows + pad
+constexpr int kSideBytes = (kGK / 2) * kPairBytes;  // one operand, one stage
+constexpr int kStageBytes = 2 * kSideBytes;     // G tile then A tile
+constexpr int kNStage = 4;
+constexpr int kGroup = kNStage * kGK;           // tokens per unrolled loop trip
 
-__device__ __forceinline__ f32x4 mfma16g(u32x4 a, u32x4 b, f32x4 c) {
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_cvoid;
+
+__shared__ __attribute__((aligned(16))) unsigned char g_lds0[kStageBytes];
+__shared__ __attribute__((aligned(16))) unsigned char g_lds1[kStageBytes];
+__shared__ __attribute__((aligned(16))) unsigned char g_lds2[kStageBytes];
+__shared__ __attribute__((aligned(16))) unsigned char g_lds3[kStageBytes];
+
+// s_waitcnt immediate: vmcnt = N, expcnt and lgkmcnt unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ v4i16 tr_read(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+}
+
+// Four row pairs (each 64 lanes x 16 bytes = two 512-byte rows) from HBM into
+// LDS.  Issued as inline asm so that the compiler does not treat the DMA as an
+// LDS write it must drain before every later LDS read: the kernel counts these
+// loads itself (wait_vm) and orders the stages with s_barrier.  lds_addr is
+// the wave-uniform LDS byte address of the first pair (goes to m0).
+__device__ __forceinline__ void dma_pairs(const unsigned char* gsrc, uint32_t pair_step,
+                                          uint32_t lds_addr) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned char* gp = gsrc + i * pair_step;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gp), "s"(__builtin_amdgcn_readfirstlane(lds_addr + i * kPairBytes))
+                 : "memory", "m0");
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const unsigned char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(p)));
+}
+
+__device__ __forceinline__ f32x4 mfma_tr(v4i16 a0, v4i16 a1, v4i16 b0, v4i16 b1, f32x4 c) {
+  const v8i16 a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+  const v8i16 b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ u32x4 tcol(const u32x4 (&rows)[8], int c) {
-  u32x4 a;
-  const int w = c >> 1;
-  if ((c & 1) == 0) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) a[k] = (rows[2 * k][w] & 0xFFFFu) | (rows[2 * k + 1][w] << 16);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) a[k] = (rows[2 * k][w] >> 16) | (rows[2 * k + 1][w] & 0xFFFF0000u);
-  }
-  return a;
-}
-
-// MODE 0: clipped aggregation with split-K over the sorted active samples.
+// MODE 0: clipped aggregation, split-K over the active samples in ascending c.
 // MODE 1: FGC, z = sample, whole sample, no scaling.
 template <int MODE>
-__global__ void __launch_bounds__(256, 1) k_gemm_tokens(
+__global__ void __launch_bounds__(512, 1) k_gemm_tokens(
     const bf16_t* __restrict__ A, const bf16_t* __restrict__ G, int T, int d, int p,
     const float* __restrict__ cvec, const int* __restrict__ order, const int* __restrict__ count,
     int64_t split_tokens, float* __restrict__ out) {
-  extern __shared__ __align__(16) unsigned char lds[];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int m = lane & 15, g = lane >> 4;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int o0 = blockIdx.x * kGM;
   const int q0 = blockIdx.y * kGN;
   const int z = blockIdx.z;
@@ -75,160 +120,157 @@ __global__ void __launch_bounds__(256, 1) k_gemm_tokens(
     kv0 = 0;
     kv1 = T;
   }
-  float* dst = out + static_cast<int64_t>(z) * p * d;
+  const int nstage = kv1 > kv0 ? static_cast<int>((kv1 - kv0) / kGK) : 0;
 
-  // Global loads: waves 0-1 fetch the G tile, waves 2-3 the A tile; each thread
-  // one 8 x 8 unit (tokens 8 tg .. +7, columns 8 cg .. +7) per stage.
-  const int side = tid >> 7;
-  const int u = tid & 127;
-  const int tg = u & 3, cg = u >> 2;
+  // ---- LDS DMA: wave w fills row pairs (w & 3) * 4 .. + 3 (token rows
+  // 8 (w & 3) .. + 7) of side w >> 2 (0: G, 1: A); lanes 0-31 take the even
+  // row of a pair, lanes 32-63 the odd one, 16 bytes (8 columns) each.
+  const int side = wave >> 2;
+  const int pair0 = (wave & 3) * 4;
   const bf16_t* src = side == 0 ? G : A;
   const int ld = side == 0 ? p : d;
-  const int c0 = side == 0 ? o0 : q0;
-  uint32_t off[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) off[e] = static_cast<uint32_t>(((tg * 8 + e) * ld + cg * 8) * 2);
-  unsigned char* lds_w = lds + side * kLdsSide + lds_row_off(cg * 8) + tg * 16;
+  const int col0 = side == 0 ? o0 : q0;
+  const uint32_t lane_src =
+      static_cast<uint32_t>(((2 * pair0 + (lane >> 5)) * ld + col0 + (lane & 31) * 8) * 2);
+  const uint32_t pair_step = static_cast<uint32_t>(2 * ld * 2);
+  const int dst_off = side * kSideBytes + pair0 * kPairBytes;
 
-  u32x4 rows[8];
-  // Segment bookkeeping: stage kv lies in segment `seg` (a whole sample) at
-  // token offset `seg_off`; T is a multiple of the stage size.
   int64_t ld_seg = kv0 / T;
   int ld_off = static_cast<int>(kv0 - ld_seg * T);
-  auto gload = [&]() {
-    const int64_t sample = MODE == 0 ? static_cast<int64_t>(order[ld_seg]) : static_cast<int64_t>(z);
+  auto issue = [&](unsigned char* stage_lds) {
+    const int64_t sample =
+        MODE == 0 ? static_cast<int64_t>(order[ld_seg]) : static_cast<int64_t>(z);
     const unsigned char* base =
-        reinterpret_cast<const unsigned char*>(src + (sample * T + ld_off) * ld + c0);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) rows[e] = *reinterpret_cast<const u32x4*>(base + off[e]);
+        reinterpret_cast<const unsigned char*>(src + (sample * T + ld_off) * ld) + lane_src;
+    dma_pairs(base, pair_step, lds_addr_of(stage_lds) + dst_off);
     ld_off += kGK;
     if (ld_off == T) {
       ld_off = 0;
       ++ld_seg;
     }
   };
-  auto lstore = [&](int stage) {
-    unsigned char* w = lds_w + stage * kLdsStage;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(w + c * kLdsRow) = tcol(rows, c);
-  };
 
-  f32x4 acc[8][8];
+  // ---- MFMA operand reads.  Wave tile: rows wm*128 .. +128 of M, cols
+  // wn*64 .. +64 of N.  Lane 4 j + q of group g addresses token row
+  // 8 g + 2 j + h (pair 4 g + j, row h of the pair), columns c0 + 4 q .. + 3.
+  const int wm = wave >> 2, wn = wave & 3;
+  const int g = lane >> 4, li = lane & 15;
+  const int rd_lane = (4 * g + (li >> 2)) * kPairBytes + (li & 3) * 8;
+  const int rd_a = rd_lane + wm * 128 * 2;
+  const int rd_b = kSideBytes + rd_lane + wn * 64 * 2;
+
+  f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Operand reads: lane (m, g) takes row m of each 16-row block, tokens 8 g .. +7.
-  const int rd_lane = lds_row_off(m) + g * 16;
-  auto compute = [&](int stage) {
-    const unsigned char* sg = lds + stage * kLdsStage + lds_row_off(wm * 128) + rd_lane;
-    const unsigned char* sa = lds + stage * kLdsStage + kLdsSide + lds_row_off(wn * 128) + rd_lane;
-    u32x4 av[8];
+  auto compute = [&](const unsigned char* st) {
+    v4i16 a[8][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) av[i] = *reinterpret_cast<const u32x4*>(sg + lds_row_off(16 * i));
-    u32x4 bcur = *reinterpret_cast<const u32x4*>(sa);
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 bnext = bcur;
-      if (j < 7) bnext = *reinterpret_cast<const u32x4*>(sa + lds_row_off(16 * (j + 1)));
+      for (int h = 0; h < 2; ++h) a[i][h] = tr_read(st + rd_a + h * kRowBytes + i * 32);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][j] = mfma16g(av[i], bcur, acc[i][j]);
-      bcur = bnext;
+    for (int j = 0; j < 4; ++j) {
+      const v4i16 b0 = tr_read(st + rd_b + j * 32);
+      const v4i16 b1 = tr_read(st + rd_b + kRowBytes + j * 32);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i][j] = mfma_tr(a[i][0], a[i][1], b0, b1, acc[i][j]);
     }
+  };
+
+  unsigned char* L0 = g_lds0;
+  unsigned char* L1 = g_lds1;
+  unsigned char* L2 = g_lds2;
+  unsigned char* L3 = g_lds3;
+
+  // Prologue: stages 0..2 in flight.
+  if (nstage > 0) issue(L0);
+  if (nstage > 1) issue(L1);
+  if (nstage > 2) issue(L2);
+
+  // Stage s: wait for this wave's loads of s (loads of s+1, s+2 may stay in
+  // flight), barrier, refill the slot freed by stage s-1 with s+3, compute.
+  auto stage = [&](int s, const unsigned char* cur, unsigned char* refill) {
+    const int ahead = nstage - 1 - s;
+    if (ahead >= 2)
+      wait_vm<8>();
+    else if (ahead == 1)
+      wait_vm<4>();
+    else
+      wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    if (s + 3 < nstage) issue(refill);
+    compute(cur);
   };
 
   float cur_c = 1.f;
   int64_t cur_seg = -1;
-  int64_t seg = kv0 / T;
-  int seg_off = static_cast<int>(kv0 - seg * T);
-  if (kv0 < kv1) {
-    gload();
-    lstore(0);
-    __syncthreads();
-    int stage = 0;
-    for (int64_t kv = kv0; kv < kv1; kv += kGK) {
-      const bool more = kv + kGK < kv1;
-      if (more) gload();
-      if (MODE == 0 && seg != cur_seg) {
+  for (int s = 0; s < nstage; s += kNStage) {
+    if (MODE == 0) {
+      // A group of four stages never straddles two samples (T % 128 == 0).
+      const int64_t seg = (kv0 + static_cast<int64_t>(s) * kGK) / T;
+      if (seg != cur_seg) {
         const float c_new = cvec[order[seg]];
         if (cur_seg >= 0) {
           const float ratio = cur_c / c_new;
-          // In-place rescale, one 4-register block at a time; the empty asm
-          // pins every block back to accumulator registers right away.
 #pragma unroll
           for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              acc[i][j] *= ratio;
-              asm volatile("" : "+a"(acc[i][j]));
-            }
+            for (int j = 0; j < 4; ++j) acc[i][j] *= ratio;
         }
         cur_c = c_new;
         cur_seg = seg;
       }
-      compute(stage);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
-      if (more) lstore(stage ^ 1);
-      __syncthreads();
-      stage ^= 1;
-      seg_off += kGK;
-      if (seg_off == T) {
-        seg_off = 0;
-        ++seg;
-      }
     }
+    stage(s, L0, L3);
+    if (s + 1 < nstage) stage(s + 1, L1, L0);
+    if (s + 2 < nstage) stage(s + 2, L2, L1);
+    if (s + 3 < nstage) stage(s + 3, L3, L2);
   }
   const float fin = (MODE == 0 && cur_seg >= 0) ? cur_c : 1.f;
 
-  float* tile = dst + static_cast<int64_t>(o0 + wm * 128) * d + q0 + wn * 128;
-  const uint32_t lane_off = static_cast<uint32_t>((4 * g * d + m) * 4);
+  // Epilogue: lane (n = lane % 16, g) holds rows 4 g + r of column n of each block.
+  float* dst = out + static_cast<int64_t>(z) * p * d;
+  float* tile = dst + static_cast<int64_t>(o0 + wm * 128) * d + q0 + wn * 64;
+  const uint32_t lane_off = static_cast<uint32_t>((4 * g * d + li) * 4);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      unsigned char* rowp = reinterpret_cast<unsigned char*>(tile + static_cast<int64_t>(i * 16 + r) * d);
+      unsigned char* rowp =
+          reinterpret_cast<unsigned char*>(tile + static_cast<int64_t>(i * 16 + r) * d);
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 4; ++j)
         *reinterpret_cast<float*>(rowp + lane_off + j * 64) = acc[i][j][r] * fin;
     }
 }
 
 bool mfma_gemm_ok(int T, int d, int p) {
-  return T > 0 && T % kGK == 0 && d % kGN == 0 && p % kGM == 0;
+  return T > 0 && T % kGroup == 0 && d % kGN == 0 && p % kGM == 0;
 }
 
-// Split the token range so that there are about 256 workgroups.
+// Split the token range so that there are about 256 workgroups; each split is
+// a whole number of 128-token groups.
 int mfma_gemm_splits(int B, int T, int d, int p) {
   const int64_t tiles = static_cast<int64_t>(p / kGM) * (d / kGN);
   int64_t want = (256 + tiles - 1) / (tiles > 0 ? tiles : 1);
-  const int64_t steps = static_cast<int64_t>(B) * T / kGK;
-  if (want > steps) want = steps;
+  const int64_t groups = static_cast<int64_t>(B) * T / kGroup;
+  if (want > groups) want = groups;
   if (want < 1) want = 1;
   return static_cast<int>(want);
-}
-
-// The 88 KiB LDS budget needs an explicit opt-in above the default limit.
-template <int MODE>
-static hipError_t set_lds_attr() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_tokens<MODE>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
 }
 
 hipError_t launch_aggregate_mfma(const bf16_t* A, const bf16_t* G, int B, int T, int d, int p,
                                  const float* c, const int* order, const int* count, int nsplit,
                                  float* part, hipStream_t s) {
   if (!mfma_gemm_ok(T, d, p) || nsplit < 1) return hipErrorInvalidValue;
-  hipError_t e = set_lds_attr<0>();
-  if (e != hipSuccess) return e;
   const int64_t total = static_cast<int64_t>(B) * T;
   int64_t per = (total + nsplit - 1) / nsplit;
-  per = (per + kGK - 1) / kGK * kGK;
-  hipLaunchKernelGGL(k_gemm_tokens<0>, dim3(p / kGM, d / kGN, nsplit), dim3(256), kLdsBytes, s, A,
-                     G, T, d, p, c, order, count, per, part);
+  per = (per + kGroup - 1) / kGroup * kGroup;
+  hipLaunchKernelGGL(k_gemm_tokens<0>, dim3(p / kGM, d / kGN, nsplit), dim3(64 * kWaves), 0, s,
+                     A, G, T, d, p, c, order, count, per, part);
   return hipGetLastError();
 }
 
@@ -236,10 +278,8 @@ hipError_t launch_fgc_mfma(const bf16_t* A, const bf16_t* G, int B, int T, int d
                            hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (!mfma_gemm_ok(T, d, p)) return hipErrorInvalidValue;
-  hipError_t e = set_lds_attr<1>();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gemm_tokens<1>, dim3(p / kGM, d / kGN, B), dim3(256), kLdsBytes, s, A, G, T,
-                     d, p, nullptr, nullptr, nullptr, static_cast<int64_t>(T), M);
+  hipLaunchKernelGGL(k_gemm_tokens<1>, dim3(p / kGM, d / kGN, B), dim3(64 * kWaves), 0, s, A, G,
+                     T, d, p, nullptr, nullptr, nullptr, static_cast<int64_t>(T), M);
   return hipGetLastError();
 }
 

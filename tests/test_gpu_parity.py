@@ -150,7 +150,8 @@ AGG_CASES = [
     ("ragged_f32", "f32", 3, 37, 50, 70),
     ("ragged_bf16", "bf16", 3, 37, 50, 70),
     ("tiles_bf16", "bf16", 3, 256, 256, 512),
-    ("tiles_bf16_b5", "bf16", 5, 96, 512, 256),
+    ("tiles_bf16_b5", "bf16", 5, 128, 512, 256),
+    ("split_spans_samples_bf16", "bf16", 8, 128, 2048, 2048),
 ]
 
 
@@ -178,7 +179,8 @@ def test_clip_aggregate_parity(dev, case):
     assert es <= (TOL_F32 if dtype == "f32" else 1e-4)
 
 
-@pytest.mark.parametrize("dtype,shape", [("f32", (4, 33, 20, 30)), ("bf16", (4, 64, 256, 256))])
+@pytest.mark.parametrize("dtype,shape", [("f32", (4, 33, 20, 30)), ("bf16", (4, 64, 256, 256)),
+                                         ("bf16", (4, 128, 256, 256))])
 def test_clip_nonfinite_dropped_and_flagged(dev, dtype, shape):
     B, T, d, p = shape
     A, G = linear_inputs(B, T, d, p, dtype, "llama_logu", seed=8)
@@ -196,7 +198,7 @@ def test_clip_nonfinite_dropped_and_flagged(dev, dtype, shape):
 
 
 def test_clip_all_dropped_gives_zero_sum(dev):
-    A, G = linear_inputs(2, 64, 256, 256, "bf16", "llama_logu", seed=9)
+    A, G = linear_inputs(2, 128, 256, 256, "bf16", "llama_logu", seed=9)
     n = torch.tensor([float("nan"), float("nan")], dtype=torch.float32, device=dev)
     S = torch.full((256, 256), 7.0, dtype=torch.float32, device=dev)
     dp.dp_clip_aggregate(A.to(dev), G.to(dev), n, 1.0, S)
