@@ -49,7 +49,7 @@ struct NormPlan {
   int nsplit_d = 1, nsplit_p = 1, nchunk = 1, nparts = 0;
   // offsets (bytes) into the workspace; unused ones stay 0
   size_t pf = 0, pb = 0, y = 0, yb = 0, z = 0, zp = 0, z1b = 0, v = 0, xp = 0, x = 0, p3 = 0,
-         p3b = 0, m = 0, part = 0;
+         p3b = 0, m = 0, part = 0, orth = 0;
   size_t total = 0;
 };
 
@@ -93,6 +93,7 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
              mfma_project_ok(T, d) && mfma_project_ok(T, p);
     P.pf = cv.take(Bz * P.k3 * p * f4);
     P.p3 = cv.take(Bz * P.k3 * p * f4);
+    P.orth = cv.take(hpp_orth_scratch_bytes(B, p, P.s, P.r));
     if (P.mfma) {
       P.nsplit_d = mfma_project_splits(B, T, d);
       P.nsplit_p = mfma_project_splits(B, T, p);
@@ -209,7 +210,7 @@ dp_status_t run_norm_generic_hpp(const NormPlan& P, int B, int T, int d, int p, 
   DP_TRY(launch_sketch_generic<TIn>(A, B, T, d, Z, static_cast<int64_t>(S_) * d, S_, V, s));
   DP_TRY(launch_project_generic<TIn>(G, B, T, p, V, S_, X, s));
   // Q = orth(X), W' = (I - Q Q^T) W
-  DP_TRY(launch_hpp_orth(X, S_, Pf, pbs, K3, B, p, S_, R_, P3, s));
+  DP_TRY(launch_hpp_orth(X, S_, Pf, pbs, K3, B, p, S_, R_, P3, at<double>(ws, P.orth), s));
   // pass 3: head + tail / r
   DP_TRY(launch_sketch_generic<TIn>(G, B, T, p, P3, static_cast<int64_t>(K3) * p, K3, Y, s));
   DP_TRY(launch_project_generic<TIn>(A, B, T, d, Y, K3, Z, s));
@@ -250,7 +251,8 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
   DP_TRY(launch_project_mfma(G, B, T, p, Yb, P.nsplit_p, Xp, s));
   DP_TRY(launch_sum_splits(Xp, B, P.nsplit_p, kMfmaProbeCols, p, X, nullptr, s));
   // Q = orth(X), W' = (I - Q Q^T) W
-  DP_TRY(launch_hpp_orth(X, kMfmaProbeCols, Pf, pfs, K3, B, p, S_, R_, P3, s));
+  DP_TRY(launch_hpp_orth(X, kMfmaProbeCols, Pf, pfs, K3, B, p, S_, R_, P3, at<double>(ws, P.orth),
+                         s));
   DP_TRY(launch_to_bf16_pad(P3, B, K3, kMfmaProbeCols, p, P3b, s));
   // pass 3
   DP_TRY(launch_sketch_mfma(G, B, T, p, P3b, pad_p, Yb, s));

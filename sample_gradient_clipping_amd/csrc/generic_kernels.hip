@@ -318,87 +318,183 @@ hipError_t launch_reduce_splits(const float* part, int nsplit, int64_t n, float*
 
 // ---------------------------------------------------------------------------
 // Hutch++ (summary, section 中核メカニズム, item 2): orthonormal basis Q of the
-// sketch X = O S (classical Gram-Schmidt applied twice; any stable QR spans
-// the same subspace, and the estimate depends only on that span), then the
-// deflated tail probes W' = W - Q (Q^T W).  One block per sample.  Each thread
-// owns the elements e = tid (mod blockDim) of every vector, so no thread ever
-// reads global data another thread wrote; dot products reduce through LDS.
+// sketch X = O S, then the deflated tail probes W' = W - Q (Q^T W).  Any
+// stable QR spans the same subspace and the estimate depends only on that
+// span; this one is CholeskyQR2 (Gram matrix and Cholesky factor in fp64,
+// applied twice).  A pivot that vanishes relative to the largest one (rank
+// deficiency) zeroes its column of Q; the remaining columns still span
+// range(X) and Q Q^T is the orthogonal projector onto it.  The vectors of
+// length p are rows here (X^T's columns).  Work is split over chunks of
+// kOrthChunk elements of p so that every step has many blocks:
+//   k_orth_dots    partial inner products of row sets over one chunk;
+//   k_orth_apply   sums the partials in a fixed order, factors the Gram
+//                  (redundantly per block; tiny) and writes Q = rows R^-1;
+//   k_orth_deflate W' = W - Q H from the summed partial products H = Q W^T.
 // ---------------------------------------------------------------------------
 constexpr int kOrthMaxCols = 32;
+constexpr int kOrthChunk = 256;
 
-__device__ void block_dots(double* h, int nd, double* red /*[16][kOrthMaxCols]*/) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int i = 0; i < nd; ++i) {
-    const double v = wave_sum_d(h[i]);
-    if (lane == 0) red[wid * kOrthMaxCols + i] = v;
-  }
+int orth_chunks(int p) { return (p + kOrthChunk - 1) / kOrthChunk; }
+
+// part[b][chunk][i * nv + j] = sum_{e in chunk} U[i][e] V[j][e], fp64.
+__global__ void __launch_bounds__(kOrthChunk) k_orth_dots(
+    const float* __restrict__ U, int64_t u_bstride, int nu, const float* __restrict__ V,
+    int64_t v_bstride, int nv, int p, double* __restrict__ part) {
+  __shared__ float su[kOrthMaxCols][kOrthChunk];
+  __shared__ float sv[kOrthMaxCols][kOrthChunk];
+  const int b = blockIdx.y, chunk = blockIdx.x;
+  const int e0 = chunk * kOrthChunk;
+  const int e = e0 + threadIdx.x;
+  const float* ub = U + b * u_bstride;
+  const float* vb = V + b * v_bstride;
+  for (int i = 0; i < nu; ++i) su[i][threadIdx.x] = e < p ? ub[static_cast<int64_t>(i) * p + e] : 0.f;
+  for (int j = 0; j < nv; ++j) sv[j][threadIdx.x] = e < p ? vb[static_cast<int64_t>(j) * p + e] : 0.f;
   __syncthreads();
-  for (int i = 0; i < nd; ++i) {
-    double t = 0.0;
-    for (int w = 0; w < nw; ++w) t += red[w * kOrthMaxCols + i];
-    h[i] = t;
+  const int npairs = nu * nv;
+  double* out = part + (static_cast<int64_t>(b) * gridDim.x + chunk) * npairs;
+  for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) {
+    const int i = pi / nv, j = pi % nv;
+    double acc = 0.0;
+    for (int t = 0; t < kOrthChunk; ++t)
+      acc += static_cast<double>(su[i][t]) * static_cast<double>(sv[j][t]);
+    out[pi] = acc;
   }
-  __syncthreads();
 }
 
-__global__ void __launch_bounds__(256) k_hpp_orth(const float* __restrict__ X, int xrows,
-                                                  const float* __restrict__ Pw,
-                                                  int64_t pw_bstride, int wrows, int p, int s_cols,
-                                                  int r_cols, float* __restrict__ out) {
-  __shared__ double red[16 * kOrthMaxCols];
-  const int b = blockIdx.x;
-  const float* xb = X + static_cast<int64_t>(b) * xrows * p;
-  const float* wb = Pw + b * pw_bstride;
-  float* ob = out + static_cast<int64_t>(b) * (s_cols + r_cols) * p;
-  double h[kOrthMaxCols];
-  for (int j = 0; j < s_cols; ++j) {
-    float* qj = ob + static_cast<int64_t>(j) * p;
-    for (int e = threadIdx.x; e < p; e += blockDim.x) qj[e] = xb[static_cast<int64_t>(j) * p + e];
-    for (int pass = 0; pass < 2 && j > 0; ++pass) {
-      for (int i = 0; i < j; ++i) h[i] = 0.0;
-      for (int e = threadIdx.x; e < p; e += blockDim.x) {
-        const double v = qj[e];
-        for (int i = 0; i < j; ++i) h[i] += static_cast<double>(ob[static_cast<int64_t>(i) * p + e]) * v;
-      }
-      block_dots(h, j, red);
-      for (int e = threadIdx.x; e < p; e += blockDim.x) {
-        double v = qj[e];
-        for (int i = 0; i < j; ++i) v -= h[i] * static_cast<double>(ob[static_cast<int64_t>(i) * p + e]);
-        qj[e] = static_cast<float>(v);
-      }
-    }
-    h[0] = 0.0;
-    for (int e = threadIdx.x; e < p; e += blockDim.x) h[0] += static_cast<double>(qj[e]) * qj[e];
-    block_dots(h, 1, red);
-    const double nrm = sqrt(h[0]);
-    const float inv = nrm > 0.0 ? static_cast<float>(1.0 / nrm) : 0.f;
-    for (int e = threadIdx.x; e < p; e += blockDim.x) qj[e] *= inv;
+// Sum of the chunk partials of one sample (fixed order), into LDS.
+__device__ void sum_chunks(const double* part_b, int nchunk, int npairs, double* dst) {
+  for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) {
+    double acc = 0.0;
+    for (int c = 0; c < nchunk; ++c) acc += part_b[static_cast<int64_t>(c) * npairs + pi];
+    dst[pi] = acc;
   }
-  for (int t = 0; t < r_cols; ++t) {
-    const float* w = wb + static_cast<int64_t>(s_cols + t) * p;
-    float* wo = ob + static_cast<int64_t>(s_cols + t) * p;
-    for (int i = 0; i < s_cols; ++i) h[i] = 0.0;
-    for (int e = threadIdx.x; e < p; e += blockDim.x) {
-      const double v = w[e];
-      for (int i = 0; i < s_cols; ++i) h[i] += static_cast<double>(ob[static_cast<int64_t>(i) * p + e]) * v;
+}
+
+// Cholesky of the s x s Gram (dense, gram[i * s + j]) and the inverse of its
+// factor, fp64, single thread; vanishing pivots zero their column.
+__device__ void chol_inverse(const double* gram, int s, double (*R)[kOrthMaxCols],
+                             double (*Rinv)[kOrthMaxCols]) {
+  auto g = [&](int i, int j) { return gram[(i < j ? i : j) * s + (i < j ? j : i)]; };
+  double dmax = 0.0;
+  for (int i = 0; i < s; ++i) dmax = fmax(dmax, g(i, i));
+  const double tiny = dmax * 1e-24;
+  uint32_t dead = 0;  // bit j: column j has no pivot
+  for (int j = 0; j < s; ++j) {
+    double djj = g(j, j);
+    for (int k = 0; k < j; ++k) djj -= R[k][j] * R[k][j];
+    const bool dj = !(djj > tiny);
+    if (dj) dead |= 1u << j;
+    const double rjj = dj ? 0.0 : sqrt(djj);
+    R[j][j] = rjj;
+    for (int c = j + 1; c < s; ++c) {
+      double v = g(j, c);
+      for (int k = 0; k < j; ++k) v -= R[k][j] * R[k][c];
+      R[j][c] = dj ? 0.0 : v / rjj;
     }
-    block_dots(h, s_cols, red);
-    for (int e = threadIdx.x; e < p; e += blockDim.x) {
-      double v = w[e];
-      for (int i = 0; i < s_cols; ++i) v -= h[i] * static_cast<double>(ob[static_cast<int64_t>(i) * p + e]);
-      wo[e] = static_cast<float>(v);
+    for (int c = 0; c < j; ++c) R[j][c] = 0.0;
+  }
+  // Rinv: upper triangular, R Rinv = I on the live columns; dead columns zero.
+  for (int j = 0; j < s; ++j) {
+    for (int i = 0; i < s; ++i) Rinv[i][j] = 0.0;
+    if (dead >> j & 1u) continue;
+    for (int i = j; i >= 0; --i) {
+      if (dead >> i & 1u) continue;
+      double v = i == j ? 1.0 : 0.0;
+      for (int k = i + 1; k <= j; ++k) v -= R[i][k] * Rinv[k][j];
+      Rinv[i][j] = v / R[i][i];
     }
   }
-  (void)wrows;
+}
+
+// Q[j][e] = sum_{i <= j} X[i][e] Rinv[i][j], Rinv from the Gram partials of X.
+__global__ void __launch_bounds__(kOrthChunk) k_orth_apply(
+    const float* __restrict__ Xr, int64_t x_bstride, int s, int p,
+    const double* __restrict__ part, int nchunk, float* __restrict__ Q, int64_t q_bstride) {
+  __shared__ double gram[kOrthMaxCols * kOrthMaxCols];
+  __shared__ double R[kOrthMaxCols][kOrthMaxCols];
+  __shared__ double Rinv[kOrthMaxCols][kOrthMaxCols];
+  const int b = blockIdx.y;
+  sum_chunks(part + static_cast<int64_t>(b) * nchunk * s * s, nchunk, s * s, gram);
+  __syncthreads();
+  if (threadIdx.x == 0) chol_inverse(gram, s, R, Rinv);
+  __syncthreads();
+  const int e = blockIdx.x * kOrthChunk + threadIdx.x;
+  if (e >= p) return;
+  const float* xb = Xr + b * x_bstride;
+  float* qb = Q + b * q_bstride;
+  float x[kOrthMaxCols];
+#pragma unroll
+  for (int i = 0; i < kOrthMaxCols; ++i) x[i] = i < s ? xb[static_cast<int64_t>(i) * p + e] : 0.f;
+#pragma unroll
+  for (int j = 0; j < kOrthMaxCols; ++j) {
+    if (j < s) {
+      double q = 0.0;
+#pragma unroll
+      for (int i = 0; i <= j; ++i) q += static_cast<double>(x[i]) * Rinv[i][j];
+      qb[static_cast<int64_t>(j) * p + e] = static_cast<float>(q);
+    }
+  }
+}
+
+// W'[t][e] = W[t][e] - sum_i H[i][t] Q[i][e], H = summed partials of Q W^T.
+__global__ void __launch_bounds__(kOrthChunk) k_orth_deflate(
+    const float* __restrict__ Q, int64_t q_bstride, int s, const float* __restrict__ W,
+    int64_t w_bstride, int r, int p, const double* __restrict__ part, int nchunk,
+    float* __restrict__ Wout, int64_t wo_bstride) {
+  __shared__ double H[kOrthMaxCols * kOrthMaxCols];
+  const int b = blockIdx.y;
+  sum_chunks(part + static_cast<int64_t>(b) * nchunk * s * r, nchunk, s * r, H);
+  __syncthreads();
+  const int e = blockIdx.x * kOrthChunk + threadIdx.x;
+  if (e >= p) return;
+  const float* qb = Q + b * q_bstride;
+  const float* wb = W + b * w_bstride;
+  float* ob = Wout + b * wo_bstride;
+  float q[kOrthMaxCols];
+#pragma unroll
+  for (int i = 0; i < kOrthMaxCols; ++i) q[i] = i < s ? qb[static_cast<int64_t>(i) * p + e] : 0.f;
+  for (int t = 0; t < r; ++t) {
+    double v = wb[static_cast<int64_t>(t) * p + e];
+#pragma unroll
+    for (int i = 0; i < kOrthMaxCols; ++i)
+      if (i < s) v -= H[i * r + t] * static_cast<double>(q[i]);
+    ob[static_cast<int64_t>(t) * p + e] = static_cast<float>(v);
+  }
+}
+
+size_t hpp_orth_scratch_bytes(int B, int p, int s, int r) {
+  const int npairs = s * s > s * r ? s * s : s * r;
+  return static_cast<size_t>(B) * orth_chunks(p) * (npairs > 0 ? npairs : 1) * sizeof(double);
 }
 
 hipError_t launch_hpp_orth(const float* X, int xrows, const float* Pw, int64_t pw_bstride,
                            int wrows, int B, int p, int s_cols, int r_cols, float* out,
-                           hipStream_t s) {
+                           double* scratch, hipStream_t st) {
+  (void)wrows;
   if (B <= 0) return hipSuccess;
-  if (s_cols > kOrthMaxCols) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_hpp_orth, dim3(B), dim3(256), 0, s, X, xrows, Pw, pw_bstride, wrows, p,
-                     s_cols, r_cols, out);
+  if (s_cols < 1 || s_cols > kOrthMaxCols || r_cols > kOrthMaxCols) return hipErrorInvalidValue;
+  const int nch = orth_chunks(p);
+  const int64_t xs = static_cast<int64_t>(xrows) * p;
+  const int64_t os = static_cast<int64_t>(s_cols + r_cols) * p;
+  const dim3 grid(nch, B);
+  // pass 1: Q1 = X R1^-1
+  hipLaunchKernelGGL(k_orth_dots, grid, dim3(kOrthChunk), 0, st, X, xs, s_cols, X, xs, s_cols, p,
+                     scratch);
+  hipLaunchKernelGGL(k_orth_apply, grid, dim3(kOrthChunk), 0, st, X, xs, s_cols, p, scratch, nch,
+                     out, os);
+  // pass 2: Q = Q1 R2^-1 (in place: each thread reads its element before writing it)
+  hipLaunchKernelGGL(k_orth_dots, grid, dim3(kOrthChunk), 0, st, out, os, s_cols, out, os, s_cols,
+                     p, scratch);
+  hipLaunchKernelGGL(k_orth_apply, grid, dim3(kOrthChunk), 0, st, out, os, s_cols, p, scratch, nch,
+                     out, os);
+  if (r_cols > 0) {
+    const float* W = Pw + static_cast<int64_t>(s_cols) * p;  // tail probe rows s .. s+r-1
+    hipLaunchKernelGGL(k_orth_dots, grid, dim3(kOrthChunk), 0, st, out, os, s_cols, W, pw_bstride,
+                       r_cols, p, scratch);
+    hipLaunchKernelGGL(k_orth_deflate, grid, dim3(kOrthChunk), 0, st, out, os, s_cols, W,
+                       pw_bstride, r_cols, p, scratch, nch, out + static_cast<int64_t>(s_cols) * p,
+                       os);
+  }
   return hipGetLastError();
 }
 

@@ -64,9 +64,11 @@ hipError_t launch_reduce_splits(const float* part, int nsplit, int64_t n, float*
 // Hutch++ probe for the last pass: rows 0..s-1 = orthonormal basis of the s
 // rows of X (CGS2), rows s..s+r-1 = W - Q Q^T W.  X [B][xrows][p] (rows 0..s-1
 // used), W rows s..s+r-1 of Pw [.][wrows][p].  out fp32 [B][s+r][p].
+// `scratch`: hpp_orth_scratch_bytes() of device memory for the chunk partials.
 hipError_t launch_hpp_orth(const float* X, int xrows, const float* Pw, int64_t pw_bstride,
                            int wrows, int B, int p, int s_cols, int r_cols, float* out,
-                           hipStream_t s);
+                           double* scratch, hipStream_t s);
+size_t hpp_orth_scratch_bytes(int B, int p, int s, int r);
 // out[b][j][x] = bf16(in[b][j][x]) for j < rows_in, 0 for rows_in <= j < rows_out.
 hipError_t launch_to_bf16_pad(const float* in, int B, int rows_in, int rows_out, int W,
                               bf16_t* out, hipStream_t s);
