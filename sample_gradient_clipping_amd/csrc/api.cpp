@@ -113,7 +113,8 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
       P.nchunk = frob_chunks(static_cast<int64_t>(P.k3) * d);
     }
   } else if (method == DP_NORM_GHOST) {
-    P.nparts = ghost_generic_nparts(T);
+    P.mfma = bf && mfma_ghost_ok(T, d, p);
+    P.nparts = P.mfma ? mfma_ghost_nparts(T) : ghost_generic_nparts(T);
     P.nchunk = P.nparts;
   } else {  // FGC
     P.mfma = bf && mfma_gemm_ok(T, d, p);
@@ -272,7 +273,16 @@ dp_status_t run_norm_exact(int method, const NormPlan& P, int B, int T, int d, i
   if (method == DP_NORM_GHOST) {
     int np = 0;
     DP_TRY(mk.open(s));
-    DP_TRY(launch_ghost_generic<TIn>(A, G, B, T, d, p, part, &np, s));
+    if constexpr (sizeof(TIn) == 2) {
+      if (P.mfma) {
+        np = P.nparts;
+        DP_TRY(launch_ghost_mfma(A, G, B, T, d, p, part, s));
+      } else {
+        DP_TRY(launch_ghost_generic<TIn>(A, G, B, T, d, p, part, &np, s));
+      }
+    } else {
+      DP_TRY(launch_ghost_generic<TIn>(A, G, B, T, d, p, part, &np, s));
+    }
     DP_TRY(mk.close(s));
     DP_TRY(launch_sum_parts(part, B, np, n_sq, accum ? 1 : 0, s));
     return DP_OK;

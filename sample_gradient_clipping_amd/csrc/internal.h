@@ -85,6 +85,12 @@ hipError_t launch_sketch_mfma(const bf16_t* X, int B, int T, int W, const bf16_t
 hipError_t launch_project_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* Y, int nsplit,
                                float* Zp, hipStream_t s);
 
+// Ghost norm per sample from 128 x 128 Gram tile pairs: part[b][pair] (fp64).
+bool mfma_ghost_ok(int T, int d, int p);
+int mfma_ghost_nparts(int T);
+hipError_t launch_ghost_mfma(const bf16_t* A, const bf16_t* G, int B, int T, int d, int p,
+                             double* part, hipStream_t s);
+
 bool mfma_gemm_ok(int T, int d, int p);
 int mfma_gemm_splits(int B, int T, int d, int p);
 // Clipped sum over the active samples order[0..*count) (ascending c):
