@@ -35,11 +35,44 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="cfg2_attn_proj")
+    ap.add_argument("--workload", default="attn_proj_b8_t4096_d2048")
     ap.add_argument("--method", default=None, help="override the workload's estimator")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = {"aggregate": "sample_gradient_clipping_amd/csrc/mfma_gemm.hip",
+                  "norm_est": "sample_gradient_clipping_amd/csrc/mfma_hutch.hip",
+                  "noise_update": "sample_gradient_clipping_amd/csrc/rng_kernels.hip"}
+
+
+def source_hash(rel):
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on this workload with the kernel source as it is now; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k_, v = line.split("=", 1)
+            kv[k_.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -66,7 +99,7 @@ def make_inputs(wl, copies, dev):
     return out
 
 
-def cpu_baseline(wl, method):
+def cpu_baseline(wl, method, target_s=12.0):
     """The oracle (plain fp64 numpy) on a bounded sample of the workload."""
     import numpy as np
     import oracle
@@ -81,21 +114,33 @@ def cpu_baseline(wl, method):
     if len(layers) > 7:  # a layer stack: time block 0, extrapolate to all blocks
         scale_blocks = len(layers) // 7
         layers = layers[:7]
-    Bs = 1 if wl.tokens * max(l.d + l.p for l in layers) > (1 << 27) else wl.B
-    if wl.name.startswith("cfg2"):
-        Bs = 2
-    data = []
-    for l in layers:
-        A, G = linear_inputs(Bs, wl.T, l.d, l.p, wl.dtype, wl.recipe, wl.data_seed, l.layer_id)
-        data.append((l.layer_id, A, G, np.zeros((l.p, l.d))))
-    t0 = time.perf_counter()
-    oracle.dp_step(data, method, wl.k, wl.C, wl.sigma, wl.eta, wl.method_seed, wl.noise_seed)
-    t = time.perf_counter() - t0
-    t_step = t * scale_blocks
+
+    def run(Bs, reps=1):
+        data = []
+        for l in layers:
+            A, G = linear_inputs(Bs, wl.T, l.d, l.p, wl.dtype, wl.recipe, wl.data_seed, l.layer_id)
+            data.append((l.layer_id, A, G, np.zeros((l.p, l.d))))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.dp_step(data, method, wl.k, wl.C, wl.sigma, wl.eta, wl.method_seed,
+                           wl.noise_seed)
+        return time.perf_counter() - t0
+
+    # one sample first; then as many samples (and, if the whole batch is quicker
+    # than that, repeated steps) as fill about `target_s` of CPU work
+    Bs, reps, t = 1, 1, run(1)
+    if t < target_s and wl.B > 1:
+        Bs = int(min(wl.B, max(2, target_s // max(t, 1e-3))))
+        t = run(Bs)
+        if t < 0.5 * target_s:
+            reps = int(min(20, -(-target_s // t)))
+            t = run(Bs, reps)
+    t_step = t * scale_blocks / reps
     sample = (f"{Bs} of {wl.B} samples x {wl.T} tokens, {len(layers)} of {len(wl.layers)} linear "
               f"layers" + (f", time x{scale_blocks} (extrapolated to all blocks)"
                            if scale_blocks > 1 else "")
-              + f"; full oracle step (norms, clip, aggregation, noise+update) in {t:.2f} s")
+              + f"; {reps} full oracle step(s) (norms, clip, aggregation, noise+update) "
+                f"in {t:.2f} s")
     return {"value": Bs * wl.T / t_step, "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle", "sample": sample}
 
@@ -111,6 +156,15 @@ def main():
     from sample_gradient_clipping_amd import binding as dp
     from sample_gradient_clipping_amd import roofline as rf
     from sample_gradient_clipping_amd.configs import workloads
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device copies")
+        return
 
     wl = workloads()[args.workload]
     method = args.method or wl.method
@@ -218,13 +272,19 @@ def main():
         kv["share_of_step"] = (kv["ms_per_launch"] * L) / ms_step
     dom_name = max(kernels, key=lambda k_: kernels[k_]["share_of_step"])
     dom = kernels[dom_name]
+    traffic = measured_traffic(dom_name, wl.name)
     if dom["bound"] == "hbm":
         roof = {"bound": "hbm", "achieved": dom["GBps"], "peak": rf.PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": dom["GBps"] / rf.PEAK_HBM_GBPS, "traffic": None}
+                "frac": dom["GBps"] / rf.PEAK_HBM_GBPS, "traffic": traffic}
     else:
         roof = {"bound": "mfma", "achieved": dom["TFLOPs"], "peak": rf.PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": dom["TFLOPs"] / rf.PEAK_BF16_TFLOPS, "traffic": None}
+                "unit": "TFLOP/s", "frac": dom["TFLOPs"] / rf.PEAK_BF16_TFLOPS, "traffic": traffic}
     roof["kernel"] = dom["name"]
+    roof["algorithmic_per_launch"] = (
+        {"bytes": b_norm / L} if dom["bound"] == "hbm" and dom_name == "norm_est" else
+        {"bytes": b_noise / L} if dom_name == "noise_update" else
+        {"flops": (f_agg if dom_name == "aggregate" else f_norm) / L,
+         "bytes": (b_agg if dom_name == "aggregate" else b_norm) / L})
     for kname, kv in kernels.items():
         log(f"[bench] {kname:13s} {kv['ms_per_launch'] * 1e3:9.2f} us/launch  "
             f"{kv['GBps']:8.1f} GB/s  {kv.get('TFLOPs', 0):8.1f} TF/s  frac {kv['frac']:.3f}  "

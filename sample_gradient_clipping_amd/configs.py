@@ -61,38 +61,38 @@ def llama_1b_stack(blocks=16, hidden=2048, kv=512, ffn=8192):
 def workloads():
     """The five configurations by short name."""
     w = {}
-    w["cfg1_f32_tiny"] = Workload(
-        "cfg1_f32_tiny", B=4, T=64, dtype="f32",
+    w["tiny_f32_b4_t64"] = Workload(
+        "tiny_f32_b4_t64", B=4, T=64, dtype="f32",
         layers=[Layer("linear", 0, 64, 64)], method="hutch", k=8,
         C=1.0, sigma=1.0, eta=0.1, recipe="unit_u0.1_3",
         data_seed=1001, method_seed=2001, noise_seed=3001,
         baselines=("fgc", "ghost"))
-    w["cfg2_attn_proj"] = Workload(
-        "cfg2_attn_proj", B=8, T=4096, dtype="bf16",
+    w["attn_proj_b8_t4096_d2048"] = Workload(
+        "attn_proj_b8_t4096_d2048", B=8, T=4096, dtype="bf16",
         layers=[Layer("q_proj", 0, 2048, 2048)], method="hutch", k=32,
         C=1.0, sigma=1.0, eta=1e-4, recipe="llama_logu",
         data_seed=1002, method_seed=2002, noise_seed=3002,
         baselines=("ghost", "fgc"))
-    w["cfg3_mlp_up"] = Workload(
-        "cfg3_mlp_up", B=8, T=4096, dtype="bf16",
+    w["mlp_up_b8_t4096_d2048_p8192"] = Workload(
+        "mlp_up_b8_t4096_d2048_p8192", B=8, T=4096, dtype="bf16",
         layers=[Layer("up_proj", 0, 2048, 8192)], method="hutchpp", k=32,
         C=1.0, sigma=1.0, eta=1e-4, recipe="llama_logu",
         data_seed=1003, method_seed=2003, noise_seed=3003,
         baselines=("hutch", "ghost"))
-    w["cfg3_mlp_down"] = Workload(
-        "cfg3_mlp_down", B=8, T=4096, dtype="bf16",
+    w["mlp_down_b8_t4096_d8192_p2048"] = Workload(
+        "mlp_down_b8_t4096_d8192_p2048", B=8, T=4096, dtype="bf16",
         layers=[Layer("down_proj", 0, 8192, 2048)], method="hutchpp", k=32,
         C=1.0, sigma=1.0, eta=1e-4, recipe="llama_logu",
         data_seed=1013, method_seed=2013, noise_seed=3013,
         baselines=("hutch", "ghost"))
-    w["cfg4_long_ctx"] = Workload(
-        "cfg4_long_ctx", B=2, T=16384, dtype="bf16",
+    w["long_ctx_b2_t16384_d2048_p8192"] = Workload(
+        "long_ctx_b2_t16384_d2048_p8192", B=2, T=16384, dtype="bf16",
         layers=[Layer("up_proj", 0, 2048, 8192)], method="hutch", k=32,
         C=1.0, sigma=1.0, eta=1e-4, recipe="llama_logu",
         data_seed=1004, method_seed=2004, noise_seed=3004,
         baselines=("ghost", "fgc"))
-    w["cfg5_llama_stack"] = Workload(
-        "cfg5_llama_stack", B=8, T=4096, dtype="bf16",
+    w["llama1b_stack_b8_t4096"] = Workload(
+        "llama1b_stack_b8_t4096", B=8, T=4096, dtype="bf16",
         layers=llama_1b_stack(), method="hutch", k=32,
         C=1.0, sigma=1.0, eta=1e-4, recipe="llama_logu",
         data_seed=1005, method_seed=2005, noise_seed=3005)

@@ -85,24 +85,24 @@ def _step_and_check(dev, wl, layers, method, rows_per_layer=24, baselines=()):
             assert e <= 2e-2
 
 
-def test_cfg2_attention_projection(dev):
-    wl = WL["cfg2_attn_proj"]
+def test_attention_projection(dev):
+    wl = WL["attn_proj_b8_t4096_d2048"]
     _step_and_check(dev, wl, wl.layers, "hutch", baselines=("ghost", "fgc"))
 
 
-@pytest.mark.parametrize("name", ["cfg3_mlp_up", "cfg3_mlp_down"])
-def test_cfg3_mlp_hutchpp(dev, name):
+@pytest.mark.parametrize("name", ["mlp_up_b8_t4096_d2048_p8192", "mlp_down_b8_t4096_d8192_p2048"])
+def test_mlp_hutchpp(dev, name):
     wl = WL[name]
     _step_and_check(dev, wl, wl.layers, "hutchpp")
 
 
-def test_cfg4_long_context(dev):
-    wl = WL["cfg4_long_ctx"]
+def test_long_context(dev):
+    wl = WL["long_ctx_b2_t16384_d2048_p8192"]
     _step_and_check(dev, wl, wl.layers, "hutch", rows_per_layer=8, baselines=("ghost",))
 
 
-def test_cfg5_stack_layer_shapes(dev):
-    wl = WL["cfg5_llama_stack"]
+def test_llama_stack_layer_shapes(dev):
+    wl = WL["llama1b_stack_b8_t4096"]
     seen, layers = set(), []
     for l in wl.layers:  # one layer of each distinct shape: q, k, gate, down
         if (l.d, l.p) not in seen:

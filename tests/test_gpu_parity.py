@@ -74,7 +74,7 @@ def test_noise_normals(dev, offset, n):
 # ---------------------------------------------------------------------------
 NORM_CASES = [
     # (name, dtype, B, T, d, p, k)
-    ("cfg1_f32", "f32", 4, 64, 64, 64, 8),
+    ("tiny_f32", "f32", 4, 64, 64, 64, 8),
     ("ragged_f32", "f32", 3, 37, 50, 70, 5),
     ("ragged_bf16", "bf16", 3, 37, 50, 70, 5),
     ("tiles_bf16", "bf16", 3, 256, 256, 512, 32),
@@ -146,7 +146,7 @@ def test_norm_deterministic(dev):
 # clip + aggregation
 # ---------------------------------------------------------------------------
 AGG_CASES = [
-    ("cfg1_f32", "f32", 4, 64, 64, 64),
+    ("tiny_f32", "f32", 4, 64, 64, 64),
     ("ragged_f32", "f32", 3, 37, 50, 70),
     ("ragged_bf16", "bf16", 3, 37, 50, 70),
     ("tiles_bf16", "bf16", 3, 256, 256, 512),
