@@ -96,6 +96,25 @@ __device__ __forceinline__ f32x4 mfma_tr(v4i16 a0, v4i16 a1, v4i16 b0, v4i16 b1,
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Workgroup -> (o tile, q tile, split).  Consecutive workgroups go to the
+// eight XCDs in turn, each with its own L2; the logical work list is dealt out
+// so that every XCD gets a contiguous run of it, and the list is ordered in
+// groups of four o tiles (q outer, o inner), so that a run of 32 workgroups
+// covers a 4 x 8 block of tiles of one split: 12 distinct operand panels per
+// XCD instead of up to 33 with the plain row-major order.
+__device__ __forceinline__ void tile_of(int w, int to, int tq, int n, int& ot, int& qt, int& z) {
+  constexpr int kXcd = 8, kGroupM = 4;
+  const int l = (n % kXcd == 0) ? (w % kXcd) * (n / kXcd) + w / kXcd : w;
+  const int tiles = to * tq;
+  z = l / tiles;
+  const int t = l - z * tiles;
+  const int grp = t / (kGroupM * tq);
+  const int r = t - grp * kGroupM * tq;
+  const int gm = to - grp * kGroupM < kGroupM ? to - grp * kGroupM : kGroupM;
+  qt = r / gm;
+  ot = grp * kGroupM + (r - qt * gm);
+}
+
 // MODE 0: clipped aggregation, split-K over the active samples in ascending c.
 // MODE 1: FGC, z = sample, whole sample, no scaling.
 template <int MODE>
@@ -106,9 +125,10 @@ __global__ void __launch_bounds__(512, 1) k_gemm_tokens(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int o0 = blockIdx.x * kGM;
-  const int q0 = blockIdx.y * kGN;
-  const int z = blockIdx.z;
+  int ot, qt, z;
+  tile_of(blockIdx.x, p / kGM, d / kGN, gridDim.x, ot, qt, z);
+  const int o0 = ot * kGM;
+  const int q0 = qt * kGN;
 
   // Token range of this workgroup, as positions kv in the visiting order.
   int64_t kv0, kv1;
@@ -269,7 +289,7 @@ hipError_t launch_aggregate_mfma(const bf16_t* A, const bf16_t* G, int B, int T,
   const int64_t total = static_cast<int64_t>(B) * T;
   int64_t per = (total + nsplit - 1) / nsplit;
   per = (per + kGroup - 1) / kGroup * kGroup;
-  hipLaunchKernelGGL(k_gemm_tokens<0>, dim3(p / kGM, d / kGN, nsplit), dim3(64 * kWaves), 0, s,
+  hipLaunchKernelGGL(k_gemm_tokens<0>, dim3((p / kGM) * (d / kGN) * nsplit), dim3(64 * kWaves), 0, s,
                      A, G, T, d, p, c, order, count, per, part);
   return hipGetLastError();
 }
@@ -278,7 +298,7 @@ hipError_t launch_fgc_mfma(const bf16_t* A, const bf16_t* G, int B, int T, int d
                            hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (!mfma_gemm_ok(T, d, p)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_gemm_tokens<1>, dim3(p / kGM, d / kGN, B), dim3(64 * kWaves), 0, s, A, G,
+  hipLaunchKernelGGL(k_gemm_tokens<1>, dim3((p / kGM) * (d / kGN) * B), dim3(64 * kWaves), 0, s, A, G,
                      T, d, p, nullptr, nullptr, nullptr, static_cast<int64_t>(T), M);
   return hipGetLastError();
 }
