@@ -241,6 +241,80 @@ __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// Finish (randomized-clipping summary, section 中核メカニズム, item 1: the
+// estimate is the weighted squared Frobenius norm of Z = sum of the token
+// splits).  Block (chunk, b) streams kFrobPer float4 of sample b's [32][W]
+// rows, summing the splits in order (eight loads in flight per thread), and
+// writes its fp64 partial; the last block of the sample to finish adds the
+// partials in chunk order.  part and ctr are shared between blocks that may
+// sit on different XCDs (separate L2s): they are accessed with device-scope
+// atomics, and a vmcnt wait orders the partial before the counter.
+// ---------------------------------------------------------------------------
+constexpr int kFrobPer = 512;
+
+__global__ void __launch_bounds__(256) k_frob_finish(const float* __restrict__ Zp, int nsplit, int W,
+                                                     int n0, float w0, int n1, float w1,
+                                                     double* part, uint32_t* ctr,
+                                                     float* __restrict__ n_sq, int accumulate) {
+  __shared__ double red[16];
+  const int b = blockIdx.y, chunk = blockIdx.x, nchunk = gridDim.x;
+  const int E4 = kMfmaProbeCols * W / 4;
+  const float4* zb = reinterpret_cast<const float4*>(Zp) + static_cast<int64_t>(b) * nsplit * E4;
+  const int u1 = (chunk + 1) * kFrobPer < E4 ? (chunk + 1) * kFrobPer : E4;
+  double acc = 0.0;
+  for (int u = chunk * kFrobPer + threadIdx.x; u < u1; u += blockDim.x) {
+    const int j = (4 * u) / W;
+    const float w = j < n0 ? w0 : (j < n0 + n1 ? w1 : 0.f);
+    if (w == 0.f) continue;
+    float4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int sp = s0 + i < nsplit ? s0 + i : nsplit - 1;
+        v[i] = zb[static_cast<int64_t>(sp) * E4 + u];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (s0 + i < nsplit) {
+          z.x += v[i].x;
+          z.y += v[i].y;
+          z.z += v[i].z;
+          z.w += v[i].w;
+        }
+    }
+    acc += static_cast<double>(w) *
+           (static_cast<double>(z.x) * z.x + static_cast<double>(z.y) * z.y +
+            static_cast<double>(z.z) * z.z + static_cast<double>(z.w) * z.w);
+  }
+  acc = block_sum_d(acc, red);
+  if (threadIdx.x == 0) {
+    double* pb = part + static_cast<int64_t>(b) * nchunk;
+    __hip_atomic_store(pb + chunk, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (__hip_atomic_fetch_add(ctr + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        static_cast<uint32_t>(nchunk - 1)) {
+      double t = 0.0;
+      for (int i = 0; i < nchunk; ++i)
+        t += __hip_atomic_load(pb + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      n_sq[b] = static_cast<float>(accumulate ? static_cast<double>(n_sq[b]) + t : t);
+    }
+  }
+}
+
+int frob_finish_chunks(int W) { return (kMfmaProbeCols * W / 4 + kFrobPer - 1) / kFrobPer; }
+
+hipError_t launch_frob_finish(const float* Zp, int B, int nsplit, int W, int n0, float w0, int n1,
+                              float w1, double* part, uint32_t* ctr, float* n_sq, int accumulate,
+                              hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  if (W % 4 != 0 || nsplit < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_frob_finish, dim3(frob_finish_chunks(W), B), dim3(256), 0, s, Zp, nsplit,
+                     W, n0, w0, n1, w1, part, ctr, n_sq, accumulate);
+  return hipGetLastError();
+}
+
 bool mfma_project_ok(int T, int W) { return T > 0 && T % (4 * kProjK) == 0 && W % kProjQ == 0; }
 
 // Token splits: about 1024 workgroups in all, each split a multiple of 128
