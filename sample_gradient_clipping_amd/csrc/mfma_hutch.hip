@@ -247,7 +247,7 @@ __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__
 // splits).  Block (chunk, b) streams kFrobPer float4 of sample b's [32][W]
 // rows, summing the splits in order (eight loads in flight per thread), and
 // writes its fp64 partial; the last block of the sample to finish adds the
-// partials in chunk order.  part and ctr are shared between blocks that may
+// partials (a fixed-shape block reduction).  part and ctr are shared between blocks that may
 // sit on different XCDs (separate L2s): they are accessed with device-scope
 // atomics, and a vmcnt wait orders the partial before the counter.
 // ---------------------------------------------------------------------------
@@ -258,6 +258,7 @@ __global__ void __launch_bounds__(256) k_frob_finish(const float* __restrict__ Z
                                                      double* part, uint32_t* ctr,
                                                      float* __restrict__ n_sq, int accumulate) {
   __shared__ double red[16];
+  __shared__ int s_last;
   const int b = blockIdx.y, chunk = blockIdx.x, nchunk = gridDim.x;
   const int E4 = kMfmaProbeCols * W / 4;
   const float4* zb = reinterpret_cast<const float4*>(Zp) + static_cast<int64_t>(b) * nsplit * E4;
@@ -289,18 +290,23 @@ __global__ void __launch_bounds__(256) k_frob_finish(const float* __restrict__ Z
             static_cast<double>(z.z) * z.z + static_cast<double>(z.w) * z.w);
   }
   acc = block_sum_d(acc, red);
+  double* pb = part + static_cast<int64_t>(b) * nchunk;
   if (threadIdx.x == 0) {
-    double* pb = part + static_cast<int64_t>(b) * nchunk;
     __hip_atomic_store(pb + chunk, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (__hip_atomic_fetch_add(ctr + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        static_cast<uint32_t>(nchunk - 1)) {
-      double t = 0.0;
-      for (int i = 0; i < nchunk; ++i)
-        t += __hip_atomic_load(pb + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      n_sq[b] = static_cast<float>(accumulate ? static_cast<double>(n_sq[b]) + t : t);
-    }
+    s_last = __hip_atomic_fetch_add(ctr + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             static_cast<uint32_t>(nchunk - 1);
   }
+  __syncthreads();
+  if (!s_last) return;
+  // the last block: all threads load the chunk partials at once, then a
+  // fixed-shape block reduction
+  double t = 0.0;
+  for (int i = threadIdx.x; i < nchunk; i += blockDim.x)
+    t += __hip_atomic_load(pb + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  t = block_sum_d(t, red);
+  if (threadIdx.x == 0)
+    n_sq[b] = static_cast<float>(accumulate ? static_cast<double>(n_sq[b]) + t : t);
 }
 
 int frob_finish_chunks(int W) { return (kMfmaProbeCols * W / 4 + kFrobPer - 1) / kFrobPer; }
@@ -317,11 +323,12 @@ hipError_t launch_frob_finish(const float* Zp, int B, int nsplit, int W, int n0,
 
 bool mfma_project_ok(int T, int W) { return T > 0 && T % (4 * kProjK) == 0 && W % kProjQ == 0; }
 
-// Token splits: about 1024 workgroups in all, each split a multiple of 128
+// Token splits: about 256 workgroups in all (fewer splits mean fewer fp32
+// partials to write and re-read; measured best), each split a multiple of 128
 // tokens dividing T.
 int mfma_project_splits(int B, int T, int W) {
   const int64_t base = static_cast<int64_t>(B) * (W / kProjQ);
-  int want = static_cast<int>((1024 + base - 1) / (base > 0 ? base : 1));
+  int want = static_cast<int>((256 + base - 1) / (base > 0 ? base : 1));
   const int maxs = T / (4 * kProjK);
   if (want > maxs) want = maxs;
   if (want < 1) want = 1;
