@@ -78,10 +78,15 @@ __device__ __forceinline__ void dma_pairs(const unsigned char* gsrc, uint32_t pa
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const unsigned char* gp = gsrc + i * pair_step;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gp), "s"(__builtin_amdgcn_readfirstlane(lds_addr + i * kPairBytes))
-                 : "memory", "m0");
+    // m0 carries the LDS address; it is saved and restored around the load
+    // (the compiler reserves m0 and must find it unchanged).
+    uint32_t m0_saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(m0_saved)
+        : "v"(gp), "s"(__builtin_amdgcn_readfirstlane(lds_addr + i * kPairBytes))
+        : "memory");
   }
 }
 
