@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--method", default=None, help="override the workload's estimator")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused", action="store_true",
+                    help="aggregate and update with two calls (S materialised) instead of one")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -179,11 +181,13 @@ def main():
 
     L = len(wl.layers)
     n = torch.zeros(wl.B, dtype=torch.float32, device=dev)
-    S = [torch.empty(l.p, l.d, dtype=torch.float32, device=dev) for l in wl.layers]
+    S = ([torch.empty(l.p, l.d, dtype=torch.float32, device=dev) for l in wl.layers]
+         if args.unfused else None)
     theta = [torch.zeros(l.p, l.d, dtype=torch.float32, device=dev) for l in wl.layers]
     ws_n = max(dp.dp_norm_est_workspace(method, wl.dtype, wl.B, wl.T, l.d, l.p, wl.k)
                for l in wl.layers)
-    ws_a = max(dp.dp_clip_aggregate_workspace(wl.dtype, wl.B, wl.T, l.d, l.p) for l in wl.layers)
+    ws_a = max(dp.dp_clip_aggregate_update_workspace(wl.dtype, wl.B, wl.T, l.d, l.p)
+               for l in wl.layers)
     ws_norm = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
     ws_agg = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev)
 
@@ -205,11 +209,17 @@ def main():
                            events=None if evs is None else (evs[li][0], evs[li][1]))
         for li, l in enumerate(wl.layers):
             A, G = cp[li]
-            dp.dp_clip_aggregate(A, G, n, wl.C, S[li], ws=ws_agg,
-                                 events=None if evs is None else (evs[li][2], evs[li][3]))
-            dp.dp_noise_update(theta[li], S[li], wl.sigma, wl.C, wl.eta, wl.B,
-                               wl.noise_seed + it, l.layer_id,
-                               events=None if evs is None else (evs[li][4], evs[li][5]))
+            if args.unfused:  # clipped sum to S, then noise + update: two calls
+                dp.dp_clip_aggregate(A, G, n, wl.C, S[li], ws=ws_agg,
+                                     events=None if evs is None else (evs[li][2], evs[li][3]))
+                dp.dp_noise_update(theta[li], S[li], wl.sigma, wl.C, wl.eta, wl.B,
+                                   wl.noise_seed + it, l.layer_id,
+                                   events=None if evs is None else (evs[li][4], evs[li][5]))
+            else:  # one call: clip, clipped sum, noise, update (S not stored)
+                dp.dp_clip_aggregate_update(
+                    A, G, n, wl.C, wl.sigma, wl.eta, wl.noise_seed + it, l.layer_id, theta[li],
+                    ws=ws_agg, events=None if evs is None else ((evs[li][2], evs[li][3]),
+                                                                (evs[li][4], evs[li][5])))
 
     for it in range(W):
         step(it, None)
@@ -263,7 +273,9 @@ def main():
                      "GBps": b_norm / s_norm / 1e9, "TFLOPs": f_norm / s_norm / 1e12},
         "aggregate": {"name": "clipped-sum contraction", "ms_per_launch": t_agg / launches,
                       "bound": "mfma", "GBps": b_agg / s_agg / 1e9, "TFLOPs": f_agg / s_agg / 1e12},
-        "noise_update": {"name": "Philox noise + SGD update", "ms_per_launch": t_noise / launches,
+        "noise_update": {"name": "Philox noise + SGD update" + (
+                             "" if args.unfused else " (summing the contraction's token splits)"),
+                         "ms_per_launch": t_noise / launches,
                          "bound": "hbm", "GBps": b_noise / s_noise / 1e9},
     }
     for kname, kv in kernels.items():

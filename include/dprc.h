@@ -147,6 +147,29 @@ dp_status_t dp_noise_update(int d, int p, float *theta, const float *S, float si
                             float C, float eta, int B, uint64_t seed, uint32_t layer,
                             dp_stream_t stream);
 
+/* Bytes of workspace dp_clip_aggregate_update needs, or (size_t)-1 if invalid. */
+size_t dp_clip_aggregate_update_workspace(int dtype, int B, int T, int d, int p);
+
+/*
+ * Steps 4-5 for one layer in one call: the clip factors and clipped sum of
+ * dp_clip_aggregate, then the noise and update of dp_noise_update (same seed,
+ * layer and B), i.e. theta <- theta - (eta / B) (sum_i c_i G_i^T A_i + sigma C xi)
+ * (summary, section アルゴリズム的フロー, step 5; glossary steps 3-5).  The
+ * result is bit-identical to dp_clip_aggregate followed by dp_noise_update;
+ * the clipped sum is formed inside the update pass instead of being written
+ * and read back (one launch and 8 bytes per parameter fewer when the sum is
+ * split over token ranges).
+ *  B >= 1 (it is also the |B| of the update); the other arguments as in the
+ *  two calls.  S may be NULL (then the clipped sum is not stored); theta and S
+ *  must not overlap.
+ *  ws      device workspace of ws_bytes >= dp_clip_aggregate_update_workspace(...).
+ */
+dp_status_t dp_clip_aggregate_update(int dtype, int B, int T, int d, int p, const void *A,
+                                     const void *G, const float *n_sq, float C, float sigma,
+                                     float eta, uint64_t seed, uint32_t layer, float *theta,
+                                     float *S, float *c_out, uint32_t *status, void *ws,
+                                     size_t ws_bytes, dp_stream_t stream);
+
 /* ---- timed variants: the same calls, plus live kernel timing ----
  * Identical to the call without "_timed", and additionally record the two
  * hipEvent_t handles ev_begin / ev_end (either may be NULL) on `stream`
@@ -168,6 +191,16 @@ dp_status_t dp_clip_aggregate_timed(int dtype, int B, int T, int d, int p, const
 dp_status_t dp_noise_update_timed(int d, int p, float *theta, const float *S, float sigma,
                                   float C, float eta, int B, uint64_t seed, uint32_t layer,
                                   dp_stream_t stream, void *ev_begin, void *ev_end);
+/* dp_clip_aggregate_update with two event pairs: around the clipped-sum
+ * contraction and around the (split-summing) noise + update kernel. */
+dp_status_t dp_clip_aggregate_update_timed(int dtype, int B, int T, int d, int p, const void *A,
+                                           const void *G, const float *n_sq, float C,
+                                           float sigma, float eta, uint64_t seed, uint32_t layer,
+                                           float *theta, float *S, float *c_out,
+                                           uint32_t *status, void *ws, size_t ws_bytes,
+                                           dp_stream_t stream, void *ev_agg_begin,
+                                           void *ev_agg_end, void *ev_upd_begin,
+                                           void *ev_upd_end);
 
 /* ---- test hooks: expose the random streams for bit-level parity checks ---- */
 

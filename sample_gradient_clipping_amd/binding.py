@@ -68,6 +68,13 @@ def load_library():
     L.dp_clip_aggregate_timed.restype = c_int
     L.dp_noise_update_timed.argtypes = L.dp_noise_update.argtypes + [c_p, c_p]
     L.dp_noise_update_timed.restype = c_int
+    L.dp_clip_aggregate_update_workspace.argtypes = [c_int] * 5
+    L.dp_clip_aggregate_update_workspace.restype = c_sz
+    L.dp_clip_aggregate_update.argtypes = ([c_int] * 5 + [c_p, c_p, c_p, c_f, c_f, c_f, c_u64, c_u32]
+                                           + [c_p, c_p, c_p, c_p, c_p, c_sz, c_p])
+    L.dp_clip_aggregate_update.restype = c_int
+    L.dp_clip_aggregate_update_timed.argtypes = L.dp_clip_aggregate_update.argtypes + [c_p] * 4
+    L.dp_clip_aggregate_update_timed.restype = c_int
     L.dp_philox_u32.argtypes = [c_u64, c_p, c_p, c_sz, c_p]
     L.dp_philox_u32.restype = c_int
     L.dp_probe_fill.argtypes = [c_u64, c_u32, c_u32, c_int, c_int, c_p, c_p]
@@ -188,6 +195,36 @@ def dp_clip_aggregate(A, G, n_sq, C, S, c_out=None, status=None, ws=None, stream
         st = L.dp_clip_aggregate_timed(*args, _event(events[0]), _event(events[1]))
     _check(st, "dp_clip_aggregate")
     return S
+
+
+def dp_clip_aggregate_update_workspace(dtype, B, T, d, p):
+    code = dtype if isinstance(dtype, int) else {"f32": DP_F32, "bf16": DP_BF16}[dtype]
+    n = load_library().dp_clip_aggregate_update_workspace(code, B, T, d, p)
+    return None if n == _SIZE_INVALID else n
+
+
+def dp_clip_aggregate_update(A, G, n_sq, C, sigma, eta, seed, layer, theta, S=None, c_out=None,
+                             status=None, ws=None, stream=None, events=None):
+    """Clip factors, clipped sum, noise and update of theta [p][d] in one call
+    (|B| = A.shape[0]); S, if given, receives the clipped sum.  ``events``: optional
+    ((agg_begin, agg_end), (upd_begin, upd_end)) torch.cuda.Event pairs."""
+    L = load_library()
+    B, T, d = A.shape
+    p = G.shape[2]
+    dt = _dtype_code(A)
+    nbytes = L.dp_clip_aggregate_update_workspace(dt, B, T, d, p)
+    ws_t = _workspace(nbytes, A.device, ws)
+    args = [dt, B, T, d, p, _ptr(A), _ptr(G), _ptr(n_sq), float(C), float(sigma), float(eta),
+            int(seed) & (2**64 - 1), int(layer), _ptr(theta), _ptr(S), _ptr(c_out), _ptr(status),
+            _ptr(ws_t), 0 if ws_t is None else ws_t.numel(), _stream(stream)]
+    if events is None:
+        st = L.dp_clip_aggregate_update(*args)
+    else:
+        (a0, a1), (u0, u1) = events
+        st = L.dp_clip_aggregate_update_timed(*args, _event(a0), _event(a1), _event(u0),
+                                              _event(u1))
+    _check(st, "dp_clip_aggregate_update")
+    return theta
 
 
 def dp_noise_update(theta, S, sigma, C, eta, B, seed, layer, stream=None, events=None):

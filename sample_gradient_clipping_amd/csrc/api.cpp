@@ -310,10 +310,12 @@ dp_status_t run_norm_exact(int method, const NormPlan& P, int B, int T, int d, i
 struct AggPlan {
   bool mfma = false;
   int nsplit = 1;
-  size_t c = 0, order = 0, count = 0, part = 0, total = 0;
+  size_t c = 0, order = 0, count = 0, part = 0, sbuf = 0, total = 0;
 };
 
-AggPlan plan_agg(int dtype, int B, int T, int d, int p) {
+// with_sbuf: also a [p][d] buffer for the clipped sum when the caller of the
+// fused update passes no S.
+AggPlan plan_agg(int dtype, int B, int T, int d, int p, bool with_sbuf = false) {
   AggPlan P;
   Carver cv;
   const size_t Bz = static_cast<size_t>(B > 0 ? B : 1);
@@ -325,6 +327,7 @@ AggPlan plan_agg(int dtype, int B, int T, int d, int p) {
     P.nsplit = mfma_gemm_splits(B, T, d, p);
     if (P.nsplit > 1) P.part = cv.take(static_cast<size_t>(P.nsplit) * p * d * 4);
   }
+  if (with_sbuf) P.sbuf = cv.take(static_cast<size_t>(p) * d * 4);
   P.total = cv.off;
   return P;
 }
@@ -413,39 +416,38 @@ size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p) {
   return plan_agg(dtype, B, T, d, p).total;
 }
 
-static dp_status_t clip_aggregate_impl(int dtype, int B, int T, int d, int p, const void* A,
-                                       const void* G, const float* n_sq, float C, float* c_out,
-                                       uint32_t* status, float* S, void* ws, size_t ws_bytes,
-                                       dp_stream_t stream, const Marks& mk) {
-  if (!agg_args_ok(dtype, B, T, d, p)) return DP_ERR_INVALID_ARG;
-  if (!(C > 0.f) || !std::isfinite(C)) return DP_ERR_INVALID_ARG;
-  if (S == nullptr || !aligned(S, 16)) return DP_ERR_INVALID_ARG;
-  if (B > 0 && (n_sq == nullptr || !aligned(n_sq, 4))) return DP_ERR_INVALID_ARG;
+bool agg_ptrs_ok(int B, int T, const void* A, const void* G, const float* n_sq, float C,
+                 float* c_out, uint32_t* status) {
+  if (!(C > 0.f) || !std::isfinite(C)) return false;
+  if (B > 0 && (n_sq == nullptr || !aligned(n_sq, 4))) return false;
   if (B > 0 && T > 0 && (A == nullptr || G == nullptr || !aligned(A, 16) || !aligned(G, 16)))
-    return DP_ERR_INVALID_ARG;
-  if ((c_out && !aligned(c_out, 4)) || (status && !aligned(status, 4))) return DP_ERR_INVALID_ARG;
-  const AggPlan P = plan_agg(dtype, B, T, d, p);
-  if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
-  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+    return false;
+  if ((c_out && !aligned(c_out, 4)) || (status && !aligned(status, 4))) return false;
+  return true;
+}
+
+// Clip factors, then the clipped sum: into S directly (nsplit == 1 or the
+// generic kernel), or as *nsplit planes at *planes (the workspace).  Returns
+// where the sum is and how many planes make it up.
+dp_status_t clip_and_sum(const AggPlan& P, int dtype, int B, int T, int d, int p, const void* A,
+                         const void* G, const float* n_sq, float C, float* c_out,
+                         uint32_t* status, float* S, void* ws, hipStream_t s, const Marks& mk,
+                         const float** planes, int* nplanes) {
   float* c = at<float>(ws, P.c);
   int* order = at<int>(ws, P.order);
   int* count = at<int>(ws, P.count);
   DP_TRY(launch_clip(n_sq, B, C, c, c_out, status, order, count, s));
+  *planes = S;
+  *nplanes = 1;
   if (P.mfma) {
     const bf16_t* Ab = static_cast<const bf16_t*>(A);
     const bf16_t* Gb = static_cast<const bf16_t*>(G);
-    if (P.nsplit == 1) {
-      DP_TRY(mk.open(s));
-      DP_TRY(launch_aggregate_mfma(Ab, Gb, B, T, d, p, c, order, count, 1, S, s));
-      DP_TRY(mk.close(s));
-    } else {
-      float* part = at<float>(ws, P.part);
-      DP_TRY(mk.open(s));
-      DP_TRY(launch_aggregate_mfma(Ab, Gb, B, T, d, p, c, order, count, P.nsplit, part, s));
-      DP_TRY(mk.close(s));
-      DP_TRY(launch_reduce_splits(part, P.nsplit, static_cast<int64_t>(p) * d, S, s));
-    }
+    float* dst = P.nsplit == 1 ? S : at<float>(ws, P.part);
+    DP_TRY(mk.open(s));
+    DP_TRY(launch_aggregate_mfma(Ab, Gb, B, T, d, p, c, order, count, P.nsplit, dst, s));
+    DP_TRY(mk.close(s));
+    *planes = dst;
+    *nplanes = P.nsplit;
     return DP_OK;
   }
   DP_TRY(mk.open(s));
@@ -457,6 +459,77 @@ static dp_status_t clip_aggregate_impl(int dtype, int B, int T, int d, int p, co
                                            static_cast<const float*>(G), B, T, d, p, c, S, s));
   }
   DP_TRY(mk.close(s));
+  return DP_OK;
+}
+
+static dp_status_t clip_aggregate_impl(int dtype, int B, int T, int d, int p, const void* A,
+                                       const void* G, const float* n_sq, float C, float* c_out,
+                                       uint32_t* status, float* S, void* ws, size_t ws_bytes,
+                                       dp_stream_t stream, const Marks& mk) {
+  if (!agg_args_ok(dtype, B, T, d, p)) return DP_ERR_INVALID_ARG;
+  if (!agg_ptrs_ok(B, T, A, G, n_sq, C, c_out, status)) return DP_ERR_INVALID_ARG;
+  if (S == nullptr || !aligned(S, 16)) return DP_ERR_INVALID_ARG;
+  const AggPlan P = plan_agg(dtype, B, T, d, p);
+  if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float* planes = nullptr;
+  int nplanes = 1;
+  const dp_status_t st =
+      clip_and_sum(P, dtype, B, T, d, p, A, G, n_sq, C, c_out, status, S, ws, s, mk, &planes,
+                   &nplanes);
+  if (st != DP_OK) return st;
+  if (planes != S) DP_TRY(launch_reduce_splits(planes, nplanes, static_cast<int64_t>(p) * d, S, s));
+  return DP_OK;
+}
+
+// Whether [a, a + na) and [b, b + nb) share a byte.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+bool update_args_ok(int d, int p, int B, float sigma, float C, float eta) {
+  if (d < 1 || p < 1 || B < 1) return false;
+  return sigma >= 0.f && std::isfinite(sigma) && C > 0.f && std::isfinite(C) && std::isfinite(eta);
+}
+
+static dp_status_t clip_aggregate_update_impl(int dtype, int B, int T, int d, int p,
+                                              const void* A, const void* G, const float* n_sq,
+                                              float C, float sigma, float eta, uint64_t seed,
+                                              uint32_t layer, float* theta, float* S,
+                                              float* c_out, uint32_t* status, void* ws,
+                                              size_t ws_bytes, dp_stream_t stream,
+                                              const Marks& mk_agg, const Marks& mk_upd) {
+  if (!agg_args_ok(dtype, B, T, d, p)) return DP_ERR_INVALID_ARG;
+  if (!update_args_ok(d, p, B, sigma, C, eta)) return DP_ERR_INVALID_ARG;
+  if (!agg_ptrs_ok(B, T, A, G, n_sq, C, c_out, status)) return DP_ERR_INVALID_ARG;
+  if (theta == nullptr || !aligned(theta, 16)) return DP_ERR_INVALID_ARG;
+  if (S != nullptr && !aligned(S, 16)) return DP_ERR_INVALID_ARG;
+  const size_t bytes = static_cast<size_t>(p) * d * 4;
+  if (S != nullptr && overlaps(theta, bytes, S, bytes)) return DP_ERR_INVALID_ARG;
+  const AggPlan P = plan_agg(dtype, B, T, d, p, true);
+  if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  if (overlaps(theta, bytes, ws, P.total) || (S != nullptr && overlaps(S, bytes, ws, P.total)))
+    return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* sum = S != nullptr ? S : at<float>(ws, P.sbuf);
+  const float* planes = nullptr;
+  int nplanes = 1;
+  const dp_status_t st = clip_and_sum(P, dtype, B, T, d, p, A, G, n_sq, C, c_out, status, sum,
+                                      ws, s, mk_agg, &planes, &nplanes);
+  if (st != DP_OK) return st;
+  const float sigmaC = sigma * C;
+  const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
+  const int64_t n = static_cast<int64_t>(p) * d;
+  DP_TRY(mk_upd.open(s));
+  if (planes == sum)
+    DP_TRY(launch_noise_update(theta, sum, n, sigmaC, eta_over_B, seed, layer, s));
+  else
+    DP_TRY(launch_noise_update_splits(theta, planes, nplanes, n, S, sigmaC, eta_over_B, seed,
+                                      layer, s));
+  DP_TRY(mk_upd.close(s));
   return DP_OK;
 }
 
@@ -479,16 +552,12 @@ dp_status_t dp_clip_aggregate_timed(int dtype, int B, int T, int d, int p, const
 static dp_status_t noise_update_impl(int d, int p, float* theta, const float* S, float sigma,
                                      float C, float eta, int B, uint64_t seed, uint32_t layer,
                                      dp_stream_t stream, const Marks& mk) {
-  if (d < 1 || p < 1 || B < 1) return DP_ERR_INVALID_ARG;
-  if (!(sigma >= 0.f) || !std::isfinite(sigma) || !(C > 0.f) || !std::isfinite(C) ||
-      !std::isfinite(eta))
-    return DP_ERR_INVALID_ARG;
+  if (!update_args_ok(d, p, B, sigma, C, eta)) return DP_ERR_INVALID_ARG;
   if (theta == nullptr || S == nullptr || !aligned(theta, 16) || !aligned(S, 16))
     return DP_ERR_INVALID_ARG;
   const int64_t n = static_cast<int64_t>(p) * d;
-  const uintptr_t t0 = reinterpret_cast<uintptr_t>(theta), s0 = reinterpret_cast<uintptr_t>(S);
-  const uintptr_t bytes = static_cast<uintptr_t>(n) * 4;
-  if (t0 < s0 + bytes && s0 < t0 + bytes) return DP_ERR_INVALID_ARG;  // overlap
+  if (overlaps(theta, static_cast<size_t>(n) * 4, S, static_cast<size_t>(n) * 4))
+    return DP_ERR_INVALID_ARG;
   const float sigmaC = sigma * C;
   const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -496,6 +565,36 @@ static dp_status_t noise_update_impl(int d, int p, float* theta, const float* S,
   DP_TRY(launch_noise_update(theta, S, n, sigmaC, eta_over_B, seed, layer, s));
   DP_TRY(mk.close(s));
   return DP_OK;
+}
+
+size_t dp_clip_aggregate_update_workspace(int dtype, int B, int T, int d, int p) {
+  if (!agg_args_ok(dtype, B, T, d, p)) return kInvalid;
+  return plan_agg(dtype, B, T, d, p, true).total;
+}
+
+dp_status_t dp_clip_aggregate_update(int dtype, int B, int T, int d, int p, const void* A,
+                                     const void* G, const float* n_sq, float C, float sigma,
+                                     float eta, uint64_t seed, uint32_t layer, float* theta,
+                                     float* S, float* c_out, uint32_t* status, void* ws,
+                                     size_t ws_bytes, dp_stream_t stream) {
+  return clip_aggregate_update_impl(dtype, B, T, d, p, A, G, n_sq, C, sigma, eta, seed, layer,
+                                    theta, S, c_out, status, ws, ws_bytes, stream, Marks{},
+                                    Marks{});
+}
+
+dp_status_t dp_clip_aggregate_update_timed(int dtype, int B, int T, int d, int p, const void* A,
+                                           const void* G, const float* n_sq, float C,
+                                           float sigma, float eta, uint64_t seed, uint32_t layer,
+                                           float* theta, float* S, float* c_out,
+                                           uint32_t* status, void* ws, size_t ws_bytes,
+                                           dp_stream_t stream, void* ev_agg_begin,
+                                           void* ev_agg_end, void* ev_upd_begin,
+                                           void* ev_upd_end) {
+  return clip_aggregate_update_impl(
+      dtype, B, T, d, p, A, G, n_sq, C, sigma, eta, seed, layer, theta, S, c_out, status, ws,
+      ws_bytes, stream,
+      Marks{static_cast<hipEvent_t>(ev_agg_begin), static_cast<hipEvent_t>(ev_agg_end)},
+      Marks{static_cast<hipEvent_t>(ev_upd_begin), static_cast<hipEvent_t>(ev_upd_end)});
 }
 
 dp_status_t dp_noise_update(int d, int p, float* theta, const float* S, float sigma, float C,

@@ -29,6 +29,12 @@ hipError_t launch_noise_fill(uint64_t seed, uint32_t layer, uint64_t offset, siz
                              hipStream_t s);
 hipError_t launch_noise_update(float* theta, const float* S, int64_t n, float sigmaC,
                                float eta_over_B, uint64_t seed, uint32_t layer, hipStream_t s);
+// The same update reading the clipped sum as nsplit fp32 planes part[split][e]
+// (summed in split order, bit-identical to a separate reduction); the sum is
+// also stored to S_out unless it is null.
+hipError_t launch_noise_update_splits(float* theta, const float* part, int nsplit, int64_t n,
+                                      float* S_out, float sigmaC, float eta_over_B, uint64_t seed,
+                                      uint32_t layer, hipStream_t s);
 
 // ---- generic VALU kernels, any shape, fp32 math (generic_kernels.hip) ----
 // Y[b][j][t] = sum_r X[b][t][r] * P[b or 0][j][r]; P fp32 [.][kp][W].

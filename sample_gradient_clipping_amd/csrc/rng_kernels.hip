@@ -154,6 +154,57 @@ __global__ void __launch_bounds__(256) k_noise_update(float* __restrict__ theta,
   }
 }
 
+// The same update with S = sum over nsplit planes part[split][e] formed on the
+// fly (split order, as the separate reduction), optionally stored to S_out.
+__global__ void __launch_bounds__(256) k_noise_update_splits(float* __restrict__ theta,
+                                                             const float* __restrict__ part,
+                                                             int nsplit, int64_t n,
+                                                             float* __restrict__ S_out,
+                                                             float sigmaC, float eta_over_B,
+                                                             uint32_t k0, uint32_t k1,
+                                                             uint32_t layer) {
+  const int64_t g = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t e0 = g << 2;
+  if (e0 >= n) return;
+  float z[4];
+  normals4(noise_counter(static_cast<uint64_t>(g), layer), k0, k1, z);
+  if (e0 + 3 < n) {
+    float4 sv = *reinterpret_cast<const float4*>(part + e0);
+    for (int sp = 1; sp < nsplit; ++sp) {
+      const float4 v = *reinterpret_cast<const float4*>(part + sp * n + e0);
+      sv.x += v.x;
+      sv.y += v.y;
+      sv.z += v.z;
+      sv.w += v.w;
+    }
+    if (S_out) *reinterpret_cast<float4*>(S_out + e0) = sv;
+    float4 th = *reinterpret_cast<const float4*>(theta + e0);
+    th.x -= eta_over_B * fmaf(sigmaC, z[0], sv.x);
+    th.y -= eta_over_B * fmaf(sigmaC, z[1], sv.y);
+    th.z -= eta_over_B * fmaf(sigmaC, z[2], sv.z);
+    th.w -= eta_over_B * fmaf(sigmaC, z[3], sv.w);
+    *reinterpret_cast<float4*>(theta + e0) = th;
+  } else {
+    for (int l = 0; l < 4 && e0 + l < n; ++l) {
+      float acc = 0.f;
+      for (int sp = 0; sp < nsplit; ++sp) acc += part[sp * n + e0 + l];
+      if (S_out) S_out[e0 + l] = acc;
+      theta[e0 + l] -= eta_over_B * fmaf(sigmaC, z[l], acc);
+    }
+  }
+}
+
+hipError_t launch_noise_update_splits(float* theta, const float* part, int nsplit, int64_t n,
+                                      float* S_out, float sigmaC, float eta_over_B, uint64_t seed,
+                                      uint32_t layer, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t groups = (n + 3) >> 2;
+  hipLaunchKernelGGL(k_noise_update_splits, dim3(static_cast<unsigned>((groups + 255) / 256)),
+                     dim3(256), 0, s, theta, part, nsplit, n, S_out, sigmaC, eta_over_B,
+                     static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), layer);
+  return hipGetLastError();
+}
+
 hipError_t launch_noise_update(float* theta, const float* S, int64_t n, float sigmaC,
                                float eta_over_B, uint64_t seed, uint32_t layer, hipStream_t s) {
   if (n <= 0) return hipSuccess;

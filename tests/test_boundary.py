@@ -122,6 +122,30 @@ def test_noise_update_rejects_bad_arguments(lib):
     assert f(S=ctypes.c_void_p(0x100000 + 64)) == E  # overlaps theta
 
 
+def _aggu(lib, dtype=0, B=2, T=8, d=8, p=8, A=FAKE, G=FAKE, n=FAKE, C=1.0, sigma=1.0, eta=0.1,
+          th=ctypes.c_void_p(0x400000), S=NULL, ws=ctypes.c_void_p(0x800000), ws_bytes=1 << 20):
+    return lib.dp_clip_aggregate_update(dtype, B, T, d, p, A, G, n, C, sigma, eta, 1, 0, th, S,
+                                        NULL, NULL, ws, ws_bytes, NULL)
+
+
+def test_clip_aggregate_update_rejects_bad_arguments(lib):
+    E = dp.DP_ERR_INVALID_ARG
+    assert _aggu(lib, B=0) == E                      # |B| = 0 has no update
+    assert _aggu(lib, C=0.0) == E
+    assert _aggu(lib, sigma=-1.0) == E
+    assert _aggu(lib, eta=float("nan")) == E
+    assert _aggu(lib, th=NULL) == E
+    assert _aggu(lib, th=ctypes.c_void_p(0x400004)) == E   # misaligned theta
+    assert _aggu(lib, S=ctypes.c_void_p(0x400000 + 64)) == E  # S overlaps theta
+    assert _aggu(lib, ws=ctypes.c_void_p(0x400000 + 64)) == E  # workspace overlaps theta
+    assert _aggu(lib, n=NULL) == E
+    assert _aggu(lib, d=0) == E
+    assert _aggu(lib, ws_bytes=0) == dp.DP_ERR_WORKSPACE
+    need = dp.dp_clip_aggregate_update_workspace("f32", 2, 8, 8, 8)
+    assert need >= dp.dp_clip_aggregate_workspace("f32", 2, 8, 8, 8) + 8 * 8 * 4
+    assert dp.dp_clip_aggregate_update_workspace("f32", 2, 8, 0, 8) is None
+
+
 def test_test_hooks_reject_bad_arguments(lib):
     E = dp.DP_ERR_INVALID_ARG
     assert lib.dp_philox_u32(1, NULL, FAKE, 4, NULL) == E

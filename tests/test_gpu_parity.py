@@ -220,6 +220,61 @@ def test_aggregate_deterministic(dev):
 
 
 # ---------------------------------------------------------------------------
+# clip + aggregation + noise + update in one call
+# ---------------------------------------------------------------------------
+FUSED_CASES = [
+    ("tiny_f32", "f32", 4, 64, 64, 64),              # generic contraction
+    ("ragged_bf16", "bf16", 3, 37, 50, 70),          # generic contraction, bf16
+    ("one_split_bf16", "bf16", 2, 1024, 2048, 8192),  # MFMA, single token split
+    ("splits_bf16", "bf16", 8, 128, 2048, 2048),     # MFMA, token splits summed in the update
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_clip_aggregate_update_matches_separate_calls(dev, case):
+    """The fused call equals dp_clip_aggregate + dp_noise_update bit for bit,
+    with and without the clipped sum stored, and matches the oracle."""
+    name, dtype, B, T, d, p = case
+    recipe = "unit_u0.1_3" if dtype == "f32" else "llama_logu"
+    A, G = linear_inputs(B, T, d, p, dtype, recipe, seed=31 + B)
+    Ad, Gd = A.to(dev), G.to(dev)
+    exact = oracle.norm_est("fgc", A, G) if T * d * p <= (1 << 26) else None
+    n32 = (torch.tensor(exact, dtype=torch.float32) if exact is not None
+           else torch.linspace(0.5, 50.0, B, dtype=torch.float32))
+    C = float(np.median(np.sqrt(n32.double().numpy())))
+    sigma, eta, seed, layer = 0.8, 0.05, 4004, 9
+    th0 = theta_init(p, d, seed=5).to(dev)
+    # separate calls
+    S1 = torch.empty(p, d, dtype=torch.float32, device=dev)
+    c1 = torch.empty(B, dtype=torch.float32, device=dev)
+    dp.dp_clip_aggregate(Ad, Gd, n32.to(dev), C, S1, c_out=c1)
+    th1 = th0.clone()
+    dp.dp_noise_update(th1, S1, sigma, C, eta, B, seed, layer)
+    # fused, storing S; fused, S not stored
+    S2 = torch.full((p, d), float("nan"), dtype=torch.float32, device=dev)
+    c2 = torch.empty(B, dtype=torch.float32, device=dev)
+    th2 = th0.clone()
+    dp.dp_clip_aggregate_update(Ad, Gd, n32.to(dev), C, sigma, eta, seed, layer, th2, S=S2,
+                                c_out=c2)
+    th3 = th0.clone()
+    dp.dp_clip_aggregate_update(Ad, Gd, n32.to(dev), C, sigma, eta, seed, layer, th3)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
+    assert torch.equal(S1, S2)
+    assert torch.equal(th1, th2) and torch.equal(th1, th3)
+    # against the oracle on sampled rows
+    c_ref, _ = oracle.clip_factors(n32.double().numpy(), C)
+    rows = np.sort(np.random.default_rng(B).choice(p, size=min(16, p), replace=False))
+    S_rows = oracle.aggregate_rows(A, G, c_ref, rows)
+    th_ref = oracle.noise_update(f64(th0)[rows], S_rows, sigma, C, eta, B, seed, layer, rows=rows)
+    es = max_rel_normwise(f64(S2)[rows], S_rows)
+    et = max_rel_normwise(f64(th2)[rows] - f64(th0)[rows], th_ref - f64(th0)[rows])
+    report(f"fused update {name}", S_err=es, dtheta_err=et)
+    assert es <= (TOL_F32 if dtype == "f32" else 1e-4)
+    assert et <= (TOL_F32 if dtype == "f32" else 1e-4)
+
+
+# ---------------------------------------------------------------------------
 # noise + update
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("p,d", [(64, 64), (37, 29), (512, 384)])
