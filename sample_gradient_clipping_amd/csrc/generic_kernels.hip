@@ -347,8 +347,18 @@ __global__ void __launch_bounds__(kOrthChunk) k_orth_dots(
   const int e = e0 + threadIdx.x;
   const float* ub = U + b * u_bstride;
   const float* vb = V + b * v_bstride;
-  for (int i = 0; i < nu; ++i) su[i][threadIdx.x] = e < p ? ub[static_cast<int64_t>(i) * p + e] : 0.f;
-  for (int j = 0; j < nv; ++j) sv[j][threadIdx.x] = e < p ? vb[static_cast<int64_t>(j) * p + e] : 0.f;
+  // all loads first, then the LDS stores (one memory round trip, not one per row)
+  float ru[kOrthMaxCols], rv[kOrthMaxCols];
+#pragma unroll
+  for (int i = 0; i < kOrthMaxCols; ++i) {
+    ru[i] = (i < nu && e < p) ? ub[static_cast<int64_t>(i) * p + e] : 0.f;
+    rv[i] = (i < nv && e < p) ? vb[static_cast<int64_t>(i) * p + e] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < kOrthMaxCols; ++i) {
+    if (i < nu) su[i][threadIdx.x] = ru[i];
+    if (i < nv) sv[i][threadIdx.x] = rv[i];
+  }
   __syncthreads();
   const int npairs = nu * nv;
   double* out = part + (static_cast<int64_t>(b) * gridDim.x + chunk) * npairs;
@@ -361,41 +371,84 @@ __global__ void __launch_bounds__(kOrthChunk) k_orth_dots(
   }
 }
 
-// Sum of the chunk partials of one sample (fixed order), into LDS.
-__device__ void sum_chunks(const double* part_b, int nchunk, int npairs, double* dst) {
-  for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) {
-    double acc = 0.0;
-    for (int c = 0; c < nchunk; ++c) acc += part_b[static_cast<int64_t>(c) * npairs + pi];
-    dst[pi] = acc;
+// Sum of the chunk partials of one sample into LDS dst[npairs], each entry
+// added up in chunk order.  The partials are contiguous ([chunk][pair]), so
+// tiles of whole chunks are first copied into LDS with every thread loading
+// (one memory round trip per tile), then summed from LDS.
+constexpr int kSumStage = 4096;  // doubles of LDS staging
+__device__ void sum_chunks(const double* part_b, int nchunk, int npairs, double* dst,
+                           double* stage) {
+  for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) dst[pi] = 0.0;
+  const int tile = npairs < kSumStage ? kSumStage / npairs : 1;
+  for (int c0 = 0; c0 < nchunk; c0 += tile) {
+    const int nc = nchunk - c0 < tile ? nchunk - c0 : tile;
+    __syncthreads();
+    // sixteen loads in flight per thread before the first LDS store
+    const int n = nc * npairs;
+    const double* src = part_b + static_cast<int64_t>(c0) * npairs;
+    for (int u0 = 0; u0 < n; u0 += 16 * blockDim.x) {
+      double v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int u = u0 + k * blockDim.x + threadIdx.x;
+        v[k] = u < n ? src[u] : 0.0;
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int u = u0 + k * blockDim.x + threadIdx.x;
+        if (u < n) stage[u] = v[k];
+      }
+    }
+    __syncthreads();
+    for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) {
+      double acc = dst[pi];
+      for (int c = 0; c < nc; ++c) acc += stage[c * npairs + pi];
+      dst[pi] = acc;
+    }
   }
 }
 
-// Cholesky of the s x s Gram (dense, gram[i * s + j]) and the inverse of its
-// factor, fp64, single thread; vanishing pivots zero their column.
-__device__ void chol_inverse(const double* gram, int s, double (*R)[kOrthMaxCols],
-                             double (*Rinv)[kOrthMaxCols]) {
-  auto g = [&](int i, int j) { return gram[(i < j ? i : j) * s + (i < j ? j : i)]; };
-  double dmax = 0.0;
-  for (int i = 0; i < s; ++i) dmax = fmax(dmax, g(i, i));
-  const double tiny = dmax * 1e-24;
-  uint32_t dead = 0;  // bit j: column j has no pivot
-  for (int j = 0; j < s; ++j) {
-    double djj = g(j, j);
-    for (int k = 0; k < j; ++k) djj -= R[k][j] * R[k][j];
-    const bool dj = !(djj > tiny);
-    if (dj) dead |= 1u << j;
-    const double rjj = dj ? 0.0 : sqrt(djj);
-    R[j][j] = rjj;
-    for (int c = j + 1; c < s; ++c) {
-      double v = g(j, c);
-      for (int k = 0; k < j; ++k) v -= R[k][j] * R[k][c];
-      R[j][c] = dj ? 0.0 : v / rjj;
-    }
-    for (int c = 0; c < j; ++c) R[j][c] = 0.0;
+// Cholesky of the s x s Gram (dense, gram[i * s + j]; overwritten) and the
+// inverse of its factor, fp64, by the whole block (LDS arrays, one
+// synchronisation per step).  Right-looking: at step j the pivot row is
+// scaled and the trailing upper triangle is updated, so every entry receives
+// its rank-one corrections in the same order as the textbook left-looking
+// form.  A pivot that is not above tiny = 1e-24 * (largest diagonal) marks
+// column j dead: its row and column of R and of R^-1 are zero.
+__device__ void chol_inverse(double* gram, int s, double (*R)[kOrthMaxCols],
+                             double (*Rinv)[kOrthMaxCols], double* tiny_s, uint32_t* dead_s) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (tid == 0) {
+    double dmax = 0.0;
+    for (int i = 0; i < s; ++i) dmax = fmax(dmax, gram[i * s + i]);
+    *tiny_s = dmax * 1e-24;
+    *dead_s = 0u;
   }
-  // Rinv: upper triangular, R Rinv = I on the live columns; dead columns zero.
+  for (int u = tid; u < kOrthMaxCols * kOrthMaxCols; u += nt) {
+    R[u / kOrthMaxCols][u % kOrthMaxCols] = 0.0;
+    Rinv[u / kOrthMaxCols][u % kOrthMaxCols] = 0.0;
+  }
+  __syncthreads();
   for (int j = 0; j < s; ++j) {
-    for (int i = 0; i < s; ++i) Rinv[i][j] = 0.0;
+    const double djj = gram[j * s + j];
+    const bool dj = !(djj > *tiny_s);
+    const double rjj = dj ? 0.0 : sqrt(djj);
+    const double inv = dj ? 0.0 : 1.0 / rjj;
+    // row j of R
+    for (int c = j + tid; c < s; c += nt) R[j][c] = c == j ? rjj : gram[j * s + c] * inv;
+    if (tid == 0 && dj) *dead_s |= 1u << j;
+    __syncthreads();
+    // trailing update of the upper triangle: gram[i][c] -= R[j][i] R[j][c], j < i <= c
+    const int m = s - j - 1;
+    for (int u = tid; u < m * m; u += nt) {
+      const int i = j + 1 + u / m, c = j + 1 + u % m;
+      if (c >= i) gram[i * s + c] -= R[j][i] * R[j][c];
+    }
+    __syncthreads();
+  }
+  // R^-1 (upper triangular): lane j back-substitutes column j.
+  const uint32_t dead = *dead_s;
+  for (int j = tid; j < s; j += nt) {
     if (dead >> j & 1u) continue;
     for (int i = j; i >= 0; --i) {
       if (dead >> i & 1u) continue;
@@ -404,6 +457,7 @@ __device__ void chol_inverse(const double* gram, int s, double (*R)[kOrthMaxCols
       Rinv[i][j] = v / R[i][i];
     }
   }
+  __syncthreads();
 }
 
 // Q[j][e] = sum_{i <= j} X[i][e] Rinv[i][j], Rinv from the Gram partials of X.
@@ -413,11 +467,13 @@ __global__ void __launch_bounds__(kOrthChunk) k_orth_apply(
   __shared__ double gram[kOrthMaxCols * kOrthMaxCols];
   __shared__ double R[kOrthMaxCols][kOrthMaxCols];
   __shared__ double Rinv[kOrthMaxCols][kOrthMaxCols];
+  __shared__ double stage[kSumStage];
+  __shared__ double tiny;
+  __shared__ uint32_t dead;
   const int b = blockIdx.y;
-  sum_chunks(part + static_cast<int64_t>(b) * nchunk * s * s, nchunk, s * s, gram);
+  sum_chunks(part + static_cast<int64_t>(b) * nchunk * s * s, nchunk, s * s, gram, stage);
   __syncthreads();
-  if (threadIdx.x == 0) chol_inverse(gram, s, R, Rinv);
-  __syncthreads();
+  chol_inverse(gram, s, R, Rinv, &tiny, &dead);
   const int e = blockIdx.x * kOrthChunk + threadIdx.x;
   if (e >= p) return;
   const float* xb = Xr + b * x_bstride;
@@ -442,23 +498,30 @@ __global__ void __launch_bounds__(kOrthChunk) k_orth_deflate(
     int64_t w_bstride, int r, int p, const double* __restrict__ part, int nchunk,
     float* __restrict__ Wout, int64_t wo_bstride) {
   __shared__ double H[kOrthMaxCols * kOrthMaxCols];
+  __shared__ double stage[kSumStage];
   const int b = blockIdx.y;
-  sum_chunks(part + static_cast<int64_t>(b) * nchunk * s * r, nchunk, s * r, H);
+  sum_chunks(part + static_cast<int64_t>(b) * nchunk * s * r, nchunk, s * r, H, stage);
   __syncthreads();
   const int e = blockIdx.x * kOrthChunk + threadIdx.x;
   if (e >= p) return;
   const float* qb = Q + b * q_bstride;
   const float* wb = W + b * w_bstride;
   float* ob = Wout + b * wo_bstride;
-  float q[kOrthMaxCols];
+  float q[kOrthMaxCols], w[kOrthMaxCols];
 #pragma unroll
-  for (int i = 0; i < kOrthMaxCols; ++i) q[i] = i < s ? qb[static_cast<int64_t>(i) * p + e] : 0.f;
-  for (int t = 0; t < r; ++t) {
-    double v = wb[static_cast<int64_t>(t) * p + e];
+  for (int i = 0; i < kOrthMaxCols; ++i) {
+    q[i] = i < s ? qb[static_cast<int64_t>(i) * p + e] : 0.f;
+    w[i] = i < r ? wb[static_cast<int64_t>(i) * p + e] : 0.f;
+  }
 #pragma unroll
-    for (int i = 0; i < kOrthMaxCols; ++i)
-      if (i < s) v -= H[i * r + t] * static_cast<double>(q[i]);
-    ob[static_cast<int64_t>(t) * p + e] = static_cast<float>(v);
+  for (int t = 0; t < kOrthMaxCols; ++t) {
+    if (t < r) {
+      double v = w[t];
+#pragma unroll
+      for (int i = 0; i < kOrthMaxCols; ++i)
+        if (i < s) v -= H[i * r + t] * static_cast<double>(q[i]);
+      ob[static_cast<int64_t>(t) * p + e] = static_cast<float>(v);
+    }
   }
 }
 
