@@ -39,6 +39,7 @@ from .philox import (  # noqa: F401
     box_muller,
     normals_from_counters,
     probe_matrix,
+    rademacher_probe_matrix,
     noise_vector,
     PROBE_LANES,
 )

@@ -13,7 +13,7 @@ import math
 
 import numpy as np
 
-from .philox import probe_matrix
+from .philox import probe_matrix, rademacher_probe_matrix
 
 
 def to_f64(x):
@@ -58,13 +58,21 @@ def hutch_core(A_i, G_i, P, scale):
     return float(scale * np.sum(Z * Z))
 
 
-def hutch_norm_sq(A_i, G_i, k, seed, layer, sample):
-    """Hutch estimate of ||A_i^T G_i||_F^2 with k Gaussian probes.
+def probes(seed, layer, sample, p, k, rademacher=False):
+    """The p x k probe block: Gaussian (default) or Rademacher signs."""
+    if rademacher:
+        return rademacher_probe_matrix(seed, layer, sample, p, k)
+    return probe_matrix(seed, layer, sample, p, k)
+
+
+def hutch_norm_sq(A_i, G_i, k, seed, layer, sample, rademacher=False):
+    """Hutch estimate of ||A_i^T G_i||_F^2 with k Gaussian (or sign) probes.
 
     Reading (pages print sum_j P_j^T O P_j without a 1/k): with N(0, 1)
-    entries that sum has mean k tr(O), so the estimate is divided by k.
+    entries that sum has mean k tr(O), so the estimate is divided by k.  Sign
+    probes have the same second moment (E[P P^T] = k I), so the same 1/k.
     """
-    P = probe_matrix(seed, layer, sample, G_i.shape[1], k)
+    P = probes(seed, layer, sample, G_i.shape[1], k, rademacher)
     return hutch_core(A_i, G_i, P, 1.0 / k)
 
 
@@ -111,7 +119,7 @@ def hutchpp_split(k):
     return s, k - 2 * s
 
 
-def hutchpp_norm_sq(A_i, G_i, k, seed, layer, sample):
+def hutchpp_norm_sq(A_i, G_i, k, seed, layer, sample, rademacher=False):
     """Hutch++ estimate of tr(O_i) = ||A_i^T G_i||_F^2.
 
     [RC] section 中核メカニズム, item 2: a low-rank (QR) approximation takes
@@ -127,7 +135,7 @@ def hutchpp_norm_sq(A_i, G_i, k, seed, layer, sample):
     """
     s, r = hutchpp_split(k)
     p = G_i.shape[1]
-    P = probe_matrix(seed, layer, sample, p, s + r)
+    P = probes(seed, layer, sample, p, s + r, rademacher)
     S = P[:, :s]
     W = P[:, s:s + r]
     X = G_i.T @ (A_i @ (A_i.T @ (G_i @ S)))
@@ -138,12 +146,13 @@ def hutchpp_norm_sq(A_i, G_i, k, seed, layer, sample):
     return head + tail
 
 
-def norm_est(method, A, G, k=None, seed=0, layer=0, shared=False):
+def norm_est(method, A, G, k=None, seed=0, layer=0, shared=False, rademacher=False):
     """Squared norms n[B] of one linear layer for the whole batch.
 
     A: [B][T][d], G: [B][T][p] (any array the caller upcasts with to_f64).
     method: "fgc" | "ghost" | "hutch" | "hutchpp".  ``shared`` uses the
-    sample-0 probe for every sample (one P for the batch).
+    sample-0 probe for every sample (one P for the batch); ``rademacher``
+    draws sign probes instead of Gaussian ones.
     """
     A = to_f64(A)
     G = to_f64(G)
@@ -156,9 +165,9 @@ def norm_est(method, A, G, k=None, seed=0, layer=0, shared=False):
         elif method == "ghost":
             out[i] = ghost_norm_sq(A[i], G[i])
         elif method == "hutch":
-            out[i] = hutch_norm_sq(A[i], G[i], k, seed, layer, probe_sample)
+            out[i] = hutch_norm_sq(A[i], G[i], k, seed, layer, probe_sample, rademacher)
         elif method == "hutchpp":
-            out[i] = hutchpp_norm_sq(A[i], G[i], k, seed, layer, probe_sample)
+            out[i] = hutchpp_norm_sq(A[i], G[i], k, seed, layer, probe_sample, rademacher)
         else:
             raise ValueError(method)
     return out

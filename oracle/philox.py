@@ -113,6 +113,24 @@ def probe_matrix(seed, layer, sample, p, k):
     return P[:p].copy()
 
 
+def rademacher_probe_matrix(seed, layer, sample, p, k):
+    """A {+1, -1} probe P_i in R^{p x k} (Rademacher: independent fair signs).
+
+    [RC] section 意義と主張 names {+-1}-valued sketching matrices as a way to
+    cut the overhead further.  Reading (the pages give no generator): the
+    same counters and lanes as the Gaussian probe -- entry (r, j) uses lane
+    r mod 4 of the counter (r // 4, j, sample, layer) -- and the entry is +1
+    when the top bit of that 32-bit word is 0, -1 when it is 1.
+    """
+    ngroups = (p + PROBE_LANES - 1) // PROBE_LANES
+    g = np.arange(ngroups, dtype=np.uint64)[:, None]
+    j = np.arange(k, dtype=np.uint64)[None, :]
+    w = philox4x32_10(g, j, sample, layer, seed)  # [ngroups, k, 4] uint32
+    sign = 1.0 - 2.0 * (w >> np.uint32(31)).astype(np.float64)
+    P = sign.transpose(0, 2, 1).reshape(ngroups * PROBE_LANES, k)
+    return P[:p].copy()
+
+
 def noise_vector(seed, layer, n, offset=0):
     """DP noise xi[e] ~ N(0, 1) for flat parameter indices e in [offset, offset+n).
 

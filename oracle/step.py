@@ -86,7 +86,8 @@ def noise_update(theta, S, sigma, C, eta, B, seed, layer, rows=None):
     return theta - (eta / B) * (S + sigma * C * xi)
 
 
-def dp_step(layers, method, k, C, sigma, eta, seed_norm, seed_noise, shared=False):
+def dp_step(layers, method, k, C, sigma, eta, seed_norm, seed_noise, shared=False,
+            rademacher=False):
     """One DP-SGD-RC step over a stack of linear layers.
 
     ``layers``: list of (layer_id, A [B][T][d], G [B][T][p], theta [p][d]).
@@ -98,7 +99,8 @@ def dp_step(layers, method, k, C, sigma, eta, seed_norm, seed_noise, shared=Fals
     """
     n = None
     for layer_id, A, G, _theta in layers:
-        n_l = norm_est(method, A, G, k=k, seed=seed_norm, layer=layer_id, shared=shared)
+        n_l = norm_est(method, A, G, k=k, seed=seed_norm, layer=layer_id, shared=shared,
+                       rademacher=rademacher)
         n = n_l if n is None else n + n_l
     c, _flag = clip_factors(n, C)
     S_out, theta_out = [], []
