@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--method", default=None, help="override the workload's estimator")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rademacher", action="store_true",
+                    help="sign (+-1) probes instead of Gaussian ones for Hutch / Hutch++")
     ap.add_argument("--unfused", action="store_true",
                     help="aggregate and update with two calls (S materialised) instead of one")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -101,7 +103,7 @@ def make_inputs(wl, copies, dev):
     return out
 
 
-def cpu_baseline(wl, method, target_s=12.0):
+def cpu_baseline(wl, method, target_s=12.0, rademacher=False):
     """The oracle (plain fp64 numpy) on a bounded sample of the workload."""
     import numpy as np
     import oracle
@@ -125,7 +127,7 @@ def cpu_baseline(wl, method, target_s=12.0):
         t0 = time.perf_counter()
         for _ in range(reps):
             oracle.dp_step(data, method, wl.k, wl.C, wl.sigma, wl.eta, wl.method_seed,
-                           wl.noise_seed)
+                           wl.noise_seed, rademacher=rademacher)
         return time.perf_counter() - t0
 
     # one sample first; then as many samples (and, if the whole batch is quicker
@@ -204,8 +206,10 @@ def main():
         cp = inputs[it % copies]
         for li, l in enumerate(wl.layers):
             A, G = cp[li]
+            flags = (dp.DP_ACCUMULATE if li else 0) | (
+                dp.DP_PROBE_RADEMACHER if args.rademacher else 0)
             dp.dp_norm_est(method, A, G, wl.k, wl.method_seed + it, l.layer_id, n,
-                           flags=dp.DP_ACCUMULATE if li else 0, ws=ws_norm,
+                           flags=flags, ws=ws_norm,
                            events=None if evs is None else (evs[li][0], evs[li][1]))
         for li, l in enumerate(wl.layers):
             A, G = cp[li]
@@ -305,7 +309,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        cpu = cpu_baseline(wl, method)
+        cpu = cpu_baseline(wl, method, rademacher=args.rademacher)
         log(f"[bench] cpu_baseline {cpu}")
 
     line = {
@@ -314,7 +318,8 @@ def main():
         "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "T": wl.T, "layers": len(wl.layers),
                    "shapes_dp": sorted({(l.d, l.p) for l in wl.layers}), "method": method,
-                   "k": wl.k, "C": wl.C, "sigma": wl.sigma, "eta": wl.eta,
+                   "k": wl.k, "probes": "rademacher" if args.rademacher else "gaussian",
+                   "C": wl.C, "sigma": wl.sigma, "eta": wl.eta,
                    "input_copies": copies, "global_batch": wl.B, "seq_len": wl.T},
         "roofline": roof,
         "kernels": kernels,

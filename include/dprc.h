@@ -66,6 +66,11 @@ typedef enum {
 /* dp_norm_est flags */
 #define DP_ACCUMULATE 1u   /* n_sq[i] += estimate (sum over layers) instead of n_sq[i] = estimate */
 #define DP_PROBE_SHARED 2u /* one probe matrix for the whole batch (the sample-0 stream) */
+/* Rademacher probes: entries +1 / -1 (the summary's section 意義と主張 names
+ * {+-1}-valued sketching matrices as a way to cut the overhead further) instead
+ * of N(0, 1); the same counters and lanes as the Gaussian probe, +1 when the
+ * 32-bit word's top bit is 0.  The estimate keeps the 1/k (E[P P^T] = k I). */
+#define DP_PROBE_RADEMACHER 4u
 
 /* dp_clip_aggregate status bits (ORed into *status) */
 #define DP_STATUS_NONFINITE_NORM 1u /* some n_sq[i] was NaN/Inf: its c_i was set to 0 */
@@ -98,7 +103,7 @@ size_t dp_norm_est_workspace(int method, int dtype, int B, int T, int d, int p, 
  *  layer   layer index (counter word), so layers draw independent probes.
  *          Probe entry (row r, column j) of sample i is lane r mod 4 of the
  *          counter (r / 4, j, i, layer).
- *  flags   DP_ACCUMULATE | DP_PROBE_SHARED.
+ *  flags   DP_ACCUMULATE | DP_PROBE_SHARED | DP_PROBE_RADEMACHER.
  *  n_sq    [B] fp32 device output (or accumulator with DP_ACCUMULATE).
  *  ws      device workspace of ws_bytes >= dp_norm_est_workspace(...).
  */
@@ -211,6 +216,11 @@ dp_status_t dp_philox_u32(uint64_t seed, const uint32_t *ctr, uint32_t *out, siz
 /* Pt[j][r] (fp32 device, [k][p]) = entry (r, j) of the probe P of `sample` in `layer`. */
 dp_status_t dp_probe_fill(uint64_t seed, uint32_t layer, uint32_t sample, int p, int k,
                           float *Pt, dp_stream_t stream);
+
+/* The same with probe flags: DP_PROBE_RADEMACHER gives the sign probe (fp32
+ * +1 / -1); other bits are rejected. */
+dp_status_t dp_probe_fill_ex(uint64_t seed, uint32_t layer, uint32_t sample, int p, int k,
+                             uint32_t flags, float *Pt, dp_stream_t stream);
 
 /* xi[e - offset] for e in [offset, offset + n): the noise normals (fp32 device). */
 dp_status_t dp_noise_fill(uint64_t seed, uint32_t layer, uint64_t offset, size_t n,

@@ -12,7 +12,7 @@ _BINDING_NAMES = (
     "dp_clip_aggregate", "dp_clip_aggregate_workspace", "dp_noise_update",
     "dp_clip_aggregate_update", "dp_clip_aggregate_update_workspace",
     "dp_philox_u32", "dp_probe_fill", "dp_noise_fill", "DprcError", "lib_path",
-    "load_library", "METHODS", "DP_ACCUMULATE", "DP_PROBE_SHARED",
+    "load_library", "METHODS", "DP_ACCUMULATE", "DP_PROBE_SHARED", "DP_PROBE_RADEMACHER",
 )
 
 

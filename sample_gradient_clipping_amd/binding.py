@@ -18,6 +18,7 @@ DP_F32, DP_BF16 = 0, 1
 DP_NORM_HUTCH, DP_NORM_HUTCHPP, DP_NORM_GHOST, DP_NORM_FGC = range(4)
 DP_ACCUMULATE = 1
 DP_PROBE_SHARED = 2
+DP_PROBE_RADEMACHER = 4
 DP_STATUS_NONFINITE_NORM = 1
 METHODS = {"hutch": DP_NORM_HUTCH, "hutchpp": DP_NORM_HUTCHPP, "ghost": DP_NORM_GHOST,
            "fgc": DP_NORM_FGC}
@@ -79,6 +80,8 @@ def load_library():
     L.dp_philox_u32.restype = c_int
     L.dp_probe_fill.argtypes = [c_u64, c_u32, c_u32, c_int, c_int, c_p, c_p]
     L.dp_probe_fill.restype = c_int
+    L.dp_probe_fill_ex.argtypes = [c_u64, c_u32, c_u32, c_int, c_int, c_u32, c_p, c_p]
+    L.dp_probe_fill_ex.restype = c_int
     L.dp_noise_fill.argtypes = [c_u64, c_u32, c_u64, c_sz, c_p, c_p]
     L.dp_noise_fill.restype = c_int
     _lib = L
@@ -250,10 +253,16 @@ def dp_philox_u32(seed, ctr, out, stream=None):
     return out
 
 
-def dp_probe_fill(seed, layer, sample, p, k, Pt, stream=None):
-    """Pt [k][p] fp32 = probe entries P[r][j] of (seed, layer, sample)."""
-    st = load_library().dp_probe_fill(int(seed) & (2**64 - 1), int(layer), int(sample), int(p),
-                                      int(k), _ptr(Pt), _stream(stream))
+def dp_probe_fill(seed, layer, sample, p, k, Pt, stream=None, rademacher=False):
+    """Pt [k][p] fp32 = probe entries P[r][j] of (seed, layer, sample);
+    ``rademacher`` gives the +-1 sign probe."""
+    L = load_library()
+    if rademacher:
+        st = L.dp_probe_fill_ex(int(seed) & (2**64 - 1), int(layer), int(sample), int(p), int(k),
+                                DP_PROBE_RADEMACHER, _ptr(Pt), _stream(stream))
+    else:
+        st = L.dp_probe_fill(int(seed) & (2**64 - 1), int(layer), int(sample), int(p), int(k),
+                             _ptr(Pt), _stream(stream))
     _check(st, "dp_probe_fill")
     return Pt
 

@@ -150,7 +150,7 @@ struct Marks {
 template <typename TIn>
 dp_status_t run_norm_generic_hutch(const NormPlan& P, int B, int T, int d, int p, int k,
                                    const TIn* A, const TIn* G, uint64_t seed, uint32_t layer,
-                                   bool shared, bool accum, float* n_sq, void* ws, hipStream_t s,
+                                   bool shared, bool signs, bool accum, float* n_sq, void* ws, hipStream_t s,
                                    const Marks& mk) {
   float* Pf = at<float>(ws, P.pf);
   float* Y = at<float>(ws, P.y);
@@ -158,7 +158,7 @@ dp_status_t run_norm_generic_hutch(const NormPlan& P, int B, int T, int d, int p
   double* part = at<double>(ws, P.part);
   const int nS = shared ? 1 : B;
   const int64_t pbs = shared ? 0 : static_cast<int64_t>(k) * p;
-  DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, k, k, Pf, s));
+  DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, k, k, Pf, s, signs));
   DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_generic<TIn>(G, B, T, p, Pf, pbs, k, Y, s));
   DP_TRY(launch_project_generic<TIn>(A, B, T, d, Y, k, Z, s));
@@ -170,7 +170,7 @@ dp_status_t run_norm_generic_hutch(const NormPlan& P, int B, int T, int d, int p
 
 dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, int k,
                                 const bf16_t* A, const bf16_t* G, uint64_t seed, uint32_t layer,
-                                bool shared, bool accum, float* n_sq, void* ws, hipStream_t s,
+                                bool shared, bool signs, bool accum, float* n_sq, void* ws, hipStream_t s,
                                 const Marks& mk) {
   bf16_t* Pb = at<bf16_t>(ws, P.pb);
   bf16_t* Yb = at<bf16_t>(ws, P.yb);
@@ -179,7 +179,7 @@ dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, i
   const int nS = shared ? 1 : B;
   const int64_t pbs = shared ? 0 : static_cast<int64_t>(kMfmaProbeCols) * p;
   uint32_t* ctr = at<uint32_t>(ws, P.ctr);
-  DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, k, kMfmaProbeCols, Pb, s, ctr, B));
+  DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, k, kMfmaProbeCols, Pb, s, signs, ctr, B));
   DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_mfma(G, B, T, p, Pb, pbs, Yb, s));
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
@@ -192,7 +192,7 @@ dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, i
 template <typename TIn>
 dp_status_t run_norm_generic_hpp(const NormPlan& P, int B, int T, int d, int p, const TIn* A,
                                  const TIn* G, uint64_t seed, uint32_t layer, bool shared,
-                                 bool accum, float* n_sq, void* ws, hipStream_t s,
+                                 bool signs, bool accum, float* n_sq, void* ws, hipStream_t s,
                                  const Marks& mk) {
   const int S_ = P.s, R_ = P.r, K3 = P.k3;
   float* Pf = at<float>(ws, P.pf);
@@ -204,7 +204,7 @@ dp_status_t run_norm_generic_hpp(const NormPlan& P, int B, int T, int d, int p, 
   double* part = at<double>(ws, P.part);
   const int nS = shared ? 1 : B;
   const int64_t pbs = shared ? 0 : static_cast<int64_t>(K3) * p;
-  DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, K3, K3, Pf, s));
+  DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, K3, K3, Pf, s, signs));
   // pass 1: Z1 = A^T (G S)
   DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_generic<TIn>(G, B, T, p, Pf, pbs, S_, Y, s));
@@ -225,7 +225,7 @@ dp_status_t run_norm_generic_hpp(const NormPlan& P, int B, int T, int d, int p, 
 
 dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, const bf16_t* A,
                               const bf16_t* G, uint64_t seed, uint32_t layer, bool shared,
-                              bool accum, float* n_sq, void* ws, hipStream_t s, const Marks& mk) {
+                              bool signs, bool accum, float* n_sq, void* ws, hipStream_t s, const Marks& mk) {
   const int S_ = P.s, R_ = P.r, K3 = P.k3;
   float* Pf = at<float>(ws, P.pf);
   float* P3 = at<float>(ws, P.p3);
@@ -243,8 +243,8 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
   const int64_t pad_d = static_cast<int64_t>(kMfmaProbeCols) * d;
   const int64_t pad_p = static_cast<int64_t>(kMfmaProbeCols) * p;
   uint32_t* ctr = at<uint32_t>(ws, P.ctr);
-  DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, K3, K3, Pf, s));
-  DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, S_, kMfmaProbeCols, Pb, s, ctr, B));
+  DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, K3, K3, Pf, s, signs));
+  DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, S_, kMfmaProbeCols, Pb, s, signs, ctr, B));
   // pass 1: Z1 = A^T (G S)
   DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_mfma(G, B, T, p, Pb, pbs, Yb, s));
@@ -364,7 +364,8 @@ static dp_status_t norm_est_impl(int method, int dtype, int B, int T, int d, int
                                  uint32_t flags, float* n_sq, void* ws, size_t ws_bytes,
                                  dp_stream_t stream, const Marks& mk) {
   if (!norm_args_ok(method, dtype, B, T, d, p, k)) return DP_ERR_INVALID_ARG;
-  if ((flags & ~(DP_ACCUMULATE | DP_PROBE_SHARED)) != 0) return DP_ERR_INVALID_ARG;
+  if ((flags & ~(DP_ACCUMULATE | DP_PROBE_SHARED | DP_PROBE_RADEMACHER)) != 0)
+    return DP_ERR_INVALID_ARG;
   if (B == 0) return DP_OK;
   if (n_sq == nullptr || !aligned(n_sq, 4)) return DP_ERR_INVALID_ARG;
   if (T > 0 && (A == nullptr || G == nullptr || !aligned(A, 16) || !aligned(G, 16)))
@@ -375,6 +376,7 @@ static dp_status_t norm_est_impl(int method, int dtype, int B, int T, int d, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool accum = (flags & DP_ACCUMULATE) != 0;
   const bool shared = (flags & DP_PROBE_SHARED) != 0;
+  const bool signs = (flags & DP_PROBE_RADEMACHER) != 0;
   const bool bf = dtype == DP_BF16;
   const bf16_t* Ab = static_cast<const bf16_t*>(A);
   const bf16_t* Gb = static_cast<const bf16_t*>(G);
@@ -382,13 +384,13 @@ static dp_status_t norm_est_impl(int method, int dtype, int B, int T, int d, int
   const float* Gf = static_cast<const float*>(G);
   switch (method) {
     case DP_NORM_HUTCH:
-      if (P.mfma) return run_norm_mfma_hutch(P, B, T, d, p, k, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s, mk);
-      return bf ? run_norm_generic_hutch<bf16_t>(P, B, T, d, p, k, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s, mk)
-                : run_norm_generic_hutch<float>(P, B, T, d, p, k, Af, Gf, seed, layer, shared, accum, n_sq, ws, s, mk);
+      if (P.mfma) return run_norm_mfma_hutch(P, B, T, d, p, k, Ab, Gb, seed, layer, shared, signs, accum, n_sq, ws, s, mk);
+      return bf ? run_norm_generic_hutch<bf16_t>(P, B, T, d, p, k, Ab, Gb, seed, layer, shared, signs, accum, n_sq, ws, s, mk)
+                : run_norm_generic_hutch<float>(P, B, T, d, p, k, Af, Gf, seed, layer, shared, signs, accum, n_sq, ws, s, mk);
     case DP_NORM_HUTCHPP:
-      if (P.mfma) return run_norm_mfma_hpp(P, B, T, d, p, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s, mk);
-      return bf ? run_norm_generic_hpp<bf16_t>(P, B, T, d, p, Ab, Gb, seed, layer, shared, accum, n_sq, ws, s, mk)
-                : run_norm_generic_hpp<float>(P, B, T, d, p, Af, Gf, seed, layer, shared, accum, n_sq, ws, s, mk);
+      if (P.mfma) return run_norm_mfma_hpp(P, B, T, d, p, Ab, Gb, seed, layer, shared, signs, accum, n_sq, ws, s, mk);
+      return bf ? run_norm_generic_hpp<bf16_t>(P, B, T, d, p, Ab, Gb, seed, layer, shared, signs, accum, n_sq, ws, s, mk)
+                : run_norm_generic_hpp<float>(P, B, T, d, p, Af, Gf, seed, layer, shared, signs, accum, n_sq, ws, s, mk);
     default:
       return bf ? run_norm_exact<bf16_t>(method, P, B, T, d, p, Ab, Gb, accum, n_sq, ws, s, mk)
                 : run_norm_exact<float>(method, P, B, T, d, p, Af, Gf, accum, n_sq, ws, s, mk);
@@ -623,6 +625,16 @@ dp_status_t dp_probe_fill(uint64_t seed, uint32_t layer, uint32_t sample, int p,
   if (p < 1 || k < 1 || Pt == nullptr || !aligned(Pt, 4)) return DP_ERR_INVALID_ARG;
   DP_TRY(launch_probe_fill_f32(seed, layer, sample, 1, p, k, k, Pt,
                                static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
+dp_status_t dp_probe_fill_ex(uint64_t seed, uint32_t layer, uint32_t sample, int p, int k,
+                             uint32_t flags, float* Pt, dp_stream_t stream) {
+  if ((flags & ~DP_PROBE_RADEMACHER) != 0) return DP_ERR_INVALID_ARG;
+  if (p < 1 || k < 1 || Pt == nullptr || !aligned(Pt, 4)) return DP_ERR_INVALID_ARG;
+  DP_TRY(launch_probe_fill_f32(seed, layer, sample, 1, p, k, k, Pt,
+                               static_cast<hipStream_t>(stream),
+                               (flags & DP_PROBE_RADEMACHER) != 0));
   return DP_OK;
 }
 

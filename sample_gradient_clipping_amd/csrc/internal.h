@@ -18,13 +18,15 @@ hipError_t launch_philox_u32(uint64_t seed, const uint32_t* ctr, uint32_t* out, 
                              hipStream_t s);
 // Probe P^T of `nsamp` samples (sample index = sample0 + i): out[i][j][r] for
 // j < kpad, r < p; columns j >= kfill are zero.
+// signs: Rademacher +-1 entries instead of normals (same counters and lanes).
 hipError_t launch_probe_fill_f32(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
-                                 int p, int kfill, int kpad, float* out, hipStream_t s);
+                                 int p, int kfill, int kpad, float* out, hipStream_t s,
+                                 bool signs = false);
 // The bf16 fill also clears zero[0 .. nzero) (counters used by a later kernel
 // of the same call), saving a launch.
 hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
                                   int p, int kfill, int kpad, bf16_t* out, hipStream_t s,
-                                  uint32_t* zero = nullptr, int nzero = 0);
+                                  bool signs = false, uint32_t* zero = nullptr, int nzero = 0);
 hipError_t launch_noise_fill(uint64_t seed, uint32_t layer, uint64_t offset, size_t n, float* xi,
                              hipStream_t s);
 hipError_t launch_noise_update(float* theta, const float* S, int64_t n, float sigmaC,

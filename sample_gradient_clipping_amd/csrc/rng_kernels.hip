@@ -37,10 +37,12 @@ hipError_t launch_philox_u32(uint64_t seed, const uint32_t* ctr, uint32_t* out, 
 }
 
 // One thread per (sample, column j, row group g): four rows 4g..4g+3 of column j.
+// signs != 0: Rademacher entries, +1 when the counter word's top bit is 0 and
+// -1 otherwise (summary, section 意義と主張: {+-1}-valued sketching matrices).
 template <typename TOut>
 __global__ void k_probe_fill(uint32_t k0, uint32_t k1, uint32_t layer, uint32_t sample0, int p,
                              int kfill, int kpad, TOut* __restrict__ out,
-                             uint32_t* __restrict__ zero, int nzero) {
+                             uint32_t* __restrict__ zero, int nzero, int signs) {
   const int ngroups = (p + 3) >> 2;
   const int g = blockIdx.x * blockDim.x + threadIdx.x;
   const int j = blockIdx.y;
@@ -55,7 +57,13 @@ __global__ void k_probe_fill(uint32_t k0, uint32_t k1, uint32_t layer, uint32_t 
     c.y = static_cast<uint32_t>(j);
     c.z = sample0 + static_cast<uint32_t>(i);
     c.w = layer;
-    normals4(c, k0, k1, z);
+    if (signs) {
+      const u32x4 w = philox4x32_10(c, k0, k1);
+#pragma unroll
+      for (int l = 0; l < 4; ++l) z[l] = (w[l] >> 31) ? -1.f : 1.f;
+    } else {
+      normals4(c, k0, k1, z);
+    }
   }
   TOut* row = out + (static_cast<int64_t>(i) * kpad + j) * p;
 #pragma unroll
@@ -72,26 +80,29 @@ __global__ void k_probe_fill(uint32_t k0, uint32_t k1, uint32_t layer, uint32_t 
 
 template <typename TOut>
 static hipError_t probe_fill(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp, int p,
-                             int kfill, int kpad, TOut* out, hipStream_t s, uint32_t* zero,
-                             int nzero) {
+                             int kfill, int kpad, TOut* out, hipStream_t s, bool signs,
+                             uint32_t* zero, int nzero) {
   if (nsamp <= 0 || p <= 0 || kpad <= 0) return hipSuccess;
   const int ngroups = (p + 3) >> 2;
   dim3 grid((ngroups + 255) / 256, kpad, nsamp);
   hipLaunchKernelGGL(k_probe_fill<TOut>, grid, dim3(256), 0, s, static_cast<uint32_t>(seed),
                      static_cast<uint32_t>(seed >> 32), layer, sample0, p, kfill, kpad, out, zero,
-                     nzero);
+                     nzero, signs ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_probe_fill_f32(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
-                                 int p, int kfill, int kpad, float* out, hipStream_t s) {
-  return probe_fill<float>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s, nullptr, 0);
+                                 int p, int kfill, int kpad, float* out, hipStream_t s,
+                                 bool signs) {
+  return probe_fill<float>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s, signs, nullptr,
+                           0);
 }
 
 hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
                                   int p, int kfill, int kpad, bf16_t* out, hipStream_t s,
-                                  uint32_t* zero, int nzero) {
-  return probe_fill<bf16_t>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s, zero, nzero);
+                                  bool signs, uint32_t* zero, int nzero) {
+  return probe_fill<bf16_t>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s, signs, zero,
+                            nzero);
 }
 
 __device__ __forceinline__ u32x4 noise_counter(uint64_t grp, uint32_t layer) {

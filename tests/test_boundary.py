@@ -75,6 +75,7 @@ def test_norm_est_rejects_bad_arguments(lib):
     assert _norm(lib, d=0) == E
     assert _norm(lib, B=-1) == E
     assert _norm(lib, flags=8) == E
+    assert _norm(lib, flags=dp.DP_PROBE_RADEMACHER | 16) == E
     assert _norm(lib, A=NULL) == E
     assert _norm(lib, G=FAKE_MIS) == E
     assert _norm(lib, n=NULL) == E
@@ -153,4 +154,7 @@ def test_test_hooks_reject_bad_arguments(lib):
     assert lib.dp_probe_fill(1, 0, 0, 0, 4, FAKE, NULL) == E
     assert lib.dp_probe_fill(1, 0, 0, 4, 4, NULL, NULL) == E
     assert lib.dp_noise_fill(1, 0, 0, 4, NULL, NULL) == E
+    assert lib.dp_probe_fill_ex(1, 0, 0, 4, 4, 8, FAKE, NULL) == E  # unknown flag
+    assert lib.dp_probe_fill_ex(1, 0, 0, 4, 4, dp.DP_PROBE_SHARED, FAKE, NULL) == E
+    assert lib.dp_probe_fill_ex(1, 0, 0, 0, 4, dp.DP_PROBE_RADEMACHER, FAKE, NULL) == E
     assert lib.dp_noise_fill(1, 0, 2**64 - 2, 4, FAKE, NULL) == E

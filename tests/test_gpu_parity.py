@@ -100,6 +100,50 @@ def test_norm_parity(dev, method, case):
     assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
+# ---------------------------------------------------------------------------
+# sign (Rademacher) probes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed,layer,sample,p,k", [(5, 3, 7, 37, 5), (2002, 0, 1, 2048, 32)])
+def test_rademacher_probe_bit_exact(dev, seed, layer, sample, p, k):
+    Pt = torch.zeros(k, p, dtype=torch.float32, device=dev)
+    dp.dp_probe_fill(seed, layer, sample, p, k, Pt, rademacher=True)
+    torch.cuda.synchronize()
+    ref = oracle.rademacher_probe_matrix(seed, layer, sample, p, k).T
+    assert np.array_equal(f64(Pt), ref)
+
+
+@pytest.mark.parametrize("method", ["hutch", "hutchpp"])
+@pytest.mark.parametrize("case", NORM_CASES, ids=[c[0] for c in NORM_CASES])
+def test_norm_parity_rademacher(dev, method, case):
+    name, dtype, B, T, d, p, k = case
+    recipe = "unit_u0.1_3" if dtype == "f32" else "llama_logu"
+    A, G = linear_inputs(B, T, d, p, dtype, recipe, seed=13 + T)
+    n = torch.full((B,), -1.0, dtype=torch.float32, device=dev)
+    dp.dp_norm_est(method, A.to(dev), G.to(dev), k, 778, 6, n, flags=dp.DP_PROBE_RADEMACHER)
+    torch.cuda.synchronize()
+    ref = oracle.norm_est(method, A, G, k=k, seed=778, layer=6, rademacher=True)
+    err = max_rel_elementwise(f64(n), ref)
+    report(f"norm {method} rademacher {name}", max_rel=err)
+    assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+
+
+def test_rademacher_exact_on_diagonal_O(dev):
+    # A = I (T = d), G = U diag(s) with orthonormal U: O = diag(s^2), and sign
+    # probes give tr(O) for every seed (fp32 rounding only).
+    d, p = 64, 48
+    r = np.random.default_rng(8)
+    U, _ = np.linalg.qr(r.standard_normal((d, p)))
+    sv = r.uniform(0.5, 3.0, size=p)
+    A = torch.eye(d, dtype=torch.float32).reshape(1, d, d).repeat(2, 1, 1)
+    G = torch.from_numpy((U * sv[None, :]).astype(np.float32)).reshape(1, d, p).repeat(2, 1, 1)
+    exact = oracle.norm_est("fgc", A, G)
+    for seed in range(3):
+        n = torch.zeros(2, dtype=torch.float32, device=dev)
+        dp.dp_norm_est("hutch", A.to(dev), G.to(dev), 4, seed, 0, n, flags=dp.DP_PROBE_RADEMACHER)
+        torch.cuda.synchronize()
+        assert max_rel_elementwise(f64(n), exact) <= TOL_F32
+
+
 @pytest.mark.parametrize("dtype,shape", [("f32", (3, 40, 24, 20)), ("bf16", (2, 256, 256, 256))])
 def test_norm_flags_shared_and_accumulate(dev, dtype, shape):
     B, T, d, p = shape
