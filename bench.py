@@ -149,6 +149,41 @@ def cpu_baseline(wl, method, target_s=12.0, rademacher=False):
             "kind": "oracle", "sample": sample}
 
 
+def estimator_accuracy(dp, wl, layer_inputs, dev, nseeds=8, rademacher=False):
+    """Relative RMS error of Hutch and Hutch++ (k = the workload's k) against the
+    exact norms (the FGC contraction on the GPU) on the first layer, over
+    ``nseeds`` probe seeds and all samples, with each estimator's time per
+    call.  Outside the timed steps; not part of the throughput."""
+    import torch
+    A, G = layer_inputs
+    B = A.shape[0]
+    l = wl.layers[0]
+    exact = torch.zeros(B, dtype=torch.float32, device=dev)
+    dp.dp_norm_est("fgc", A, G, 0, 0, 0, exact)
+    flags = dp.DP_PROBE_RADEMACHER if rademacher else 0
+    out = {"layer": l.name, "k": wl.k, "seeds": nseeds, "exact": "FGC contraction on the GPU",
+           "probes": "rademacher" if rademacher else "gaussian"}
+    for m in ("hutch", "hutchpp"):
+        ws = torch.empty(dp.dp_norm_est_workspace(m, wl.dtype, B, wl.T, l.d, l.p, wl.k),
+                         dtype=torch.uint8, device=dev)
+        n = torch.zeros(B, dtype=torch.float32, device=dev)
+        dp.dp_norm_est(m, A, G, wl.k, 0, l.layer_id, n, flags=flags, ws=ws)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        errs = []
+        ms = 0.0
+        for sd in range(nseeds):
+            e0.record()
+            dp.dp_norm_est(m, A, G, wl.k, 9000 + sd, l.layer_id, n, flags=flags, ws=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ms += e0.elapsed_time(e1)
+            errs.append((n.double() / exact.double() - 1.0).cpu())
+        e = torch.stack(errs)
+        out[f"{m}_rel_rms"] = float(torch.sqrt(torch.mean(e * e)))
+        out[f"{m}_us_per_call"] = ms / nseeds * 1e3
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -306,6 +341,9 @@ def main():
             f"{kv['GBps']:8.1f} GB/s  {kv.get('TFLOPs', 0):8.1f} TF/s  frac {kv['frac']:.3f}  "
             f"share {kv['share_of_step']:.2f}")
 
+    accuracy = estimator_accuracy(dp, wl, inputs[0][0], dev, rademacher=args.rademacher)
+    log(f"[bench] estimator accuracy {accuracy}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
@@ -323,6 +361,7 @@ def main():
                    "input_copies": copies, "global_batch": wl.B, "seq_len": wl.T},
         "roofline": roof,
         "kernels": kernels,
+        "estimator_accuracy": accuracy,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -59,7 +59,7 @@ def llama_1b_stack(blocks=16, hidden=2048, kv=512, ffn=8192):
 
 
 def workloads():
-    """The five configurations by short name."""
+    """The workloads by name: five configurations and one spectrum-structured layer."""
     w = {}
     w["tiny_f32_b4_t64"] = Workload(
         "tiny_f32_b4_t64", B=4, T=64, dtype="f32",
@@ -91,6 +91,14 @@ def workloads():
         C=1.0, sigma=1.0, eta=1e-4, recipe="llama_logu",
         data_seed=1004, method_seed=2004, noise_seed=3004,
         baselines=("ghost", "fgc"))
+    # a spectrum-structured layer (rank-8 signal + 5% noise in A and G): the
+    # head that Hutch++ takes exactly carries most of tr(O)
+    w["lowrank_attn_b8_t4096_d2048"] = Workload(
+        "lowrank_attn_b8_t4096_d2048", B=8, T=4096, dtype="bf16",
+        layers=[Layer("q_proj", 0, 2048, 2048)], method="hutchpp", k=32,
+        C=1.0, sigma=1.0, eta=1e-4, recipe="lowrank",
+        data_seed=1006, method_seed=2006, noise_seed=3006,
+        baselines=("hutch", "fgc"))
     w["llama1b_stack_b8_t4096"] = Workload(
         "llama1b_stack_b8_t4096", B=8, T=4096, dtype="bf16",
         layers=llama_1b_stack(), method="hutch", k=32,

@@ -80,9 +80,19 @@ def linear_inputs_device(B, T, d, p, dtype, recipe, seed, layer_id, device):
     gen.manual_seed((int(seed) * 1_000_003 + int(layer_id)) & 0x7FFFFFFFFFFFFFFF)
     td = torch_dtype(dtype)
     s = torch.from_numpy(sample_scales(B, recipe, seed, layer_id).astype(np.float32)).to(device)
-    A = torch.randn((B, T, d), generator=gen, device=device, dtype=torch.float32).to(td)
-    G = torch.randn((B, T, p), generator=gen, device=device, dtype=torch.float32)
-    if recipe == "llama_logu":
-        G *= 0.01
+    if recipe == "lowrank":
+        def lowrank(n, rank=8, noise=0.05):
+            U = torch.randn((B, T, rank), generator=gen, device=device, dtype=torch.float32)
+            V = torch.randn((B, rank, n), generator=gen, device=device,
+                            dtype=torch.float32) / float(np.sqrt(rank))
+            E = torch.randn((B, T, n), generator=gen, device=device, dtype=torch.float32)
+            return torch.bmm(U, V) + noise * E
+        A = lowrank(d).to(td)
+        G = lowrank(p) * 0.01
+    else:
+        A = torch.randn((B, T, d), generator=gen, device=device, dtype=torch.float32).to(td)
+        G = torch.randn((B, T, p), generator=gen, device=device, dtype=torch.float32)
+        if recipe == "llama_logu":
+            G *= 0.01
     G = (G * s[:, None, None]).to(td)
     return A, G

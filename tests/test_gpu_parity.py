@@ -100,6 +100,53 @@ def test_norm_parity(dev, method, case):
     assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
+LOWRANK_CASES = [
+    # (name, dtype, B, T, d, p, k): rank-8 signal plus noise (decaying spectrum)
+    ("lowrank_f32", "f32", 3, 96, 64, 80, 12),
+    ("lowrank_bf16", "bf16", 2, 256, 256, 512, 32),  # MFMA path
+]
+
+
+@pytest.mark.parametrize("method", ["hutch", "hutchpp", "ghost", "fgc"])
+@pytest.mark.parametrize("case", LOWRANK_CASES, ids=[c[0] for c in LOWRANK_CASES])
+def test_norm_parity_lowrank(dev, method, case):
+    name, dtype, B, T, d, p, k = case
+    A, G = linear_inputs(B, T, d, p, dtype, "lowrank", seed=17 + T)
+    n = torch.full((B,), -1.0, dtype=torch.float32, device=dev)
+    dp.dp_norm_est(method, A.to(dev), G.to(dev), k, 779, 2, n)
+    torch.cuda.synchronize()
+    ref = oracle.norm_est(method, A, G, k=k, seed=779, layer=2)
+    err = max_rel_elementwise(f64(n), ref)
+    report(f"norm {method} {name}", max_rel=err)
+    assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
+
+
+def test_hutchpp_more_accurate_on_lowrank(dev):
+    # On a decaying spectrum the sketch captures the head of tr(O) exactly and
+    # only the small tail is estimated; on i.i.d. data (flat spectrum) the
+    # plain estimator with all k probes on the trace has the smaller error.
+    B, T, d, p, k = 4, 512, 256, 256, 32
+
+    def rel_rms(recipe, method):
+        A, G = linear_inputs(B, T, d, p, "bf16", recipe, seed=5)
+        A, G = A.to(dev), G.to(dev)
+        exact = torch.zeros(B, dtype=torch.float32, device=dev)
+        dp.dp_norm_est("fgc", A, G, 0, 0, 0, exact)
+        errs = []
+        for s in range(8):
+            n = torch.zeros(B, dtype=torch.float32, device=dev)
+            dp.dp_norm_est(method, A, G, k, 100 + s, 2, n)
+            errs.append(f64(n) / f64(exact) - 1.0)
+        return float(np.sqrt(np.mean(np.square(errs))))
+
+    lr = {m: rel_rms("lowrank", m) for m in ("hutch", "hutchpp")}
+    iid = {m: rel_rms("llama_logu", m) for m in ("hutch", "hutchpp")}
+    report("rel rms lowrank", **lr)
+    report("rel rms iid", **iid)
+    assert lr["hutchpp"] < 1e-2 * lr["hutch"]
+    assert iid["hutch"] < iid["hutchpp"]
+
+
 # ---------------------------------------------------------------------------
 # sign (Rademacher) probes
 # ---------------------------------------------------------------------------

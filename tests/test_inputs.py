@@ -31,3 +31,16 @@ def test_theta_init():
     assert torch.count_nonzero(theta_init(4, 5, 1, zero=True)) == 0
     t = theta_init(64, 64, 1)
     assert abs(t.std().item() - 0.02) < 0.002
+
+
+def test_lowrank_recipe_spectrum():
+    # rank-8 signal plus 0.05 noise: for T >> 8 the top 8 singular values of
+    # each A_i hold almost all of its energy, the 9th drops to the noise floor
+    A, G = linear_inputs(2, 512, 96, 80, "f32", "lowrank", seed=3)
+    for X in (A, G):
+        for i in range(2):
+            sv = np.linalg.svd(X[i].double().numpy(), compute_uv=False)
+            assert sv[8] < 0.1 * sv[7]
+            assert np.sum(sv[:8] ** 2) > 0.97 * np.sum(sv ** 2)
+    s = sample_scales(2, "lowrank", 3)
+    assert np.all((s >= 0.1) & (s <= 10))
