@@ -97,7 +97,8 @@ size_t dp_norm_est_workspace(int method, int dtype, int B, int T, int d, int p, 
  *  B, T    batch size (>= 0) and tokens per sample (>= 0); B = 0 is a no-op,
  *          T = 0 gives n_i = 0.
  *  d, p    layer input / output widths (>= 1).
- *  k       probes: HUTCH 1 <= k <= p; HUTCHPP 3 <= k <= p; ignored for exact methods.
+ *  k       probes: HUTCH 1 <= k <= p; HUTCHPP 3 <= k <= p with s = k/3 <= 32 and
+ *          r = k - 2s <= 32 (so k <= 96, k != 95); ignored for exact methods.
  *  A       [B][T][d] device, dtype.      G  [B][T][p] device, dtype.
  *  seed    64-bit Philox4x32-10 key of the probe stream.
  *  layer   layer index (counter word), so layers draw independent probes.

@@ -61,7 +61,8 @@ bool norm_args_ok(int method, int dtype, int B, int T, int d, int p, int k) {
   if (B < 0 || T < 0 || d < 1 || p < 1) return false;
   if (static_cast<int64_t>(T) * (d > p ? d : p) > (static_cast<int64_t>(1) << 40)) return false;
   if (method == DP_NORM_HUTCH && (k < 1 || k > p)) return false;
-  if (method == DP_NORM_HUTCHPP && (k < 3 || k > p || k / 3 > 32)) return false;
+  if (method == DP_NORM_HUTCHPP && (k < 3 || k > p || k / 3 > 32 || k - 2 * (k / 3) > 32))
+    return false;
   return true;
 }
 
@@ -103,7 +104,6 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
       P.zp = cv.take(Bz * P.nsplit_d * kMfmaProbeCols * d * f4);
       P.z1b = cv.take(Bz * kMfmaProbeCols * d * h2);
       P.xp = cv.take(Bz * P.nsplit_p * kMfmaProbeCols * p * f4);
-      P.x = cv.take(Bz * kMfmaProbeCols * p * f4);
       P.p3b = cv.take(Bz * kMfmaProbeCols * p * h2);
       P.ctr = cv.take(Bz * 4);
       P.nchunk = frob_finish_chunks(d);
@@ -213,7 +213,8 @@ dp_status_t run_norm_generic_hpp(const NormPlan& P, int B, int T, int d, int p, 
   DP_TRY(launch_sketch_generic<TIn>(A, B, T, d, Z, static_cast<int64_t>(S_) * d, S_, V, s));
   DP_TRY(launch_project_generic<TIn>(G, B, T, p, V, S_, X, s));
   // Q = orth(X), W' = (I - Q Q^T) W
-  DP_TRY(launch_hpp_orth(X, S_, Pf, pbs, K3, B, p, S_, R_, P3, at<double>(ws, P.orth), s));
+  DP_TRY(launch_hpp_orth(X, 1, 0, static_cast<int64_t>(S_) * p, Pf + static_cast<int64_t>(S_) * p,
+                         pbs, B, p, S_, R_, P3, nullptr, 0, at<double>(ws, P.orth), s));
   // pass 3: head + tail / r
   DP_TRY(launch_sketch_generic<TIn>(G, B, T, p, P3, static_cast<int64_t>(K3) * p, K3, Y, s));
   DP_TRY(launch_project_generic<TIn>(A, B, T, d, Y, K3, Z, s));
@@ -234,7 +235,6 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
   float* Zp = at<float>(ws, P.zp);
   bf16_t* Z1b = at<bf16_t>(ws, P.z1b);
   float* Xp = at<float>(ws, P.xp);
-  float* X = at<float>(ws, P.x);
   bf16_t* P3b = at<bf16_t>(ws, P.p3b);
   double* part = at<double>(ws, P.part);
   const int nS = shared ? 1 : B;
@@ -253,11 +253,9 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
   // pass 2: X = G^T (A Z1)
   DP_TRY(launch_sketch_mfma(A, B, T, d, Z1b, pad_d, Yb, s));
   DP_TRY(launch_project_mfma(G, B, T, p, Yb, P.nsplit_p, Xp, s));
-  DP_TRY(launch_sum_splits(Xp, B, P.nsplit_p, kMfmaProbeCols, p, X, nullptr, s));
-  // Q = orth(X), W' = (I - Q Q^T) W
-  DP_TRY(launch_hpp_orth(X, kMfmaProbeCols, Pf, pfs, K3, B, p, S_, R_, P3, at<double>(ws, P.orth),
-                         s));
-  DP_TRY(launch_to_bf16_pad(P3, B, K3, kMfmaProbeCols, p, P3b, s));
+  // Q = orth(X) over the projection's split partials, W' = (I - Q Q^T) W, as bf16 rows
+  DP_TRY(launch_hpp_orth(Xp, P.nsplit_p, pad_p, P.nsplit_p * pad_p, Pf + static_cast<int64_t>(S_) * p,
+                         pfs, B, p, S_, R_, P3, P3b, kMfmaProbeCols, at<double>(ws, P.orth), s));
   // pass 3
   DP_TRY(launch_sketch_mfma(G, B, T, p, P3b, pad_p, Yb, s));
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));

@@ -320,264 +320,510 @@ hipError_t launch_reduce_splits(const float* part, int nsplit, int64_t n, float*
 // Hutch++ (summary, section 中核メカニズム, item 2): orthonormal basis Q of the
 // sketch X = O S, then the deflated tail probes W' = W - Q (Q^T W).  Any
 // stable QR spans the same subspace and the estimate depends only on that
-// span; this one is CholeskyQR2 (Gram matrix and Cholesky factor in fp64,
-// applied twice).  A pivot that vanishes relative to the largest one (rank
-// deficiency) zeroes its column of Q; the remaining columns still span
-// range(X) and Q Q^T is the orthogonal projector onto it.  The vectors of
-// length p are rows here (X^T's columns).  Work is split over chunks of
-// kOrthChunk elements of p so that every step has many blocks:
-//   k_orth_dots    partial inner products of row sets over one chunk;
-//   k_orth_apply   sums the partials in a fixed order, factors the Gram
-//                  (redundantly per block; tiny) and writes Q = rows R^-1;
-//   k_orth_deflate W' = W - Q H from the summed partial products H = Q W^T.
+// span; this one is CholeskyQR (Gram matrix and its factor in fp64), repeated
+// once on Q1 when Q1 is not yet orthonormal to fp32 precision (CholeskyQR2;
+// ill-conditioned or rank-deficient sketches).  A pivot that vanishes
+// relative to the largest diagonal entry zeroes its column of Q; the
+// remaining columns still span range(X) and Q Q^T is the orthogonal
+// projector onto it.  The vectors of length p are rows here (X^T's columns),
+// split into chunks of kOrthChunk elements, one block per (chunk, sample);
+// every reduction over p is a set of per-chunk fp64 partials that the next
+// launch sums in chunk order.  Three launches:
+//   k_orth_gram   X = the sum of the sketch's split partials; Gram(X) partials.
+//   k_orth_first  R1 from Gram(X); Q1 = X R1^-1 (stored); partials of
+//                 Gram(Q1) and H1 = Q1 W^T.
+//   k_orth_final  R2 from Gram(Q1) (the identity when Gram(Q1) is within
+//                 kOrthTol of I); Q = Q1 R2^-1; H = Q W^T = R2^-T H1;
+//                 W' = W - H^T Q; writes [Q; W'] in fp32 or as zero-padded
+//                 bf16 rows.
+// Every step here is latency-bound (a few hundred KB per call), so the code
+// is arranged around memory and LDS round trips: partial sums are loaded
+// before the operands, the factorisation runs on one wave, and no global
+// load sits under a condition.
 // ---------------------------------------------------------------------------
 constexpr int kOrthMaxCols = 32;
 constexpr int kOrthChunk = 256;
+constexpr int kOrthRow = kOrthChunk + 4;  // LDS row stride: 16-byte aligned, rows on distinct banks
+constexpr double kOrthTol = 1e-7;  // |Gram(Q1) - I| entries below this skip the second factor
 
 int orth_chunks(int p) { return (p + kOrthChunk - 1) / kOrthChunk; }
+__host__ __device__ inline int orth_gram_pairs(int s) { return s * (s + 1) / 2; }  // packed upper triangle
 
-// part[b][chunk][i * nv + j] = sum_{e in chunk} U[i][e] V[j][e], fp64.
-__global__ void __launch_bounds__(kOrthChunk) k_orth_dots(
-    const float* __restrict__ U, int64_t u_bstride, int nu, const float* __restrict__ V,
-    int64_t v_bstride, int nv, int p, double* __restrict__ part) {
-  __shared__ float su[kOrthMaxCols][kOrthChunk];
-  __shared__ float sv[kOrthMaxCols][kOrthChunk];
-  const int b = blockIdx.y, chunk = blockIdx.x;
-  const int e0 = chunk * kOrthChunk;
-  const int e = e0 + threadIdx.x;
-  const float* ub = U + b * u_bstride;
-  const float* vb = V + b * v_bstride;
-  // all loads first, then the LDS stores (one memory round trip, not one per row)
-  float ru[kOrthMaxCols], rv[kOrthMaxCols];
-#pragma unroll
-  for (int i = 0; i < kOrthMaxCols; ++i) {
-    ru[i] = (i < nu && e < p) ? ub[static_cast<int64_t>(i) * p + e] : 0.f;
-    rv[i] = (i < nv && e < p) ? vb[static_cast<int64_t>(i) * p + e] : 0.f;
+__device__ __forceinline__ int packed_index(int i, int j) { return j * (j + 1) / 2 + i; }
+__device__ __forceinline__ void unpack_index(int pi, int* i, int* j) {
+  int c = 0;
+  while ((c + 1) * (c + 2) / 2 <= pi) ++c;
+  *j = c;
+  *i = pi - c * (c + 1) / 2;
+}
+
+// sum_t a[t] b[t] over one chunk held in LDS; exact fp32 products, fp64 sums
+// in four interleaved accumulators combined in a fixed order.
+__device__ __forceinline__ double chunk_dot(const float* a, const float* b) {
+  double acc0 = 0.0, acc1 = 0.0, acc2 = 0.0, acc3 = 0.0;
+#pragma unroll 4
+  for (int t = 0; t < kOrthChunk; t += 4) {
+    const float4 va = *reinterpret_cast<const float4*>(a + t);
+    const float4 vb = *reinterpret_cast<const float4*>(b + t);
+    acc0 = fma(static_cast<double>(va.x), static_cast<double>(vb.x), acc0);
+    acc1 = fma(static_cast<double>(va.y), static_cast<double>(vb.y), acc1);
+    acc2 = fma(static_cast<double>(va.z), static_cast<double>(vb.z), acc2);
+    acc3 = fma(static_cast<double>(va.w), static_cast<double>(vb.w), acc3);
   }
-#pragma unroll
-  for (int i = 0; i < kOrthMaxCols; ++i) {
-    if (i < nu) su[i][threadIdx.x] = ru[i];
-    if (i < nv) sv[i][threadIdx.x] = rv[i];
-  }
-  __syncthreads();
-  const int npairs = nu * nv;
-  double* out = part + (static_cast<int64_t>(b) * gridDim.x + chunk) * npairs;
-  for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) {
-    const int i = pi / nv, j = pi % nv;
-    double acc = 0.0;
-    for (int t = 0; t < kOrthChunk; ++t)
-      acc += static_cast<double>(su[i][t]) * static_cast<double>(sv[j][t]);
-    out[pi] = acc;
-  }
+  return (acc0 + acc1) + (acc2 + acc3);
 }
 
 // Sum of the chunk partials of one sample into LDS dst[npairs], each entry
-// added up in chunk order.  The partials are contiguous ([chunk][pair]), so
-// tiles of whole chunks are first copied into LDS with every thread loading
-// (one memory round trip per tile), then summed from LDS.
-constexpr int kSumStage = 4096;  // doubles of LDS staging
-__device__ void sum_chunks(const double* part_b, int nchunk, int npairs, double* dst,
-                           double* stage) {
-  for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) dst[pi] = 0.0;
-  const int tile = npairs < kSumStage ? kSumStage / npairs : 1;
-  for (int c0 = 0; c0 < nchunk; c0 += tile) {
+// added up in chunk order, by a block of kOrthChunk threads (a constant: the
+// block size read at run time is a memory load that would wait for every
+// load issued before it).  The partials are contiguous ([chunk][pair]); tiles
+// of whole chunks, kSumStage doubles at most, go through LDS.  The loads of
+// the first tile are issued by partials_issue() so that a kernel can put them
+// ahead of its operand loads: the memory counter drains in issue order, and
+// waiting for the partials then does not wait for the operands.
+constexpr int kSumStage = 4096;  // doubles of LDS staging, 16 per thread
+constexpr int kSumPer = kSumStage / kOrthChunk;
+
+__host__ __device__ inline int sum_tile_chunks(int npairs) {
+  return npairs < kSumStage ? kSumStage / npairs : 1;
+}
+
+__device__ __forceinline__ void partials_issue(const double* part_b, int nchunk, int npairs,
+                                               double (&v)[kSumPer]) {
+  const int tile = sum_tile_chunks(npairs);
+  const int n = (nchunk < tile ? nchunk : tile) * npairs;
+#pragma unroll
+  for (int k = 0; k < kSumPer; ++k) {  // clamped: no load under a condition
+    const int u = k * kOrthChunk + threadIdx.x;
+    v[k] = part_b[u < n ? u : n - 1];
+  }
+}
+
+__device__ void partials_sum(const double* part_b, int nchunk, int npairs, double (&v)[kSumPer],
+                             double* dst, double* stage) {
+  const int tile = sum_tile_chunks(npairs);
+  // first tile, straight-line: the stage holds exactly kSumPer values per
+  // thread, so every store is in bounds (entries past the tile are not read)
+  const int nc0 = nchunk < tile ? nchunk : tile;
+#pragma unroll
+  for (int k = 0; k < kSumPer; ++k) stage[k * kOrthChunk + threadIdx.x] = v[k];
+  __syncthreads();
+  for (int pi = threadIdx.x; pi < npairs; pi += kOrthChunk) {
+    double acc = 0.0;
+    for (int c = 0; c < nc0; ++c) acc += stage[c * npairs + pi];
+    dst[pi] = acc;
+  }
+  for (int c0 = tile; c0 < nchunk; c0 += tile) {
     const int nc = nchunk - c0 < tile ? nchunk - c0 : tile;
-    __syncthreads();
-    // sixteen loads in flight per thread before the first LDS store
     const int n = nc * npairs;
     const double* src = part_b + static_cast<int64_t>(c0) * npairs;
-    for (int u0 = 0; u0 < n; u0 += 16 * blockDim.x) {
-      double v[16];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int u = u0 + k * blockDim.x + threadIdx.x;
-        v[k] = u < n ? src[u] : 0.0;
-      }
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int u = u0 + k * blockDim.x + threadIdx.x;
-        if (u < n) stage[u] = v[k];
-      }
+    for (int k = 0; k < kSumPer; ++k) {
+      const int u = k * kOrthChunk + threadIdx.x;
+      v[k] = src[u < n ? u : n - 1];
     }
     __syncthreads();
-    for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) {
+#pragma unroll
+    for (int k = 0; k < kSumPer; ++k) stage[k * kOrthChunk + threadIdx.x] = v[k];
+    __syncthreads();
+    for (int pi = threadIdx.x; pi < npairs; pi += kOrthChunk) {
       double acc = dst[pi];
       for (int c = 0; c < nc; ++c) acc += stage[c * npairs + pi];
       dst[pi] = acc;
     }
   }
+  __syncthreads();
 }
 
-// Cholesky of the s x s Gram (dense, gram[i * s + j]; overwritten) and the
-// inverse of its factor, fp64, by the whole block (LDS arrays, one
-// synchronisation per step).  Right-looking: at step j the pivot row is
-// scaled and the trailing upper triangle is updated, so every entry receives
-// its rank-one corrections in the same order as the textbook left-looking
-// form.  A pivot that is not above tiny = 1e-24 * (largest diagonal) marks
-// column j dead: its row and column of R and of R^-1 are zero.
-__device__ void chol_inverse(double* gram, int s, double (*R)[kOrthMaxCols],
-                             double (*Rinv)[kOrthMaxCols], double* tiny_s, uint32_t* dead_s) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  if (tid == 0) {
-    double dmax = 0.0;
-    for (int i = 0; i < s; ++i) dmax = fmax(dmax, gram[i * s + i]);
-    *tiny_s = dmax * 1e-24;
-    *dead_s = 0u;
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), lane));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), lane));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// 1/d and 1/sqrt(d) for normal d > 0: the hardware estimate and two Newton
+// steps (each roughly doubles the correct bits), a few ulp from the rounded
+// quotient and far shorter than the IEEE division sequence, which matters in
+// the one-wave dependent chains below.
+__device__ __forceinline__ double recip_f64(double d) {
+  double r = __builtin_amdgcn_rcp(d);
+  r = fma(fma(-d, r, 1.0), r, r);
+  return fma(fma(-d, r, 1.0), r, r);
+}
+__device__ __forceinline__ double rsqrt_f64(double d) {
+  double y = __builtin_amdgcn_rsq(d);
+  y = fma(0.5 * y, fma(-d * y, y, 1.0), y);
+  return fma(0.5 * y, fma(-d * y, y, 1.0), y);
+}
+
+// Inverse Cholesky factor of the s x s Gram matrix given as a packed upper
+// triangle gp[packed_index(i, j)] (LDS).  Writes the transpose of R^-1,
+// RinvT[j * S + i] = R^-1[i][j] (zero for i > j), with Gram = R^T R = L D L^T
+// (L unit lower triangular), so R^-1 = L^-T D^-1/2.  A pivot not above 1e-24
+// x the largest diagonal entry marks its column dead (zero row and column of
+// R^-1).  Run by the first wave of the block; the caller synchronises after.
+//   Elimination: lane i holds row i of the trailing matrix in registers.  At
+//   step j lane j publishes its row in LDS (ws[0, S)) and every lane reads it
+//   back as broadcasts.  The trailing block stays symmetric, so lane i's
+//   multiplier L[i][j] = G[i][j] / d_j is entry i of the published row; it is
+//   stored at ws[S + i * S + j].  Entries left of the pivot are not read again
+//   and are left stale.  A wave executes its LDS operations in order, so the
+//   publish and the reads need no barrier, only a compiler fence.
+//   Inverse: lane c forms column c of L^-1 by forward substitution over the
+//   stored multipliers, all columns at once.
+// ws: LDS scratch of S * (S + 2) doubles.
+template <int S>
+__device__ __forceinline__ void inverse_cholesky_wave(const double* gp, int s, double* RinvT,
+                                                      double* ws) {
+  const int lane = threadIdx.x;
+  double* prow = ws;              // [S] published pivot row
+  double* Lm = ws + S;            // [S][S] multipliers
+  double* rs = ws + S + S * S;    // [S] 1/sqrt(d_j), 0 when dead
+  double g[S];
+  double diag = 0.0;
+#pragma unroll
+  for (int c = 0; c < S; ++c) {
+    const int i = lane < c ? lane : c, j = lane < c ? c : lane;
+    g[c] = (lane < s && c < s) ? gp[packed_index(i, j)] : 0.0;
+    diag = c == lane ? g[c] : diag;
   }
-  for (int u = tid; u < kOrthMaxCols * kOrthMaxCols; u += nt) {
-    R[u / kOrthMaxCols][u % kOrthMaxCols] = 0.0;
-    Rinv[u / kOrthMaxCols][u % kOrthMaxCols] = 0.0;
-  }
-  __syncthreads();
+  if (lane < S) prow[lane] = diag;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  double dmax = 0.0;
+#pragma unroll
+  for (int c = 0; c < S; ++c) dmax = fmax(dmax, prow[c]);  // zero beyond s
+  const double tiny = dmax * 1e-24;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const int me = lane < S ? lane : S - 1;
+  double piv = 0.0;  // lane j: its pivot, 0 when dead
+  const double2* prow2 = reinterpret_cast<const double2*>(prow);
+#pragma unroll 1
   for (int j = 0; j < s; ++j) {
-    const double djj = gram[j * s + j];
-    const bool dj = !(djj > *tiny_s);
-    const double rjj = dj ? 0.0 : sqrt(djj);
-    const double inv = dj ? 0.0 : 1.0 / rjj;
-    // row j of R
-    for (int c = j + tid; c < s; c += nt) R[j][c] = c == j ? rjj : gram[j * s + c] * inv;
-    if (tid == 0 && dj) *dead_s |= 1u << j;
-    __syncthreads();
-    // trailing update of the upper triangle: gram[i][c] -= R[j][i] R[j][c], j < i <= c
-    const int m = s - j - 1;
-    for (int u = tid; u < m * m; u += nt) {
-      const int i = j + 1 + u / m, c = j + 1 + u % m;
-      if (c >= i) gram[i * s + c] -= R[j][i] * R[j][c];
+    if (lane == j) {
+#pragma unroll
+      for (int c = 0; c < S; c += 2) reinterpret_cast<double2*>(prow)[c / 2] = make_double2(g[c], g[c + 1]);
     }
-    __syncthreads();
-  }
-  // R^-1 (upper triangular): lane j back-substitutes column j.
-  const uint32_t dead = *dead_s;
-  for (int j = tid; j < s; j += nt) {
-    if (dead >> j & 1u) continue;
-    for (int i = j; i >= 0; --i) {
-      if (dead >> i & 1u) continue;
-      double v = i == j ? 1.0 : 0.0;
-      for (int k = i + 1; k <= j; ++k) v -= R[i][k] * Rinv[k][j];
-      Rinv[i][j] = v / R[i][i];
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const double dj = prow[j];
+    const double gi = prow[me];
+    double pr[S];
+#pragma unroll
+    for (int c = 0; c < S; c += 2) {
+      const double2 v = prow2[c / 2];
+      pr[c] = v.x;
+      pr[c + 1] = v.y;
     }
+    const bool live = dj > tiny;
+    const double f = (live && lane > j && lane < s) ? gi * recip_f64(dj) : 0.0;
+    if (lane == j) piv = live ? dj : 0.0;
+    if (lane < S) Lm[lane * S + j] = f;
+#pragma unroll
+    for (int c = 0; c < S; ++c) g[c] = fma(-f, pr[c], g[c]);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
-  __syncthreads();
+  if (lane < S) rs[lane] = piv > 0.0 ? rsqrt_f64(piv) : 0.0;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  // column c = lane of L^-1: y_c = 1, y_i = -sum_{c <= k < i} L[i][k] y_k (i > c)
+  double y[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    double acc = 0.0;
+#pragma unroll
+    for (int k = 0; k < i; ++k) acc = fma(-Lm[i * S + k], y[k], acc);
+    y[i] = i == lane ? 1.0 : (i > lane && i < s ? acc : 0.0);
+  }
+  // R^-1[c][i] = L^-1[i][c] / sqrt(d_i), stored as RinvT[i][c]
+  if (lane < S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) RinvT[i * S + lane] = lane < s ? y[i] * rs[i] : 0.0;
+  }
 }
 
-// Q[j][e] = sum_{i <= j} X[i][e] Rinv[i][j], Rinv from the Gram partials of X.
-__global__ void __launch_bounds__(kOrthChunk) k_orth_apply(
-    const float* __restrict__ Xr, int64_t x_bstride, int s, int p,
-    const double* __restrict__ part, int nchunk, float* __restrict__ Q, int64_t q_bstride) {
-  __shared__ double gram[kOrthMaxCols * kOrthMaxCols];
-  __shared__ double R[kOrthMaxCols][kOrthMaxCols];
-  __shared__ double Rinv[kOrthMaxCols][kOrthMaxCols];
-  __shared__ double stage[kSumStage];
-  __shared__ double tiny;
-  __shared__ uint32_t dead;
-  const int b = blockIdx.y;
-  sum_chunks(part + static_cast<int64_t>(b) * nchunk * s * s, nchunk, s * s, gram, stage);
-  __syncthreads();
-  chol_inverse(gram, s, R, Rinv, &tiny, &dead);
-  const int e = blockIdx.x * kOrthChunk + threadIdx.x;
-  if (e >= p) return;
-  const float* xb = Xr + b * x_bstride;
-  float* qb = Q + b * q_bstride;
-  float x[kOrthMaxCols];
+// y[j] = sum_{i <= j} x[i] R^-1[i][j] for j < s (zero beyond), fp64, reading
+// row j of RinvT with 16-byte LDS loads; terms in ascending i.
+template <int S>
+__device__ __forceinline__ void apply_rinv(const float (&x)[S], const double* RinvT, int s,
+                                           double (&y)[S]) {
 #pragma unroll
-  for (int i = 0; i < kOrthMaxCols; ++i) x[i] = i < s ? xb[static_cast<int64_t>(i) * p + e] : 0.f;
-#pragma unroll
-  for (int j = 0; j < kOrthMaxCols; ++j) {
+  for (int j = 0; j < S; ++j) {
+    double acc = 0.0;
     if (j < s) {
-      double q = 0.0;
+      const double2* row = reinterpret_cast<const double2*>(RinvT + j * S);
 #pragma unroll
-      for (int i = 0; i <= j; ++i) q += static_cast<double>(x[i]) * Rinv[i][j];
-      qb[static_cast<int64_t>(j) * p + e] = static_cast<float>(q);
+      for (int i2 = 0; 2 * i2 <= j; ++i2) {
+        const double2 rv = row[i2];
+        acc = fma(static_cast<double>(x[2 * i2]), rv.x, acc);
+        if (2 * i2 + 1 <= j) acc = fma(static_cast<double>(x[2 * i2 + 1]), rv.y, acc);
+      }
     }
+    y[j] = acc;
   }
 }
 
-// W'[t][e] = W[t][e] - sum_i H[i][t] Q[i][e], H = summed partials of Q W^T.
-__global__ void __launch_bounds__(kOrthChunk) k_orth_deflate(
-    const float* __restrict__ Q, int64_t q_bstride, int s, const float* __restrict__ W,
-    int64_t w_bstride, int r, int p, const double* __restrict__ part, int nchunk,
-    float* __restrict__ Wout, int64_t wo_bstride) {
-  __shared__ double H[kOrthMaxCols * kOrthMaxCols];
-  __shared__ double stage[kSumStage];
-  const int b = blockIdx.y;
-  sum_chunks(part + static_cast<int64_t>(b) * nchunk * s * r, nchunk, s * r, H, stage);
-  __syncthreads();
-  const int e = blockIdx.x * kOrthChunk + threadIdx.x;
-  if (e >= p) return;
-  const float* qb = Q + b * q_bstride;
-  const float* wb = W + b * w_bstride;
-  float* ob = Wout + b * wo_bstride;
-  float q[kOrthMaxCols], w[kOrthMaxCols];
+// Global loads below are unconditional from clamped (always valid) addresses,
+// with out-of-range values replaced afterwards: a load under a condition
+// makes the compiler wait for it before the branch joins, which serialises
+// the whole batch of row loads into one memory latency each.
+
+// v[i] = rows[i][e] for i < nrows and e < p, else 0 (nrows >= 1, p >= 1).
+template <int N>
+__device__ __forceinline__ void load_rows(const float* base, int nrows, int p, int e,
+                                          float (&v)[N]) {
+  const int ec = e < p ? e : p - 1;
 #pragma unroll
-  for (int i = 0; i < kOrthMaxCols; ++i) {
-    q[i] = i < s ? qb[static_cast<int64_t>(i) * p + e] : 0.f;
-    w[i] = i < r ? wb[static_cast<int64_t>(i) * p + e] : 0.f;
+  for (int i = 0; i < N; ++i) v[i] = base[static_cast<int64_t>(i < nrows ? i : nrows - 1) * p + ec];
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = (i < nrows && e < p) ? v[i] : 0.f;
+}
+
+// Marks values as used at this point: arithmetic on them cannot be hoisted
+// above it, so waiting for the loads that produced them happens here.
+template <int N>
+__device__ __forceinline__ void use_here(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+// The sketch is the sum of the projection's split partials: x[i] = sum_sp
+// X[b][sp][i][e] (i < s), added in split order.  sketch_issue() loads splits
+// 0 and 1 (split 0 twice when there is one); sketch_finish() adds them and
+// any further splits.
+template <int S>
+__device__ __forceinline__ void sketch_issue(const float* xb, int nsplit, int64_t split_stride,
+                                             int s, int p, int e, float (&v0)[S], float (&v1)[S]) {
+  load_rows<S>(xb, s, p, e, v0);
+  load_rows<S>(xb + (nsplit > 1 ? split_stride : 0), s, p, e, v1);
+}
+
+template <int S>
+__device__ __forceinline__ void sketch_finish(const float* xb, int nsplit, int64_t split_stride,
+                                              int s, int p, int e, const float (&v0)[S],
+                                              const float (&v1)[S], float (&x)[S]) {
+#pragma unroll
+  for (int i = 0; i < S; ++i) x[i] = nsplit > 1 ? v0[i] + v1[i] : v0[i];
+  for (int sp = 2; sp < nsplit; ++sp) {
+    float v[S];
+    load_rows<S>(xb + sp * split_stride, s, p, e, v);
+#pragma unroll
+    for (int i = 0; i < S; ++i) x[i] += v[i];
+  }
+}
+
+// part1[b][chunk][packed (i, j)] = sum_{e in chunk} X[i][e] X[j][e].
+template <int S>
+__global__ void __launch_bounds__(kOrthChunk) k_orth_gram(
+    const float* __restrict__ Xp, int nsplit, int64_t split_stride, int64_t x_bstride, int s,
+    int p, double* __restrict__ part1) {
+  __shared__ __align__(16) float rows[S][kOrthRow];
+  const int b = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  const int e = chunk * kOrthChunk + tid;
+  const float* xb = Xp + b * x_bstride;
+  float x0[S], x1[S], x[S];
+  sketch_issue<S>(xb, nsplit, split_stride, s, p, e, x0, x1);
+  sketch_finish<S>(xb, nsplit, split_stride, s, p, e, x0, x1, x);
+#pragma unroll
+  for (int i = 0; i < S; ++i)
+    if (i < s) rows[i][tid] = x[i];
+  __syncthreads();
+  const int np = orth_gram_pairs(s);
+  double* out = part1 + (static_cast<int64_t>(b) * gridDim.x + chunk) * np;
+  for (int pi = tid; pi < np; pi += kOrthChunk) {
+    int i, j;
+    unpack_index(pi, &i, &j);
+    out[pi] = chunk_dot(rows[i], rows[j]);
+  }
+}
+
+// Q1 = X R1^-1 into Q1 rows 0..s-1; part2[b][chunk][.] = packed Gram(Q1)
+// partials, then H1[i][t] = sum_e Q1[i][e] W[t][e] at packed_pairs + i * r + t.
+// S, R: the largest s and r the instance handles.
+template <int S, int R>
+__global__ void __launch_bounds__(kOrthChunk) k_orth_first(
+    const float* __restrict__ Xp, int nsplit, int64_t split_stride, int64_t x_bstride, int s,
+    int p, const double* __restrict__ part1, const float* __restrict__ W, int64_t w_bstride, int r,
+    float* __restrict__ Q1, int64_t q_bstride, double* __restrict__ part2) {
+  __shared__ double stage[kSumStage];
+  __shared__ double gp[S * (S + 1) / 2];
+  __shared__ __align__(16) double RinvT[S * S];
+  __shared__ __align__(16) double chol_ws[S * (S + 2)];
+  __shared__ __align__(16) float rows[S + R][kOrthRow];
+  const int b = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x, nch = gridDim.x;
+  const int e = chunk * kOrthChunk + tid;
+  // partials first, then the operands: their latency overlaps the partial
+  // sums and the factorisation
+  const int np1 = orth_gram_pairs(s);
+  const double* pb = part1 + static_cast<int64_t>(b) * nch * np1;
+  double pv[kSumPer];
+  partials_issue(pb, nch, np1, pv);
+  const float* xb = Xp + b * x_bstride;
+  float x0[S], x1[S], x[S], w[R];
+  sketch_issue<S>(xb, nsplit, split_stride, s, p, e, x0, x1);
+  load_rows<R>(W + b * w_bstride, r, p, e, w);
+  partials_sum(pb, nch, np1, pv, gp, stage);
+  if (tid < 64) inverse_cholesky_wave<S>(gp, s, RinvT, chol_ws);
+  __syncthreads();
+  use_here<S>(x0);
+  use_here<S>(x1);
+  use_here<R>(w);
+  sketch_finish<S>(xb, nsplit, split_stride, s, p, e, x0, x1, x);
+  float* qb = Q1 + b * q_bstride;
+  double q[S];
+  apply_rinv<S>(x, RinvT, s, q);
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    if (j < s) {
+      const float qf = e < p ? static_cast<float>(q[j]) : 0.f;
+      rows[j][tid] = qf;
+      if (e < p) qb[static_cast<int64_t>(j) * p + e] = qf;
+    }
   }
 #pragma unroll
-  for (int t = 0; t < kOrthMaxCols; ++t) {
+  for (int t = 0; t < R; ++t)
+    if (t < r) rows[S + t][tid] = w[t];
+  __syncthreads();
+  const int np2 = np1 + s * r;
+  double* out = part2 + (static_cast<int64_t>(b) * nch + chunk) * np2;
+  for (int pi = tid; pi < np2; pi += kOrthChunk) {
+    int i, j;
+    if (pi < np1) {
+      unpack_index(pi, &i, &j);
+    } else {
+      i = (pi - np1) / r;
+      j = S + (pi - np1) % r;
+    }
+    out[pi] = chunk_dot(rows[i], rows[j]);
+  }
+}
+
+// Q = Q1 R2^-1, H = R2^-T H1, W' = W - H^T Q; rows 0..s-1 = Q, s..s+r-1 = W',
+// then zero rows up to out_rows.  TOut float: in place over Q1's buffer is
+// allowed (every thread reads its own elements before writing them).
+template <int S, int R, typename TOut>
+__global__ void __launch_bounds__(kOrthChunk) k_orth_final(
+    const float* Q1, int64_t q_bstride, int s, int p, const double* __restrict__ part2,
+    const float* __restrict__ W, int64_t w_bstride, int r, TOut* out, int64_t o_bstride,
+    int out_rows) {
+  __shared__ double stage[kSumStage];
+  __shared__ double gh[S * (S + 1) / 2 + S * R];
+  __shared__ __align__(16) double RinvT[S * S];
+  __shared__ __align__(16) double chol_ws[S * (S + 2)];
+  __shared__ __align__(16) double HT[R * S];  // HT[t * S + j] = H[j][t]
+  const int b = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x, nch = gridDim.x;
+  const int e = chunk * kOrthChunk + tid;
+  const int np1 = orth_gram_pairs(s);
+  const int np2 = np1 + s * r;
+  const double* pb = part2 + static_cast<int64_t>(b) * nch * np2;
+  double pv[kSumPer];
+  partials_issue(pb, nch, np2, pv);
+  float q1[S], w[R];
+  load_rows<S>(Q1 + b * q_bstride, s, p, e, q1);
+  load_rows<R>(W + b * w_bstride, r, p, e, w);
+  partials_sum(pb, nch, np2, pv, gh, stage);
+  // When Gram(Q1) is within kOrthTol of I, Q1 is already orthonormal to fp32
+  // precision (the precision Q is stored in), and the second factor is the
+  // identity; otherwise (ill-conditioned or rank-deficient sketches) factor it.
+  bool far = false;
+  for (int pi = tid; pi < np1; pi += kOrthChunk) {
+    int i, j;
+    unpack_index(pi, &i, &j);
+    far |= !(fabs(gh[pi] - (i == j ? 1.0 : 0.0)) <= kOrthTol);
+  }
+  if (__syncthreads_or(far)) {
+    if (tid < 64) inverse_cholesky_wave<S>(gh, s, RinvT, chol_ws);
+  } else {
+    for (int u = tid; u < S * S; u += kOrthChunk)
+      RinvT[u] = (u / S == u % S && u % S < s) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  // H[j][t] = sum_{i <= j} R2^-1[i][j] H1[i][t]
+  for (int u = tid; u < s * r; u += kOrthChunk) {
+    const int j = u / r, t = u % r;
+    double h = 0.0;
+    for (int i = 0; i <= j; ++i) h = fma(RinvT[j * S + i], gh[np1 + i * r + t], h);
+    HT[t * S + j] = h;
+  }
+  const int nz = S - s;  // rows t < r are read in full: zero their entries j >= s
+  for (int u = tid; u < r * nz; u += kOrthChunk) HT[(u / nz) * S + s + u % nz] = 0.0;
+  __syncthreads();
+  use_here<S>(q1);
+  use_here<R>(w);
+  if (e >= p) return;
+  double qd[S];
+  apply_rinv<S>(q1, RinvT, s, qd);
+  float q[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) q[j] = static_cast<float>(qd[j]);
+  TOut* ob = out + b * o_bstride;
+#pragma unroll
+  for (int j = 0; j < S; ++j)
+    if (j < s) ob[static_cast<int64_t>(j) * p + e] = to_out<TOut>(q[j]);
+#pragma unroll
+  for (int t = 0; t < R; ++t) {
     if (t < r) {
+      const double2* row = reinterpret_cast<const double2*>(HT + t * S);
       double v = w[t];
 #pragma unroll
-      for (int i = 0; i < kOrthMaxCols; ++i)
-        if (i < s) v -= H[i * r + t] * static_cast<double>(q[i]);
-      ob[static_cast<int64_t>(t) * p + e] = static_cast<float>(v);
+      for (int j2 = 0; j2 < S / 2; ++j2) {
+        const double2 hv = row[j2];
+        v = fma(-hv.x, static_cast<double>(q[2 * j2]), v);
+        v = fma(-hv.y, static_cast<double>(q[2 * j2 + 1]), v);
+      }
+      ob[static_cast<int64_t>(s + t) * p + e] = to_out<TOut>(static_cast<float>(v));
     }
   }
+  for (int row = s + r; row < out_rows; ++row) ob[static_cast<int64_t>(row) * p + e] = to_out<TOut>(0.f);
 }
 
 size_t hpp_orth_scratch_bytes(int B, int p, int s, int r) {
-  const int npairs = s * s > s * r ? s * s : s * r;
-  return static_cast<size_t>(B) * orth_chunks(p) * (npairs > 0 ? npairs : 1) * sizeof(double);
+  const int np1 = orth_gram_pairs(s), np2 = np1 + s * r;
+  return static_cast<size_t>(B) * orth_chunks(p) * (np1 + np2) * sizeof(double);
 }
 
-hipError_t launch_hpp_orth(const float* X, int xrows, const float* Pw, int64_t pw_bstride,
-                           int wrows, int B, int p, int s_cols, int r_cols, float* out,
-                           double* scratch, hipStream_t st) {
-  (void)wrows;
-  if (B <= 0) return hipSuccess;
-  if (s_cols < 1 || s_cols > kOrthMaxCols || r_cols > kOrthMaxCols) return hipErrorInvalidValue;
+template <int S, int R>
+static hipError_t orth_launch(const float* Xp, int nsplit, int64_t split_stride,
+                              int64_t x_bstride, const float* W, int64_t w_bstride, int B, int p,
+                              int s, int r, float* P3, bf16_t* P3b, int p3b_rows, double* scratch,
+                              hipStream_t st) {
   const int nch = orth_chunks(p);
-  const int64_t xs = static_cast<int64_t>(xrows) * p;
-  const int64_t os = static_cast<int64_t>(s_cols + r_cols) * p;
   const dim3 grid(nch, B);
-  // pass 1: Q1 = X R1^-1
-  hipLaunchKernelGGL(k_orth_dots, grid, dim3(kOrthChunk), 0, st, X, xs, s_cols, X, xs, s_cols, p,
-                     scratch);
-  hipLaunchKernelGGL(k_orth_apply, grid, dim3(kOrthChunk), 0, st, X, xs, s_cols, p, scratch, nch,
-                     out, os);
-  // pass 2: Q = Q1 R2^-1 (in place: each thread reads its element before writing it)
-  hipLaunchKernelGGL(k_orth_dots, grid, dim3(kOrthChunk), 0, st, out, os, s_cols, out, os, s_cols,
-                     p, scratch);
-  hipLaunchKernelGGL(k_orth_apply, grid, dim3(kOrthChunk), 0, st, out, os, s_cols, p, scratch, nch,
-                     out, os);
-  if (r_cols > 0) {
-    const float* W = Pw + static_cast<int64_t>(s_cols) * p;  // tail probe rows s .. s+r-1
-    hipLaunchKernelGGL(k_orth_dots, grid, dim3(kOrthChunk), 0, st, out, os, s_cols, W, pw_bstride,
-                       r_cols, p, scratch);
-    hipLaunchKernelGGL(k_orth_deflate, grid, dim3(kOrthChunk), 0, st, out, os, s_cols, W,
-                       pw_bstride, r_cols, p, scratch, nch, out + static_cast<int64_t>(s_cols) * p,
-                       os);
+  double* part1 = scratch;
+  double* part2 = scratch + static_cast<int64_t>(B) * nch * orth_gram_pairs(s);
+  const int64_t p3s = static_cast<int64_t>(s + r) * p;
+  hipLaunchKernelGGL(k_orth_gram<S>, grid, dim3(kOrthChunk), 0, st, Xp, nsplit, split_stride,
+                     x_bstride, s, p, part1);
+  hipLaunchKernelGGL((k_orth_first<S, R>), grid, dim3(kOrthChunk), 0, st, Xp, nsplit,
+                     split_stride, x_bstride, s, p, part1, W, w_bstride, r, P3, p3s, part2);
+  if (P3b) {
+    hipLaunchKernelGGL((k_orth_final<S, R, bf16_t>), grid, dim3(kOrthChunk), 0, st, P3, p3s, s,
+                       p, part2, W, w_bstride, r, P3b, static_cast<int64_t>(p3b_rows) * p,
+                       p3b_rows);
+  } else {
+    hipLaunchKernelGGL((k_orth_final<S, R, float>), grid, dim3(kOrthChunk), 0, st, P3, p3s, s, p,
+                       part2, W, w_bstride, r, P3, p3s, s + r);
   }
   return hipGetLastError();
 }
 
-__global__ void k_to_bf16_pad(const float* __restrict__ in, int rows_in, int rows_out, int W,
-                              bf16_t* __restrict__ out) {
-  const int b = blockIdx.y;
-  const int64_t E = static_cast<int64_t>(rows_out) * W;
-  const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (e >= E) return;
-  const int j = static_cast<int>(e / W);
-  const float v = j < rows_in ? in[(static_cast<int64_t>(b) * rows_in) * W + e] : 0.f;
-  out[static_cast<int64_t>(b) * E + e] = f32_to_bf16(v);
-}
-
-hipError_t launch_to_bf16_pad(const float* in, int B, int rows_in, int rows_out, int W,
-                              bf16_t* out, hipStream_t s) {
+hipError_t launch_hpp_orth(const float* Xp, int nsplit, int64_t split_stride, int64_t x_bstride,
+                           const float* W, int64_t w_bstride, int B, int p, int s, int r,
+                           float* P3, bf16_t* P3b, int p3b_rows, double* scratch, hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_to_bf16_pad, dim3(cdiv(static_cast<int64_t>(rows_out) * W, 256), B),
-                     dim3(256), 0, s, in, rows_in, rows_out, W, out);
-  return hipGetLastError();
+  if (s < 1 || s > kOrthMaxCols || r < 1 || r > kOrthMaxCols || nsplit < 1 || p < 1)
+    return hipErrorInvalidValue;
+  if (P3b && p3b_rows < s + r) return hipErrorInvalidValue;
+#define DPRC_ORTH(SS, RR)                                                                       \
+  return orth_launch<SS, RR>(Xp, nsplit, split_stride, x_bstride, W, w_bstride, B, p, s, r, P3, \
+                             P3b, p3b_rows, scratch, st)
+  if (s <= 16) {
+    if (r <= 16) DPRC_ORTH(16, 16);
+    DPRC_ORTH(16, 32);
+  }
+  if (r <= 16) DPRC_ORTH(32, 16);
+  DPRC_ORTH(32, 32);
+#undef DPRC_ORTH
 }
 
 #define DPRC_INSTANTIATE(TIn)                                                                      \

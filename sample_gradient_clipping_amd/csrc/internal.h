@@ -73,16 +73,16 @@ hipError_t launch_clip(const float* n, int B, float C, float* c, float* c_out, u
 // out[e] = sum_{sp < nsplit} part[sp][e].
 hipError_t launch_reduce_splits(const float* part, int nsplit, int64_t n, float* out, hipStream_t s);
 // Hutch++ probe for the last pass: rows 0..s-1 = orthonormal basis of the s
-// rows of X (CGS2), rows s..s+r-1 = W - Q Q^T W.  X [B][xrows][p] (rows 0..s-1
-// used), W rows s..s+r-1 of Pw [.][wrows][p].  out fp32 [B][s+r][p].
-// `scratch`: hpp_orth_scratch_bytes() of device memory for the chunk partials.
-hipError_t launch_hpp_orth(const float* X, int xrows, const float* Pw, int64_t pw_bstride,
-                           int wrows, int B, int p, int s_cols, int r_cols, float* out,
-                           double* scratch, hipStream_t s);
+// sketch rows (CholeskyQR2), rows s..s+r-1 = W - Q Q^T W.  The sketch is the
+// sum over nsplit partials: X[b][i][e] = sum_sp Xp[b * x_bstride + sp *
+// split_stride + i * p + e].  W rows t < r at W[b * w_bstride + t * p].
+// P3 fp32 [B][s+r][p] holds the first-pass basis and, when P3b is null, the
+// result; otherwise the result goes to P3b bf16 [B][p3b_rows][p] with zero
+// rows from s+r on.  `scratch`: hpp_orth_scratch_bytes() of device memory.
+hipError_t launch_hpp_orth(const float* Xp, int nsplit, int64_t split_stride, int64_t x_bstride,
+                           const float* W, int64_t w_bstride, int B, int p, int s, int r,
+                           float* P3, bf16_t* P3b, int p3b_rows, double* scratch, hipStream_t st);
 size_t hpp_orth_scratch_bytes(int B, int p, int s, int r);
-// out[b][j][x] = bf16(in[b][j][x]) for j < rows_in, 0 for rows_in <= j < rows_out.
-hipError_t launch_to_bf16_pad(const float* in, int B, int rows_in, int rows_out, int W,
-                              bf16_t* out, hipStream_t s);
 
 // ---- MFMA kernels for bf16 inputs (mfma_hutch.hip, mfma_gemm.hip) ----
 constexpr int kMfmaProbeCols = 32;  // padded probe width of the MFMA Hutch path

@@ -52,6 +52,10 @@ def test_workspace_queries(lib):
     # invalid: k > p, k < 3 for Hutch++, bad method/dtype, negative sizes
     assert dp.dp_norm_est_workspace("hutch", "f32", 4, 64, 64, 64, 65) is None
     assert dp.dp_norm_est_workspace("hutchpp", "f32", 4, 64, 64, 64, 2) is None
+    # Hutch++ column limits: s = k/3 <= 32 and r = k - 2s <= 32
+    assert dp.dp_norm_est_workspace("hutchpp", "f32", 2, 64, 64, 128, 96) > 0
+    assert dp.dp_norm_est_workspace("hutchpp", "f32", 2, 64, 64, 128, 95) is None
+    assert dp.dp_norm_est_workspace("hutchpp", "f32", 2, 64, 64, 128, 97) is None
     assert dp.load_library().dp_norm_est_workspace(9, 0, 1, 1, 1, 1, 1) == ctypes.c_size_t(-1).value
     assert dp.load_library().dp_norm_est_workspace(0, 7, 1, 1, 1, 1, 1) == ctypes.c_size_t(-1).value
     assert dp.dp_norm_est_workspace("hutch", "f32", -1, 64, 64, 64, 8) is None

@@ -80,6 +80,8 @@ NORM_CASES = [
     ("tiles_bf16", "bf16", 3, 256, 256, 512, 32),
     ("tiles_bf16_wide_d", "bf16", 2, 384, 512, 256, 32),
     ("tiles_bf16_k7", "bf16", 2, 128, 128, 256, 7),
+    ("wide_sketch_f32", "f32", 2, 64, 48, 300, 60),   # s = 20 > 16 sketch columns, ragged p
+    ("rank_deficient_f32", "f32", 2, 4, 30, 40, 24),  # T = 4 < s = 8: dead pivots in the QR
 ]
 
 
