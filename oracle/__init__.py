@@ -20,6 +20,7 @@ Sources it follows (cited by page title and section throughout):
 * [DPSGD] "DP-SGD（差分プライバシー確率的勾配降下法）とは？", section
   DP-SGDのアルゴリズム (algorithm), steps 3-5: clip, Gaussian noise
   N(0, sigma^2 C^2 I) added to the clipped sum, SGD update theta - eta G/|B|.
+  Step 1 (Poisson subsampling of the minibatch) is in ``sampling.py``.
 * Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
   easy as 1, 2, 3", SC'11 (the published counter-based generator).
 
@@ -60,4 +61,12 @@ from .step import (  # noqa: F401
     aggregate_rows,
     noise_update,
     dp_step,
+)
+from .sampling import (  # noqa: F401
+    POISSON_C3,
+    poisson_threshold,
+    poisson_words,
+    poisson_sample,
+    norm_est_ragged,
+    aggregate_ragged,
 )
