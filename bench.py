@@ -184,6 +184,30 @@ def estimator_accuracy(dp, wl, layer_inputs, dev, nseeds=8, rademacher=False):
     return out
 
 
+def poisson_timing(dp, dev, reps=20):
+    """Time the Poisson subsampling call (step 1 of DP-SGD) for two training-set
+    sizes, with q chosen so that the expected minibatch is 8 sequences.
+    Outside the timed steps."""
+    import torch
+    out = []
+    for N in (1 << 20, 1 << 26):
+        q = 8.0 / N
+        idx = torch.empty(1024, dtype=torch.int64, device=dev)
+        count = torch.empty(1, dtype=torch.int64, device=dev)
+        ws = torch.empty(dp.dp_poisson_sample_workspace(N), dtype=torch.uint8, device=dev)
+        dp.dp_poisson_sample(1, 0, N, q, idx, count, ws=ws)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(reps):
+            dp.dp_poisson_sample(1, t, N, q, idx, count, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        out.append({"N": N, "q": q, "us_per_call": us, "examples_per_s": N / (us * 1e-6),
+                    "last_batch": int(count.item())})
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -343,6 +367,8 @@ def main():
 
     accuracy = estimator_accuracy(dp, wl, inputs[0][0], dev, rademacher=args.rademacher)
     log(f"[bench] estimator accuracy {accuracy}")
+    sampler = poisson_timing(dp, dev)
+    log(f"[bench] poisson sampler {sampler}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -362,6 +388,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "estimator_accuracy": accuracy,
+        "poisson_sampler": sampler,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -208,6 +208,37 @@ dp_status_t dp_clip_aggregate_update_timed(int dtype, int B, int T, int d, int p
                                            void *ev_agg_end, void *ev_upd_begin,
                                            void *ev_upd_end);
 
+/* ---- Poisson subsampling of the minibatch ----
+ *
+ * Glossary page, section DP-SGDのアルゴリズム, step 1: each step draws its
+ * minibatch by Poisson subsampling, every one of the N training examples
+ * independently with probability q (so |B| is random); step 5 divides the
+ * noisy clipped sum by |B|.
+ *
+ * Example n is in step `step`'s minibatch when word n mod 4 of Philox4x32-10
+ * at the counter (lo(n / 4), hi(n / 4), step, 0xFFFFFFFE) under key `seed` is
+ * below floor(q 2^32) (integer comparison: q = 1 takes every example, q = 0
+ * none).  Layer ids must stay below 0xFFFFFFFE so that this stream, the probe
+ * stream and the noise stream never share a counter.
+ *
+ *  N       examples, 0 <= N <= 2^40; q in [0, 1].
+ *  idx     int64 device array of idx_cap entries (NULL when idx_cap == 0):
+ *          the first min(|B|, idx_cap) selected indices, ascending.
+ *  count   int64 device scalar: |B| (also when it exceeds idx_cap).
+ *  ws      device workspace, ws_bytes >= dp_poisson_sample_workspace(N).
+ * Deterministic: the same arguments give the same indices on every call.
+ * The caller gathers the selected examples into the first |B| slots of the
+ * batch and passes B = |B| to the calls above, whose update divides by B
+ * (the realized batch size).  For another denominator (the expected size
+ * q N, say), pass eta' = eta B / denominator.  An empty minibatch has no
+ * clipped sum; its noise-only update is dp_noise_update with S = 0, B = 1
+ * and eta' = eta / denominator.
+ */
+size_t dp_poisson_sample_workspace(int64_t N); /* bytes, or (size_t)-1 if N is out of range */
+dp_status_t dp_poisson_sample(uint64_t seed, uint32_t step, int64_t N, double q, int64_t *idx,
+                              int64_t idx_cap, int64_t *count, void *ws, size_t ws_bytes,
+                              dp_stream_t stream);
+
 /* ---- test hooks: expose the random streams for bit-level parity checks ---- */
 
 /* out[4 n] = Philox4x32-10 words of the n counters ctr[4 n] (device arrays). */

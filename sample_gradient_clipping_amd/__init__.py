@@ -11,7 +11,8 @@ _BINDING_NAMES = (
     "dp_abi_version", "dp_status_string", "dp_norm_est", "dp_norm_est_workspace",
     "dp_clip_aggregate", "dp_clip_aggregate_workspace", "dp_noise_update",
     "dp_clip_aggregate_update", "dp_clip_aggregate_update_workspace",
-    "dp_philox_u32", "dp_probe_fill", "dp_noise_fill", "DprcError", "lib_path",
+    "dp_philox_u32", "dp_probe_fill", "dp_noise_fill", "dp_poisson_sample",
+    "dp_poisson_sample_workspace", "DprcError", "lib_path",
     "load_library", "METHODS", "DP_ACCUMULATE", "DP_PROBE_SHARED", "DP_PROBE_RADEMACHER",
 )
 

@@ -84,6 +84,11 @@ def load_library():
     L.dp_probe_fill_ex.restype = c_int
     L.dp_noise_fill.argtypes = [c_u64, c_u32, c_u64, c_sz, c_p, c_p]
     L.dp_noise_fill.restype = c_int
+    c_i64, c_dbl = ctypes.c_int64, ctypes.c_double
+    L.dp_poisson_sample_workspace.argtypes = [c_i64]
+    L.dp_poisson_sample_workspace.restype = c_sz
+    L.dp_poisson_sample.argtypes = [c_u64, c_u32, c_i64, c_dbl, c_p, c_i64, c_p, c_p, c_sz, c_p]
+    L.dp_poisson_sample.restype = c_int
     _lib = L
     return L
 
@@ -273,3 +278,30 @@ def dp_noise_fill(seed, layer, offset, xi, stream=None):
                                       xi.numel(), _ptr(xi), _stream(stream))
     _check(st, "dp_noise_fill")
     return xi
+
+
+def dp_poisson_sample_workspace(N):
+    """Workspace bytes for dp_poisson_sample over N examples, or None if N is out of range."""
+    n = load_library().dp_poisson_sample_workspace(int(N))
+    return None if n == _SIZE_INVALID else n
+
+
+def dp_poisson_sample(seed, step, N, q, idx, count, ws=None, stream=None):
+    """Poisson-subsampled minibatch of step ``step``: ascending indices into
+    ``idx`` (int64 device tensor; its length is the capacity) and |B| into
+    ``count`` (int64 device tensor of one element).  ``ws``: optional uint8
+    device workspace (allocated here when omitted)."""
+    import torch
+    L = load_library()
+    if ws is None:
+        nbytes = dp_poisson_sample_workspace(N)
+        if nbytes is None:
+            raise ValueError(f"N = {N} out of range")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=count.device)
+    st = L.dp_poisson_sample(int(seed) & (2**64 - 1), int(step) & 0xFFFFFFFF, int(N), float(q),
+                             _ptr(idx) if idx is not None and idx.numel() else None,
+                             idx.numel() if idx is not None else 0, _ptr(count), _ptr(ws),
+                             ws.numel(), _stream(stream))
+    _check(st, "dp_poisson_sample")
+    return idx, count
+

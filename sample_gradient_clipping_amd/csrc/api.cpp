@@ -645,4 +645,26 @@ dp_status_t dp_noise_fill(uint64_t seed, uint32_t layer, uint64_t offset, size_t
   return DP_OK;
 }
 
+size_t dp_poisson_sample_workspace(int64_t N) {
+  if (N < 0 || N > (static_cast<int64_t>(1) << 40)) return kInvalid;
+  const int64_t nblk = poisson_blocks(N);
+  return static_cast<size_t>(nblk > 0 ? nblk : 1) * sizeof(int64_t);
+}
+
+dp_status_t dp_poisson_sample(uint64_t seed, uint32_t step, int64_t N, double q, int64_t* idx,
+                              int64_t idx_cap, int64_t* count, void* ws, size_t ws_bytes,
+                              dp_stream_t stream) {
+  const size_t need = dp_poisson_sample_workspace(N);
+  if (need == kInvalid || !(q >= 0.0 && q <= 1.0) || idx_cap < 0) return DP_ERR_INVALID_ARG;
+  if (count == nullptr || !aligned(count, 8)) return DP_ERR_INVALID_ARG;
+  if (idx_cap > 0 && (idx == nullptr || !aligned(idx, 8))) return DP_ERR_INVALID_ARG;
+  if (ws_bytes < need) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  // floor(q 2^32): scaling a double by 2^32 is exact, and so is the floor
+  const uint64_t thr = static_cast<uint64_t>(std::floor(q * 4294967296.0));
+  DP_TRY(launch_poisson_sample(seed, step, N, thr, idx, idx_cap, count, static_cast<int64_t*>(ws),
+                               static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
 }  // extern "C"

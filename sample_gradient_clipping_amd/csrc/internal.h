@@ -84,6 +84,14 @@ hipError_t launch_hpp_orth(const float* Xp, int nsplit, int64_t split_stride, in
                            float* P3, bf16_t* P3b, int p3b_rows, double* scratch, hipStream_t st);
 size_t hpp_orth_scratch_bytes(int B, int p, int s, int r);
 
+// Poisson subsampling: idx[0, min(|B|, cap)) = ascending indices n < N whose
+// membership word is below thr; *count = |B| (device).  counts: workspace of
+// poisson_blocks(N) int64.
+int64_t poisson_blocks(int64_t N);
+hipError_t launch_poisson_sample(uint64_t seed, uint32_t step, int64_t N, uint64_t thr,
+                                 int64_t* idx, int64_t cap, int64_t* count, int64_t* counts,
+                                 hipStream_t s);
+
 // ---- MFMA kernels for bf16 inputs (mfma_hutch.hip, mfma_gemm.hip) ----
 constexpr int kMfmaProbeCols = 32;  // padded probe width of the MFMA Hutch path
 bool mfma_sketch_ok(int T, int W);

@@ -226,4 +226,132 @@ hipError_t launch_noise_update(float* theta, const float* S, int64_t n, float si
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Poisson subsampling of the minibatch (glossary page, section
+// DP-SGDのアルゴリズム, step 1: every example is in independently with
+// probability q).  Example n of N is in step `step`'s minibatch when word
+// n mod 4 of the counter (lo(n / 4), hi(n / 4), step, kPoissonC3) is below
+// thr = floor(q 2^32): an integer comparison, exact on any device.  The
+// indices come out in ascending order: per tile of kPoisTile examples a
+// count, one exclusive scan of the counts, then every tile recomputes its
+// draws and writes them at its offset (three launches, deterministic).
+// ---------------------------------------------------------------------------
+constexpr uint32_t kPoissonC3 = 0xFFFFFFFEu;
+constexpr int kPoisThreads = 256;
+constexpr int kPoisPer = 16;                        // examples per thread: four counters
+constexpr int kPoisTile = kPoisThreads * kPoisPer;  // examples per block
+constexpr int kScanThreads = 1024;
+
+// Membership bits of examples e0 .. e0 + 15 (e0 a multiple of 16).
+__device__ __forceinline__ uint32_t poisson_bits(uint32_t k0, uint32_t k1, uint32_t step,
+                                                 uint64_t thr, int64_t e0, int64_t N) {
+  uint32_t bits = 0;
+  const uint64_t g0 = static_cast<uint64_t>(e0) >> 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint64_t g = g0 + j;
+    u32x4 c;
+    c.x = static_cast<uint32_t>(g);
+    c.y = static_cast<uint32_t>(g >> 32);
+    c.z = step;
+    c.w = kPoissonC3;
+    const u32x4 w = philox4x32_10(c, k0, k1);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const bool in = e0 + 4 * j + l < N && static_cast<uint64_t>(ws[l]) < thr;
+      bits |= (in ? 1u : 0u) << (4 * j + l);
+    }
+  }
+  return bits;
+}
+
+// Exclusive prefix sum over the block (blockDim.x == NT, a multiple of 64);
+// *total gets the block total.  red: LDS of NT / 64 values.
+template <typename T, int NT>
+__device__ __forceinline__ T block_exclusive_scan(T v, T* red, T* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  T x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const T y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) red[wid] = x;
+  __syncthreads();
+  T before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    before += w < wid ? red[w] : T(0);
+    tot += red[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + x - v;
+}
+
+__global__ void __launch_bounds__(kPoisThreads) k_poisson_count(uint32_t k0, uint32_t k1,
+                                                                uint32_t step, uint64_t thr,
+                                                                int64_t N,
+                                                                int64_t* __restrict__ counts) {
+  __shared__ int red[kPoisThreads / 64];
+  const int64_t e0 = static_cast<int64_t>(blockIdx.x) * kPoisTile + threadIdx.x * kPoisPer;
+  const int c = __popc(poisson_bits(k0, k1, step, thr, e0, N));
+  int total;
+  block_exclusive_scan<int, kPoisThreads>(c, red, &total);
+  if (threadIdx.x == 0) counts[blockIdx.x] = total;
+}
+
+// One block: counts[0, nblk) -> exclusive offsets in place; *count = sum.
+__global__ void __launch_bounds__(kScanThreads) k_poisson_scan(int64_t* __restrict__ counts,
+                                                              int64_t nblk,
+                                                              int64_t* __restrict__ count) {
+  __shared__ int64_t red[kScanThreads / 64];
+  int64_t carry = 0;
+  for (int64_t b0 = 0; b0 < nblk; b0 += kScanThreads) {
+    const int64_t b = b0 + threadIdx.x;
+    const int64_t v = b < nblk ? counts[b] : 0;
+    int64_t total;
+    const int64_t ex = block_exclusive_scan<int64_t, kScanThreads>(v, red, &total);
+    if (b < nblk) counts[b] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) *count = carry;
+}
+
+__global__ void __launch_bounds__(kPoisThreads) k_poisson_write(
+    uint32_t k0, uint32_t k1, uint32_t step, uint64_t thr, int64_t N,
+    const int64_t* __restrict__ offsets, int64_t* __restrict__ idx, int64_t cap) {
+  __shared__ int red[kPoisThreads / 64];
+  const int64_t e0 = static_cast<int64_t>(blockIdx.x) * kPoisTile + threadIdx.x * kPoisPer;
+  const uint32_t bits = poisson_bits(k0, k1, step, thr, e0, N);
+  int total;
+  const int ex = block_exclusive_scan<int, kPoisThreads>(__popc(bits), red, &total);
+  int64_t pos = offsets[blockIdx.x] + ex;
+#pragma unroll
+  for (int j = 0; j < kPoisPer; ++j) {
+    if (bits >> j & 1u) {
+      if (pos < cap) idx[pos] = e0 + j;
+      ++pos;
+    }
+  }
+}
+
+int64_t poisson_blocks(int64_t N) { return (N + kPoisTile - 1) / kPoisTile; }
+
+hipError_t launch_poisson_sample(uint64_t seed, uint32_t step, int64_t N, uint64_t thr,
+                                 int64_t* idx, int64_t cap, int64_t* count, int64_t* counts,
+                                 hipStream_t s) {
+  const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
+  const int64_t nblk = poisson_blocks(N);
+  if (nblk > 0)
+    hipLaunchKernelGGL(k_poisson_count, dim3(static_cast<unsigned>(nblk)), dim3(kPoisThreads), 0,
+                       s, k0, k1, step, thr, N, counts);
+  hipLaunchKernelGGL(k_poisson_scan, dim3(1), dim3(kScanThreads), 0, s, counts, nblk, count);
+  if (nblk > 0 && cap > 0)
+    hipLaunchKernelGGL(k_poisson_write, dim3(static_cast<unsigned>(nblk)), dim3(kPoisThreads), 0,
+                       s, k0, k1, step, thr, N, counts, idx, cap);
+  return hipGetLastError();
+}
+
 }  // namespace dprc

@@ -12,6 +12,8 @@ Recipes (the value distributions of the five workloads):
     log-uniform over [0.1, 10].
   * "lowrank":     A = U_a V_a^T + 0.05 N and G likewise, rank-8 signal plus
     noise, for estimator-accuracy checks on a decaying spectrum.
+Ragged batches (``ragged_lengths``): per-sample lengths T_i <= T; the caller
+zeroes G's rows from T_i on (the pad), as a masked backward pass leaves them.
 Host draws use numpy's PCG64 seeded with (seed, layer_id, tensor_tag); values
 are drawn in fp32 and rounded to nearest-even bf16 when the dtype is bf16.
 """
@@ -19,7 +21,7 @@ are drawn in fp32 and rounded to nearest-even bf16 when the dtype is bf16.
 import numpy as np
 import torch
 
-TAG_A, TAG_G, TAG_SCALE, TAG_THETA = 0, 1, 2, 3
+TAG_A, TAG_G, TAG_SCALE, TAG_THETA, TAG_LEN = 0, 1, 2, 3, 4
 
 
 def _rng(seed, layer_id, tag):
@@ -62,6 +64,18 @@ def linear_inputs(B, T, d, p, dtype, recipe, seed, layer_id=0):
     G *= s[:, None, None]
     td = torch_dtype(dtype)
     return torch.from_numpy(A).to(td), torch.from_numpy(G).to(td)
+
+
+def ragged_lengths(B, T, seed, min_len=1):
+    """Per-sample sequence lengths T_i for a ragged batch padded to T tokens:
+    sample 0 has the full T, the last sample min_len, the others are uniform
+    on [min_len, T] (numpy PCG64 seeded with (seed, 0, TAG_LEN))."""
+    r = _rng(seed, 0, TAG_LEN)
+    lengths = r.integers(min_len, T, endpoint=True, size=B)
+    lengths[0] = T
+    if B > 1:
+        lengths[-1] = min_len
+    return [int(x) for x in lengths]
 
 
 def theta_init(p, d, seed, layer_id=0, std=0.02, zero=False):

@@ -162,3 +162,26 @@ def test_test_hooks_reject_bad_arguments(lib):
     assert lib.dp_probe_fill_ex(1, 0, 0, 4, 4, dp.DP_PROBE_SHARED, FAKE, NULL) == E
     assert lib.dp_probe_fill_ex(1, 0, 0, 0, 4, dp.DP_PROBE_RADEMACHER, FAKE, NULL) == E
     assert lib.dp_noise_fill(1, 0, 2**64 - 2, 4, FAKE, NULL) == E
+
+
+def test_poisson_sample_rejects_bad_arguments(lib):
+    E, W = dp.DP_ERR_INVALID_ARG, dp.DP_ERR_WORKSPACE
+    assert dp.dp_poisson_sample_workspace(0) > 0
+    assert dp.dp_poisson_sample_workspace(4096) == 8
+    assert dp.dp_poisson_sample_workspace(4097) == 16
+    assert dp.dp_poisson_sample_workspace(-1) is None
+    assert dp.dp_poisson_sample_workspace((1 << 40) + 1) is None
+
+    def call(N=10, q=0.5, idx=FAKE, cap=4, count=FAKE, ws=FAKE, ws_bytes=1 << 20):
+        return lib.dp_poisson_sample(1, 0, N, q, idx, cap, count, ws, ws_bytes, NULL)
+
+    assert call(N=-1) == E
+    assert call(q=-0.1) == E
+    assert call(q=1.5) == E
+    assert call(q=float("nan")) == E
+    assert call(cap=-1) == E
+    assert call(idx=NULL) == E            # capacity without a buffer
+    assert call(count=NULL) == E
+    assert call(count=FAKE_MIS) == E      # int64 needs 8-byte alignment
+    assert call(ws=NULL) == E
+    assert call(ws_bytes=0) == W

@@ -44,3 +44,11 @@ def test_lowrank_recipe_spectrum():
             assert np.sum(sv[:8] ** 2) > 0.97 * np.sum(sv ** 2)
     s = sample_scales(2, "lowrank", 3)
     assert np.all((s >= 0.1) & (s <= 10))
+
+
+def test_ragged_lengths_recipe():
+    from sample_gradient_clipping_amd.inputs import ragged_lengths
+    L = ragged_lengths(6, 100, 7, min_len=3)
+    assert L[0] == 100 and L[-1] == 3 and all(3 <= x <= 100 for x in L)
+    assert L == ragged_lengths(6, 100, 7, min_len=3)
+    assert ragged_lengths(1, 10, 1) == [10]
