@@ -20,7 +20,9 @@ Sources it follows (cited by page title and section throughout):
 * [DPSGD] "DP-SGD（差分プライバシー確率的勾配降下法）とは？", section
   DP-SGDのアルゴリズム (algorithm), steps 3-5: clip, Gaussian noise
   N(0, sigma^2 C^2 I) added to the clipped sum, SGD update theta - eta G/|B|.
-  Step 1 (Poisson subsampling of the minibatch) is in ``sampling.py``.
+  Step 1 (Poisson subsampling of the minibatch) is in ``sampling.py``; the
+  per-sample gradients of RMSNorm gains and embedding tables (the parameters
+  that are not linear layers) in ``other_layers.py``.
 * Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
   easy as 1, 2, 3", SC'11 (the published counter-based generator).
 
@@ -61,6 +63,14 @@ from .step import (  # noqa: F401
     aggregate_rows,
     noise_update,
     dp_step,
+)
+from .other_layers import (  # noqa: F401
+    rmsnorm_grad,
+    rmsnorm_norm_sq,
+    rmsnorm_aggregate,
+    embedding_rows,
+    embedding_norm_sq,
+    embedding_aggregate,
 )
 from .sampling import (  # noqa: F401
     POISSON_C3,
