@@ -208,6 +208,33 @@ def poisson_timing(dp, dev, reps=20):
     return out
 
 
+def rmsnorm_timing(dp, wl, dev, reps=20):
+    """Time the RMSNorm-gain norm pass (per-sample v_i and ||v_i||^2) at the
+    workload's B and T, d = the first layer's input width, bf16.  Outside the
+    timed steps; reported against HBM (it reads xhat and delta once)."""
+    import torch
+    from sample_gradient_clipping_amd.inputs import linear_inputs_device
+    d = wl.layers[0].d
+    copies = [linear_inputs_device(wl.B, wl.T, d, d, "bf16", "llama_logu", 4242 + c, 0, dev)
+              for c in range(3)]  # rotated, so the 256 MB MALL cannot hold the inputs
+    n = torch.zeros(wl.B, dtype=torch.float32, device=dev)
+    v = torch.zeros(wl.B, d, dtype=torch.float32, device=dev)
+    for X, D in copies:
+        dp.dp_rmsnorm_norm(X, D, n, v=v)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):
+        X, D = copies[r % 3]
+        dp.dp_rmsnorm_norm(X, D, n, v=v)
+    e1.record()
+    torch.cuda.synchronize()
+    del copies
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = 2 * wl.B * wl.T * d * 2
+    return {"B": wl.B, "T": wl.T, "d": d, "us_per_call": us, "GBps": nbytes / (us * 1e-6) / 1e9,
+            "frac_hbm": nbytes / (us * 1e-6) / 8e12, "inputs": "3 rotated copies"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -369,6 +396,8 @@ def main():
     log(f"[bench] estimator accuracy {accuracy}")
     sampler = poisson_timing(dp, dev)
     log(f"[bench] poisson sampler {sampler}")
+    rms = rmsnorm_timing(dp, wl, dev) if wl.dtype == "bf16" else None
+    log(f"[bench] rmsnorm gain norms {rms}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -389,6 +418,7 @@ def main():
         "kernels": kernels,
         "estimator_accuracy": accuracy,
         "poisson_sampler": sampler,
+        "rmsnorm_gain_norms": rms,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

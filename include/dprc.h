@@ -208,6 +208,34 @@ dp_status_t dp_clip_aggregate_update_timed(int dtype, int B, int T, int d, int p
                                            void *ev_agg_end, void *ev_upd_begin,
                                            void *ev_upd_end);
 
+/* ---- RMSNorm gains (a parameter that is not a linear layer) ----
+ *
+ * The glossary page (section DP-SGDのアルゴリズム, steps 2-3) clips each
+ * sample's whole gradient; for a gain gamma of RMSNorm (y_t = gamma * xhat_t)
+ * sample i's gradient is v_i[c] = sum_t xhat_{i,t}[c] * delta_{i,t}[c], with
+ * delta = dl_i/dy.  dp_rmsnorm_norm writes v (if not NULL) and n_sq[i] (=, or
+ * += with DP_ACCUMULATE, to sum with the other layers) = ||v_i||^2.
+ *  xhat, delta  [B][T][d], fp32 or bf16 (dtype), 16-byte aligned.
+ *  v            [B][d] fp32 device, or NULL.
+ *  ws           device workspace, ws_bytes >= dp_rmsnorm_norm_workspace(...).
+ * dp_rmsnorm_clip_aggregate_update then takes the clip factors
+ * c_i = min(1, C / sqrt(n_i)) of the summed norms (the same rule as
+ * dp_clip_aggregate: non-finite n_i gives c_i = 0 and the status bit) and
+ * updates gamma [d] fp32: gamma <- gamma - (eta / B) (sum_i c_i v_i + sigma C xi),
+ * xi from the noise stream of `layer` (give each parameter its own layer id).
+ * S [d] (optional) receives the clipped sum; c_out [B] and status optional.
+ */
+size_t dp_rmsnorm_norm_workspace(int dtype, int B, int T, int d);
+dp_status_t dp_rmsnorm_norm(int dtype, int B, int T, int d, const void *xhat, const void *delta,
+                            uint32_t flags, float *n_sq, float *v, void *ws, size_t ws_bytes,
+                            dp_stream_t stream);
+size_t dp_rmsnorm_update_workspace(int B, int d);
+dp_status_t dp_rmsnorm_clip_aggregate_update(int B, int d, const float *v, const float *n_sq,
+                                             float C, float sigma, float eta, uint64_t seed,
+                                             uint32_t layer, float *gamma, float *S,
+                                             float *c_out, uint32_t *status, void *ws,
+                                             size_t ws_bytes, dp_stream_t stream);
+
 /* ---- Poisson subsampling of the minibatch ----
  *
  * Glossary page, section DP-SGDのアルゴリズム, step 1: each step draws its

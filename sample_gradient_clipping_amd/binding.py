@@ -89,6 +89,15 @@ def load_library():
     L.dp_poisson_sample_workspace.restype = c_sz
     L.dp_poisson_sample.argtypes = [c_u64, c_u32, c_i64, c_dbl, c_p, c_i64, c_p, c_p, c_sz, c_p]
     L.dp_poisson_sample.restype = c_int
+    L.dp_rmsnorm_norm_workspace.argtypes = [c_int] * 4
+    L.dp_rmsnorm_norm_workspace.restype = c_sz
+    L.dp_rmsnorm_norm.argtypes = [c_int] * 4 + [c_p, c_p, c_u32, c_p, c_p, c_p, c_sz, c_p]
+    L.dp_rmsnorm_norm.restype = c_int
+    L.dp_rmsnorm_update_workspace.argtypes = [c_int, c_int]
+    L.dp_rmsnorm_update_workspace.restype = c_sz
+    L.dp_rmsnorm_clip_aggregate_update.argtypes = [c_int, c_int, c_p, c_p, c_f, c_f, c_f, c_u64,
+                                                   c_u32, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]
+    L.dp_rmsnorm_clip_aggregate_update.restype = c_int
     _lib = L
     return L
 
@@ -304,4 +313,32 @@ def dp_poisson_sample(seed, step, N, q, idx, count, ws=None, stream=None):
                              ws.numel(), _stream(stream))
     _check(st, "dp_poisson_sample")
     return idx, count
+
+
+def dp_rmsnorm_norm(xhat, delta, n_sq, v=None, flags=0, ws=None, stream=None):
+    """RMSNorm gain: v[i] = sum_t xhat[i,t] * delta[i,t] (if ``v`` is given, fp32 [B][d])
+    and n_sq[i] (=, or += with DP_ACCUMULATE) ||v_i||^2.  xhat, delta: [B][T][d]."""
+    L = load_library()
+    B, T, d = xhat.shape
+    dt = _dtype_code(xhat)
+    ws_t = _workspace(L.dp_rmsnorm_norm_workspace(dt, B, T, d), xhat.device, ws)
+    st = L.dp_rmsnorm_norm(dt, B, T, d, _ptr(xhat), _ptr(delta), int(flags), _ptr(n_sq), _ptr(v),
+                           _ptr(ws_t), 0 if ws_t is None else ws_t.numel(), _stream(stream))
+    _check(st, "dp_rmsnorm_norm")
+    return n_sq
+
+
+def dp_rmsnorm_clip_aggregate_update(v, n_sq, C, sigma, eta, seed, layer, gamma, S=None,
+                                     c_out=None, status=None, ws=None, stream=None):
+    """gamma[d] <- gamma - (eta / B) (sum_i c_i v_i + sigma C xi), c_i = min(1, C / sqrt(n_i))."""
+    L = load_library()
+    B, d = v.shape
+    ws_t = _workspace(L.dp_rmsnorm_update_workspace(B, d), v.device, ws)
+    st = L.dp_rmsnorm_clip_aggregate_update(B, d, _ptr(v), _ptr(n_sq), float(C), float(sigma),
+                                            float(eta), int(seed) & (2**64 - 1), int(layer),
+                                            _ptr(gamma), _ptr(S), _ptr(c_out), _ptr(status),
+                                            _ptr(ws_t), 0 if ws_t is None else ws_t.numel(),
+                                            _stream(stream))
+    _check(st, "dp_rmsnorm_clip_aggregate_update")
+    return gamma
 

@@ -667,4 +667,90 @@ dp_status_t dp_poisson_sample(uint64_t seed, uint32_t step, int64_t N, double q,
   return DP_OK;
 }
 
+// ---- RMSNorm gains ----
+// [part: B][nsplit][d] fp32 | [sq: B][chunks] fp64
+static size_t rmsnorm_part_bytes(int B, int T, int d) {
+  return align_up(static_cast<size_t>(B) * rmsnorm_splits(B, T, d) * d * sizeof(float) + 16);
+}
+
+size_t dp_rmsnorm_norm_workspace(int dtype, int B, int T, int d) {
+  if (!valid_dtype(dtype) || B < 0 || T < 0 || d < 1) return kInvalid;
+  return rmsnorm_part_bytes(B, T, d) +
+         align_up(static_cast<size_t>(B > 0 ? B : 1) * rmsnorm_sq_chunks(d) * sizeof(double));
+}
+
+dp_status_t dp_rmsnorm_norm(int dtype, int B, int T, int d, const void* xhat, const void* delta,
+                            uint32_t flags, float* n_sq, float* v, void* ws, size_t ws_bytes,
+                            dp_stream_t stream) {
+  const size_t need = dp_rmsnorm_norm_workspace(dtype, B, T, d);
+  if (need == kInvalid || (flags & ~DP_ACCUMULATE) != 0) return DP_ERR_INVALID_ARG;
+  if (B == 0) return DP_OK;
+  if (n_sq == nullptr || !aligned(n_sq, 4) || (v != nullptr && !aligned(v, 4)))
+    return DP_ERR_INVALID_ARG;
+  if (T > 0 && (xhat == nullptr || delta == nullptr || !aligned(xhat, 16) || !aligned(delta, 16)))
+    return DP_ERR_INVALID_ARG;
+  if (ws_bytes < need) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nsplit = rmsnorm_splits(B, T, d);
+  const int acc = (flags & DP_ACCUMULATE) ? 1 : 0;
+  double* sq = at<double>(ws, rmsnorm_part_bytes(B, T, d));
+  if (dtype == DP_BF16)
+    DP_TRY(launch_rmsnorm_norm(static_cast<const bf16_t*>(xhat), static_cast<const bf16_t*>(delta),
+                               B, T, d, static_cast<float*>(ws), nsplit, sq, v, n_sq, acc, s));
+  else
+    DP_TRY(launch_rmsnorm_norm(static_cast<const float*>(xhat), static_cast<const float*>(delta),
+                               B, T, d, static_cast<float*>(ws), nsplit, sq, v, n_sq, acc, s));
+  return DP_OK;
+}
+
+struct GainPlan {
+  size_t c = 0, order = 0, count = 0, sbuf = 0, total = 0;
+};
+
+static GainPlan plan_gain(int B, int d) {
+  GainPlan P;
+  Carver cv;
+  const size_t Bz = static_cast<size_t>(B > 0 ? B : 1);
+  P.c = cv.take(Bz * sizeof(float));
+  P.order = cv.take(Bz * sizeof(int));
+  P.count = cv.take(sizeof(int));
+  P.sbuf = cv.take(static_cast<size_t>(d) * sizeof(float));
+  P.total = cv.off;
+  return P;
+}
+
+size_t dp_rmsnorm_update_workspace(int B, int d) {
+  if (B < 1 || d < 1) return kInvalid;
+  return plan_gain(B, d).total;
+}
+
+dp_status_t dp_rmsnorm_clip_aggregate_update(int B, int d, const float* v, const float* n_sq,
+                                             float C, float sigma, float eta, uint64_t seed,
+                                             uint32_t layer, float* gamma, float* S,
+                                             float* c_out, uint32_t* status, void* ws,
+                                             size_t ws_bytes, dp_stream_t stream) {
+  if (!update_args_ok(d, 1, B, sigma, C, eta)) return DP_ERR_INVALID_ARG;
+  if (v == nullptr || n_sq == nullptr || gamma == nullptr || !aligned(v, 4) ||
+      !aligned(n_sq, 4) || !aligned(gamma, 16))
+    return DP_ERR_INVALID_ARG;
+  if ((S != nullptr && !aligned(S, 16)) || (c_out && !aligned(c_out, 4)) ||
+      (status && !aligned(status, 4)))
+    return DP_ERR_INVALID_ARG;
+  const size_t bytes = static_cast<size_t>(d) * 4;
+  if (S != nullptr && overlaps(gamma, bytes, S, bytes)) return DP_ERR_INVALID_ARG;
+  const GainPlan P = plan_gain(B, d);
+  if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  if (overlaps(gamma, bytes, ws, P.total)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* c = at<float>(ws, P.c);
+  float* sum = S != nullptr ? S : at<float>(ws, P.sbuf);
+  DP_TRY(launch_clip(n_sq, B, C, c, c_out, status, at<int>(ws, P.order), at<int>(ws, P.count), s));
+  DP_TRY(launch_weighted_rows(v, c, B, d, sum, s));
+  const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
+  DP_TRY(launch_noise_update(gamma, sum, d, sigma * C, eta_over_B, seed, layer, s));
+  return DP_OK;
+}
+
 }  // extern "C"

@@ -92,6 +92,20 @@ hipError_t launch_poisson_sample(uint64_t seed, uint32_t step, int64_t N, uint64
                                  int64_t* idx, int64_t cap, int64_t* count, int64_t* counts,
                                  hipStream_t s);
 
+// ---- parameters that are not linear layers (other_layers.hip) ----
+// RMSNorm gain: part [B][nsplit][d] fp32 scratch; v [B][d] (may be null);
+// n_sq[b] (= or +=) ||v_b||^2.
+// sq [B][rmsnorm_sq_chunks(d)] fp64 scratch.
+int rmsnorm_splits(int B, int T, int d);
+int rmsnorm_sq_chunks(int d);
+template <typename TIn>
+hipError_t launch_rmsnorm_norm(const TIn* X, const TIn* D, int B, int T, int d, float* part,
+                               int nsplit, double* sq, float* v, float* n_sq, int accumulate,
+                               hipStream_t s);
+// S[c] = sum_i c_i v[i][c].
+hipError_t launch_weighted_rows(const float* v, const float* c, int B, int d, float* S,
+                                hipStream_t s);
+
 // ---- MFMA kernels for bf16 inputs (mfma_hutch.hip, mfma_gemm.hip) ----
 constexpr int kMfmaProbeCols = 32;  // padded probe width of the MFMA Hutch path
 bool mfma_sketch_ok(int T, int W);

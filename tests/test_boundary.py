@@ -185,3 +185,33 @@ def test_poisson_sample_rejects_bad_arguments(lib):
     assert call(count=FAKE_MIS) == E      # int64 needs 8-byte alignment
     assert call(ws=NULL) == E
     assert call(ws_bytes=0) == W
+
+
+def test_rmsnorm_entry_points_reject_bad_arguments(lib):
+    E, W = dp.DP_ERR_INVALID_ARG, dp.DP_ERR_WORKSPACE
+    assert lib.dp_rmsnorm_norm_workspace(0, 2, 8, 8) > 0
+    assert lib.dp_rmsnorm_norm_workspace(5, 2, 8, 8) == ctypes.c_size_t(-1).value
+    assert lib.dp_rmsnorm_norm_workspace(0, 2, 8, 0) == ctypes.c_size_t(-1).value
+
+    def norm(dtype=0, B=2, T=8, d=8, x=FAKE, dl=FAKE, flags=0, n=FAKE, v=NULL, ws=FAKE,
+             ws_bytes=1 << 20):
+        return lib.dp_rmsnorm_norm(dtype, B, T, d, x, dl, flags, n, v, ws, ws_bytes, NULL)
+
+    assert norm(dtype=3) == E
+    assert norm(flags=dp.DP_PROBE_SHARED) == E   # only DP_ACCUMULATE applies
+    assert norm(x=FAKE_MIS) == E
+    assert norm(n=NULL) == E
+    assert norm(ws=NULL) == E
+    assert norm(ws_bytes=0) == W
+
+    def upd(B=2, d=8, v=FAKE, n=FAKE, C=1.0, sigma=1.0, eta=0.1, gamma=FAKE, ws=FAKE,
+            ws_bytes=1 << 20):
+        return lib.dp_rmsnorm_clip_aggregate_update(B, d, v, n, C, sigma, eta, 1, 0, gamma, NULL,
+                                                    NULL, NULL, ws, ws_bytes, NULL)
+
+    assert upd(B=0) == E
+    assert upd(C=0.0) == E
+    assert upd(sigma=-1.0) == E
+    assert upd(gamma=FAKE_MIS) == E
+    assert upd(v=NULL) == E
+    assert upd(ws_bytes=0) == W
