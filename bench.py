@@ -235,6 +235,40 @@ def rmsnorm_timing(dp, wl, dev, reps=20):
             "frac_hbm": nbytes / (us * 1e-6) / 8e12, "inputs": "3 rotated copies"}
 
 
+def embedding_timing(dp, wl, dev, V=128256, reps=10):
+    """Time the embedding-table norm pass and the table update (every row
+    noised) at the workload's B and T, d = the first layer's input width, bf16,
+    with a Llama-3.2-sized vocabulary and Zipf-like token ids.  Outside the
+    timed steps."""
+    import numpy as np
+    import torch
+    from sample_gradient_clipping_amd.inputs import linear_inputs_device
+    B, T, d = wl.B, wl.T, wl.layers[0].d
+    r = np.random.default_rng(77)
+    ids = torch.from_numpy(np.minimum(r.zipf(1.3, size=(B, T)) - 1, V - 1).astype(np.int32)).to(dev)
+    _, D = linear_inputs_device(B, T, 8, d, "bf16", "llama_logu", 4343, 0, dev)
+    E = torch.zeros(V, d, dtype=torch.float32, device=dev)
+    n = torch.zeros(B, dtype=torch.float32, device=dev)
+    dp.dp_embedding_norm(ids, D, n)
+    dp.dp_embedding_clip_aggregate_update(ids, D, n, 1.0, 1.0, 1e-4, 7, 5000, E)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for _ in range(reps):
+        dp.dp_embedding_norm(ids, D, n)
+    ev[1].record()
+    for _ in range(reps):
+        dp.dp_embedding_clip_aggregate_update(ids, D, n, 1.0, 1.0, 1e-4, 7, 5000, E)
+    ev[2].record()
+    torch.cuda.synchronize()
+    us_n = ev[0].elapsed_time(ev[1]) / reps * 1e3
+    us_u = ev[1].elapsed_time(ev[2]) / reps * 1e3
+    bytes_n = B * T * d * 2
+    bytes_u = 8 * V * d + B * T * d * 2  # E read and written, delta rows read once
+    return {"B": B, "T": T, "d": d, "V": V, "distinct_ids_sample0": int(ids[0].unique().numel()),
+            "norm_us": us_n, "norm_GBps": bytes_n / (us_n * 1e-6) / 1e9,
+            "update_us": us_u, "update_GBps": bytes_u / (us_u * 1e-6) / 1e9}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -398,6 +432,8 @@ def main():
     log(f"[bench] poisson sampler {sampler}")
     rms = rmsnorm_timing(dp, wl, dev) if wl.dtype == "bf16" else None
     log(f"[bench] rmsnorm gain norms {rms}")
+    emb = embedding_timing(dp, wl, dev) if wl.dtype == "bf16" else None
+    log(f"[bench] embedding {emb}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -419,6 +455,7 @@ def main():
         "estimator_accuracy": accuracy,
         "poisson_sampler": sampler,
         "rmsnorm_gain_norms": rms,
+        "embedding": emb,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -236,6 +236,32 @@ dp_status_t dp_rmsnorm_clip_aggregate_update(int B, int d, const float *v, const
                                              float *c_out, uint32_t *status, void *ws,
                                              size_t ws_bytes, dp_stream_t stream);
 
+/* ---- embedding tables (a parameter that is not a linear layer) ----
+ *
+ * For an embedding table E [V][d] (h_t = E[id_t]) sample i's gradient has
+ * row v equal to the sum of delta_{i,t} (= dl_i/dh_t) over the tokens with
+ * id_t = v; dp_embedding_norm writes n_sq[i] (=, or += with DP_ACCUMULATE)
+ * = the sum over the distinct ids of the squared row norms.
+ *  ids    [B][T] int32 device; delta [B][T][d] fp32 or bf16 (16-byte aligned).
+ *  T      0 <= T <= 16384 (the per-sample sort runs in LDS).
+ * dp_embedding_clip_aggregate_update updates every row of E [V][d] fp32:
+ * E <- E - (eta / B) (sum_i c_i grad_i + sigma C xi), with c_i = min(1,
+ * C / sqrt(n_i)) as in dp_clip_aggregate and xi from the noise stream of
+ * `layer` at flat index v d + column (the noise covers rows no token uses).
+ * Ids outside [0, V) contribute nothing to the update.
+ */
+size_t dp_embedding_norm_workspace(int dtype, int B, int T, int d);
+dp_status_t dp_embedding_norm(int dtype, int B, int T, int d, const int32_t *ids,
+                              const void *delta, uint32_t flags, float *n_sq, void *ws,
+                              size_t ws_bytes, dp_stream_t stream);
+size_t dp_embedding_update_workspace(int dtype, int B, int T, int d, int V);
+dp_status_t dp_embedding_clip_aggregate_update(int dtype, int B, int T, int d, int V,
+                                               const int32_t *ids, const void *delta,
+                                               const float *n_sq, float C, float sigma,
+                                               float eta, uint64_t seed, uint32_t layer, float *E,
+                                               float *c_out, uint32_t *status, void *ws,
+                                               size_t ws_bytes, dp_stream_t stream);
+
 /* ---- Poisson subsampling of the minibatch ----
  *
  * Glossary page, section DP-SGDのアルゴリズム, step 1: each step draws its

@@ -98,6 +98,16 @@ def load_library():
     L.dp_rmsnorm_clip_aggregate_update.argtypes = [c_int, c_int, c_p, c_p, c_f, c_f, c_f, c_u64,
                                                    c_u32, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]
     L.dp_rmsnorm_clip_aggregate_update.restype = c_int
+    L.dp_embedding_norm_workspace.argtypes = [c_int] * 4
+    L.dp_embedding_norm_workspace.restype = c_sz
+    L.dp_embedding_norm.argtypes = [c_int] * 4 + [c_p, c_p, c_u32, c_p, c_p, c_sz, c_p]
+    L.dp_embedding_norm.restype = c_int
+    L.dp_embedding_update_workspace.argtypes = [c_int] * 5
+    L.dp_embedding_update_workspace.restype = c_sz
+    L.dp_embedding_clip_aggregate_update.argtypes = ([c_int] * 5 + [c_p, c_p, c_p, c_f, c_f, c_f,
+                                                                    c_u64, c_u32, c_p, c_p, c_p,
+                                                                    c_p, c_sz, c_p])
+    L.dp_embedding_clip_aggregate_update.restype = c_int
     _lib = L
     return L
 
@@ -341,4 +351,35 @@ def dp_rmsnorm_clip_aggregate_update(v, n_sq, C, sigma, eta, seed, layer, gamma,
                                             _stream(stream))
     _check(st, "dp_rmsnorm_clip_aggregate_update")
     return gamma
+
+
+def dp_embedding_norm(ids, delta, n_sq, flags=0, ws=None, stream=None):
+    """Embedding table: n_sq[i] (=, or += with DP_ACCUMULATE) = sum over the distinct ids
+    of sample i of ||sum of its delta rows||^2.  ids: int32 [B][T]; delta: [B][T][d]."""
+    L = load_library()
+    B, T, d = delta.shape
+    dt = _dtype_code(delta)
+    ws_t = _workspace(L.dp_embedding_norm_workspace(dt, B, T, d), delta.device, ws)
+    st = L.dp_embedding_norm(dt, B, T, d, _ptr(ids), _ptr(delta), int(flags), _ptr(n_sq),
+                             _ptr(ws_t), 0 if ws_t is None else ws_t.numel(), _stream(stream))
+    _check(st, "dp_embedding_norm")
+    return n_sq
+
+
+def dp_embedding_clip_aggregate_update(ids, delta, n_sq, C, sigma, eta, seed, layer, E,
+                                       c_out=None, status=None, ws=None, stream=None):
+    """E [V][d] <- E - (eta / B) (sum_i c_i grad_i + sigma C xi) over every row of E."""
+    L = load_library()
+    B, T, d = delta.shape
+    V = E.shape[0]
+    dt = _dtype_code(delta)
+    ws_t = _workspace(L.dp_embedding_update_workspace(dt, B, T, d, V), delta.device, ws)
+    st = L.dp_embedding_clip_aggregate_update(dt, B, T, d, V, _ptr(ids), _ptr(delta), _ptr(n_sq),
+                                              float(C), float(sigma), float(eta),
+                                              int(seed) & (2**64 - 1), int(layer), _ptr(E),
+                                              _ptr(c_out), _ptr(status), _ptr(ws_t),
+                                              0 if ws_t is None else ws_t.numel(),
+                                              _stream(stream))
+    _check(st, "dp_embedding_clip_aggregate_update")
+    return E
 

@@ -753,4 +753,133 @@ dp_status_t dp_rmsnorm_clip_aggregate_update(int B, int d, const float* v, const
   return DP_OK;
 }
 
+// ---- embedding tables ----
+constexpr int kEmbMaxTokens = 16384;
+
+struct EmbPlan {
+  int nsplit = 1, nchunk = 1;
+  size_t spos = 0, sid = 0, gidp = 0, ustart = 0, uid = 0, ng = 0, head = 0, tail = 0, part = 0,
+         cpart = 0, gsum = 0, rowmap = 0, c = 0, order = 0, count = 0, total = 0;
+};
+
+static EmbPlan plan_emb(int B, int T, int d, int V) {
+  EmbPlan P;
+  Carver cv;
+  const size_t Bz = static_cast<size_t>(B > 0 ? B : 1), Tz = static_cast<size_t>(T > 0 ? T : 1);
+  P.nsplit = emb_splits(B, T, d);
+  P.nchunk = (d + 2047) / 2048;
+  P.spos = cv.take(Bz * Tz * 4);
+  P.sid = cv.take(Bz * Tz * 4);
+  P.gidp = cv.take(Bz * Tz * 4);
+  P.ustart = cv.take(Bz * (Tz + 1) * 4);
+  P.uid = cv.take(Bz * Tz * 4);
+  P.ng = cv.take(Bz * 4);
+  P.head = cv.take(Bz * P.nsplit * static_cast<size_t>(d) * 4);
+  P.tail = cv.take(Bz * P.nsplit * static_cast<size_t>(d) * 4);
+  if (V == 0) {
+    P.part = cv.take(Bz * P.nsplit * P.nchunk * sizeof(double));
+    P.cpart = cv.take(Bz * emb_combine_chunks(d) * sizeof(double));
+  } else {
+    P.gsum = cv.take(Bz * Tz * static_cast<size_t>(d) * 4);
+    P.rowmap = cv.take(Bz * static_cast<size_t>(V) * 4);
+    P.c = cv.take(Bz * sizeof(float));
+    P.order = cv.take(Bz * sizeof(int));
+    P.count = cv.take(sizeof(int));
+  }
+  P.total = cv.off;
+  return P;
+}
+
+static bool emb_args_ok(int dtype, int B, int T, int d) {
+  return valid_dtype(dtype) && B >= 0 && T >= 0 && T <= kEmbMaxTokens && d >= 1;
+}
+
+size_t dp_embedding_norm_workspace(int dtype, int B, int T, int d) {
+  if (!emb_args_ok(dtype, B, T, d)) return kInvalid;
+  return plan_emb(B, T, d, 0).total;
+}
+
+dp_status_t dp_embedding_norm(int dtype, int B, int T, int d, const int32_t* ids,
+                              const void* delta, uint32_t flags, float* n_sq, void* ws,
+                              size_t ws_bytes, dp_stream_t stream) {
+  if (!emb_args_ok(dtype, B, T, d) || (flags & ~DP_ACCUMULATE) != 0) return DP_ERR_INVALID_ARG;
+  if (B == 0) return DP_OK;
+  if (n_sq == nullptr || !aligned(n_sq, 4)) return DP_ERR_INVALID_ARG;
+  if (T > 0 && (ids == nullptr || delta == nullptr || !aligned(ids, 4) || !aligned(delta, 16)))
+    return DP_ERR_INVALID_ARG;
+  const EmbPlan P = plan_emb(B, T, d, 0);
+  if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int acc = (flags & DP_ACCUMULATE) ? 1 : 0;
+  if (T == 0) {
+    DP_TRY(launch_emb_zero_norm(B, n_sq, acc, s));
+    return DP_OK;
+  }
+  int32_t* spos = at<int32_t>(ws, P.spos);
+  int32_t* sid = at<int32_t>(ws, P.sid);
+  int32_t* gidp = at<int32_t>(ws, P.gidp);
+  DP_TRY(launch_emb_sort(ids, B, T, spos, sid, gidp, at<int32_t>(ws, P.ustart),
+                         at<int32_t>(ws, P.uid), at<int32_t>(ws, P.ng), s));
+  double* part = at<double>(ws, P.part);
+  double* cpart = at<double>(ws, P.cpart);
+  float* head = at<float>(ws, P.head);
+  float* tail = at<float>(ws, P.tail);
+  if (dtype == DP_BF16)
+    DP_TRY(launch_emb_norm(static_cast<const bf16_t*>(delta), B, T, d, spos, sid, gidp, P.nsplit,
+                           part, head, tail, cpart, n_sq, acc, s));
+  else
+    DP_TRY(launch_emb_norm(static_cast<const float*>(delta), B, T, d, spos, sid, gidp, P.nsplit,
+                           part, head, tail, cpart, n_sq, acc, s));
+  return DP_OK;
+}
+
+size_t dp_embedding_update_workspace(int dtype, int B, int T, int d, int V) {
+  if (!emb_args_ok(dtype, B, T, d) || B < 1 || V < 1) return kInvalid;
+  return plan_emb(B, T, d, V).total;
+}
+
+dp_status_t dp_embedding_clip_aggregate_update(int dtype, int B, int T, int d, int V,
+                                               const int32_t* ids, const void* delta,
+                                               const float* n_sq, float C, float sigma,
+                                               float eta, uint64_t seed, uint32_t layer, float* E,
+                                               float* c_out, uint32_t* status, void* ws,
+                                               size_t ws_bytes, dp_stream_t stream) {
+  if (!emb_args_ok(dtype, B, T, d) || V < 1) return DP_ERR_INVALID_ARG;
+  if (!update_args_ok(d, V, B, sigma, C, eta)) return DP_ERR_INVALID_ARG;
+  if (n_sq == nullptr || E == nullptr || !aligned(n_sq, 4) || !aligned(E, 16))
+    return DP_ERR_INVALID_ARG;
+  if (T > 0 && (ids == nullptr || delta == nullptr || !aligned(ids, 4) || !aligned(delta, 16)))
+    return DP_ERR_INVALID_ARG;
+  if ((c_out && !aligned(c_out, 4)) || (status && !aligned(status, 4))) return DP_ERR_INVALID_ARG;
+  const EmbPlan P = plan_emb(B, T, d, V);
+  if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  if (overlaps(E, static_cast<size_t>(V) * d * 4, ws, P.total)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* c = at<float>(ws, P.c);
+  DP_TRY(launch_clip(n_sq, B, C, c, c_out, status, at<int>(ws, P.order), at<int>(ws, P.count), s));
+  int32_t* spos = at<int32_t>(ws, P.spos);
+  int32_t* sid = at<int32_t>(ws, P.sid);
+  int32_t* gidp = at<int32_t>(ws, P.gidp);
+  int32_t* uid = at<int32_t>(ws, P.uid);
+  int32_t* ng = at<int32_t>(ws, P.ng);
+  float* gsum = at<float>(ws, P.gsum);
+  if (T > 0) {
+    DP_TRY(launch_emb_sort(ids, B, T, spos, sid, gidp, at<int32_t>(ws, P.ustart), uid, ng, s));
+    if (dtype == DP_BF16)
+      DP_TRY(launch_emb_group_sums(static_cast<const bf16_t*>(delta), B, T, d, spos, sid, gidp,
+                                   P.nsplit, at<float>(ws, P.head), at<float>(ws, P.tail), gsum,
+                                   s));
+    else
+      DP_TRY(launch_emb_group_sums(static_cast<const float*>(delta), B, T, d, spos, sid, gidp,
+                                   P.nsplit, at<float>(ws, P.head), at<float>(ws, P.tail), gsum,
+                                   s));
+  }
+  const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
+  DP_TRY(launch_emb_update(gsum, B, T, d, uid, ng, at<int32_t>(ws, P.rowmap), V, c, E, sigma * C,
+                           eta_over_B, seed, layer, s));
+  return DP_OK;
+}
+
 }  // extern "C"

@@ -82,6 +82,17 @@ __device__ __forceinline__ void box_muller(uint32_t a, uint32_t b, float& z0, fl
   z1 = rho * s;
 }
 
+// Counter of the DP-noise stream for the group of four flat parameter indices
+// 4 grp .. 4 grp + 3 of `layer`: (lo(grp), hi(grp), 0xFFFFFFFF, layer).
+__device__ __forceinline__ u32x4 noise_counter(uint64_t grp, uint32_t layer) {
+  u32x4 c;
+  c.x = static_cast<uint32_t>(grp);
+  c.y = static_cast<uint32_t>(grp >> 32);
+  c.z = kNoiseC2;
+  c.w = layer;
+  return c;
+}
+
 __device__ __forceinline__ void normals4(u32x4 ctr, uint32_t k0, uint32_t k1, float z[4]) {
   const u32x4 w = philox4x32_10(ctr, k0, k1);
   box_muller(w.x, w.y, z[0], z[1]);

@@ -106,6 +106,31 @@ hipError_t launch_rmsnorm_norm(const TIn* X, const TIn* D, int B, int T, int d, 
 hipError_t launch_weighted_rows(const float* v, const float* c, int B, int d, float* S,
                                 hipStream_t s);
 
+// Embedding table: per-sample sort of (id, position) (1 <= T <= 16384); the
+// segmented sums over splits of the sorted positions (pieces of the groups
+// that cross splits in head/tail [B][nsplit][d], joined in split order); the
+// table update through a per-sample row map [B][V] and group sums [B][T][d].
+int emb_splits(int B, int T, int d);
+int emb_combine_chunks(int d);
+hipError_t launch_emb_sort(const int32_t* ids, int B, int T, int32_t* spos, int32_t* sid,
+                           int32_t* gidp, int32_t* ustart, int32_t* uid, int32_t* ng,
+                           hipStream_t s);
+// part [B][nsplit][ceil(d / 2048)] and cpart [B][emb_combine_chunks(d)] fp64.
+template <typename TIn>
+hipError_t launch_emb_norm(const TIn* D, int B, int T, int d, const int32_t* spos,
+                           const int32_t* sid, const int32_t* gidp, int nsplit, double* part,
+                           float* head, float* tail, double* cpart, float* n_sq, int accumulate,
+                           hipStream_t s);
+template <typename TIn>
+hipError_t launch_emb_group_sums(const TIn* D, int B, int T, int d, const int32_t* spos,
+                                 const int32_t* sid, const int32_t* gidp, int nsplit, float* head,
+                                 float* tail, float* gsum, hipStream_t s);
+hipError_t launch_emb_update(const float* gsum, int B, int T, int d, const int32_t* uid,
+                             const int32_t* ng, int32_t* rowmap, int V, const float* c, float* E,
+                             float sigmaC, float eta_over_B, uint64_t seed, uint32_t layer,
+                             hipStream_t s);
+hipError_t launch_emb_zero_norm(int B, float* n_sq, int accumulate, hipStream_t s);
+
 // ---- MFMA kernels for bf16 inputs (mfma_hutch.hip, mfma_gemm.hip) ----
 constexpr int kMfmaProbeCols = 32;  // padded probe width of the MFMA Hutch path
 bool mfma_sketch_ok(int T, int W);

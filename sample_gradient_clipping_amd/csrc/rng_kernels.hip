@@ -105,15 +105,6 @@ hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample
                             nzero);
 }
 
-__device__ __forceinline__ u32x4 noise_counter(uint64_t grp, uint32_t layer) {
-  u32x4 c;
-  c.x = static_cast<uint32_t>(grp);
-  c.y = static_cast<uint32_t>(grp >> 32);
-  c.z = kNoiseC2;
-  c.w = layer;
-  return c;
-}
-
 // xi[e - offset] for e in [offset, offset + n); one thread per counter group.
 __global__ void k_noise_fill(uint32_t k0, uint32_t k1, uint32_t layer, uint64_t offset, size_t n,
                              float* __restrict__ xi) {

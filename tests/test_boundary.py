@@ -215,3 +215,31 @@ def test_rmsnorm_entry_points_reject_bad_arguments(lib):
     assert upd(gamma=FAKE_MIS) == E
     assert upd(v=NULL) == E
     assert upd(ws_bytes=0) == W
+
+
+def test_embedding_entry_points_reject_bad_arguments(lib):
+    E, W = dp.DP_ERR_INVALID_ARG, dp.DP_ERR_WORKSPACE
+    inv = ctypes.c_size_t(-1).value
+    assert lib.dp_embedding_norm_workspace(0, 2, 16384, 8) > 0
+    assert lib.dp_embedding_norm_workspace(0, 2, 16385, 8) == inv   # the per-sample sort's limit
+    assert lib.dp_embedding_update_workspace(0, 2, 8, 8, 0) == inv
+
+    def norm(dtype=0, B=2, T=8, d=8, ids=FAKE, dl=FAKE, flags=0, n=FAKE, ws=FAKE,
+             ws_bytes=1 << 20):
+        return lib.dp_embedding_norm(dtype, B, T, d, ids, dl, flags, n, ws, ws_bytes, NULL)
+
+    assert norm(T=16385) == E
+    assert norm(flags=dp.DP_PROBE_RADEMACHER) == E
+    assert norm(ids=NULL) == E
+    assert norm(dl=FAKE_MIS) == E
+    assert norm(ws_bytes=0) == W
+
+    def upd(B=2, T=8, d=8, V=16, C=1.0, Ep=FAKE, ws_bytes=1 << 20):
+        return lib.dp_embedding_clip_aggregate_update(0, B, T, d, V, FAKE, FAKE, FAKE, C, 1.0, 0.1,
+                                                      1, 0, Ep, NULL, NULL, FAKE, ws_bytes, NULL)
+
+    assert upd(V=0) == E
+    assert upd(B=0) == E
+    assert upd(C=-1.0) == E
+    assert upd(Ep=FAKE_MIS) == E
+    assert upd(ws_bytes=16) == W
