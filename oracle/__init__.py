@@ -22,7 +22,9 @@ Sources it follows (cited by page title and section throughout):
   N(0, sigma^2 C^2 I) added to the clipped sum, SGD update theta - eta G/|B|.
   Step 1 (Poisson subsampling of the minibatch) is in ``sampling.py``; the
   per-sample gradients of RMSNorm gains and embedding tables (the parameters
-  that are not linear layers) in ``other_layers.py``.
+  that are not linear layers) in ``other_layers.py``; the forward pass and
+  backward pass 1 of a Llama-shaped MLP block ([RC] アルゴリズム的フロー, steps
+  1-2) and that block's whole step in ``mlp_block.py``.
 * Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
   easy as 1, 2, 3", SC'11 (the published counter-based generator).
 
@@ -79,4 +81,16 @@ from .sampling import (  # noqa: F401
     poisson_sample,
     norm_est_ragged,
     aggregate_ragged,
+)
+from .mlp_block import (  # noqa: F401
+    rmsnorm_forward,
+    rmsnorm_backward,
+    linear_forward,
+    swiglu_forward,
+    swiglu_backward,
+    mlp_forward,
+    mlp_backward,
+    mlp_per_sample_grads,
+    mlp_dp_step,
+    MLP_LAYERS,
 )
