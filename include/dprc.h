@@ -293,6 +293,55 @@ dp_status_t dp_poisson_sample(uint64_t seed, uint32_t step, int64_t N, double q,
                               int64_t idx_cap, int64_t *count, void *ws, size_t ws_bytes,
                               dp_stream_t stream);
 
+/* ---- Forward pass and backward pass 1 of a Llama MLP block ----
+ *
+ * The randomized-clipping summary (section アルゴリズム的フロー, steps 1-2)
+ * runs a forward pass for the activations, then backward pass 1 for every
+ * layer's per-sample output gradient; steps 3-5 are the calls above.  The
+ * block is the MLP half of a Llama decoder layer (M = B T token rows, width d,
+ * hidden width f; bf16 activations, fp32 accumulation):
+ *   rstd = 1 / sqrt(mean(x^2) + eps), xhat = x rstd, y = gamma xhat     (RMSNorm)
+ *   g = y Wg^T, u = y Wu^T, h = silu(g) u, out = x + h Wd^T   (SwiGLU, residual)
+ * and, given the output gradient R = dL/d(out) from the layers above,
+ *   G_down = R, dh = R Wd, G_gate = dh u silu'(g), G_up = dh silu(g),
+ *   dy = G_gate Wg + G_up Wu, dx = rstd (gamma dy - xhat mean(gamma dy xhat)) + R.
+ * The DP step then takes (A, G) = (y, G_gate), (y, G_up), (h, R) for the
+ * three linears and (xhat, dy) for the gain (dp_rmsnorm_norm).
+ *
+ * Layouts: activations row-major [M][width] bf16, 16-byte aligned; weights
+ * Wg, Wu [f][d] and Wd [d][f] bf16 (dp_weights_bf16 of the fp32 parameters);
+ * the backward takes their transposes WgT, WuT [d][f] and WdT [f][d].  d and f
+ * multiples of 256; any M >= 0.  Every buffer is caller-owned device memory;
+ * outputs must not overlap inputs (out may equal x).  No workspace.
+ */
+
+/* W [p][d] = bf16(theta) and Wt [d][p] = its transpose (round to nearest
+ * even); theta fp32 [p][d]; p, d multiples of 64; theta, W 16-byte aligned,
+ * Wt 8-byte aligned. */
+dp_status_t dp_weights_bf16(int p, int d, const float *theta, void *W, void *Wt,
+                            dp_stream_t stream);
+
+/* C [M][N] = bf16(A W^T (+ residual)): the forward of one linear layer.
+ * A [M][K], W [N][K], residual [M][N] or NULL, C [M][N], all bf16; K a
+ * multiple of 32, N of 256; A, W 16-byte aligned, residual and C 8-byte.
+ * C must not overlap A or W. */
+dp_status_t dp_linear_forward(int64_t M, int N, int K, const void *A, const void *W,
+                              const void *residual, void *C, dp_stream_t stream);
+
+/* Forward: x [M][d] -> xhat, y [M][d], rstd [M] fp32, g, u, h [M][f], out [M][d].
+ * gamma [d] fp32 16-byte aligned; eps >= 0. */
+dp_status_t dp_mlp_forward(int B, int T, int d, int f, float eps, const void *x,
+                           const float *gamma, const void *Wg, const void *Wu, const void *Wd,
+                           void *xhat, void *y, float *rstd, void *g, void *u, void *h, void *out,
+                           dp_stream_t stream);
+
+/* Backward pass 1: from x, rstd, g, u of the forward and dout = R [M][d],
+ * writes G_gate, G_up [M][f], dy [M][d] and dx [M][d]. */
+dp_status_t dp_mlp_backward(int B, int T, int d, int f, const void *x, const float *rstd,
+                            const float *gamma, const void *g, const void *u, const void *WgT,
+                            const void *WuT, const void *WdT, const void *dout, void *G_gate,
+                            void *G_up, void *dy, void *dx, dp_stream_t stream);
+
 /* ---- test hooks: expose the random streams for bit-level parity checks ---- */
 
 /* out[4 n] = Philox4x32-10 words of the n counters ctr[4 n] (device arrays). */

@@ -108,6 +108,14 @@ def load_library():
                                                                     c_u64, c_u32, c_p, c_p, c_p,
                                                                     c_p, c_sz, c_p])
     L.dp_embedding_clip_aggregate_update.restype = c_int
+    L.dp_weights_bf16.argtypes = [c_int, c_int, c_p, c_p, c_p, c_p]
+    L.dp_weights_bf16.restype = c_int
+    L.dp_linear_forward.argtypes = [c_i64, c_int, c_int, c_p, c_p, c_p, c_p, c_p]
+    L.dp_linear_forward.restype = c_int
+    L.dp_mlp_forward.argtypes = [c_int] * 4 + [c_f] + [c_p] * 12 + [c_p]
+    L.dp_mlp_forward.restype = c_int
+    L.dp_mlp_backward.argtypes = [c_int] * 4 + [c_p] * 13 + [c_p]
+    L.dp_mlp_backward.restype = c_int
     _lib = L
     return L
 
@@ -383,3 +391,68 @@ def dp_embedding_clip_aggregate_update(ids, delta, n_sq, C, sigma, eta, seed, la
     _check(st, "dp_embedding_clip_aggregate_update")
     return E
 
+
+def dp_weights_bf16(theta, W=None, Wt=None, stream=None):
+    """(W, Wt): bf16 copies of fp32 parameters theta [p][d] and of their transpose."""
+    L = load_library()
+    p, d = theta.shape
+    W = torch.empty(p, d, dtype=torch.bfloat16, device=theta.device) if W is None else W
+    Wt = torch.empty(d, p, dtype=torch.bfloat16, device=theta.device) if Wt is None else Wt
+    _check(L.dp_weights_bf16(p, d, _ptr(theta), _ptr(W), _ptr(Wt), _stream(stream)),
+           "dp_weights_bf16")
+    return W, Wt
+
+
+def dp_linear_forward(A, W, residual=None, C=None, stream=None):
+    """C = bf16(A W^T (+ residual)); A [..][K], W [N][K] bf16."""
+    L = load_library()
+    K = A.shape[-1]
+    M = A.numel() // K if K else 0
+    N = W.shape[0]
+    C = torch.empty(*A.shape[:-1], N, dtype=torch.bfloat16, device=A.device) if C is None else C
+    _check(L.dp_linear_forward(M, N, K, _ptr(A), _ptr(W), _ptr(residual), _ptr(C),
+                               _stream(stream)), "dp_linear_forward")
+    return C
+
+
+MLP_FORWARD_OUTPUTS = ("xhat", "y", "rstd", "g", "u", "h", "out")
+MLP_BACKWARD_OUTPUTS = ("G_gate", "G_up", "dy", "dx")
+
+
+def dp_mlp_forward(x, gamma, Wg, Wu, Wd, eps=1e-5, acts=None, stream=None):
+    """Forward of the MLP block: x [B][T][d] bf16; gamma [d] fp32; Wg, Wu [f][d],
+    Wd [d][f] bf16.  Returns (and fills ``acts`` if given) a dict with xhat, y,
+    rstd [B][T] fp32, g, u, h [B][T][f] and out."""
+    L = load_library()
+    B, T, d = x.shape
+    f = Wg.shape[0]
+    acts = {} if acts is None else acts
+    for name in MLP_FORWARD_OUTPUTS:
+        if name not in acts:
+            width = f if name in ("g", "u", "h") else d
+            acts[name] = (torch.empty(B, T, dtype=torch.float32, device=x.device) if name == "rstd"
+                          else torch.empty(B, T, width, dtype=torch.bfloat16, device=x.device))
+    st = L.dp_mlp_forward(B, T, d, f, float(eps), _ptr(x), _ptr(gamma), _ptr(Wg), _ptr(Wu),
+                          _ptr(Wd), *(_ptr(acts[n]) for n in MLP_FORWARD_OUTPUTS),
+                          _stream(stream))
+    _check(st, "dp_mlp_forward")
+    return acts
+
+
+def dp_mlp_backward(x, rstd, gamma, g, u, WgT, WuT, WdT, dout, grads=None, stream=None):
+    """Backward pass 1 of the MLP block: dict with G_gate, G_up [B][T][f], dy and
+    dx [B][T][d] (bf16) from the forward's x, rstd, g, u, the transposed bf16
+    weights and dout = dL/d(out)."""
+    L = load_library()
+    B, T, d = x.shape
+    f = g.shape[-1]
+    grads = {} if grads is None else grads
+    for name in MLP_BACKWARD_OUTPUTS:
+        if name not in grads:
+            width = f if name in ("G_gate", "G_up") else d
+            grads[name] = torch.empty(B, T, width, dtype=torch.bfloat16, device=x.device)
+    st = L.dp_mlp_backward(B, T, d, f, _ptr(x), _ptr(rstd), _ptr(gamma), _ptr(g), _ptr(u),
+                           _ptr(WgT), _ptr(WuT), _ptr(WdT), _ptr(dout),
+                           *(_ptr(grads[n]) for n in MLP_BACKWARD_OUTPUTS), _stream(stream))
+    _check(st, "dp_mlp_backward")
+    return grads

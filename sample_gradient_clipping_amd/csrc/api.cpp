@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <initializer_list>
 
 #include "dprc.h"
 #include "internal.h"
@@ -881,5 +882,144 @@ dp_status_t dp_embedding_clip_aggregate_update(int dtype, int B, int T, int d, i
                            eta_over_B, seed, layer, s));
   return DP_OK;
 }
+
+// ---- MLP block: forward pass and backward pass 1 ----
+
+struct Region {
+  const void* p;
+  size_t n;
+};
+
+// True if two of the outputs overlap, or an output overlaps an input (an
+// output equal to an input pointer with the same size is allowed only where
+// the caller marks it with `same`).
+static bool regions_clash(const Region* outs, int no, const Region* ins, int ni,
+                          const void* same_out = nullptr, const void* same_in = nullptr) {
+  for (int a = 0; a < no; ++a) {
+    for (int b = a + 1; b < no; ++b)
+      if (overlaps(outs[a].p, outs[a].n, outs[b].p, outs[b].n)) return true;
+    for (int b = 0; b < ni; ++b) {
+      if (outs[a].p == same_out && ins[b].p == same_in && same_out != nullptr) continue;
+      if (overlaps(outs[a].p, outs[a].n, ins[b].p, ins[b].n)) return true;
+    }
+  }
+  return false;
+}
+
+static bool mlp_dims_ok(int B, int T, int d, int f) {
+  if (B < 0 || T < 0 || d < 256 || f < 256 || d % 256 != 0 || f % 256 != 0) return false;
+  return static_cast<int64_t>(B) * T <= (int64_t{1} << 30);
+}
+
+static bool all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr || !aligned(p, 16)) return false;
+  return true;
+}
+
+dp_status_t dp_weights_bf16(int p, int d, const float* theta, void* W, void* Wt,
+                            dp_stream_t stream) {
+  if (p < 0 || d < 0 || p % 64 != 0 || d % 64 != 0) return DP_ERR_INVALID_ARG;
+  if (p == 0 || d == 0) return DP_OK;
+  if (!all_aligned16({theta, W}) || Wt == nullptr || !aligned(Wt, 8)) return DP_ERR_INVALID_ARG;
+  const size_t n = static_cast<size_t>(p) * d;
+  const Region outs[] = {{W, n * 2}, {Wt, n * 2}};
+  const Region ins[] = {{theta, n * 4}};
+  if (regions_clash(outs, 2, ins, 1)) return DP_ERR_INVALID_ARG;
+  DP_TRY(launch_cast_transpose(theta, p, d, static_cast<bf16_t*>(W), static_cast<bf16_t*>(Wt),
+                               static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
+dp_status_t dp_linear_forward(int64_t M, int N, int K, const void* A, const void* W,
+                              const void* residual, void* C, dp_stream_t stream) {
+  if (M < 0 || M > (int64_t{1} << 30) || N <= 0 || N % 256 != 0 || K <= 0 || K % 32 != 0)
+    return DP_ERR_INVALID_ARG;
+  if (M == 0) return DP_OK;
+  if (!all_aligned16({A, W}) || C == nullptr || !aligned(C, 8) ||
+      (residual != nullptr && !aligned(residual, 8)))
+    return DP_ERR_INVALID_ARG;
+  const size_t mn = static_cast<size_t>(M) * N * 2;
+  const Region outs[] = {{C, mn}};
+  const Region ins[] = {{A, static_cast<size_t>(M) * K * 2}, {W, static_cast<size_t>(N) * K * 2},
+                        {residual, residual ? mn : 0}};
+  if (regions_clash(outs, 1, ins, 3, C, residual)) return DP_ERR_INVALID_ARG;
+  DP_TRY(launch_gemm_nt(static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(W), K, nullptr,
+                        nullptr, 0, M, N, static_cast<const bf16_t*>(residual),
+                        static_cast<bf16_t*>(C), static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
+dp_status_t dp_mlp_forward(int B, int T, int d, int f, float eps, const void* x,
+                           const float* gamma, const void* Wg, const void* Wu, const void* Wd,
+                           void* xhat, void* y, float* rstd, void* g, void* u, void* h, void* out,
+                           dp_stream_t stream) {
+  if (!mlp_dims_ok(B, T, d, f) || !(eps >= 0.f) || !std::isfinite(eps)) return DP_ERR_INVALID_ARG;
+  const int64_t M = static_cast<int64_t>(B) * T;
+  if (M == 0) return DP_OK;
+  if (!all_aligned16({x, gamma, Wg, Wu, Wd, xhat, y, g, u, h, out}) || rstd == nullptr ||
+      !aligned(rstd, 4))
+    return DP_ERR_INVALID_ARG;
+  const size_t md = static_cast<size_t>(M) * d * 2, mf = static_cast<size_t>(M) * f * 2,
+               w = static_cast<size_t>(d) * f * 2;
+  const Region outs[] = {{xhat, md}, {y, md}, {rstd, static_cast<size_t>(M) * 4},
+                         {g, mf},    {u, mf}, {h, mf},
+                         {out, md}};
+  const Region ins[] = {{x, md}, {gamma, static_cast<size_t>(d) * 4}, {Wg, w}, {Wu, w}, {Wd, w}};
+  if (regions_clash(outs, 7, ins, 5, out, x)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  bf16_t* yb = static_cast<bf16_t*>(y);
+  bf16_t* gb = static_cast<bf16_t*>(g);
+  bf16_t* ub = static_cast<bf16_t*>(u);
+  bf16_t* hb = static_cast<bf16_t*>(h);
+  DP_TRY(launch_rmsnorm_fwd(xb, gamma, M, d, eps, static_cast<bf16_t*>(xhat), yb, rstd, s));
+  DP_TRY(launch_gemm_nt(yb, static_cast<const bf16_t*>(Wg), d, nullptr, nullptr, 0, M, f, nullptr,
+                        gb, s));
+  DP_TRY(launch_gemm_nt(yb, static_cast<const bf16_t*>(Wu), d, nullptr, nullptr, 0, M, f, nullptr,
+                        ub, s));
+  DP_TRY(launch_swiglu_fwd(gb, ub, M * f, hb, s));
+  DP_TRY(launch_gemm_nt(hb, static_cast<const bf16_t*>(Wd), f, nullptr, nullptr, 0, M, d, xb,
+                        static_cast<bf16_t*>(out), s));
+  return DP_OK;
+}
+
+dp_status_t dp_mlp_backward(int B, int T, int d, int f, const void* x, const float* rstd,
+                            const float* gamma, const void* g, const void* u, const void* WgT,
+                            const void* WuT, const void* WdT, const void* dout, void* G_gate,
+                            void* G_up, void* dy, void* dx, dp_stream_t stream) {
+  if (!mlp_dims_ok(B, T, d, f)) return DP_ERR_INVALID_ARG;
+  const int64_t M = static_cast<int64_t>(B) * T;
+  if (M == 0) return DP_OK;
+  if (!all_aligned16({x, gamma, g, u, WgT, WuT, WdT, dout, G_gate, G_up, dy, dx}) ||
+      rstd == nullptr || !aligned(rstd, 4))
+    return DP_ERR_INVALID_ARG;
+  const size_t md = static_cast<size_t>(M) * d * 2, mf = static_cast<size_t>(M) * f * 2,
+               w = static_cast<size_t>(d) * f * 2;
+  const Region outs[] = {{G_gate, mf}, {G_up, mf}, {dy, md}, {dx, md}};
+  const Region ins[] = {{x, md},   {rstd, static_cast<size_t>(M) * 4}, {gamma, static_cast<size_t>(d) * 4},
+                        {g, mf},   {u, mf},
+                        {WgT, w},  {WuT, w},
+                        {WdT, w},  {dout, md}};
+  if (regions_clash(outs, 4, ins, 9)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bf16_t* gg = static_cast<bf16_t*>(G_gate);
+  bf16_t* gu = static_cast<bf16_t*>(G_up);
+  const bf16_t* db = static_cast<const bf16_t*>(dout);
+  // dh = R Wd into G_gate; SwiGLU backward turns it into dL/dg in place.
+  DP_TRY(launch_gemm_nt(db, static_cast<const bf16_t*>(WdT), d, nullptr, nullptr, 0, M, f, nullptr,
+                        gg, s));
+  DP_TRY(launch_swiglu_bwd(gg, static_cast<const bf16_t*>(g), static_cast<const bf16_t*>(u), M * f,
+                           gu, s));
+  // dy = G_gate Wg + G_up Wu: one product over the two k ranges.
+  DP_TRY(launch_gemm_nt(gg, static_cast<const bf16_t*>(WgT), f, gu,
+                        static_cast<const bf16_t*>(WuT), f, M, d, nullptr,
+                        static_cast<bf16_t*>(dy), s));
+  DP_TRY(launch_rmsnorm_bwd(static_cast<const bf16_t*>(x), rstd, gamma,
+                            static_cast<const bf16_t*>(dy), db, M, d, static_cast<bf16_t*>(dx),
+                            s));
+  return DP_OK;
+}
+
 
 }  // extern "C"

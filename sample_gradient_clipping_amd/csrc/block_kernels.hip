@@ -1,0 +1,479 @@
+// Forward pass and backward pass 1 of a Llama MLP block on gfx950 (the
+// randomized-clipping summary, section アルゴリズム的フロー, steps 1 and 2:
+// activations, then every layer's per-sample output gradient).
+//
+//   RMSNorm   rstd = 1 / sqrt(mean(x^2) + eps), xhat = x rstd, y = gamma xhat
+//   linears   g = y Wg^T, u = y Wu^T, out = x + h Wd^T           (NT products)
+//   SwiGLU    h = silu(g) u
+//   backward  dh = R Wd, (dg, du) from dh, dy = dg Wg + du Wu,
+//             dx = rstd (gamma dy - xhat mean(gamma dy xhat)) + R
+//
+// The products are NT: C[m][n] = sum_k A[m][k] B[n][k] with both operands
+// contiguous along k, activations token-major and weights in their [out][in]
+// layout; the backward-data products take the transposed bf16 weight copy, so
+// they are NT too.
+//
+// NT GEMM data path.  A workgroup computes a 256 x 256 tile with eight waves of
+// 128 (m) x 64 (n).  Stages of 32 k go from HBM into LDS with global_load_lds
+// (16 bytes a lane, no registers), four stages, three in flight.  In LDS a
+// stage holds 256 rows of 64 bytes per operand; the four 16-byte chunks of row
+// r sit in the order c ^ s(r), s(r) = ((r >> 1) ^ (r >> 3)) & 3, so that the
+// 16-byte MFMA operand reads of 8 (and of 16) consecutive rows touch every LDS
+// bank once.  The DMA writes 1 KB of consecutive LDS per instruction, so the
+// swizzle is applied on the global side: the lane that fills LDS chunk c of
+// row r fetches global chunk c ^ s(r).  v_mfma_f32_16x16x32_bf16 takes the
+// weight fragment as its first operand, so that each lane's four accumulator
+// registers are four consecutive n of one m: one 8-byte bf16 store.
+#include "common.h"
+#include "internal.h"
+
+namespace dprc {
+namespace {
+
+constexpr int kNtM = 256, kNtN = 256, kNtK = 32;
+constexpr int kNtRowBytes = kNtK * 2;                 // 64
+constexpr int kNtSideBytes = kNtM * kNtRowBytes;      // 16 KB
+constexpr int kNtStageBytes = 2 * kNtSideBytes;       // A side, then B side
+constexpr int kNtWaves = 8;
+
+__shared__ __attribute__((aligned(16))) unsigned char nt_lds0[kNtStageBytes];
+__shared__ __attribute__((aligned(16))) unsigned char nt_lds1[kNtStageBytes];
+__shared__ __attribute__((aligned(16))) unsigned char nt_lds2[kNtStageBytes];
+__shared__ __attribute__((aligned(16))) unsigned char nt_lds3[kNtStageBytes];
+
+typedef __attribute__((address_space(3))) void nt_lds_void;
+typedef __attribute__((address_space(3))) const u32x4 nt_lds_u32x4;
+
+__device__ __forceinline__ u32x4 nt_read16(const unsigned char* p) {
+  return *(nt_lds_u32x4*)(p);
+}
+
+template <int N>
+__device__ __forceinline__ void nt_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ uint32_t nt_lds_addr(const unsigned char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((nt_lds_void*)(p)));
+}
+
+__host__ __device__ __forceinline__ int nt_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// One 1 KB DMA instruction: lane i's 16 global bytes land at LDS m0 + 16 i.
+// m0 is saved and restored around the load (the compiler keeps its own value
+// there).  The kernel counts these loads itself (vmcnt) and orders stages with
+// s_barrier; as inline asm they are not LDS writes the compiler would drain
+// before every LDS read.
+__device__ __forceinline__ void nt_dma(const unsigned char* gp, uint32_t lds_addr) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(gp), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory");
+}
+
+__device__ __forceinline__ f32x4 nt_mfma(u32x4 w, u32x4 x, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
+                                                 __builtin_bit_cast(bf16x8, x), c, 0, 0, 0);
+}
+
+// Workgroup -> (m tile, n tile): the eight XCDs (consecutive workgroups go to
+// them in turn) each get a contiguous run of the logical order, which walks n
+// inside groups of four m tiles.
+__device__ __forceinline__ void nt_tile_of(int w, int tm, int tn, int nwg, int& mt, int& nt) {
+  constexpr int kXcd = 8, kGroupM = 4;
+  const int l = (nwg % kXcd == 0) ? (w % kXcd) * (nwg / kXcd) + w / kXcd : w;
+  const int grp = l / (kGroupM * tn);
+  const int r = l - grp * kGroupM * tn;
+  const int gm = tm - grp * kGroupM < kGroupM ? tm - grp * kGroupM : kGroupM;
+  nt = r / gm;
+  mt = grp * kGroupM + (r - nt * gm);
+}
+
+// C[m][n] = bf16( sum_k A1[m][k] B1[n][k] + sum_k A2[m][k] B2[n][k] (+ Rz[m][n]) ).
+// K1, K2 multiples of 32 (K2 may be 0), N a multiple of 256, any M >= 1: rows
+// of A beyond M are read from row M - 1 and their results not stored.
+template <bool RESID>
+__global__ void __launch_bounds__(512, 1) k_gemm_nt(
+    const bf16_t* __restrict__ A1, const bf16_t* __restrict__ B1, int K1,
+    const bf16_t* __restrict__ A2, const bf16_t* __restrict__ B2, int K2, int M, int N,
+    const bf16_t* __restrict__ Rz, bf16_t* __restrict__ C) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int mt, ntile;
+  nt_tile_of(blockIdx.x, (M + kNtM - 1) / kNtM, N / kNtN, gridDim.x, mt, ntile);
+  const int m0 = mt * kNtM, n0 = ntile * kNtN;
+  const int ns1 = K1 / kNtK;
+  const int nstage = ns1 + K2 / kNtK;
+
+  // DMA: wave w fills rows (w & 3) * 64 .. + 63 of side w >> 2 (0: A, 1: B),
+  // 16 rows per instruction; lane i -> row i / 4, LDS chunk i % 4.
+  const int side = wave >> 2;
+  const int rbase = (wave & 3) * 64;
+  const int dst_off = side * kNtSideBytes + rbase * kNtRowBytes;
+  int64_t goff1[4], goff2[4];  // element offsets of this lane's chunk, per instruction
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = rbase + i * 16 + (lane >> 2);
+    const int gchunk = (lane & 3) ^ nt_swz(r);
+    int grow;
+    if (side == 0) {
+      grow = m0 + r < M ? m0 + r : M - 1;
+    } else {
+      grow = n0 + r;
+    }
+    goff1[i] = static_cast<int64_t>(grow) * K1 + gchunk * 8;
+    goff2[i] = static_cast<int64_t>(grow) * K2 + gchunk * 8;
+  }
+  const bf16_t* src1 = side == 0 ? A1 : B1;
+  const bf16_t* src2 = side == 0 ? A2 : B2;
+
+  auto issue = [&](int s, unsigned char* stage_lds) {
+    const uint32_t base = nt_lds_addr(stage_lds) + dst_off;
+    if (s < ns1) {
+      const bf16_t* p = src1 + s * kNtK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        nt_dma(reinterpret_cast<const unsigned char*>(p + goff1[i]), base + i * 1024);
+    } else {
+      const bf16_t* p = src2 + (s - ns1) * kNtK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        nt_dma(reinterpret_cast<const unsigned char*>(p + goff2[i]), base + i * 1024);
+    }
+  };
+
+  // Operand reads: wave tile rows wm * 128 + mb * 16 + (lane % 16) of A and
+  // wn * 64 + nb * 16 + (lane % 16) of B, chunk g = lane / 16 of each (k slots
+  // 8 g .. 8 g + 7 for both operands).
+  const int wm = wave >> 2, wn = wave & 3;
+  const int li = lane & 15, g = lane >> 4;
+  int rd_a[8], rd_b[4];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const int r = wm * 128 + mb * 16 + li;
+    rd_a[mb] = r * kNtRowBytes + ((g ^ nt_swz(r)) << 4);
+  }
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int r = wn * 64 + nb * 16 + li;
+    rd_b[nb] = kNtSideBytes + r * kNtRowBytes + ((g ^ nt_swz(r)) << 4);
+  }
+
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const unsigned char* st) {
+    u32x4 xa[8], wb[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) wb[nb] = nt_read16(st + rd_b[nb]);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) xa[mb] = nt_read16(st + rd_a[mb]);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = nt_mfma(wb[nb], xa[mb], acc[mb][nb]);
+  };
+
+  unsigned char* L0 = nt_lds0;
+  unsigned char* L1 = nt_lds1;
+  unsigned char* L2 = nt_lds2;
+  unsigned char* L3 = nt_lds3;
+
+  if (nstage > 0) issue(0, L0);
+  if (nstage > 1) issue(1, L1);
+  if (nstage > 2) issue(2, L2);
+
+  // Stage s: wait for this wave's loads of s (those of s + 1, s + 2 may stay in
+  // flight), barrier, refill the slot of stage s - 1 with s + 3, compute.
+  auto stage = [&](int s, const unsigned char* cur, unsigned char* refill) {
+    const int ahead = nstage - 1 - s;
+    if (ahead >= 2)
+      nt_wait_vm<8>();
+    else if (ahead == 1)
+      nt_wait_vm<4>();
+    else
+      nt_wait_vm<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (s + 3 < nstage) issue(s + 3, refill);
+    compute(cur);
+  };
+
+  for (int s = 0; s < nstage; s += 4) {
+    stage(s, L0, L3);
+    if (s + 1 < nstage) stage(s + 1, L1, L0);
+    if (s + 2 < nstage) stage(s + 2, L2, L1);
+    if (s + 3 < nstage) stage(s + 3, L3, L2);
+  }
+
+  // Epilogue: lane (li, g) holds C[m][n .. n + 3] of block (mb, nb), m = row li
+  // of the block, n = 4 g.
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const int m = m0 + wm * 128 + mb * 16 + li;
+    if (m >= M) continue;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int n = n0 + wn * 64 + nb * 16 + 4 * g;
+      const int64_t off = static_cast<int64_t>(m) * N + n;
+      f32x4 v = acc[mb][nb];
+      if constexpr (RESID) {
+        const uint2 r = *reinterpret_cast<const uint2*>(Rz + off);
+        v[0] += __uint_as_float(r.x << 16);
+        v[1] += __uint_as_float(r.x & 0xFFFF0000u);
+        v[2] += __uint_as_float(r.y << 16);
+        v[3] += __uint_as_float(r.y & 0xFFFF0000u);
+      }
+      uint2 o;
+      o.x = pack_bf16x2(v[0], v[1]);
+      o.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(C + off) = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Elementwise and row kernels.  Rows are token rows of width d (d % 8 == 0);
+// one wave per row, 16-byte accesses (8 bf16 a lane).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void unpack8(u32x4 v, float f[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float f[8]) {
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return v;
+}
+
+constexpr int kRowWaves = 4;  // rows per 256-thread block
+
+__global__ void __launch_bounds__(256) k_rmsnorm_fwd(const bf16_t* __restrict__ x,
+                                                     const float* __restrict__ gamma, int M, int d,
+                                                     float eps, bf16_t* __restrict__ xhat,
+                                                     bf16_t* __restrict__ y,
+                                                     float* __restrict__ rstd) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowWaves + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const bf16_t* xr = x + row * d;
+  const int nc = d >> 3;
+  float ss = 0.f;
+  for (int c = lane; c < nc; c += 64) {
+    float f[8];
+    unpack8(*reinterpret_cast<const u32x4*>(xr + 8 * c), f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
+  }
+  ss = wave_sum(ss);
+  const float rs = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
+  if (lane == 0) rstd[row] = rs;
+  for (int c = lane; c < nc; c += 64) {
+    float f[8], yv[8];
+    unpack8(*reinterpret_cast<const u32x4*>(xr + 8 * c), f);
+    const float4 g0 = *reinterpret_cast<const float4*>(gamma + 8 * c);
+    const float4 g1 = *reinterpret_cast<const float4*>(gamma + 8 * c + 4);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      f[i] *= rs;
+      yv[i] = gv[i] * f[i];
+    }
+    *reinterpret_cast<u32x4*>(xhat + row * d + 8 * c) = pack8(f);
+    *reinterpret_cast<u32x4*>(y + row * d + 8 * c) = pack8(yv);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_rmsnorm_bwd(const bf16_t* __restrict__ x,
+                                                     const float* __restrict__ rstd,
+                                                     const float* __restrict__ gamma,
+                                                     const bf16_t* __restrict__ dy,
+                                                     const bf16_t* __restrict__ dout, int M, int d,
+                                                     bf16_t* __restrict__ dx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowWaves + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const float rs = rstd[row];
+  const int nc = d >> 3;
+  float dot = 0.f;  // sum_q gamma dy xhat
+  for (int c = lane; c < nc; c += 64) {
+    float xf[8], df[8];
+    unpack8(*reinterpret_cast<const u32x4*>(x + row * d + 8 * c), xf);
+    unpack8(*reinterpret_cast<const u32x4*>(dy + row * d + 8 * c), df);
+    const float4 g0 = *reinterpret_cast<const float4*>(gamma + 8 * c);
+    const float4 g1 = *reinterpret_cast<const float4*>(gamma + 8 * c + 4);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dot += gv[i] * df[i] * (xf[i] * rs);
+  }
+  const float mean = wave_sum(dot) / static_cast<float>(d);
+  for (int c = lane; c < nc; c += 64) {
+    float xf[8], df[8], rf[8], o[8];
+    unpack8(*reinterpret_cast<const u32x4*>(x + row * d + 8 * c), xf);
+    unpack8(*reinterpret_cast<const u32x4*>(dy + row * d + 8 * c), df);
+    unpack8(*reinterpret_cast<const u32x4*>(dout + row * d + 8 * c), rf);
+    const float4 g0 = *reinterpret_cast<const float4*>(gamma + 8 * c);
+    const float4 g1 = *reinterpret_cast<const float4*>(gamma + 8 * c + 4);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = rs * (gv[i] * df[i] - xf[i] * rs * mean) + rf[i];
+    *reinterpret_cast<u32x4*>(dx + row * d + 8 * c) = pack8(o);
+  }
+}
+
+__device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// h = silu(g) u over n8 groups of 8 elements.
+__global__ void __launch_bounds__(256) k_swiglu_fwd(const bf16_t* __restrict__ g,
+                                                    const bf16_t* __restrict__ u, int64_t n8,
+                                                    bf16_t* __restrict__ h) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float gf[8], uf[8], hf[8];
+    unpack8(reinterpret_cast<const u32x4*>(g)[i], gf);
+    unpack8(reinterpret_cast<const u32x4*>(u)[i], uf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hf[e] = gf[e] * sigmoidf(gf[e]) * uf[e];
+    reinterpret_cast<u32x4*>(h)[i] = pack8(hf);
+  }
+}
+
+// In place: dgh holds dL/dh on entry and dL/dg on exit; du receives dL/du.
+__global__ void __launch_bounds__(256) k_swiglu_bwd(bf16_t* __restrict__ dgh,
+                                                    const bf16_t* __restrict__ g,
+                                                    const bf16_t* __restrict__ u, int64_t n8,
+                                                    bf16_t* __restrict__ du) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float hf[8], gf[8], uf[8], dg[8], dv[8];
+    unpack8(reinterpret_cast<const u32x4*>(dgh)[i], hf);
+    unpack8(reinterpret_cast<const u32x4*>(g)[i], gf);
+    unpack8(reinterpret_cast<const u32x4*>(u)[i], uf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float s = sigmoidf(gf[e]);
+      dg[e] = hf[e] * uf[e] * s * (1.0f + gf[e] * (1.0f - s));
+      dv[e] = hf[e] * gf[e] * s;
+    }
+    reinterpret_cast<u32x4*>(dgh)[i] = pack8(dg);
+    reinterpret_cast<u32x4*>(du)[i] = pack8(dv);
+  }
+}
+
+// theta fp32 [p][d] -> W bf16 [p][d] and Wt bf16 [d][p], 64 x 64 tiles through
+// LDS (p, d multiples of 64).
+__global__ void __launch_bounds__(256) k_cast_transpose(const float* __restrict__ theta, int p,
+                                                        int d, bf16_t* __restrict__ W,
+                                                        bf16_t* __restrict__ Wt) {
+  __shared__ bf16_t tile[64][64 + 2];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = tr + 16 * k;
+    const float4 v = *reinterpret_cast<const float4*>(theta + static_cast<int64_t>(r0 + r) * d + c0 + tc);
+    uint2 o;
+    o.x = pack_bf16x2(v.x, v.y);
+    o.y = pack_bf16x2(v.z, v.w);
+    *reinterpret_cast<uint2*>(W + static_cast<int64_t>(r0 + r) * d + c0 + tc) = o;
+    tile[r][tc + 0] = static_cast<bf16_t>(o.x & 0xFFFFu);
+    tile[r][tc + 1] = static_cast<bf16_t>(o.x >> 16);
+    tile[r][tc + 2] = static_cast<bf16_t>(o.y & 0xFFFFu);
+    tile[r][tc + 3] = static_cast<bf16_t>(o.y >> 16);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = tr + 16 * k;  // column of theta = row of Wt
+    uint2 o;
+    o.x = static_cast<uint32_t>(tile[tc + 0][c]) | (static_cast<uint32_t>(tile[tc + 1][c]) << 16);
+    o.y = static_cast<uint32_t>(tile[tc + 2][c]) | (static_cast<uint32_t>(tile[tc + 3][c]) << 16);
+    *reinterpret_cast<uint2*>(Wt + static_cast<int64_t>(c0 + c) * p + r0 + tc) = o;
+  }
+}
+
+int elementwise_blocks(int64_t n8) {
+  const int64_t want = (n8 + 255) / 256;
+  return static_cast<int>(want < 4096 ? (want > 0 ? want : 1) : 4096);
+}
+
+}  // namespace
+
+bool gemm_nt_ok(int64_t M, int N, int K1, int K2) {
+  return M >= 1 && M <= (int64_t{1} << 30) && N > 0 && N % kNtN == 0 && K1 > 0 &&
+         K1 % kNtK == 0 && K2 >= 0 && K2 % kNtK == 0;
+}
+
+hipError_t launch_gemm_nt(const bf16_t* A1, const bf16_t* B1, int K1, const bf16_t* A2,
+                          const bf16_t* B2, int K2, int64_t M, int N, const bf16_t* Rz, bf16_t* C,
+                          hipStream_t s) {
+  if (!gemm_nt_ok(M, N, K1, K2)) return hipErrorInvalidValue;
+  const int64_t tiles = ((M + kNtM - 1) / kNtM) * (N / kNtN);
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(tiles)), block(64 * kNtWaves);
+  const int m = static_cast<int>(M);
+  if (Rz)
+    hipLaunchKernelGGL(k_gemm_nt<true>, grid, block, 0, s, A1, B1, K1, A2, B2, K2, m, N, Rz, C);
+  else
+    hipLaunchKernelGGL(k_gemm_nt<false>, grid, block, 0, s, A1, B1, K1, A2, B2, K2, m, N, Rz, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_fwd(const bf16_t* x, const float* gamma, int64_t M, int d, float eps,
+                              bf16_t* xhat, bf16_t* y, float* rstd, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (d <= 0 || d % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(static_cast<unsigned>((M + kRowWaves - 1) / kRowWaves)),
+                     dim3(256), 0, s, x, gamma, static_cast<int>(M), d, eps, xhat, y, rstd);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bwd(const bf16_t* x, const float* rstd, const float* gamma,
+                              const bf16_t* dy, const bf16_t* dout, int64_t M, int d, bf16_t* dx,
+                              hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (d <= 0 || d % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(static_cast<unsigned>((M + kRowWaves - 1) / kRowWaves)),
+                     dim3(256), 0, s, x, rstd, gamma, dy, dout, static_cast<int>(M), d, dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_fwd(const bf16_t* g, const bf16_t* u, int64_t n, bf16_t* h, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_swiglu_fwd, dim3(elementwise_blocks(n / 8)), dim3(256), 0, s, g, u, n / 8, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(bf16_t* dgh, const bf16_t* g, const bf16_t* u, int64_t n, bf16_t* du,
+                             hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_swiglu_bwd, dim3(elementwise_blocks(n / 8)), dim3(256), 0, s, dgh, g, u,
+                     n / 8, du);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_transpose(const float* theta, int p, int d, bf16_t* W, bf16_t* Wt,
+                                 hipStream_t s) {
+  if (p <= 0 || d <= 0) return hipSuccess;
+  if (p % 64 != 0 || d % 64 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_cast_transpose, dim3(d / 64, p / 64), dim3(256), 0, s, theta, p, d, W, Wt);
+  return hipGetLastError();
+}
+
+}  // namespace dprc

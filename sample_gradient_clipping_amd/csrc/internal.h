@@ -168,4 +168,20 @@ hipError_t launch_aggregate_mfma(const bf16_t* A, const bf16_t* G, int B, int T,
 hipError_t launch_fgc_mfma(const bf16_t* A, const bf16_t* G, int B, int T, int d, int p, float* M,
                            hipStream_t s);
 
+// ---- MLP block forward / backward pass 1 (block_kernels.hip) ----
+bool gemm_nt_ok(int64_t M, int N, int K1, int K2);
+hipError_t launch_gemm_nt(const bf16_t* A1, const bf16_t* B1, int K1, const bf16_t* A2,
+                          const bf16_t* B2, int K2, int64_t M, int N, const bf16_t* Rz, bf16_t* C,
+                          hipStream_t s);
+hipError_t launch_rmsnorm_fwd(const bf16_t* x, const float* gamma, int64_t M, int d, float eps,
+                              bf16_t* xhat, bf16_t* y, float* rstd, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const bf16_t* x, const float* rstd, const float* gamma,
+                              const bf16_t* dy, const bf16_t* dout, int64_t M, int d, bf16_t* dx,
+                              hipStream_t s);
+hipError_t launch_swiglu_fwd(const bf16_t* g, const bf16_t* u, int64_t n, bf16_t* h, hipStream_t s);
+hipError_t launch_swiglu_bwd(bf16_t* dgh, const bf16_t* g, const bf16_t* u, int64_t n, bf16_t* du,
+                             hipStream_t s);
+hipError_t launch_cast_transpose(const float* theta, int p, int d, bf16_t* W, bf16_t* Wt,
+                                 hipStream_t s);
+
 }  // namespace dprc

@@ -12,6 +12,9 @@ Recipes (the value distributions of the five workloads):
     log-uniform over [0.1, 10].
   * "lowrank":     A = U_a V_a^T + 0.05 N and G likewise, rank-8 signal plus
     noise, for estimator-accuracy checks on a decaying spectrum.
+  * MLP block (``mlp_block_inputs``): x ~ N(0, 1) (the residual stream),
+    gamma = 1 + 0.1 N(0, 1), weights N(0, 0.02^2) in fp32 (as theta_init), and
+    the output gradient R = dL/d(out) ~ N(0, 1e-4) times s_i = 10^U(-1, 1).
 Ragged batches (``ragged_lengths``): per-sample lengths T_i <= T; the caller
 zeroes G's rows from T_i on (the pad), as a masked backward pass leaves them.
 Host draws use numpy's PCG64 seeded with (seed, layer_id, tensor_tag); values
@@ -22,6 +25,7 @@ import numpy as np
 import torch
 
 TAG_A, TAG_G, TAG_SCALE, TAG_THETA, TAG_LEN = 0, 1, 2, 3, 4
+TAG_GAMMA = 5
 
 
 def _rng(seed, layer_id, tag):
@@ -110,3 +114,36 @@ def linear_inputs_device(B, T, d, p, dtype, recipe, seed, layer_id, device):
             G *= 0.01
     G = (G * s[:, None, None]).to(td)
     return A, G
+
+
+def mlp_block_inputs(B, T, d, f, seed, block=0):
+    """(x [B][T][d] bf16, gamma [d] fp32, {"W_gate": [f][d], "W_up": [f][d],
+    "W_down": [d][f]} fp32, R [B][T][d] bf16) on the CPU; the three weights use
+    layer ids 7 block + {0, 1, 2} of the theta stream."""
+    x = _rng(seed, 7 * block, TAG_A).standard_normal((B, T, d), dtype=np.float32)
+    gamma = 1.0 + 0.1 * _rng(seed, 7 * block, TAG_GAMMA).standard_normal(d, dtype=np.float32)
+    thetas = {name: theta_init(shape[0], shape[1], seed, 7 * block + i)
+              for i, (name, shape) in enumerate((("W_gate", (f, d)), ("W_up", (f, d)),
+                                                 ("W_down", (d, f))))}
+    s = sample_scales(B, "llama_logu", seed, 7 * block).astype(np.float32)
+    R = _rng(seed, 7 * block, TAG_G).standard_normal((B, T, d), dtype=np.float32)
+    R *= np.float32(0.01) * s[:, None, None]
+    return (torch.from_numpy(x).to(torch.bfloat16), torch.from_numpy(gamma.astype(np.float32)),
+            thetas, torch.from_numpy(R).to(torch.bfloat16))
+
+
+def mlp_block_inputs_device(B, T, d, f, seed, device):
+    """The same shapes and law drawn on the device (bench only; not bit-identical
+    to :func:`mlp_block_inputs`)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) & 0x7FFFFFFFFFFFFFFF)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+
+    x = randn(B, T, d).to(torch.bfloat16)
+    gamma = 1.0 + 0.1 * randn(d)
+    thetas = {"W_gate": 0.02 * randn(f, d), "W_up": 0.02 * randn(f, d), "W_down": 0.02 * randn(d, f)}
+    s = torch.from_numpy(sample_scales(B, "llama_logu", seed).astype(np.float32)).to(device)
+    R = (0.01 * randn(B, T, d) * s[:, None, None]).to(torch.bfloat16)
+    return x, gamma, thetas, R

@@ -243,3 +243,49 @@ def test_embedding_entry_points_reject_bad_arguments(lib):
     assert upd(C=-1.0) == E
     assert upd(Ep=FAKE_MIS) == E
     assert upd(ws_bytes=16) == W
+
+
+def _addr(i):
+    """Distinct, well separated fake device addresses (never dereferenced)."""
+    return ctypes.c_void_p(0x10000000 + i * 0x10000000)
+
+
+def test_mlp_block_entry_points_reject_bad_arguments(lib):
+    E = dp.DP_ERR_INVALID_ARG
+    assert lib.dp_weights_bf16(64, 100, FAKE, _addr(1), _addr(2), NULL) == E     # d % 64
+    assert lib.dp_weights_bf16(0, 64, FAKE, FAKE, FAKE, NULL) == dp.DP_OK       # empty: no-op
+    assert lib.dp_weights_bf16(64, 64, FAKE_MIS, _addr(1), _addr(2), NULL) == E
+    assert lib.dp_weights_bf16(64, 64, _addr(0), _addr(1), _addr(1), NULL) == E  # W, Wt overlap
+
+    def lin(M=512, N=256, K=64, A=_addr(0), W=_addr(1), R=NULL, C=_addr(2)):
+        return lib.dp_linear_forward(M, N, K, A, W, R, C, NULL)
+
+    assert lin(N=300) == E
+    assert lin(K=48) == E
+    assert lin(M=-1) == E
+    assert lin(M=0) == dp.DP_OK
+    assert lin(C=_addr(0)) == E                           # C overlaps A
+    assert lin(A=FAKE_MIS) == E
+    assert lin(R=ctypes.c_void_p(_addr(2).value + 2)) == E  # residual overlaps C, not equal
+
+    def fwd(B=2, T=128, d=256, f=512, eps=1e-5, out=_addr(11), x=_addr(0)):
+        return lib.dp_mlp_forward(B, T, d, f, eps, x, _addr(1), _addr(2), _addr(3), _addr(4),
+                                  _addr(5), _addr(6), _addr(7), _addr(8), _addr(9), _addr(10), out,
+                                  NULL)
+
+    assert fwd(d=200) == E
+    assert fwd(f=384) == E
+    assert fwd(eps=-1.0) == E
+    assert fwd(eps=float("nan")) == E
+    assert fwd(out=_addr(5)) == E                         # out overlaps xhat
+    assert fwd(B=0) == dp.DP_OK
+
+    def bwd(B=2, T=128, d=256, f=512, dx=_addr(16), G=_addr(13)):
+        return lib.dp_mlp_backward(B, T, d, f, _addr(0), _addr(1), _addr(2), _addr(3), _addr(4),
+                                   _addr(5), _addr(6), _addr(7), _addr(8), G, _addr(14), _addr(15),
+                                   dx, NULL)
+
+    assert bwd(d=128) == E
+    assert bwd(dx=_addr(8)) == E                          # dx overlaps dout
+    assert bwd(G=FAKE_MIS) == E
+    assert bwd(T=0) == dp.DP_OK
