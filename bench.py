@@ -269,6 +269,82 @@ def embedding_timing(dp, wl, dev, V=128256, reps=10):
             "update_us": us_u, "update_GBps": bytes_u / (us_u * 1e-6) / 1e9}
 
 
+def mlp_block_timing(dp, wl, dev, d=2048, f=8192, k=32, reps=5):
+    """One DP-SGD-RC step of a Llama-3.2-1B-shaped MLP block (RMSNorm, SwiGLU
+    gate/up/down, residual) at the workload's B and T: forward pass, backward
+    pass 1, then norms (Hutch for the three linears, the gain exactly), clip,
+    clipped sums, noise and updates of all four parameters.  Outside the timed
+    steps; the NT GEMM of the forward pass is also timed alone."""
+    import torch
+    from sample_gradient_clipping_amd.inputs import mlp_block_inputs_device
+    B, T = wl.B, wl.T
+    M = B * T
+    x, gamma, thetas, R = mlp_block_inputs_device(B, T, d, f, 5151, dev)
+    Wb = {name: dp.dp_weights_bf16(t) for name, t in thetas.items()}
+    acts, grads = {}, {}
+    n = torch.zeros(B, dtype=torch.float32, device=dev)
+    v = torch.empty(B, d, dtype=torch.float32, device=dev)
+    ids = {"W_gate": 0, "W_up": 1, "W_down": 2, "gamma": 3}
+
+    def forward():
+        dp.dp_mlp_forward(x, gamma, Wb["W_gate"][0], Wb["W_up"][0], Wb["W_down"][0], acts=acts)
+
+    def backward():
+        dp.dp_mlp_backward(x, acts["rstd"], gamma, acts["g"], acts["u"], Wb["W_gate"][1],
+                           Wb["W_up"][1], Wb["W_down"][1], R, grads=grads)
+
+    def dp_part(it):
+        lin = {"W_gate": (acts["y"], grads["G_gate"]), "W_up": (acts["y"], grads["G_up"]),
+               "W_down": (acts["h"], R)}
+        dp.dp_rmsnorm_norm(acts["xhat"], grads["dy"], n, v=v)
+        for name, (A, G) in lin.items():
+            dp.dp_norm_est("hutch", A, G, k, 900 + it, ids[name], n, flags=dp.DP_ACCUMULATE)
+        for name, (A, G) in lin.items():
+            dp.dp_clip_aggregate_update(A, G, n, 1.0, 1.0, 1e-4, 1900 + it, ids[name],
+                                        thetas[name])
+        dp.dp_rmsnorm_clip_aggregate_update(v, n, 1.0, 1.0, 1e-4, 1900 + it, ids["gamma"], gamma)
+
+    def gemm():
+        dp.dp_linear_forward(acts["y"], Wb["W_gate"][0], C=acts["g"])
+
+    forward(); backward(); dp_part(0); gemm()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    ev[0].record()
+    for _ in range(reps):
+        gemm()
+    ev[1].record()
+    for _ in range(reps):
+        forward()
+    ev[2].record()
+    torch.cuda.synchronize()
+    t_gemm = ev[0].elapsed_time(ev[1]) / reps
+    t_fwd = ev[1].elapsed_time(ev[2]) / reps
+    ev[0].record()
+    for _ in range(reps):
+        backward()
+    ev[1].record()
+    for it in range(reps):
+        dp_part(it + 1)
+    ev[2].record()
+    for it in range(reps):
+        forward(); backward(); dp_part(it + 1)
+    ev[3].record()
+    torch.cuda.synchronize()
+    t_bwd = ev[0].elapsed_time(ev[1]) / reps
+    t_dp = ev[1].elapsed_time(ev[2]) / reps
+    t_step = ev[2].elapsed_time(ev[3]) / reps
+    gemm_flops = 2.0 * M * d * f
+    del acts, grads
+    return {"B": B, "T": T, "d": d, "f": f, "k": k, "method": "hutch",
+            "nt_gemm_us": t_gemm * 1e3, "nt_gemm_TFLOPs": gemm_flops / (t_gemm * 1e-3) / 1e12,
+            "nt_gemm_frac_mfma": gemm_flops / (t_gemm * 1e-3) / 2.5e15,
+            "forward_ms": t_fwd, "forward_TFLOPs": 3 * gemm_flops / (t_fwd * 1e-3) / 1e12,
+            "backward1_ms": t_bwd, "backward1_TFLOPs": 3 * gemm_flops / (t_bwd * 1e-3) / 1e12,
+            "dp_step_ms": t_dp, "block_step_ms": t_step,
+            "block_step_tokens_per_s": M / (t_step * 1e-3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -434,6 +510,10 @@ def main():
     log(f"[bench] rmsnorm gain norms {rms}")
     emb = embedding_timing(dp, wl, dev) if wl.dtype == "bf16" else None
     log(f"[bench] embedding {emb}")
+    del inputs
+    torch.cuda.empty_cache()
+    mlp = mlp_block_timing(dp, wl, dev) if wl.dtype == "bf16" else None
+    log(f"[bench] mlp block {mlp}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -456,6 +536,7 @@ def main():
         "poisson_sampler": sampler,
         "rmsnorm_gain_norms": rms,
         "embedding": emb,
+        "mlp_block": mlp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
