@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--method", default=None, help="override the workload's estimator")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-step", action="store_true",
+                    help="time the steps only: no side measurements and no CPU baseline (for "
+                         "profiler passes whose per-kernel means must cover the step alone)")
     ap.add_argument("--rademacher", action="store_true",
                     help="sign (+-1) probes instead of Gaussian ones for Hutch / Hutch++")
     ap.add_argument("--unfused", action="store_true",
@@ -502,21 +505,23 @@ def main():
             f"{kv['GBps']:8.1f} GB/s  {kv.get('TFLOPs', 0):8.1f} TF/s  frac {kv['frac']:.3f}  "
             f"share {kv['share_of_step']:.2f}")
 
-    accuracy = estimator_accuracy(dp, wl, inputs[0][0], dev, rademacher=args.rademacher)
-    log(f"[bench] estimator accuracy {accuracy}")
-    sampler = poisson_timing(dp, dev)
-    log(f"[bench] poisson sampler {sampler}")
-    rms = rmsnorm_timing(dp, wl, dev) if wl.dtype == "bf16" else None
-    log(f"[bench] rmsnorm gain norms {rms}")
-    emb = embedding_timing(dp, wl, dev) if wl.dtype == "bf16" else None
-    log(f"[bench] embedding {emb}")
-    del inputs
-    torch.cuda.empty_cache()
-    mlp = mlp_block_timing(dp, wl, dev) if wl.dtype == "bf16" else None
-    log(f"[bench] mlp block {mlp}")
+    accuracy = sampler = rms = emb = mlp = None
+    if not args.only_step:
+        accuracy = estimator_accuracy(dp, wl, inputs[0][0], dev, rademacher=args.rademacher)
+        log(f"[bench] estimator accuracy {accuracy}")
+        sampler = poisson_timing(dp, dev)
+        log(f"[bench] poisson sampler {sampler}")
+        rms = rmsnorm_timing(dp, wl, dev) if wl.dtype == "bf16" else None
+        log(f"[bench] rmsnorm gain norms {rms}")
+        emb = embedding_timing(dp, wl, dev) if wl.dtype == "bf16" else None
+        log(f"[bench] embedding {emb}")
+        del inputs
+        torch.cuda.empty_cache()
+        mlp = mlp_block_timing(dp, wl, dev) if wl.dtype == "bf16" else None
+        log(f"[bench] mlp block {mlp}")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.only_step:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(wl, method, rademacher=args.rademacher)
         log(f"[bench] cpu_baseline {cpu}")
