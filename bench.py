@@ -401,39 +401,62 @@ def main():
                 e.record()
     torch.cuda.synchronize()
 
-    def step(it, evs):
+    def step(it, evs, only=None):
+        """One step.  evs: per layer the six events (norm_est, aggregate, noise_update
+        pairs), or None; with ``only`` set, just that kernel's pair is recorded."""
+        def pair(li, name):
+            if evs is None or (only is not None and only != name):
+                return None
+            j = {"norm_est": 0, "aggregate": 2, "noise_update": 4}[name]
+            return (evs[li][j], evs[li][j + 1])
         cp = inputs[it % copies]
         for li, l in enumerate(wl.layers):
             A, G = cp[li]
             flags = (dp.DP_ACCUMULATE if li else 0) | (
                 dp.DP_PROBE_RADEMACHER if args.rademacher else 0)
             dp.dp_norm_est(method, A, G, wl.k, wl.method_seed + it, l.layer_id, n,
-                           flags=flags, ws=ws_norm,
-                           events=None if evs is None else (evs[li][0], evs[li][1]))
+                           flags=flags, ws=ws_norm, events=pair(li, "norm_est"))
         for li, l in enumerate(wl.layers):
             A, G = cp[li]
             if args.unfused:  # clipped sum to S, then noise + update: two calls
-                dp.dp_clip_aggregate(A, G, n, wl.C, S[li], ws=ws_agg,
-                                     events=None if evs is None else (evs[li][2], evs[li][3]))
+                dp.dp_clip_aggregate(A, G, n, wl.C, S[li], ws=ws_agg, events=pair(li, "aggregate"))
                 dp.dp_noise_update(theta[li], S[li], wl.sigma, wl.C, wl.eta, wl.B,
-                                   wl.noise_seed + it, l.layer_id,
-                                   events=None if evs is None else (evs[li][4], evs[li][5]))
+                                   wl.noise_seed + it, l.layer_id, events=pair(li, "noise_update"))
             else:  # one call: clip, clipped sum, noise, update (S not stored)
+                ea, eu = pair(li, "aggregate"), pair(li, "noise_update")
                 dp.dp_clip_aggregate_update(
                     A, G, n, wl.C, wl.sigma, wl.eta, wl.noise_seed + it, l.layer_id, theta[li],
-                    ws=ws_agg, events=None if evs is None else ((evs[li][2], evs[li][3]),
-                                                                (evs[li][4], evs[li][5])))
+                    ws=ws_agg, events=None if ea is None and eu is None else (ea, eu))
 
     for it in range(W):
         step(it, None)
     torch.cuda.synchronize()
+
+    # An instrumented pass outside the timed region: every kernel group's duration,
+    # which picks the dominant kernel.  Inside the timed steps only the dominant
+    # kernel's launches are bracketed by events (each event record costs GPU time).
+    KI = min(K, 10)
+    ev_i = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
+            for _ in range(KI)]
+    for it in range(KI):
+        step(W + it, ev_i[it])
+    torch.cuda.synchronize()
+    t_inst = {"norm_est": 0.0, "aggregate": 0.0, "noise_update": 0.0}
+    for it in range(KI):
+        for li in range(L):
+            e = ev_i[it][li]
+            t_inst["norm_est"] += e[0].elapsed_time(e[1]) / KI
+            t_inst["aggregate"] += e[2].elapsed_time(e[3]) / KI
+            t_inst["noise_update"] += e[4].elapsed_time(e[5]) / KI
+    dom_name = max(t_inst, key=t_inst.get)
+
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record()
     for it in range(K):
-        step(W + it, ev[it])
+        step(W + KI + it, ev[it], only=dom_name)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -443,14 +466,14 @@ def main():
     log(f"[bench] {K} steps in {ms_total:.3f} ms (wall {wall * 1e3:.1f} ms): {ms_step:.4f} ms/step, "
         f"{tokens_per_s / 1e6:.2f} M tokens/s")
 
-    # Per-kernel durations from the library's events, summed over the timed steps.
-    t_norm = t_agg = t_noise = 0.0
-    for it in range(K):
-        for li in range(L):
-            e = ev[it][li]
-            t_norm += e[0].elapsed_time(e[1])
-            t_agg += e[2].elapsed_time(e[3])
-            t_noise += e[4].elapsed_time(e[5])
+    # Per-step durations: the dominant kernel from its events in the timed steps, the
+    # others from the instrumented pass.
+    t_step = dict(t_inst)
+    j = {"norm_est": 0, "aggregate": 2, "noise_update": 4}[dom_name]
+    t_step[dom_name] = sum(ev[it][li][j].elapsed_time(ev[it][li][j + 1])
+                           for it in range(K) for li in range(L)) / K
+    t_norm, t_agg, t_noise = (t_step["norm_est"] * K, t_step["aggregate"] * K,
+                              t_step["noise_update"] * K)
     launches = K * L
     if method in ("hutch",):
         b_norm = sum(rf.hutch_bytes(wl.B, wl.T, l.d, l.p, wl.dtype) for l in wl.layers)
@@ -485,7 +508,9 @@ def main():
         kv["frac"] = (kv["GBps"] / rf.PEAK_HBM_GBPS if kv["bound"] == "hbm"
                       else kv["TFLOPs"] / rf.PEAK_BF16_TFLOPS)
         kv["share_of_step"] = (kv["ms_per_launch"] * L) / ms_step
-    dom_name = max(kernels, key=lambda k_: kernels[k_]["share_of_step"])
+    for kname, kv in kernels.items():
+        kv["timing"] = ("HIP events in the timed steps" if kname == dom_name else
+                        f"HIP events in an instrumented pass of {KI} steps before the timed ones")
     dom = kernels[dom_name]
     traffic = measured_traffic(dom_name, wl.name)
     if dom["bound"] == "hbm":

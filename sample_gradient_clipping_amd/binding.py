@@ -255,7 +255,9 @@ def dp_clip_aggregate_update(A, G, n_sq, C, sigma, eta, seed, layer, theta, S=No
     if events is None:
         st = L.dp_clip_aggregate_update(*args)
     else:
-        (a0, a1), (u0, u1) = events
+        ea, eu = events  # either pair may be None
+        a0, a1 = ea if ea is not None else (None, None)
+        u0, u1 = eu if eu is not None else (None, None)
         st = L.dp_clip_aggregate_update_timed(*args, _event(a0), _event(a1), _event(u0),
                                               _event(u1))
     _check(st, "dp_clip_aggregate_update")
