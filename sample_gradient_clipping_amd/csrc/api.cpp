@@ -974,11 +974,9 @@ dp_status_t dp_mlp_forward(int B, int T, int d, int f, float eps, const void* x,
   bf16_t* ub = static_cast<bf16_t*>(u);
   bf16_t* hb = static_cast<bf16_t*>(h);
   DP_TRY(launch_rmsnorm_fwd(xb, gamma, M, d, eps, static_cast<bf16_t*>(xhat), yb, rstd, s));
-  DP_TRY(launch_gemm_nt(yb, static_cast<const bf16_t*>(Wg), d, nullptr, nullptr, 0, M, f, nullptr,
-                        gb, s));
-  DP_TRY(launch_gemm_nt(yb, static_cast<const bf16_t*>(Wu), d, nullptr, nullptr, 0, M, f, nullptr,
-                        ub, s));
-  DP_TRY(launch_swiglu_fwd(gb, ub, M * f, hb, s));
+  // gate and up in one product; its epilogue writes g, u and h = silu(g) u
+  DP_TRY(launch_gemm_nt_swiglu(yb, static_cast<const bf16_t*>(Wg), static_cast<const bf16_t*>(Wu),
+                               d, M, f, gb, ub, hb, s));
   DP_TRY(launch_gemm_nt(hb, static_cast<const bf16_t*>(Wd), f, nullptr, nullptr, 0, M, d, xb,
                         static_cast<bf16_t*>(out), s));
   return DP_OK;
@@ -1006,11 +1004,10 @@ dp_status_t dp_mlp_backward(int B, int T, int d, int f, const void* x, const flo
   bf16_t* gg = static_cast<bf16_t*>(G_gate);
   bf16_t* gu = static_cast<bf16_t*>(G_up);
   const bf16_t* db = static_cast<const bf16_t*>(dout);
-  // dh = R Wd into G_gate; SwiGLU backward turns it into dL/dg in place.
-  DP_TRY(launch_gemm_nt(db, static_cast<const bf16_t*>(WdT), d, nullptr, nullptr, 0, M, f, nullptr,
-                        gg, s));
-  DP_TRY(launch_swiglu_bwd(gg, static_cast<const bf16_t*>(g), static_cast<const bf16_t*>(u), M * f,
-                           gu, s));
+  // dh = R Wd stays in registers: the product's epilogue writes dL/dg and dL/du.
+  DP_TRY(launch_gemm_nt_swiglu_bwd(db, static_cast<const bf16_t*>(WdT), d, M, f,
+                                   static_cast<const bf16_t*>(g), static_cast<const bf16_t*>(u), gg,
+                                   gu, s));
   // dy = G_gate Wg + G_up Wu: one product over the two k ranges.
   DP_TRY(launch_gemm_nt(gg, static_cast<const bf16_t*>(WgT), f, gu,
                         static_cast<const bf16_t*>(WuT), f, M, d, nullptr,

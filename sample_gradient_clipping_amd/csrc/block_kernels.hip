@@ -24,6 +24,14 @@
 // row r fetches global chunk c ^ s(r).  v_mfma_f32_16x16x32_bf16 takes the
 // weight fragment as its first operand, so that each lane's four accumulator
 // registers are four consecutive n of one m: one 8-byte bf16 store.
+//
+// SwiGLU lives in the products' epilogues.  Forward: gate and up are one product
+// whose weight side alternates 16-row blocks of Wg and Wu, so a wave's 64
+// output columns are g, u, g, u blocks of the same hidden columns and each lane
+// holds g and u of the same four outputs: it writes g, u and h = silu(g) u.
+// Backward: the product dh = R Wd turns into dL/dg = dh u silu'(g) and
+// dL/du = dh silu(g) in its epilogue, reading the stored g and u; dh itself
+// never goes to memory.
 #include "common.h"
 #include "internal.h"
 
@@ -93,14 +101,38 @@ __device__ __forceinline__ void nt_tile_of(int w, int tm, int tn, int nwg, int& 
   mt = grp * kGroupM + (r - nt * gm);
 }
 
-// C[m][n] = bf16( sum_k A1[m][k] B1[n][k] + sum_k A2[m][k] B2[n][k] (+ Rz[m][n]) ).
+constexpr int kEpiStore = 0, kEpiResid = 1, kEpiSwiglu = 2, kEpiSwigluBwd = 3;
+
+__device__ __forceinline__ float nt_sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+struct NtArgs {
+  const bf16_t* A1;
+  const bf16_t* B1;
+  const bf16_t* B1u;  // kEpiSwiglu: the up weight
+  const bf16_t* A2;
+  const bf16_t* B2;
+  const bf16_t* Rz;   // kEpiResid: residual; kEpiSwigluBwd: g
+  const bf16_t* Rz2;  // kEpiSwigluBwd: u
+  bf16_t* C;
+  bf16_t* C2;
+  bf16_t* C3;
+  int K1, K2, M, N;
+};
+
+// acc[m][n] = sum_k A1[m][k] B1[n][k] + sum_k A2[m][k] B2[n][k], then by EPI:
+//   kEpiStore   C = bf16(acc)
+//   kEpiResid   C = bf16(acc + Rz)
+//   kEpiSwiglu  weight rows alternate 16-row blocks of B1 (gate) and B1u (up);
+//               C = g, C2 = u, C3 = h = silu(g) u, each [M][N / 2]
+//   kEpiSwigluBwd  acc = dh; C = dh u silu'(g), C2 = dh silu(g), with g = Rz,
+//               u = Rz2 ([M][N])
 // K1, K2 multiples of 32 (K2 may be 0), N a multiple of 256, any M >= 1: rows
 // of A beyond M are read from row M - 1 and their results not stored.
-template <bool RESID>
-__global__ void __launch_bounds__(512, 1) k_gemm_nt(
-    const bf16_t* __restrict__ A1, const bf16_t* __restrict__ B1, int K1,
-    const bf16_t* __restrict__ A2, const bf16_t* __restrict__ B2, int K2, int M, int N,
-    const bf16_t* __restrict__ Rz, bf16_t* __restrict__ C) {
+template <int EPI>
+__global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
+  const bf16_t* __restrict__ A1 = a.A1;
+  const bf16_t* __restrict__ A2 = a.A2;
+  const int K1 = a.K1, K2 = a.K2, M = a.M, N = a.N;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -123,22 +155,27 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(
     int grow;
     if (side == 0) {
       grow = m0 + r < M ? m0 + r : M - 1;
+    } else if (EPI == kEpiSwiglu) {
+      grow = n0 / 2 + (r >> 5) * 16 + (r & 15);  // block r / 16: gate if even, up if odd
     } else {
       grow = n0 + r;
     }
     goff1[i] = static_cast<int64_t>(grow) * K1 + gchunk * 8;
     goff2[i] = static_cast<int64_t>(grow) * K2 + gchunk * 8;
   }
-  const bf16_t* src1 = side == 0 ? A1 : B1;
-  const bf16_t* src2 = side == 0 ? A2 : B2;
+  // Instruction i covers rows 16 i + rbase / 16 ..; rbase / 16 is even, so the
+  // 16-row block of instruction i is a gate block for even i, an up block for odd.
+  const bf16_t* src1[2] = {side == 0 ? A1 : a.B1,
+                           side == 0 ? A1 : (EPI == kEpiSwiglu ? a.B1u : a.B1)};
+  const bf16_t* src2 = side == 0 ? A2 : a.B2;
 
   auto issue = [&](int s, unsigned char* stage_lds) {
     const uint32_t base = nt_lds_addr(stage_lds) + dst_off;
     if (s < ns1) {
-      const bf16_t* p = src1 + s * kNtK;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        nt_dma(reinterpret_cast<const unsigned char*>(p + goff1[i]), base + i * 1024);
+        nt_dma(reinterpret_cast<const unsigned char*>(src1[i & 1] + s * kNtK + goff1[i]),
+               base + i * 1024);
     } else {
       const bf16_t* p = src2 + (s - ns1) * kNtK;
 #pragma unroll
@@ -215,28 +252,60 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(
     if (s + 3 < nstage) stage(s + 3, L3, L2);
   }
 
-  // Epilogue: lane (li, g) holds C[m][n .. n + 3] of block (mb, nb), m = row li
-  // of the block, n = 4 g.
+  // Epilogue: lane (li, g) holds acc[m][n .. n + 3] of block (mb, nb), m = row
+  // li of the block, n = 4 g.
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
     const int m = m0 + wm * 128 + mb * 16 + li;
     if (m >= M) continue;
+    if constexpr (EPI == kEpiSwiglu) {
+      // blocks nb = 0, 1 (and 2, 3) are gate and up of the same 16 hidden columns
+      const int F = N / 2;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int n = n0 + wn * 64 + nb * 16 + 4 * g;
-      const int64_t off = static_cast<int64_t>(m) * N + n;
-      f32x4 v = acc[mb][nb];
-      if constexpr (RESID) {
-        const uint2 r = *reinterpret_cast<const uint2*>(Rz + off);
-        v[0] += __uint_as_float(r.x << 16);
-        v[1] += __uint_as_float(r.x & 0xFFFF0000u);
-        v[2] += __uint_as_float(r.y << 16);
-        v[3] += __uint_as_float(r.y & 0xFFFF0000u);
+      for (int pr = 0; pr < 2; ++pr) {
+        const int col = n0 / 2 + wn * 32 + pr * 16 + 4 * g;
+        const int64_t off = static_cast<int64_t>(m) * F + col;
+        const f32x4 gv = acc[mb][2 * pr], uv = acc[mb][2 * pr + 1];
+        float h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[e] = gv[e] * nt_sigmoid(gv[e]) * uv[e];
+        *reinterpret_cast<uint2*>(a.C + off) = uint2{pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3])};
+        *reinterpret_cast<uint2*>(a.C2 + off) = uint2{pack_bf16x2(uv[0], uv[1]), pack_bf16x2(uv[2], uv[3])};
+        *reinterpret_cast<uint2*>(a.C3 + off) = uint2{pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3])};
       }
-      uint2 o;
-      o.x = pack_bf16x2(v[0], v[1]);
-      o.y = pack_bf16x2(v[2], v[3]);
-      *reinterpret_cast<uint2*>(C + off) = o;
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const int n = n0 + wn * 64 + nb * 16 + 4 * g;
+        const int64_t off = static_cast<int64_t>(m) * N + n;
+        f32x4 v = acc[mb][nb];
+        if constexpr (EPI == kEpiSwigluBwd) {
+          const uint2 gr = *reinterpret_cast<const uint2*>(a.Rz + off);
+          const uint2 ur = *reinterpret_cast<const uint2*>(a.Rz2 + off);
+          const float gf[4] = {__uint_as_float(gr.x << 16), __uint_as_float(gr.x & 0xFFFF0000u),
+                               __uint_as_float(gr.y << 16), __uint_as_float(gr.y & 0xFFFF0000u)};
+          const float uf[4] = {__uint_as_float(ur.x << 16), __uint_as_float(ur.x & 0xFFFF0000u),
+                               __uint_as_float(ur.y << 16), __uint_as_float(ur.y & 0xFFFF0000u)};
+          float dg[4], du[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float sg = nt_sigmoid(gf[e]);
+            dg[e] = v[e] * uf[e] * sg * (1.0f + gf[e] * (1.0f - sg));
+            du[e] = v[e] * gf[e] * sg;
+          }
+          *reinterpret_cast<uint2*>(a.C + off) = uint2{pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3])};
+          *reinterpret_cast<uint2*>(a.C2 + off) = uint2{pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3])};
+        } else {
+          if constexpr (EPI == kEpiResid) {
+            const uint2 r = *reinterpret_cast<const uint2*>(a.Rz + off);
+            v[0] += __uint_as_float(r.x << 16);
+            v[1] += __uint_as_float(r.x & 0xFFFF0000u);
+            v[2] += __uint_as_float(r.y << 16);
+            v[3] += __uint_as_float(r.y & 0xFFFF0000u);
+          }
+          *reinterpret_cast<uint2*>(a.C + off) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+      }
     }
   }
 }
@@ -335,45 +404,6 @@ __global__ void __launch_bounds__(256) k_rmsnorm_bwd(const bf16_t* __restrict__ 
   }
 }
 
-__device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
-
-// h = silu(g) u over n8 groups of 8 elements.
-__global__ void __launch_bounds__(256) k_swiglu_fwd(const bf16_t* __restrict__ g,
-                                                    const bf16_t* __restrict__ u, int64_t n8,
-                                                    bf16_t* __restrict__ h) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float gf[8], uf[8], hf[8];
-    unpack8(reinterpret_cast<const u32x4*>(g)[i], gf);
-    unpack8(reinterpret_cast<const u32x4*>(u)[i], uf);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) hf[e] = gf[e] * sigmoidf(gf[e]) * uf[e];
-    reinterpret_cast<u32x4*>(h)[i] = pack8(hf);
-  }
-}
-
-// In place: dgh holds dL/dh on entry and dL/dg on exit; du receives dL/du.
-__global__ void __launch_bounds__(256) k_swiglu_bwd(bf16_t* __restrict__ dgh,
-                                                    const bf16_t* __restrict__ g,
-                                                    const bf16_t* __restrict__ u, int64_t n8,
-                                                    bf16_t* __restrict__ du) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n8;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float hf[8], gf[8], uf[8], dg[8], dv[8];
-    unpack8(reinterpret_cast<const u32x4*>(dgh)[i], hf);
-    unpack8(reinterpret_cast<const u32x4*>(g)[i], gf);
-    unpack8(reinterpret_cast<const u32x4*>(u)[i], uf);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float s = sigmoidf(gf[e]);
-      dg[e] = hf[e] * uf[e] * s * (1.0f + gf[e] * (1.0f - s));
-      dv[e] = hf[e] * gf[e] * s;
-    }
-    reinterpret_cast<u32x4*>(dgh)[i] = pack8(dg);
-    reinterpret_cast<u32x4*>(du)[i] = pack8(dv);
-  }
-}
-
 // theta fp32 [p][d] -> W bf16 [p][d] and Wt bf16 [d][p], 64 x 64 tiles through
 // LDS (p, d multiples of 64).
 __global__ void __launch_bounds__(256) k_cast_transpose(const float* __restrict__ theta, int p,
@@ -418,19 +448,46 @@ bool gemm_nt_ok(int64_t M, int N, int K1, int K2) {
          K1 % kNtK == 0 && K2 >= 0 && K2 % kNtK == 0;
 }
 
+static hipError_t launch_nt(const NtArgs& a, int epi, hipStream_t s) {
+  const int64_t tiles = ((static_cast<int64_t>(a.M) + kNtM - 1) / kNtM) * (a.N / kNtN);
+  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(tiles)), block(64 * kNtWaves);
+  switch (epi) {
+    case kEpiStore: hipLaunchKernelGGL(k_gemm_nt<kEpiStore>, grid, block, 0, s, a); break;
+    case kEpiResid: hipLaunchKernelGGL(k_gemm_nt<kEpiResid>, grid, block, 0, s, a); break;
+    case kEpiSwiglu: hipLaunchKernelGGL(k_gemm_nt<kEpiSwiglu>, grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL(k_gemm_nt<kEpiSwigluBwd>, grid, block, 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_nt(const bf16_t* A1, const bf16_t* B1, int K1, const bf16_t* A2,
                           const bf16_t* B2, int K2, int64_t M, int N, const bf16_t* Rz, bf16_t* C,
                           hipStream_t s) {
   if (!gemm_nt_ok(M, N, K1, K2)) return hipErrorInvalidValue;
-  const int64_t tiles = ((M + kNtM - 1) / kNtM) * (N / kNtN);
-  if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(tiles)), block(64 * kNtWaves);
-  const int m = static_cast<int>(M);
-  if (Rz)
-    hipLaunchKernelGGL(k_gemm_nt<true>, grid, block, 0, s, A1, B1, K1, A2, B2, K2, m, N, Rz, C);
-  else
-    hipLaunchKernelGGL(k_gemm_nt<false>, grid, block, 0, s, A1, B1, K1, A2, B2, K2, m, N, Rz, C);
-  return hipGetLastError();
+  NtArgs a{};
+  a.A1 = A1; a.B1 = B1; a.A2 = A2; a.B2 = B2; a.Rz = Rz; a.C = C;
+  a.K1 = K1; a.K2 = K2; a.M = static_cast<int>(M); a.N = N;
+  return launch_nt(a, Rz ? kEpiResid : kEpiStore, s);
+}
+
+hipError_t launch_gemm_nt_swiglu(const bf16_t* y, const bf16_t* Wg, const bf16_t* Wu, int d,
+                                 int64_t M, int f, bf16_t* g, bf16_t* u, bf16_t* h, hipStream_t s) {
+  if (f % (kNtN / 2) != 0 || !gemm_nt_ok(M, 2 * f, d, 0)) return hipErrorInvalidValue;
+  NtArgs a{};
+  a.A1 = y; a.B1 = Wg; a.B1u = Wu; a.C = g; a.C2 = u; a.C3 = h;
+  a.K1 = d; a.K2 = 0; a.M = static_cast<int>(M); a.N = 2 * f;
+  return launch_nt(a, kEpiSwiglu, s);
+}
+
+hipError_t launch_gemm_nt_swiglu_bwd(const bf16_t* dout, const bf16_t* WdT, int d, int64_t M, int f,
+                                     const bf16_t* g, const bf16_t* u, bf16_t* dg, bf16_t* du,
+                                     hipStream_t s) {
+  if (!gemm_nt_ok(M, f, d, 0)) return hipErrorInvalidValue;
+  NtArgs a{};
+  a.A1 = dout; a.B1 = WdT; a.Rz = g; a.Rz2 = u; a.C = dg; a.C2 = du;
+  a.K1 = d; a.K2 = 0; a.M = static_cast<int>(M); a.N = f;
+  return launch_nt(a, kEpiSwigluBwd, s);
 }
 
 hipError_t launch_rmsnorm_fwd(const bf16_t* x, const float* gamma, int64_t M, int d, float eps,
@@ -449,22 +506,6 @@ hipError_t launch_rmsnorm_bwd(const bf16_t* x, const float* rstd, const float* g
   if (d <= 0 || d % 8 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(static_cast<unsigned>((M + kRowWaves - 1) / kRowWaves)),
                      dim3(256), 0, s, x, rstd, gamma, dy, dout, static_cast<int>(M), d, dx);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu_fwd(const bf16_t* g, const bf16_t* u, int64_t n, bf16_t* h, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  if (n % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_swiglu_fwd, dim3(elementwise_blocks(n / 8)), dim3(256), 0, s, g, u, n / 8, h);
-  return hipGetLastError();
-}
-
-hipError_t launch_swiglu_bwd(bf16_t* dgh, const bf16_t* g, const bf16_t* u, int64_t n, bf16_t* du,
-                             hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  if (n % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_swiglu_bwd, dim3(elementwise_blocks(n / 8)), dim3(256), 0, s, dgh, g, u,
-                     n / 8, du);
   return hipGetLastError();
 }
 

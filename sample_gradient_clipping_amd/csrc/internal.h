@@ -178,9 +178,13 @@ hipError_t launch_rmsnorm_fwd(const bf16_t* x, const float* gamma, int64_t M, in
 hipError_t launch_rmsnorm_bwd(const bf16_t* x, const float* rstd, const float* gamma,
                               const bf16_t* dy, const bf16_t* dout, int64_t M, int d, bf16_t* dx,
                               hipStream_t s);
-hipError_t launch_swiglu_fwd(const bf16_t* g, const bf16_t* u, int64_t n, bf16_t* h, hipStream_t s);
-hipError_t launch_swiglu_bwd(bf16_t* dgh, const bf16_t* g, const bf16_t* u, int64_t n, bf16_t* du,
-                             hipStream_t s);
+// y [M][d] against Wg, Wu [f][d]: g, u and h = silu(g) u, each [M][f] (f % 128 == 0).
+hipError_t launch_gemm_nt_swiglu(const bf16_t* y, const bf16_t* Wg, const bf16_t* Wu, int d,
+                                 int64_t M, int f, bf16_t* g, bf16_t* u, bf16_t* h, hipStream_t s);
+// dh = dout WdT^T ([M][f], not stored), then dg = dh u silu'(g), du = dh silu(g).
+hipError_t launch_gemm_nt_swiglu_bwd(const bf16_t* dout, const bf16_t* WdT, int d, int64_t M, int f,
+                                     const bf16_t* g, const bf16_t* u, bf16_t* dg, bf16_t* du,
+                                     hipStream_t s);
 hipError_t launch_cast_transpose(const float* theta, int p, int d, bf16_t* W, bf16_t* Wt,
                                  hipStream_t s);
 
