@@ -24,7 +24,8 @@ Sources it follows (cited by page title and section throughout):
   per-sample gradients of RMSNorm gains and embedding tables (the parameters
   that are not linear layers) in ``other_layers.py``; the forward pass and
   backward pass 1 of a Llama-shaped MLP block ([RC] アルゴリズム的フロー, steps
-  1-2) and that block's whole step in ``mlp_block.py``.
+  1-2) and that block's whole step in ``mlp_block.py``; the attention half of
+  the decoder layer (grouped heads, RoPE, causal softmax) in ``attn_block.py``.
 * Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
   easy as 1, 2, 3", SC'11 (the published counter-based generator).
 
@@ -93,4 +94,14 @@ from .mlp_block import (  # noqa: F401
     mlp_per_sample_grads,
     mlp_dp_step,
     MLP_LAYERS,
+)
+from .attn_block import (  # noqa: F401
+    rope,
+    attention_forward,
+    attention_backward,
+    attn_forward,
+    attn_backward,
+    attn_per_sample_grads,
+    attn_dp_step,
+    ATTN_LAYERS,
 )
