@@ -342,6 +342,40 @@ dp_status_t dp_mlp_backward(int B, int T, int d, int f, const void *x, const flo
                             const void *WuT, const void *WdT, const void *dout, void *G_gate,
                             void *G_up, void *dy, void *dx, dp_stream_t stream);
 
+/* ---- Forward pass and backward pass 1 of a Llama attention block ----
+ *
+ * The attention half of a Llama decoder layer (the randomized-clipping
+ * summary, section アルゴリズム的フロー, steps 1-2), head width 64, H query
+ * heads sharing KV key/value heads (head h uses key/value head h / (H / KV)):
+ *   xhat, y = RMSNorm(x), gamma xhat
+ *   q = y Wq^T [M][64 H], k = y Wk^T, v = y Wv^T [M][64 KV]
+ *   q, k <- RoPE: in each head the pair (i, i + 32) is rotated by
+ *           t base^(-i / 32) at position t (t = row % T)
+ *   o_h = softmax(q_h k^T / 8 + causal mask) v,  out = x + o Wo^T
+ * Layouts as for the MLP block; Wq [64 H][d], Wk, Wv [64 KV][d], Wo [d][64 H]
+ * bf16; lse [B][H][T] fp32 is the natural log of each softmax row's
+ * normaliser (the backward pass reads it).  T a multiple of 64, d, 64 H and
+ * 64 KV multiples of 256.  No workspace.
+ */
+
+/* In place RoPE of x [M][64 n_heads] bf16 (16-byte aligned); inverse = 1 rotates
+ * by the opposite angle (the transpose, used on gradients). */
+dp_status_t dp_rope(int64_t M, int T, int n_heads, double base, int inverse, void *x,
+                    dp_stream_t stream);
+
+/* Causal grouped-query attention of B sequences of T tokens: q [B T][64 H],
+ * k, v [B T][64 KV] -> o [B T][64 H], lse [B][H][T]. */
+dp_status_t dp_attention_forward(int B, int T, int H, int KV, const void *q, const void *k,
+                                 const void *v, void *o, float *lse, dp_stream_t stream);
+
+/* The whole block forward: x [B T][d] -> xhat, y [B T][d], rstd [B T], q, k, v
+ * (after RoPE), o, lse and out = x + o Wo^T. */
+dp_status_t dp_attn_forward(int B, int T, int d, int H, int KV, float eps, double rope_base,
+                            const void *x, const float *gamma, const void *Wq, const void *Wk,
+                            const void *Wv, const void *Wo, void *xhat, void *y, float *rstd,
+                            void *q, void *k, void *v, void *o, float *lse, void *out,
+                            dp_stream_t stream);
+
 /* ---- test hooks: expose the random streams for bit-level parity checks ---- */
 
 /* out[4 n] = Philox4x32-10 words of the n counters ctr[4 n] (device arrays). */

@@ -116,6 +116,12 @@ def load_library():
     L.dp_mlp_forward.restype = c_int
     L.dp_mlp_backward.argtypes = [c_int] * 4 + [c_p] * 13 + [c_p]
     L.dp_mlp_backward.restype = c_int
+    L.dp_rope.argtypes = [c_i64, c_int, c_int, c_dbl, c_int, c_p, c_p]
+    L.dp_rope.restype = c_int
+    L.dp_attention_forward.argtypes = [c_int] * 4 + [c_p] * 6
+    L.dp_attention_forward.restype = c_int
+    L.dp_attn_forward.argtypes = [c_int] * 5 + [c_f, c_dbl] + [c_p] * 15 + [c_p]
+    L.dp_attn_forward.restype = c_int
     _lib = L
     return L
 
@@ -458,3 +464,49 @@ def dp_mlp_backward(x, rstd, gamma, g, u, WgT, WuT, WdT, dout, grads=None, strea
                            *(_ptr(grads[n]) for n in MLP_BACKWARD_OUTPUTS), _stream(stream))
     _check(st, "dp_mlp_backward")
     return grads
+
+
+def dp_rope(x, T, n_heads, base=500000.0, inverse=False, stream=None):
+    """In place RoPE of x [..][64 n_heads] bf16 (row index % T is the position)."""
+    L = load_library()
+    M = x.numel() // (64 * n_heads)
+    _check(L.dp_rope(M, int(T), int(n_heads), float(base), 1 if inverse else 0, _ptr(x),
+                     _stream(stream)), "dp_rope")
+    return x
+
+
+def dp_attention_forward(q, k, v, n_heads, n_kv, o=None, lse=None, stream=None):
+    """Causal grouped-query attention: q [B][T][64 H], k, v [B][T][64 KV] bf16 ->
+    (o [B][T][64 H] bf16, lse [B][H][T] fp32)."""
+    L = load_library()
+    B, T = q.shape[0], q.shape[1]
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty(B, n_heads, T, dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(L.dp_attention_forward(B, T, n_heads, n_kv, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(lse), _stream(stream)), "dp_attention_forward")
+    return o, lse
+
+
+ATTN_FORWARD_OUTPUTS = ("xhat", "y", "rstd", "q", "k", "v", "o", "lse", "out")
+
+
+def dp_attn_forward(x, gamma, Wq, Wk, Wv, Wo, n_heads, n_kv, eps=1e-5, rope_base=500000.0,
+                    acts=None, stream=None):
+    """Forward of the attention block: x [B][T][d] bf16; gamma [d] fp32; Wq [64 H][d],
+    Wk, Wv [64 KV][d], Wo [d][64 H] bf16.  Returns (and fills ``acts``) a dict with
+    xhat, y, rstd, q, k, v (after RoPE), o, lse [B][H][T] and out."""
+    L = load_library()
+    B, T, d = x.shape
+    acts = {} if acts is None else acts
+    shapes = {"xhat": (B, T, d), "y": (B, T, d), "rstd": (B, T), "q": (B, T, 64 * n_heads),
+              "k": (B, T, 64 * n_kv), "v": (B, T, 64 * n_kv), "o": (B, T, 64 * n_heads),
+              "lse": (B, n_heads, T), "out": (B, T, d)}
+    for name in ATTN_FORWARD_OUTPUTS:
+        if name not in acts:
+            dt = torch.float32 if name in ("rstd", "lse") else torch.bfloat16
+            acts[name] = torch.empty(shapes[name], dtype=dt, device=x.device)
+    st = L.dp_attn_forward(B, T, d, n_heads, n_kv, float(eps), float(rope_base), _ptr(x),
+                           _ptr(gamma), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(Wo),
+                           *(_ptr(acts[n]) for n in ATTN_FORWARD_OUTPUTS), _stream(stream))
+    _check(st, "dp_attn_forward")
+    return acts

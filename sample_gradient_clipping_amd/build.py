@@ -21,7 +21,8 @@ LIB = os.path.join(PKG, "libdprc.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "rng_kernels.hip", "generic_kernels.hip", "mfma_hutch.hip", "mfma_gemm.hip",
-           "mfma_ghost.hip", "other_layers.hip", "block_kernels.hip"]
+           "mfma_ghost.hip", "other_layers.hip", "block_kernels.hip",
+           "attn_kernels.hip"]
 
 # Packed-fp32 VALU forms are switched off for all device code.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

@@ -1019,4 +1019,87 @@ dp_status_t dp_mlp_backward(int B, int T, int d, int f, const void* x, const flo
 }
 
 
+// ---- attention block: forward pass ----
+
+static bool attn_dims_ok(int B, int T, int d, int H, int KV) {
+  if (B < 0 || T < 0 || d < 256 || d % 256 != 0 || H < 1 || KV < 1 || H % KV != 0) return false;
+  if ((H * 64) % 256 != 0 || (KV * 64) % 256 != 0) return false;
+  if (T > 0 && !attn_shape_ok(T, H, KV)) return false;
+  return static_cast<int64_t>(B) * T <= (int64_t{1} << 30);
+}
+
+dp_status_t dp_rope(int64_t M, int T, int n_heads, double base, int inverse, void* x,
+                    dp_stream_t stream) {
+  if (M < 0 || T < 1 || n_heads < 1 || !(base > 1.0) || !std::isfinite(base) ||
+      (inverse != 0 && inverse != 1))
+    return DP_ERR_INVALID_ARG;
+  if (M == 0) return DP_OK;
+  if (x == nullptr || !aligned(x, 16)) return DP_ERR_INVALID_ARG;
+  DP_TRY(launch_rope(static_cast<bf16_t*>(x), M, T, n_heads, base, inverse != 0,
+                     static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
+dp_status_t dp_attention_forward(int B, int T, int H, int KV, const void* q, const void* k,
+                                 const void* v, void* o, float* lse, dp_stream_t stream) {
+  if (B < 0 || T < 0 || H < 1 || KV < 1 || H % KV != 0) return DP_ERR_INVALID_ARG;
+  if (B == 0 || T == 0) return DP_OK;
+  if (!attn_shape_ok(T, H, KV)) return DP_ERR_INVALID_ARG;
+  if (!all_aligned16({q, k, v, o}) || lse == nullptr || !aligned(lse, 4)) return DP_ERR_INVALID_ARG;
+  const size_t M = static_cast<size_t>(B) * T;
+  const Region outs[] = {{o, M * H * 128}, {lse, M * H * 4}};
+  const Region ins[] = {{q, M * H * 128}, {k, M * KV * 128}, {v, M * KV * 128}};
+  if (regions_clash(outs, 2, ins, 3)) return DP_ERR_INVALID_ARG;
+  DP_TRY(launch_attn_fwd(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                         static_cast<const bf16_t*>(v), B, T, H, KV, static_cast<bf16_t*>(o), lse,
+                         static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
+dp_status_t dp_attn_forward(int B, int T, int d, int H, int KV, float eps, double rope_base,
+                            const void* x, const float* gamma, const void* Wq, const void* Wk,
+                            const void* Wv, const void* Wo, void* xhat, void* y, float* rstd,
+                            void* q, void* k, void* v, void* o, float* lse, void* out,
+                            dp_stream_t stream) {
+  if (!attn_dims_ok(B, T, d, H, KV) || !(eps >= 0.f) || !std::isfinite(eps) ||
+      !(rope_base > 1.0) || !std::isfinite(rope_base))
+    return DP_ERR_INVALID_ARG;
+  const int64_t M = static_cast<int64_t>(B) * T;
+  if (M == 0) return DP_OK;
+  if (!all_aligned16({x, gamma, Wq, Wk, Wv, Wo, xhat, y, q, k, v, o, out}) || rstd == nullptr ||
+      !aligned(rstd, 4) || lse == nullptr || !aligned(lse, 4))
+    return DP_ERR_INVALID_ARG;
+  const int nq = H * 64, nk = KV * 64;
+  const size_t md = static_cast<size_t>(M) * d * 2;
+  const Region outs[] = {{xhat, md}, {y, md}, {rstd, static_cast<size_t>(M) * 4},
+                         {q, static_cast<size_t>(M) * nq * 2}, {k, static_cast<size_t>(M) * nk * 2},
+                         {v, static_cast<size_t>(M) * nk * 2}, {o, static_cast<size_t>(M) * nq * 2},
+                         {lse, static_cast<size_t>(M) * H * 4}, {out, md}};
+  const Region ins[] = {{x, md}, {gamma, static_cast<size_t>(d) * 4},
+                        {Wq, static_cast<size_t>(nq) * d * 2}, {Wk, static_cast<size_t>(nk) * d * 2},
+                        {Wv, static_cast<size_t>(nk) * d * 2}, {Wo, static_cast<size_t>(d) * nq * 2}};
+  if (regions_clash(outs, 9, ins, 6, out, x)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  bf16_t* yb = static_cast<bf16_t*>(y);
+  bf16_t* qb = static_cast<bf16_t*>(q);
+  bf16_t* kb = static_cast<bf16_t*>(k);
+  bf16_t* vb = static_cast<bf16_t*>(v);
+  bf16_t* ob = static_cast<bf16_t*>(o);
+  DP_TRY(launch_rmsnorm_fwd(xb, gamma, M, d, eps, static_cast<bf16_t*>(xhat), yb, rstd, s));
+  DP_TRY(launch_gemm_nt(yb, static_cast<const bf16_t*>(Wq), d, nullptr, nullptr, 0, M, nq, nullptr,
+                        qb, s));
+  DP_TRY(launch_gemm_nt(yb, static_cast<const bf16_t*>(Wk), d, nullptr, nullptr, 0, M, nk, nullptr,
+                        kb, s));
+  DP_TRY(launch_gemm_nt(yb, static_cast<const bf16_t*>(Wv), d, nullptr, nullptr, 0, M, nk, nullptr,
+                        vb, s));
+  DP_TRY(launch_rope(qb, M, T, H, rope_base, false, s));
+  DP_TRY(launch_rope(kb, M, T, KV, rope_base, false, s));
+  DP_TRY(launch_attn_fwd(qb, kb, vb, B, T, H, KV, ob, lse, s));
+  DP_TRY(launch_gemm_nt(ob, static_cast<const bf16_t*>(Wo), nq, nullptr, nullptr, 0, M, d, xb,
+                        static_cast<bf16_t*>(out), s));
+  return DP_OK;
+}
+
+
 }  // extern "C"

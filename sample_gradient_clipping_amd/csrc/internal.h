@@ -188,4 +188,14 @@ hipError_t launch_gemm_nt_swiglu_bwd(const bf16_t* dout, const bf16_t* WdT, int 
 hipError_t launch_cast_transpose(const float* theta, int p, int d, bf16_t* W, bf16_t* Wt,
                                  hipStream_t s);
 
+// ---- attention block (attn_kernels.hip): head width 64, T % 64 == 0 ----
+bool attn_shape_ok(int T, int H, int KV);
+// In place RoPE on x [M][nh * 64] (row % T is the position); inverse rotates back.
+hipError_t launch_rope(bf16_t* x, int64_t M, int T, int nh, double base, bool inverse,
+                       hipStream_t s);
+// Causal grouped-query attention: q [B T][H 64], k, v [B T][KV 64] -> o [B T][H 64]
+// and lse [B][H][T] (natural log of each softmax row's normaliser).
+hipError_t launch_attn_fwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int B, int T, int H,
+                           int KV, bf16_t* o, float* lse, hipStream_t s);
+
 }  // namespace dprc
