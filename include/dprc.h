@@ -376,6 +376,29 @@ dp_status_t dp_attn_forward(int B, int T, int d, int H, int KV, float eps, doubl
                             void *q, void *k, void *v, void *o, float *lse, void *out,
                             dp_stream_t stream);
 
+/* Backward of the attention: from q, k, v, o, lse of the forward and dO [B T][64 H],
+ * dq [B T][64 H], dk, dv [B T][64 KV] (dk, dv summed over each group's query
+ * heads).  ws: device workspace, ws_bytes >= dp_attention_backward_workspace. */
+size_t dp_attention_backward_workspace(int B, int T, int H);
+dp_status_t dp_attention_backward(int B, int T, int H, int KV, const void *q, const void *k,
+                                  const void *v, const void *o, const float *lse, const void *dO,
+                                  void *dq, void *dk, void *dv, void *ws, size_t ws_bytes,
+                                  dp_stream_t stream);
+
+/* The whole block's backward pass 1: from the forward's x, rstd, q, k, v, o, lse,
+ * the transposed bf16 weights WqT [d][64 H], WkT, WvT [d][64 KV], WoT [64 H][d]
+ * and dout = R [B T][d], writes G_q [B T][64 H], G_k, G_v [B T][64 KV] (the output
+ * gradients of the q, k, v projections, through RoPE's transpose), dy and dx
+ * [B T][d].  The o projection's output gradient is R itself.
+ * ws_bytes >= dp_attn_backward_workspace(B, T, H). */
+size_t dp_attn_backward_workspace(int B, int T, int H);
+dp_status_t dp_attn_backward(int B, int T, int d, int H, int KV, double rope_base, const void *x,
+                             const float *rstd, const float *gamma, const void *q, const void *k,
+                             const void *v, const void *o, const float *lse, const void *WqT,
+                             const void *WkT, const void *WvT, const void *WoT, const void *dout,
+                             void *G_q, void *G_k, void *G_v, void *dy, void *dx, void *ws,
+                             size_t ws_bytes, dp_stream_t stream);
+
 /* ---- test hooks: expose the random streams for bit-level parity checks ---- */
 
 /* out[4 n] = Philox4x32-10 words of the n counters ctr[4 n] (device arrays). */

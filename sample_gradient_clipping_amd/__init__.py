@@ -15,7 +15,8 @@ _BINDING_NAMES = (
     "dp_poisson_sample_workspace", "dp_rmsnorm_norm", "dp_rmsnorm_clip_aggregate_update",
     "dp_embedding_norm", "dp_embedding_clip_aggregate_update",
     "dp_weights_bf16", "dp_linear_forward", "dp_mlp_forward", "dp_mlp_backward",
-    "dp_rope", "dp_attention_forward", "dp_attn_forward",
+    "dp_rope", "dp_attention_forward", "dp_attn_forward", "dp_attention_backward",
+    "dp_attn_backward",
     "DprcError", "lib_path",
     "load_library", "METHODS", "DP_ACCUMULATE", "DP_PROBE_SHARED", "DP_PROBE_RADEMACHER",
 )

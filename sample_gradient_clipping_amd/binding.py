@@ -122,6 +122,14 @@ def load_library():
     L.dp_attention_forward.restype = c_int
     L.dp_attn_forward.argtypes = [c_int] * 5 + [c_f, c_dbl] + [c_p] * 15 + [c_p]
     L.dp_attn_forward.restype = c_int
+    L.dp_attention_backward_workspace.argtypes = [c_int] * 3
+    L.dp_attention_backward_workspace.restype = c_sz
+    L.dp_attention_backward.argtypes = [c_int] * 4 + [c_p] * 10 + [c_sz, c_p]
+    L.dp_attention_backward.restype = c_int
+    L.dp_attn_backward_workspace.argtypes = [c_int] * 3
+    L.dp_attn_backward_workspace.restype = c_sz
+    L.dp_attn_backward.argtypes = [c_int] * 5 + [c_dbl] + [c_p] * 19 + [c_sz, c_p]
+    L.dp_attn_backward.restype = c_int
     _lib = L
     return L
 
@@ -510,3 +518,40 @@ def dp_attn_forward(x, gamma, Wq, Wk, Wv, Wo, n_heads, n_kv, eps=1e-5, rope_base
                            *(_ptr(acts[n]) for n in ATTN_FORWARD_OUTPUTS), _stream(stream))
     _check(st, "dp_attn_forward")
     return acts
+
+
+def dp_attention_backward(q, k, v, o, lse, dO, n_heads, n_kv, ws=None, stream=None):
+    """(dq, dk, dv) of causal grouped-query attention from dO [B][T][64 H]."""
+    L = load_library()
+    B, T = q.shape[0], q.shape[1]
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws_t = _workspace(L.dp_attention_backward_workspace(B, T, n_heads), q.device, ws)
+    _check(L.dp_attention_backward(B, T, n_heads, n_kv, _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                   _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws_t),
+                                   0 if ws_t is None else ws_t.numel(), _stream(stream)),
+           "dp_attention_backward")
+    return dq, dk, dv
+
+
+ATTN_BACKWARD_OUTPUTS = ("G_q", "G_k", "G_v", "dy", "dx")
+
+
+def dp_attn_backward(x, acts, gamma, WqT, WkT, WvT, WoT, dout, n_heads, n_kv,
+                     rope_base=500000.0, grads=None, ws=None, stream=None):
+    """Backward pass 1 of the attention block from the forward's ``acts`` (rstd, q, k,
+    v, o, lse) and dout = dL/d(out): dict with G_q, G_k, G_v, dy and dx (bf16)."""
+    L = load_library()
+    B, T, d = x.shape
+    grads = {} if grads is None else grads
+    widths = {"G_q": 64 * n_heads, "G_k": 64 * n_kv, "G_v": 64 * n_kv, "dy": d, "dx": d}
+    for name in ATTN_BACKWARD_OUTPUTS:
+        if name not in grads:
+            grads[name] = torch.empty(B, T, widths[name], dtype=torch.bfloat16, device=x.device)
+    ws_t = _workspace(L.dp_attn_backward_workspace(B, T, n_heads), x.device, ws)
+    st = L.dp_attn_backward(B, T, d, n_heads, n_kv, float(rope_base), _ptr(x), _ptr(acts["rstd"]),
+                            _ptr(gamma), _ptr(acts["q"]), _ptr(acts["k"]), _ptr(acts["v"]),
+                            _ptr(acts["o"]), _ptr(acts["lse"]), _ptr(WqT), _ptr(WkT), _ptr(WvT),
+                            _ptr(WoT), _ptr(dout), *(_ptr(grads[n]) for n in ATTN_BACKWARD_OUTPUTS),
+                            _ptr(ws_t), 0 if ws_t is None else ws_t.numel(), _stream(stream))
+    _check(st, "dp_attn_backward")
+    return grads

@@ -1102,4 +1102,94 @@ dp_status_t dp_attn_forward(int B, int T, int d, int H, int KV, float eps, doubl
 }
 
 
+// ---- attention block: backward pass 1 ----
+
+size_t dp_attention_backward_workspace(int B, int T, int H) {
+  if (B < 0 || T < 0 || H < 1) return kInvalid;
+  return align_up(attn_bwd_scratch_bytes(B > 0 ? B : 1, T > 0 ? T : 1, H));
+}
+
+dp_status_t dp_attention_backward(int B, int T, int H, int KV, const void* q, const void* k,
+                                  const void* v, const void* o, const float* lse, const void* dO,
+                                  void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                                  dp_stream_t stream) {
+  const size_t need = dp_attention_backward_workspace(B, T, H);
+  if (need == kInvalid || KV < 1 || H % KV != 0) return DP_ERR_INVALID_ARG;
+  if (B == 0 || T == 0) return DP_OK;
+  if (!attn_shape_ok(T, H, KV)) return DP_ERR_INVALID_ARG;
+  if (!all_aligned16({q, k, v, o, dO, dq, dk, dv}) || lse == nullptr || !aligned(lse, 4))
+    return DP_ERR_INVALID_ARG;
+  if (ws_bytes < need) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  const size_t M = static_cast<size_t>(B) * T;
+  const Region outs[] = {{dq, M * H * 128}, {dk, M * KV * 128}, {dv, M * KV * 128}, {ws, need}};
+  const Region ins[] = {{q, M * H * 128}, {k, M * KV * 128}, {v, M * KV * 128},
+                        {o, M * H * 128}, {lse, M * H * 4},  {dO, M * H * 128}};
+  if (regions_clash(outs, 4, ins, 6)) return DP_ERR_INVALID_ARG;
+  DP_TRY(launch_attn_bwd(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                         static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(o), lse,
+                         static_cast<const bf16_t*>(dO), B, T, H, KV, static_cast<float*>(ws),
+                         static_cast<bf16_t*>(dq), static_cast<bf16_t*>(dk),
+                         static_cast<bf16_t*>(dv), static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
+size_t dp_attn_backward_workspace(int B, int T, int H) {
+  if (B < 0 || T < 0 || H < 1) return kInvalid;
+  const size_t M = static_cast<size_t>(B > 0 ? B : 1) * (T > 0 ? T : 1);
+  return align_up(M * H * 64 * 2) + dp_attention_backward_workspace(B, T, H);
+}
+
+dp_status_t dp_attn_backward(int B, int T, int d, int H, int KV, double rope_base, const void* x,
+                             const float* rstd, const float* gamma, const void* q, const void* k,
+                             const void* v, const void* o, const float* lse, const void* WqT,
+                             const void* WkT, const void* WvT, const void* WoT, const void* dout,
+                             void* G_q, void* G_k, void* G_v, void* dy, void* dx, void* ws,
+                             size_t ws_bytes, dp_stream_t stream) {
+  if (!attn_dims_ok(B, T, d, H, KV) || !(rope_base > 1.0) || !std::isfinite(rope_base))
+    return DP_ERR_INVALID_ARG;
+  const int64_t M = static_cast<int64_t>(B) * T;
+  if (M == 0) return DP_OK;
+  const size_t need = dp_attn_backward_workspace(B, T, H);
+  if (!all_aligned16({x, gamma, q, k, v, o, WqT, WkT, WvT, WoT, dout, G_q, G_k, G_v, dy, dx}) ||
+      rstd == nullptr || !aligned(rstd, 4) || lse == nullptr || !aligned(lse, 4))
+    return DP_ERR_INVALID_ARG;
+  if (ws_bytes < need) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  const int nq = H * 64, nk = KV * 64;
+  const size_t md = static_cast<size_t>(M) * d * 2, mq = static_cast<size_t>(M) * nq * 2,
+               mk = static_cast<size_t>(M) * nk * 2;
+  const Region outs[] = {{G_q, mq}, {G_k, mk}, {G_v, mk}, {dy, md}, {dx, md}, {ws, need}};
+  const Region ins[] = {{x, md},    {rstd, static_cast<size_t>(M) * 4}, {gamma, static_cast<size_t>(d) * 4},
+                        {q, mq},    {k, mk},  {v, mk},  {o, mq},  {lse, static_cast<size_t>(M) * H * 4},
+                        {WqT, static_cast<size_t>(nq) * d * 2}, {WkT, static_cast<size_t>(nk) * d * 2},
+                        {WvT, static_cast<size_t>(nk) * d * 2}, {WoT, static_cast<size_t>(nq) * d * 2},
+                        {dout, md}};
+  if (regions_clash(outs, 6, ins, 13)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bf16_t* dO = static_cast<bf16_t*>(ws);
+  float* Dvec = at<float>(ws, align_up(mq));
+  bf16_t* gq = static_cast<bf16_t*>(G_q);
+  bf16_t* gk = static_cast<bf16_t*>(G_k);
+  bf16_t* gv = static_cast<bf16_t*>(G_v);
+  const bf16_t* db = static_cast<const bf16_t*>(dout);
+  // dO = R Wo (the output gradient of the attention heads)
+  DP_TRY(launch_gemm_nt(db, static_cast<const bf16_t*>(WoT), d, nullptr, nullptr, 0, M, nq, nullptr,
+                        dO, s));
+  DP_TRY(launch_attn_bwd(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                         static_cast<const bf16_t*>(v), static_cast<const bf16_t*>(o), lse, dO, B,
+                         T, H, KV, Dvec, gq, gk, gv, s));
+  // back through RoPE: the transpose of the rotation
+  DP_TRY(launch_rope(gq, M, T, H, rope_base, true, s));
+  DP_TRY(launch_rope(gk, M, T, KV, rope_base, true, s));
+  // dy = G_q Wq + G_k Wk + G_v Wv: one product over three k ranges
+  DP_TRY(launch_gemm_nt3(gq, static_cast<const bf16_t*>(WqT), nq, gk,
+                         static_cast<const bf16_t*>(WkT), nk, gv, static_cast<const bf16_t*>(WvT),
+                         nk, M, d, nullptr, static_cast<bf16_t*>(dy), s));
+  DP_TRY(launch_rmsnorm_bwd(static_cast<const bf16_t*>(x), rstd, gamma,
+                            static_cast<const bf16_t*>(dy), db, M, d, static_cast<bf16_t*>(dx), s));
+  return DP_OK;
+}
+
+
 }  // extern "C"

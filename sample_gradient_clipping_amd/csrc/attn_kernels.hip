@@ -177,6 +177,190 @@ __global__ void __launch_bounds__(256) k_attn_fwd(const bf16_t* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
+// Backward.  Dvec[b][h][t] = sum over the head's 64 columns of dO * O.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_attn_bwd_dot(const bf16_t* __restrict__ dO,
+                                                      const bf16_t* __restrict__ O, int64_t M,
+                                                      int T, int H, float* __restrict__ Dvec) {
+  const int64_t n = M * H;
+  for (int64_t id = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; id < n;
+       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t row = id / H;
+    const int h = static_cast<int>(id - row * H);
+    const bf16_t* a = dO + row * H * kDh + h * kDh;
+    const bf16_t* c = O + row * H * kDh + h * kDh;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(a + 8 * j);
+      const u32x4 y = *reinterpret_cast<const u32x4*>(c + 8 * j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc += __uint_as_float(x[e] << 16) * __uint_as_float(y[e] << 16);
+        acc += __uint_as_float(x[e] & 0xFFFF0000u) * __uint_as_float(y[e] & 0xFFFF0000u);
+      }
+    }
+    const int64_t b = row / T, t = row - b * T;
+    Dvec[(b * H + h) * T + t] = acc;
+  }
+}
+
+// dK, dV of 64 keys of one key/value head: wave w owns keys 16 w .. + 15 (the
+// key in the lane, S = Q K^T), and the workgroup walks the group's query heads
+// and, causally, the query blocks from its own on.  The head sums stay in
+// registers: no atomics, a fixed order.
+__global__ void __launch_bounds__(256) k_attn_bwd_kv(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dvec,
+    int T, int H, int KV, float scale_log2, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv) {
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[kBlk * kBlk];
+  __shared__ __attribute__((aligned(16))) bf16_t Qt[kBlk * kBlk];
+  __shared__ __attribute__((aligned(16))) bf16_t Ds[kBlk * kBlk];
+  __shared__ __attribute__((aligned(16))) bf16_t Dt[kBlk * kBlk];
+  __shared__ float Ls[kBlk], Dd[kBlk];
+  const int kbk = blockIdx.x, gkv = blockIdx.y, b = blockIdx.z;
+  const int grp = H / KV;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t ldq = static_cast<int64_t>(H) * kDh, ldk = static_cast<int64_t>(KV) * kDh;
+  const int tk = kbk * kBlk + w * 16 + li;  // this lane's key
+  const bf16_t* krow = k + (static_cast<int64_t>(b) * T + tk) * ldk + gkv * kDh;
+  const bf16_t* vrow = v + (static_cast<int64_t>(b) * T + tk) * ldk + gkv * kDh;
+  const u32x4 kf0 = *reinterpret_cast<const u32x4*>(krow + 8 * lg);
+  const u32x4 kf1 = *reinterpret_cast<const u32x4*>(krow + 32 + 8 * lg);
+  const u32x4 vf0 = *reinterpret_cast<const u32x4*>(vrow + 8 * lg);
+  const u32x4 vf1 = *reinterpret_cast<const u32x4*>(vrow + 32 + 8 * lg);
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  f32x4 adk[4], adv[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    adk[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    adv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int kk = w * 16 + li;  // key within the block
+  for (int j = 0; j < grp; ++j) {
+    const int h = gkv * grp + j;
+    for (int qb = kbk; qb < T / kBlk; ++qb) {
+      __syncthreads();
+      const int64_t qrow0 = static_cast<int64_t>(b) * T + qb * kBlk;
+      stage<true, true>(q + qrow0 * ldq + h * kDh, ldq, Qs, Qt);
+      stage<true, true>(dO + qrow0 * ldq + h * kDh, ldq, Ds, Dt);
+      if (threadIdx.x < kBlk) {
+        const int64_t si = (static_cast<int64_t>(b) * H + h) * T + qb * kBlk + threadIdx.x;
+        Ls[threadIdx.x] = lse[si] * kLog2e;
+        Dd[threadIdx.x] = Dvec[si];
+      }
+      __syncthreads();
+      f32x4 P[4], dS[4];
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb) {  // 16-query blocks
+        const int r0 = sb * 16 + li;
+        f32x4 sc = mma(rd16(Qs, r0, lg), kf0, f32x4{0.f, 0.f, 0.f, 0.f});
+        sc = mma(rd16(Qs, r0, 4 + lg), kf1, sc);
+        f32x4 dp = mma(rd16(Ds, r0, lg), vf0, f32x4{0.f, 0.f, 0.f, 0.f});
+        dp = mma(rd16(Ds, r0, 4 + lg), vf1, dp);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qq = sb * 16 + 4 * lg + r;  // query within the block
+          float p = exp2f(sc[r] * scale_log2 - Ls[qq]);
+          if (qb == kbk && kk > qq) p = 0.f;
+          P[sb][r] = p;
+          dS[sb][r] = p * (dp[r] - Dd[qq]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 pb{pk(P[2 * t][0], P[2 * t][1]), pk(P[2 * t][2], P[2 * t][3]),
+                       pk(P[2 * t + 1][0], P[2 * t + 1][1]), pk(P[2 * t + 1][2], P[2 * t + 1][3])};
+        const u32x4 sbv{pk(dS[2 * t][0], dS[2 * t][1]), pk(dS[2 * t][2], dS[2 * t][3]),
+                        pk(dS[2 * t + 1][0], dS[2 * t + 1][1]),
+                        pk(dS[2 * t + 1][2], dS[2 * t + 1][3])};
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          adv[db] = mma(rd_tr8(Dt, 16 * db + li, t, lg), pb, adv[db]);
+          adk[db] = mma(rd_tr8(Qt, 16 * db + li, t, lg), sbv, adk[db]);
+        }
+      }
+    }
+  }
+  bf16_t* dkrow = dk + (static_cast<int64_t>(b) * T + tk) * ldk + gkv * kDh;
+  bf16_t* dvrow = dv + (static_cast<int64_t>(b) * T + tk) * ldk + gkv * kDh;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const f32x4 a = adk[db] * 0.125f;  // 1 / sqrt(64)
+    *reinterpret_cast<uint2*>(dkrow + 16 * db + 4 * lg) = uint2{pk(a[0], a[1]), pk(a[2], a[3])};
+    const f32x4 c = adv[db];
+    *reinterpret_cast<uint2*>(dvrow + 16 * db + 4 * lg) = uint2{pk(c[0], c[1]), pk(c[2], c[3])};
+  }
+}
+
+// dQ of 64 queries of one head: wave w owns queries 16 w .. + 15 (the query in
+// the lane, S^T = K Q^T as in the forward); key tiles 0 .. the diagonal.
+__global__ void __launch_bounds__(256) k_attn_bwd_q(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+    const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dvec,
+    int T, int H, int KV, float scale_log2, bf16_t* __restrict__ dq) {
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[kBlk * kBlk];
+  __shared__ __attribute__((aligned(16))) bf16_t Kt[kBlk * kBlk];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[kBlk * kBlk];
+  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int gkv = h / (H / KV);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t ldq = static_cast<int64_t>(H) * kDh, ldk = static_cast<int64_t>(KV) * kDh;
+  const int tq = qb * kBlk + w * 16 + li;
+  const bf16_t* qrow = q + (static_cast<int64_t>(b) * T + tq) * ldq + h * kDh;
+  const bf16_t* drow = dO + (static_cast<int64_t>(b) * T + tq) * ldq + h * kDh;
+  const u32x4 qf0 = *reinterpret_cast<const u32x4*>(qrow + 8 * lg);
+  const u32x4 qf1 = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * lg);
+  const u32x4 df0 = *reinterpret_cast<const u32x4*>(drow + 8 * lg);
+  const u32x4 df1 = *reinterpret_cast<const u32x4*>(drow + 32 + 8 * lg);
+  const int64_t si = (static_cast<int64_t>(b) * H + h) * T + tq;
+  const float lq = lse[si] * 1.4426950408889634f, dd = Dvec[si];
+
+  f32x4 adq[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) adq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int qq = w * 16 + li;
+  for (int kt = 0; kt <= qb; ++kt) {
+    __syncthreads();
+    const int64_t krow0 = static_cast<int64_t>(b) * T + kt * kBlk;
+    stage<true, true>(k + krow0 * ldk + gkv * kDh, ldk, Ks, Kt);
+    stage<true, false>(v + krow0 * ldk + gkv * kDh, ldk, Vs, nullptr);
+    __syncthreads();
+    f32x4 dS[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int r0 = kb * 16 + li;
+      f32x4 st = mma(rd16(Ks, r0, lg), qf0, f32x4{0.f, 0.f, 0.f, 0.f});
+      st = mma(rd16(Ks, r0, 4 + lg), qf1, st);
+      f32x4 dp = mma(rd16(Vs, r0, lg), df0, f32x4{0.f, 0.f, 0.f, 0.f});
+      dp = mma(rd16(Vs, r0, 4 + lg), df1, dp);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = exp2f(st[r] * scale_log2 - lq);
+        if (kt == qb && kb * 16 + 4 * lg + r > qq) p = 0.f;
+        dS[kb][r] = p * (dp[r] - dd);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 sbv{pk(dS[2 * t][0], dS[2 * t][1]), pk(dS[2 * t][2], dS[2 * t][3]),
+                      pk(dS[2 * t + 1][0], dS[2 * t + 1][1]), pk(dS[2 * t + 1][2], dS[2 * t + 1][3])};
+#pragma unroll
+      for (int db = 0; db < 4; ++db) adq[db] = mma(rd_tr8(Kt, 16 * db + li, t, lg), sbv, adq[db]);
+    }
+  }
+  bf16_t* dqrow = dq + (static_cast<int64_t>(b) * T + tq) * ldq + h * kDh;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const f32x4 a = adq[db] * 0.125f;
+    *reinterpret_cast<uint2*>(dqrow + 16 * db + 4 * lg) = uint2{pk(a[0], a[1]), pk(a[2], a[3])};
+  }
+}
+
+// ---------------------------------------------------------------------------
 // RoPE in place on x [B T][nh * 64]: in each head the pair (i, i + 32) is
 // rotated by pos * base^(-i / 32), pos = row % T; the angle and its sine and
 // cosine are taken in fp64.  One thread per (row, head, 8 pairs).
@@ -241,6 +425,28 @@ hipError_t launch_attn_fwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, in
   const float scale_log2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
   hipLaunchKernelGGL(k_attn_fwd, dim3(T / kBlk, H, B), dim3(256), 0, s, q, k, v, T, H, KV,
                      scale_log2, o, lse);
+  return hipGetLastError();
+}
+
+size_t attn_bwd_scratch_bytes(int B, int T, int H) {
+  return static_cast<size_t>(B) * H * T * sizeof(float);
+}
+
+hipError_t launch_attn_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* o,
+                           const float* lse, const bf16_t* dO, int B, int T, int H, int KV,
+                           float* Dvec, bf16_t* dq, bf16_t* dk, bf16_t* dv, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  if (!attn_shape_ok(T, H, KV)) return hipErrorInvalidValue;
+  const int64_t M = static_cast<int64_t>(B) * T;
+  const int64_t n = M * H;
+  const int64_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+  hipLaunchKernelGGL(k_attn_bwd_dot, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, dO, o,
+                     M, T, H, Dvec);
+  const float scale_log2 = 1.4426950408889634f / 8.0f;
+  hipLaunchKernelGGL(k_attn_bwd_kv, dim3(T / kBlk, KV, B), dim3(256), 0, s, q, k, v, dO, lse,
+                     Dvec, T, H, KV, scale_log2, dk, dv);
+  hipLaunchKernelGGL(k_attn_bwd_q, dim3(T / kBlk, H, B), dim3(256), 0, s, q, k, v, dO, lse, Dvec,
+                     T, H, KV, scale_log2, dq);
   return hipGetLastError();
 }
 

@@ -111,28 +111,31 @@ struct NtArgs {
   const bf16_t* B1u;  // kEpiSwiglu: the up weight
   const bf16_t* A2;
   const bf16_t* B2;
+  const bf16_t* A3;
+  const bf16_t* B3;
   const bf16_t* Rz;   // kEpiResid: residual; kEpiSwigluBwd: g
   const bf16_t* Rz2;  // kEpiSwigluBwd: u
   bf16_t* C;
   bf16_t* C2;
   bf16_t* C3;
-  int K1, K2, M, N;
+  int K1, K2, K3, M, N;
 };
 
-// acc[m][n] = sum_k A1[m][k] B1[n][k] + sum_k A2[m][k] B2[n][k], then by EPI:
+// acc[m][n] = sum_k A1[m][k] B1[n][k] + sum_k A2[m][k] B2[n][k] + sum_k A3[m][k] B3[n][k],
+// then by EPI:
 //   kEpiStore   C = bf16(acc)
 //   kEpiResid   C = bf16(acc + Rz)
 //   kEpiSwiglu  weight rows alternate 16-row blocks of B1 (gate) and B1u (up);
 //               C = g, C2 = u, C3 = h = silu(g) u, each [M][N / 2]
 //   kEpiSwigluBwd  acc = dh; C = dh u silu'(g), C2 = dh silu(g), with g = Rz,
 //               u = Rz2 ([M][N])
-// K1, K2 multiples of 32 (K2 may be 0), N a multiple of 256, any M >= 1: rows
+// K1, K2, K3 multiples of 32 (K2, K3 may be 0), N a multiple of 256, any M >= 1: rows
 // of A beyond M are read from row M - 1 and their results not stored.
 template <int EPI>
 __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
   const bf16_t* __restrict__ A1 = a.A1;
   const bf16_t* __restrict__ A2 = a.A2;
-  const int K1 = a.K1, K2 = a.K2, M = a.M, N = a.N;
+  const int K1 = a.K1, K2 = a.K2, K3 = a.K3, M = a.M, N = a.N;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,14 +143,15 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
   nt_tile_of(blockIdx.x, (M + kNtM - 1) / kNtM, N / kNtN, gridDim.x, mt, ntile);
   const int m0 = mt * kNtM, n0 = ntile * kNtN;
   const int ns1 = K1 / kNtK;
-  const int nstage = ns1 + K2 / kNtK;
+  const int ns12 = ns1 + K2 / kNtK;
+  const int nstage = ns12 + K3 / kNtK;
 
   // DMA: wave w fills rows (w & 3) * 64 .. + 63 of side w >> 2 (0: A, 1: B),
   // 16 rows per instruction; lane i -> row i / 4, LDS chunk i % 4.
   const int side = wave >> 2;
   const int rbase = (wave & 3) * 64;
   const int dst_off = side * kNtSideBytes + rbase * kNtRowBytes;
-  int64_t goff1[4], goff2[4];  // element offsets of this lane's chunk, per instruction
+  int64_t goff1[4], goff2[4], goff3[4];  // element offsets of this lane's chunk, per instruction
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = rbase + i * 16 + (lane >> 2);
@@ -162,12 +166,14 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
     }
     goff1[i] = static_cast<int64_t>(grow) * K1 + gchunk * 8;
     goff2[i] = static_cast<int64_t>(grow) * K2 + gchunk * 8;
+    goff3[i] = static_cast<int64_t>(grow) * K3 + gchunk * 8;
   }
   // Instruction i covers rows 16 i + rbase / 16 ..; rbase / 16 is even, so the
   // 16-row block of instruction i is a gate block for even i, an up block for odd.
   const bf16_t* src1[2] = {side == 0 ? A1 : a.B1,
                            side == 0 ? A1 : (EPI == kEpiSwiglu ? a.B1u : a.B1)};
   const bf16_t* src2 = side == 0 ? A2 : a.B2;
+  const bf16_t* src3 = side == 0 ? a.A3 : a.B3;
 
   auto issue = [&](int s, unsigned char* stage_lds) {
     const uint32_t base = nt_lds_addr(stage_lds) + dst_off;
@@ -176,11 +182,16 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
       for (int i = 0; i < 4; ++i)
         nt_dma(reinterpret_cast<const unsigned char*>(src1[i & 1] + s * kNtK + goff1[i]),
                base + i * 1024);
-    } else {
+    } else if (s < ns12) {
       const bf16_t* p = src2 + (s - ns1) * kNtK;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         nt_dma(reinterpret_cast<const unsigned char*>(p + goff2[i]), base + i * 1024);
+    } else {
+      const bf16_t* p = src3 + (s - ns12) * kNtK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        nt_dma(reinterpret_cast<const unsigned char*>(p + goff3[i]), base + i * 1024);
     }
   };
 
@@ -443,9 +454,10 @@ int elementwise_blocks(int64_t n8) {
 
 }  // namespace
 
-bool gemm_nt_ok(int64_t M, int N, int K1, int K2) {
+bool gemm_nt_ok(int64_t M, int N, int K1, int K2, int K3) {
   return M >= 1 && M <= (int64_t{1} << 30) && N > 0 && N % kNtN == 0 && K1 > 0 &&
-         K1 % kNtK == 0 && K2 >= 0 && K2 % kNtK == 0;
+         K1 % kNtK == 0 && K2 >= 0 && K2 % kNtK == 0 && K3 >= 0 && K3 % kNtK == 0 &&
+         (K3 == 0 || K2 > 0);
 }
 
 static hipError_t launch_nt(const NtArgs& a, int epi, hipStream_t s) {
@@ -464,16 +476,22 @@ static hipError_t launch_nt(const NtArgs& a, int epi, hipStream_t s) {
 hipError_t launch_gemm_nt(const bf16_t* A1, const bf16_t* B1, int K1, const bf16_t* A2,
                           const bf16_t* B2, int K2, int64_t M, int N, const bf16_t* Rz, bf16_t* C,
                           hipStream_t s) {
-  if (!gemm_nt_ok(M, N, K1, K2)) return hipErrorInvalidValue;
+  return launch_gemm_nt3(A1, B1, K1, A2, B2, K2, nullptr, nullptr, 0, M, N, Rz, C, s);
+}
+
+hipError_t launch_gemm_nt3(const bf16_t* A1, const bf16_t* B1, int K1, const bf16_t* A2,
+                           const bf16_t* B2, int K2, const bf16_t* A3, const bf16_t* B3, int K3,
+                           int64_t M, int N, const bf16_t* Rz, bf16_t* C, hipStream_t s) {
+  if (!gemm_nt_ok(M, N, K1, K2, K3)) return hipErrorInvalidValue;
   NtArgs a{};
-  a.A1 = A1; a.B1 = B1; a.A2 = A2; a.B2 = B2; a.Rz = Rz; a.C = C;
-  a.K1 = K1; a.K2 = K2; a.M = static_cast<int>(M); a.N = N;
+  a.A1 = A1; a.B1 = B1; a.A2 = A2; a.B2 = B2; a.A3 = A3; a.B3 = B3; a.Rz = Rz; a.C = C;
+  a.K1 = K1; a.K2 = K2; a.K3 = K3; a.M = static_cast<int>(M); a.N = N;
   return launch_nt(a, Rz ? kEpiResid : kEpiStore, s);
 }
 
 hipError_t launch_gemm_nt_swiglu(const bf16_t* y, const bf16_t* Wg, const bf16_t* Wu, int d,
                                  int64_t M, int f, bf16_t* g, bf16_t* u, bf16_t* h, hipStream_t s) {
-  if (f % (kNtN / 2) != 0 || !gemm_nt_ok(M, 2 * f, d, 0)) return hipErrorInvalidValue;
+  if (f % (kNtN / 2) != 0 || !gemm_nt_ok(M, 2 * f, d, 0, 0)) return hipErrorInvalidValue;
   NtArgs a{};
   a.A1 = y; a.B1 = Wg; a.B1u = Wu; a.C = g; a.C2 = u; a.C3 = h;
   a.K1 = d; a.K2 = 0; a.M = static_cast<int>(M); a.N = 2 * f;
@@ -483,7 +501,7 @@ hipError_t launch_gemm_nt_swiglu(const bf16_t* y, const bf16_t* Wg, const bf16_t
 hipError_t launch_gemm_nt_swiglu_bwd(const bf16_t* dout, const bf16_t* WdT, int d, int64_t M, int f,
                                      const bf16_t* g, const bf16_t* u, bf16_t* dg, bf16_t* du,
                                      hipStream_t s) {
-  if (!gemm_nt_ok(M, f, d, 0)) return hipErrorInvalidValue;
+  if (!gemm_nt_ok(M, f, d, 0, 0)) return hipErrorInvalidValue;
   NtArgs a{};
   a.A1 = dout; a.B1 = WdT; a.Rz = g; a.Rz2 = u; a.C = dg; a.C2 = du;
   a.K1 = d; a.K2 = 0; a.M = static_cast<int>(M); a.N = f;

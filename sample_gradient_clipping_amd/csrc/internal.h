@@ -169,10 +169,14 @@ hipError_t launch_fgc_mfma(const bf16_t* A, const bf16_t* G, int B, int T, int d
                            hipStream_t s);
 
 // ---- MLP block forward / backward pass 1 (block_kernels.hip) ----
-bool gemm_nt_ok(int64_t M, int N, int K1, int K2);
+bool gemm_nt_ok(int64_t M, int N, int K1, int K2, int K3);
 hipError_t launch_gemm_nt(const bf16_t* A1, const bf16_t* B1, int K1, const bf16_t* A2,
                           const bf16_t* B2, int K2, int64_t M, int N, const bf16_t* Rz, bf16_t* C,
                           hipStream_t s);
+// The same over three (A, B) pairs (K3 > 0 needs K2 > 0).
+hipError_t launch_gemm_nt3(const bf16_t* A1, const bf16_t* B1, int K1, const bf16_t* A2,
+                           const bf16_t* B2, int K2, const bf16_t* A3, const bf16_t* B3, int K3,
+                           int64_t M, int N, const bf16_t* Rz, bf16_t* C, hipStream_t s);
 hipError_t launch_rmsnorm_fwd(const bf16_t* x, const float* gamma, int64_t M, int d, float eps,
                               bf16_t* xhat, bf16_t* y, float* rstd, hipStream_t s);
 hipError_t launch_rmsnorm_bwd(const bf16_t* x, const float* rstd, const float* gamma,
@@ -197,5 +201,10 @@ hipError_t launch_rope(bf16_t* x, int64_t M, int T, int nh, double base, bool in
 // and lse [B][H][T] (natural log of each softmax row's normaliser).
 hipError_t launch_attn_fwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, int B, int T, int H,
                            int KV, bf16_t* o, float* lse, hipStream_t s);
+// dq, dk, dv from dO (Dvec: B H T floats of scratch for rowsum(dO o)).
+size_t attn_bwd_scratch_bytes(int B, int T, int H);
+hipError_t launch_attn_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* o,
+                           const float* lse, const bf16_t* dO, int B, int T, int H, int KV,
+                           float* Dvec, bf16_t* dq, bf16_t* dk, bf16_t* dv, hipStream_t s);
 
 }  // namespace dprc

@@ -141,3 +141,95 @@ def test_attn_block_forward(dev, B, T, d, H, KV):
         report(f"attn forward end-to-end {k_}", max_rel=e)
         assert e <= 2e-2
     assert np.all(np.abs(got["lse"] - ref["lse"]) <= 2e-2 * (1 + np.abs(ref["lse"])))
+
+
+@pytest.mark.parametrize("B,T,H,KV", [(2, 128, 8, 2), (1, 64, 4, 4), (2, 192, 4, 1)])
+def test_attention_backward(dev, B, T, H, KV):
+    r = np.random.default_rng(T * 5 + H)
+    q = _rand_bf16(r, (B, T, 64 * H), 0.5).to(dev)
+    k = _rand_bf16(r, (B, T, 64 * KV), 0.5).to(dev)
+    v = _rand_bf16(r, (B, T, 64 * KV)).to(dev)
+    dO = _rand_bf16(r, (B, T, 64 * H)).to(dev)
+    o, lse = dp.dp_attention_forward(q, k, v, H, KV)
+    dq, dk, dv = dp.dp_attention_backward(q, k, v, o, lse, dO, H, KV)
+    torch.cuda.synchronize()
+    for i in range(B):
+        ref = oracle.attention_backward(_bf(q[i]), _bf(k[i]), _bf(v[i]), _bf(dO[i]), H, KV, 64)
+        for name, got, rf in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+            e = max_rel_normwise(_bf(got[i]), rf)
+            report(f"attention backward {name} B={B} T={T} H={H} KV={KV} sample {i}", max_rel=e)
+            assert e <= 2e-2
+
+
+def _gpu_attn_block(dev, x, gamma, R, Wb, H, KV):
+    xd, gd, Rd = x.to(dev), gamma.to(dev), R.to(dev)
+    acts = dp.dp_attn_forward(xd, gd, Wb["W_q"][0], Wb["W_k"][0], Wb["W_v"][0], Wb["W_o"][0], H, KV,
+                              eps=EPS, rope_base=BASE)
+    grads = dp.dp_attn_backward(xd, acts, gd, Wb["W_q"][1], Wb["W_k"][1], Wb["W_v"][1],
+                                Wb["W_o"][1], Rd, H, KV, rope_base=BASE)
+    return xd, gd, Rd, acts, grads
+
+
+@pytest.mark.parametrize("B,T,d,H,KV", BLOCK_CASES)
+def test_attn_block_backward(dev, B, T, d, H, KV):
+    x, gamma, thetas, R, Wb = _block(dev, B, T, d, H, KV, 103)
+    _, _, _, acts, grads = _gpu_attn_block(dev, x, gamma, R, Wb, H, KV)
+    torch.cuda.synchronize()
+    W = {k_: _bf(v_[0]) for k_, v_ in Wb.items()}
+    xf, gm, Rf = _bf(x), gamma.double().numpy(), _bf(R)
+    got = {k_: _bf(v_) for k_, v_ in grads.items()}
+    M = B * T
+    # dy on the GPU's G (one product over three k ranges)
+    Gcat = np.concatenate([got["G_q"].reshape(M, -1), got["G_k"].reshape(M, -1),
+                           got["G_v"].reshape(M, -1)], axis=1)
+    Wcat = np.concatenate([W["W_q"], W["W_k"], W["W_v"]], axis=0).T  # [d][64 (H + 2 KV)]
+    dy_r = Gcat @ Wcat.T
+    K = Gcat.shape[1]
+    assert_within("attn backward dy", got["dy"].reshape(M, -1), dy_r,
+                  U8 * np.abs(dy_r) + (1 + U8) * K * U24 * (np.abs(Gcat) @ np.abs(Wcat).T) * 1.01
+                  + 1e-30)
+    # end to end, fp64 throughout
+    fwd = oracle.attn_forward(xf, gm, W["W_q"], W["W_k"], W["W_v"], W["W_o"], EPS, H, KV, 64, BASE)
+    ref = oracle.attn_backward(xf, gm, W["W_q"], W["W_k"], W["W_v"], W["W_o"], EPS, H, KV, 64,
+                               BASE, Rf, fwd)
+    for k_ in ("G_q", "G_k", "G_v", "dy", "dx"):
+        e = max_rel_normwise(got[k_], ref[k_])
+        report(f"attn backward end-to-end {k_}", max_rel=e)
+        assert e <= 2e-2
+
+
+def test_attn_block_dp_step_fgc_matches_oracle(dev):
+    B, T, d, H, KV = 3, 128, 256, 4, 4
+    x, gamma, thetas, R, Wb = _block(dev, B, T, d, H, KV, 107)
+    xd, gd, Rd, acts, grads = _gpu_attn_block(dev, x, gamma, R, Wb, H, KV)
+    C, sigma, eta, seed_n, seed_z = 0.01, 0.7, 0.5, 11, 13
+    ids = dict(oracle.ATTN_LAYERS)
+    lin = {"W_q": (acts["y"], grads["G_q"]), "W_k": (acts["y"], grads["G_k"]),
+           "W_v": (acts["y"], grads["G_v"]), "W_o": (acts["o"], Rd)}
+    n = torch.zeros(B, dtype=torch.float32, device=dev)
+    v = torch.empty(B, d, dtype=torch.float32, device=dev)
+    dp.dp_rmsnorm_norm(acts["xhat"], grads["dy"], n, v=v)
+    for name, (A, G) in lin.items():
+        dp.dp_norm_est("fgc", A, G, 0, seed_n, ids[name], n, flags=dp.DP_ACCUMULATE)
+    theta = {name: t.to(dev).clone() for name, t in thetas.items()}
+    for name, (A, G) in lin.items():
+        dp.dp_clip_aggregate_update(A, G, n, C, sigma, eta, seed_z, ids[name], theta[name])
+    gam = gd.clone()
+    dp.dp_rmsnorm_clip_aggregate_update(v, n, C, sigma, eta, seed_z, ids["gamma"], gam)
+    torch.cuda.synchronize()
+    host = {"y": acts["y"], "o": acts["o"], "xhat": acts["xhat"], "G_q": grads["G_q"],
+            "G_k": grads["G_k"], "G_v": grads["G_v"], "G_o": Rd, "dy": grads["dy"]}
+    host = {k_: _bf(t) for k_, t in host.items()}
+    n_r, c_r, new_r = oracle.attn_dp_step(host, gamma.double().numpy(),
+                                          {k_: t.double().numpy() for k_, t in thetas.items()},
+                                          "fgc", 0, C, sigma, eta, seed_n, seed_z)
+    assert np.all(c_r < 1.0)
+    e_n = float(np.max(np.abs(f64(n) - n_r) / n_r))
+    report("attn block step fgc n", max_rel=e_n)
+    assert e_n <= 1e-5
+    got = {**{k_: f64(t) for k_, t in theta.items()}, "gamma": f64(gam)}
+    for name in new_r:
+        base = gamma.double().numpy() if name == "gamma" else thetas[name].double().numpy()
+        e = max_rel_normwise(got[name] - base, new_r[name] - base)
+        report(f"attn block step fgc {name}", max_rel=e)
+        assert e <= 1e-4
