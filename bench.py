@@ -348,6 +348,95 @@ def mlp_block_timing(dp, wl, dev, d=2048, f=8192, k=32, reps=5):
             "block_step_tokens_per_s": M / (t_step * 1e-3)}
 
 
+def attn_block_timing(dp, wl, dev, d=2048, H=32, KV=8, k=32, reps=5):
+    """One DP-SGD-RC step of a Llama-3.2-1B-shaped attention block (RMSNorm, q/k/v
+    projections, RoPE, causal grouped-query attention, o projection, residual) at
+    the workload's B and T: forward pass, backward pass 1, then Hutch norms of the
+    four linears, the gain's exact norm, clip, clipped sums, noise and updates.
+    Outside the timed steps; the attention kernels are also timed alone."""
+    import torch
+    B, T = wl.B, wl.T
+    M = B * T
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6161)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+
+    x = randn(B, T, d).to(torch.bfloat16)
+    gamma = 1.0 + 0.1 * randn(d)
+    thetas = {"W_q": 0.02 * randn(64 * H, d), "W_k": 0.02 * randn(64 * KV, d),
+              "W_v": 0.02 * randn(64 * KV, d), "W_o": 0.02 * randn(d, 64 * H)}
+    R = (0.01 * randn(B, T, d)).to(torch.bfloat16)
+    Wb = {name: dp.dp_weights_bf16(t) for name, t in thetas.items()}
+    acts, grads = {}, {}
+    ws = torch.empty(dp.load_library().dp_attn_backward_workspace(B, T, H), dtype=torch.uint8,
+                     device=dev)
+    n = torch.zeros(B, dtype=torch.float32, device=dev)
+    v = torch.empty(B, d, dtype=torch.float32, device=dev)
+    ids = {"W_q": 0, "W_k": 1, "W_v": 2, "W_o": 3, "gamma": 4}
+
+    def forward():
+        dp.dp_attn_forward(x, gamma, Wb["W_q"][0], Wb["W_k"][0], Wb["W_v"][0], Wb["W_o"][0], H, KV,
+                           acts=acts)
+
+    def backward():
+        dp.dp_attn_backward(x, acts, gamma, Wb["W_q"][1], Wb["W_k"][1], Wb["W_v"][1], Wb["W_o"][1],
+                            R, H, KV, grads=grads, ws=ws)
+
+    def dp_part(it):
+        lin = {"W_q": (acts["y"], grads["G_q"]), "W_k": (acts["y"], grads["G_k"]),
+               "W_v": (acts["y"], grads["G_v"]), "W_o": (acts["o"], R)}
+        dp.dp_rmsnorm_norm(acts["xhat"], grads["dy"], n, v=v)
+        for name, (A, G) in lin.items():
+            dp.dp_norm_est("hutch", A, G, k, 700 + it, ids[name], n, flags=dp.DP_ACCUMULATE)
+        for name, (A, G) in lin.items():
+            dp.dp_clip_aggregate_update(A, G, n, 1.0, 1.0, 1e-4, 1700 + it, ids[name],
+                                        thetas[name])
+        dp.dp_rmsnorm_clip_aggregate_update(v, n, 1.0, 1.0, 1e-4, 1700 + it, ids["gamma"], gamma)
+
+    dO = (0.01 * randn(B, T, 64 * H)).to(torch.bfloat16)
+
+    def attn_only_fwd():
+        dp.dp_attention_forward(acts["q"], acts["k"], acts["v"], H, KV, o=acts["o"], lse=acts["lse"])
+
+    def attn_only_bwd():
+        dp.dp_attention_backward(acts["q"], acts["k"], acts["v"], acts["o"], acts["lse"], dO, H, KV)
+
+    forward(); backward(); dp_part(0); attn_only_fwd(); attn_only_bwd()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+    ev[0].record()
+    for _ in range(reps):
+        attn_only_fwd()
+    ev[1].record()
+    for _ in range(reps):
+        attn_only_bwd()
+    ev[2].record()
+    for _ in range(reps):
+        forward()
+    ev[3].record()
+    for _ in range(reps):
+        backward()
+    ev[4].record()
+    for it in range(reps):
+        dp_part(it + 1)
+    ev[5].record()
+    for it in range(reps):
+        forward(); backward(); dp_part(it + 1)
+    ev[6].record()
+    torch.cuda.synchronize()
+    t = [ev[i].elapsed_time(ev[i + 1]) / reps for i in range(6)]
+    attn_flops = 128.0 * B * H * T * T / 2  # causal: q k^T and p v over the lower triangle
+    del acts, grads
+    return {"B": B, "T": T, "d": d, "H": H, "KV": KV, "k": k, "method": "hutch",
+            "attention_fwd_ms": t[0], "attention_fwd_TFLOPs": attn_flops / (t[0] * 1e-3) / 1e12,
+            "attention_bwd_ms": t[1],
+            "attention_bwd_TFLOPs": 3.5 * attn_flops / (t[1] * 1e-3) / 1e12,
+            "forward_ms": t[2], "backward1_ms": t[3], "dp_step_ms": t[4], "block_step_ms": t[5],
+            "block_step_tokens_per_s": M / (t[5] * 1e-3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -530,7 +619,7 @@ def main():
             f"{kv['GBps']:8.1f} GB/s  {kv.get('TFLOPs', 0):8.1f} TF/s  frac {kv['frac']:.3f}  "
             f"share {kv['share_of_step']:.2f}")
 
-    accuracy = sampler = rms = emb = mlp = None
+    accuracy = sampler = rms = emb = mlp = attn = None
     if not args.only_step:
         accuracy = estimator_accuracy(dp, wl, inputs[0][0], dev, rademacher=args.rademacher)
         log(f"[bench] estimator accuracy {accuracy}")
@@ -544,6 +633,9 @@ def main():
         torch.cuda.empty_cache()
         mlp = mlp_block_timing(dp, wl, dev) if wl.dtype == "bf16" else None
         log(f"[bench] mlp block {mlp}")
+        torch.cuda.empty_cache()
+        attn = attn_block_timing(dp, wl, dev) if wl.dtype == "bf16" and wl.T % 64 == 0 else None
+        log(f"[bench] attention block {attn}")
 
     cpu = None
     if not args.no_cpu_baseline and not args.only_step:
@@ -567,6 +659,7 @@ def main():
         "rmsnorm_gain_norms": rms,
         "embedding": emb,
         "mlp_block": mlp,
+        "attn_block": attn,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
