@@ -427,7 +427,7 @@ def attn_block_timing(dp, wl, dev, d=2048, H=32, KV=8, k=32, reps=5):
     ev[6].record()
     torch.cuda.synchronize()
     t = [ev[i].elapsed_time(ev[i + 1]) / reps for i in range(6)]
-    attn_flops = 128.0 * B * H * T * T / 2  # causal: q k^T and p v over the lower triangle
+    attn_flops = 128.0 * B * H * T * T  # two products of 2 * 64 flops per (query, key), causal half
     del acts, grads
     return {"B": B, "T": T, "d": d, "H": H, "KV": KV, "k": k, "method": "hutch",
             "attention_fwd_ms": t[0], "attention_fwd_TFLOPs": attn_flops / (t[0] * 1e-3) / 1e12,
@@ -634,7 +634,7 @@ def main():
         mlp = mlp_block_timing(dp, wl, dev) if wl.dtype == "bf16" else None
         log(f"[bench] mlp block {mlp}")
         torch.cuda.empty_cache()
-        attn = attn_block_timing(dp, wl, dev) if wl.dtype == "bf16" and wl.T % 64 == 0 else None
+        attn = attn_block_timing(dp, wl, dev) if wl.dtype == "bf16" and wl.T % 128 == 0 else None
         log(f"[bench] attention block {attn}")
 
     cpu = None

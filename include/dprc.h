@@ -354,7 +354,7 @@ dp_status_t dp_mlp_backward(int B, int T, int d, int f, const void *x, const flo
  *   o_h = softmax(q_h k^T / 8 + causal mask) v,  out = x + o Wo^T
  * Layouts as for the MLP block; Wq [64 H][d], Wk, Wv [64 KV][d], Wo [d][64 H]
  * bf16; lse [B][H][T] fp32 is the natural log of each softmax row's
- * normaliser (the backward pass reads it).  T a multiple of 64, d, 64 H and
+ * normaliser (the backward pass reads it).  T a multiple of 128, d, 64 H and
  * 64 KV multiples of 256.  No workspace.
  */
 

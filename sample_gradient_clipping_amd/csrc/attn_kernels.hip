@@ -1,7 +1,7 @@
 // Forward pass and backward pass 1 of a Llama attention block on gfx950 (the
 // randomized-clipping summary, section アルゴリズム的フロー, steps 1-2): rotary
 // position embedding, and causal grouped-query attention with head width 64 as
-// flash-style tiles (no T x T matrix in memory).
+// flash-style tiles (no T x T matrix in memory); T a multiple of 128.
 //
 // MFMA facts used (v_mfma_f32_16x16x32_bf16, wave64): lane l supplies row
 // l % 16 of the first operand and column l % 16 of the second, each with the 8
@@ -52,6 +52,32 @@ __device__ __forceinline__ int tr_off(int row, int col) {
   return col * kBlk + ((((row >> 2) ^ (col & 15))) << 2) + (row & 3);
 }
 
+// Row-major tile read by ds_read_b64_tr_b16 (V in the forward): chunk c of row
+// r at c ^ sv(r); 4 consecutive rows (from a multiple of 4) map a 16-byte chunk
+// pair to 4 different pairs and 8 consecutive rows to 8 different chunks.
+__device__ __forceinline__ int sv(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int rv_off(int r, int c) { return r * kBlk + ((c ^ sv(r)) << 3); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 at_lds_v4i16;
+
+// 8 contraction slots for the operand "row n = column n0 + (l % 16) of the tile,
+// slots = tile rows 32 t + 4 grp .. + 3, then 32 t + 16 + 4 grp .. + 3", read from
+// a row-major (sv-swizzled) tile with two transposing reads: in each group of 16
+// lanes, lane 4 j + c addresses row (base + j), columns n0 + 4 c .. + 3, and
+// receives slot j of column n0 + (l % 16).
+__device__ __forceinline__ u32x4 rd_rm_tr8(const bf16_t* tile, int n0, int t, int grp, int lane16) {
+  const int j = lane16 >> 2, c = lane16 & 3;
+  const int col = n0 + 4 * c;
+  const int r0 = 32 * t + 4 * grp + j, r1 = r0 + 16;
+  const bf16_t* p0 = tile + r0 * kBlk + ((((col >> 3) ^ sv(r0)) << 3) | (col & 7));
+  const bf16_t* p1 = tile + r1 * kBlk + ((((col >> 3) ^ sv(r1)) << 3) | (col & 7));
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_v4i16*)(p0));
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((at_lds_v4i16*)(p1));
+  const u32x2 aa = __builtin_bit_cast(u32x2, a), bb = __builtin_bit_cast(u32x2, b);
+  return u32x4{aa.x, aa.y, bb.x, bb.y};
+}
+
 __device__ __forceinline__ u32x4 rd16(const bf16_t* tile, int r, int c) {
   return *(at_lds_u32x4*)(tile + rm_off(r, c));
 }
@@ -85,39 +111,116 @@ __device__ __forceinline__ void stage(const bf16_t* src, int64_t ld, bf16_t* rm,
 
 __device__ __forceinline__ uint32_t pk(float a, float b) { return pack_bf16x2(a, b); }
 
+// 2^x with v_exp_f32 alone: the softmax only takes it of x <= 0, where a result
+// below 2^-126 flushing to zero changes nothing the bf16 products can see.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __attribute__((address_space(3))) void at_lds_void;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((at_lds_void*)(p)));
+}
+
+// One 1 KB global -> LDS DMA instruction: lane i's 16 global bytes land at LDS
+// m0 + 16 i.  m0 is saved and restored around it.  As inline asm the load is not
+// an LDS write the compiler would drain before LDS reads: the kernel counts
+// these loads itself (vmcnt) and orders the stages with s_barrier.
+__device__ __forceinline__ void dma16(const bf16_t* gp, uint32_t lds) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(gp), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
+}
+
+// s_waitcnt with vmcnt = N (other counters unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
-// Forward: one workgroup = 64 queries of one head; wave w owns queries
-// 16 w .. + 15.  Online softmax in the log2 domain.
+// Forward: one workgroup = 128 queries of one head, wave w owns queries
+// 16 w .. + 15; 64-key tiles of K (row-major) and V (row-major, read with
+// transposing reads), the next tile's loads issued before the current tile's
+// MFMAs.  Online softmax in the log2 domain.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_attn_fwd(const bf16_t* __restrict__ q,
+constexpr int kFwdQ = 128;
+constexpr int kFwdStages = 4;
+constexpr int kTileElems = kBlk * kBlk;  // one 64 x 64 tile
+
+__global__ void __launch_bounds__(512) k_attn_fwd(const bf16_t* __restrict__ q,
                                                   const bf16_t* __restrict__ k,
                                                   const bf16_t* __restrict__ v, int T, int H,
                                                   int KV, float scale_log2,
                                                   bf16_t* __restrict__ o,
                                                   float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kBlk * kBlk];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[kBlk * kBlk];
+  // stage s: K tile at KV_s[s][0], V tile at KV_s[s][1]
+  __shared__ __attribute__((aligned(16))) bf16_t KVs[kFwdStages][2][kTileElems];
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int gkv = h / (H / KV);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int li = lane & 15, lg = lane >> 4;
   const int64_t ldq = static_cast<int64_t>(H) * kDh, ldk = static_cast<int64_t>(KV) * kDh;
-  const int tq = qb * kBlk + w * 16 + li;  // this lane's query
+  const int tq = qb * kFwdQ + w * 16 + li;  // this lane's query
   const bf16_t* qrow = q + (static_cast<int64_t>(b) * T + tq) * ldq + h * kDh;
   const u32x4 qf0 = *reinterpret_cast<const u32x4*>(qrow + 8 * lg);
   const u32x4 qf1 = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * lg);
+  // Use the query fragments here, before the first DMA: the compiler then waits
+  // for them now, and not (with a count that the DMA loads would inflate) inside
+  // the tile loop.
+  asm volatile("" ::"v"(qf0), "v"(qf1));
+
+  // DMA: wave w fills rows 8 w .. 8 w + 7 of the K tile and of the V tile, one
+  // instruction each; lane i -> row 8 w + i / 8, LDS chunk i % 8, which holds
+  // global chunk (i % 8) ^ swizzle(row).
+  const int dr = 8 * w + (lane >> 3), dp = lane & 7;
+  const int64_t kv0 = static_cast<int64_t>(b) * T * ldk + gkv * kDh + dr * ldk;
+  const bf16_t* kg = k + kv0 + 8 * (dp ^ (dr & 7));
+  const bf16_t* vg = v + kv0 + 8 * (dp ^ sv(dr));
+  const int nkt = (qb * kFwdQ + kFwdQ) / kBlk;  // key tiles up to the diagonal
+  auto issue = [&](int kt) {
+    const int64_t off = static_cast<int64_t>(kt) * kBlk * ldk;
+    bf16_t* st = &KVs[kt % kFwdStages][0][0];
+    dma16(kg + off, lds_addr(st + 8 * w * kBlk));
+    dma16(vg + off, lds_addr(st + kTileElems + 8 * w * kBlk));
+  };
+  issue(0);
+  if (nkt > 1) issue(1);
+  if (nkt > 2) issue(2);
 
   float m = -INFINITY, l = 0.f;
   f32x4 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int qlast = qb * kFwdQ + w * 16 + 15;  // the wave's last query
 
-  for (int kt = 0; kt <= qb; ++kt) {
-    __syncthreads();
-    const int64_t krow0 = static_cast<int64_t>(b) * T + kt * kBlk;
-    stage<true, false>(k + krow0 * ldk + gkv * kDh, ldk, Ks, nullptr);
-    stage<false, true>(v + krow0 * ldk + gkv * kDh, ldk, nullptr, Vt);
-    __syncthreads();
+  for (int kt = 0; kt < nkt; ++kt) {
+    // this wave's loads of tile kt are done (those of kt + 1, kt + 2 may be in
+    // flight); after the barrier every wave's are, and every wave is done with
+    // the stage of tile kt - 1, which tile kt + 3 refills
+    const int ahead = nkt - 1 - kt;
+    if (ahead >= 2)
+      wait_vm<4>();
+    else if (ahead == 1)
+      wait_vm<2>();
+    else
+      wait_vm<0>();
+    bar();
+    if (kt + 3 < nkt) issue(kt + 3);
+    if (kt * kBlk > qlast) continue;  // every key of the tile is after the wave's queries
+    const bf16_t* Ks = &KVs[kt % kFwdStages][0][0];
+    const bf16_t* Vs = Ks + kTileElems;
 
     f32x4 s[4];
 #pragma unroll
@@ -126,27 +229,26 @@ __global__ void __launch_bounds__(256) k_attn_fwd(const bf16_t* __restrict__ q,
       s[kb] = mma(rd16(Ks, r, lg), qf0, f32x4{0.f, 0.f, 0.f, 0.f});
       s[kb] = mma(rd16(Ks, r, 4 + lg), qf1, s[kb]);
     }
+    // raw scores; the scale (> 0) goes into the max and the exponent's fma
     float mx = -INFINITY;
-    const int qq = w * 16 + li;  // query within the block
+    const bool diag = (kt + 1) * kBlk > qb * kFwdQ + w * 16;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float x = s[kb][r] * scale_log2;
-        if (kt == qb && kb * 16 + 4 * lg + r > qq) x = -INFINITY;
-        s[kb][r] = x;
-        mx = fmaxf(mx, x);
+        if (diag && kt * kBlk + kb * 16 + 4 * lg + r > tq) s[kb][r] = -INFINITY;
+        mx = fmaxf(mx, s[kb][r]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2f(m - mn);
+    const float mn = fmaxf(m, mx * scale_log2);
+    const float alpha = ex2(m - mn);
     float sum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(s[kb][r] - mn);
+        const float p = ex2(fmaf(s[kb][r], scale_log2, -mn));
         s[kb][r] = p;
         sum += p;
       }
@@ -161,7 +263,7 @@ __global__ void __launch_bounds__(256) k_attn_fwd(const bf16_t* __restrict__ q,
       const u32x4 pb{pk(s[2 * t][0], s[2 * t][1]), pk(s[2 * t][2], s[2 * t][3]),
                      pk(s[2 * t + 1][0], s[2 * t + 1][1]), pk(s[2 * t + 1][2], s[2 * t + 1][3])};
 #pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] = mma(rd_tr8(Vt, 16 * db + li, t, lg), pb, acc[db]);
+      for (int db = 0; db < 4; ++db) acc[db] = mma(rd_rm_tr8(Vs, 16 * db, t, lg, li), pb, acc[db]);
     }
   }
 
@@ -263,7 +365,7 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qq = sb * 16 + 4 * lg + r;  // query within the block
-          float p = exp2f(sc[r] * scale_log2 - Ls[qq]);
+          float p = ex2(sc[r] * scale_log2 - Ls[qq]);
           if (qb == kbk && kk > qq) p = 0.f;
           P[sb][r] = p;
           dS[sb][r] = p * (dp[r] - Dd[qq]);
@@ -339,7 +441,7 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
       dp = mma(rd16(Vs, r0, 4 + lg), df1, dp);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float p = exp2f(st[r] * scale_log2 - lq);
+        float p = ex2(st[r] * scale_log2 - lq);
         if (kt == qb && kb * 16 + 4 * lg + r > qq) p = 0.f;
         dS[kb][r] = p * (dp[r] - dd);
       }
@@ -404,7 +506,7 @@ __global__ void __launch_bounds__(256) k_rope(bf16_t* __restrict__ x, int64_t M,
 }  // namespace
 
 bool attn_shape_ok(int T, int H, int KV) {
-  return T > 0 && T % kBlk == 0 && H > 0 && KV > 0 && H % KV == 0 && T <= (1 << 20);
+  return T > 0 && T % kFwdQ == 0 && H > 0 && KV > 0 && H % KV == 0 && T <= (1 << 20);
 }
 
 hipError_t launch_rope(bf16_t* x, int64_t M, int T, int nh, double base, bool inverse,
@@ -423,7 +525,7 @@ hipError_t launch_attn_fwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, in
   if (B <= 0) return hipSuccess;
   if (!attn_shape_ok(T, H, KV)) return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / 8.0f;  // log2(e) / sqrt(64)
-  hipLaunchKernelGGL(k_attn_fwd, dim3(T / kBlk, H, B), dim3(256), 0, s, q, k, v, T, H, KV,
+  hipLaunchKernelGGL(k_attn_fwd, dim3(T / kFwdQ, H, B), dim3(512), 0, s, q, k, v, T, H, KV,
                      scale_log2, o, lse);
   return hipGetLastError();
 }

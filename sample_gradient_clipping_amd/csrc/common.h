@@ -18,16 +18,17 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
-}
+// Round-to-nearest-even fp32 -> bf16 (NaN stays NaN) with gfx950's
+// v_cvt_pk_bf16_f32: one instruction for a pair, no branch.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2_hw v{static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return static_cast<bf16_t>(pack_bf16x2(f, 0.f) & 0xFFFFu);
 }
 
 template <typename T> __device__ __forceinline__ float load_f32(const T* p);

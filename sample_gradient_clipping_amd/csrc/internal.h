@@ -192,7 +192,7 @@ hipError_t launch_gemm_nt_swiglu_bwd(const bf16_t* dout, const bf16_t* WdT, int 
 hipError_t launch_cast_transpose(const float* theta, int p, int d, bf16_t* W, bf16_t* Wt,
                                  hipStream_t s);
 
-// ---- attention block (attn_kernels.hip): head width 64, T % 64 == 0 ----
+// ---- attention block (attn_kernels.hip): head width 64, T % 128 == 0 ----
 bool attn_shape_ok(int T, int H, int KV);
 // In place RoPE on x [M][nh * 64] (row % T is the position); inverse rotates back.
 hipError_t launch_rope(bf16_t* x, int64_t M, int T, int nh, double base, bool inverse,
