@@ -19,10 +19,11 @@
 // same key order.  Every product of the backward pass uses one of these two
 // orientations (query in the lane, or key in the lane) the same way.
 //
-// LDS tiles (64 x 64 bf16, 8 KB): row-major with the 16-byte chunk c of row r
-// at c ^ (r & 7) (16-byte reads of 8 consecutive rows hit distinct banks), or
-// transposed (line = column) with the 8-byte chunk c of line n at c ^ (n & 15)
-// (8-byte reads of 16 consecutive lines hit distinct banks).
+// LDS tiles (64 x 64 bf16, 8 KB) are row-major with the 16-byte chunk c of row
+// r stored at a swizzled position: 16-byte operand reads of 8 consecutive rows
+// hit distinct banks, and the transposed operands (V^T, Q^T, dO^T, K^T) come from
+// the same row-major tiles through ds_read_b64_tr_b16, whose 16-lane groups read
+// 4 consecutive rows, also at distinct banks.
 #include <cmath>
 
 #include "common.h"
@@ -47,10 +48,6 @@ __device__ __forceinline__ f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
 // Element offset of the 16-byte chunk c (columns 8 c .. 8 c + 7) of row r in a
 // row-major swizzled tile.
 __device__ __forceinline__ int rm_off(int r, int c) { return r * kBlk + ((c ^ (r & 7)) << 3); }
-// Element offset of (row, column) in a transposed swizzled tile.
-__device__ __forceinline__ int tr_off(int row, int col) {
-  return col * kBlk + ((((row >> 2) ^ (col & 15))) << 2) + (row & 3);
-}
 
 // Row-major tile read by ds_read_b64_tr_b16 (V in the forward): chunk c of row
 // r at c ^ sv(r); 4 consecutive rows (from a multiple of 4) map a 16-byte chunk
@@ -78,38 +75,30 @@ __device__ __forceinline__ u32x4 rd_rm_tr8(const bf16_t* tile, int n0, int t, in
   return u32x4{aa.x, aa.y, bb.x, bb.y};
 }
 
+// 16-byte read of chunk c of row r of an sv-swizzled row-major tile (sv gives 8
+// consecutive rows 8 different chunk positions, so these reads are
+// conflict-free too).
+__device__ __forceinline__ u32x4 rd16v(const bf16_t* tile, int r, int c) {
+  return *(at_lds_u32x4*)(tile + rv_off(r, c));
+}
+
 __device__ __forceinline__ u32x4 rd16(const bf16_t* tile, int r, int c) {
   return *(at_lds_u32x4*)(tile + rm_off(r, c));
 }
-// 8 contraction slots of transposed line n: rows 32 t + 4 grp .. + 3, then
-// 32 t + 16 + 4 grp .. + 3.
-__device__ __forceinline__ u32x4 rd_tr8(const bf16_t* tile, int n, int t, int grp) {
-  const u32x2 lo = *(at_lds_u32x2*)(tile + tr_off(32 * t + 4 * grp, n));
-  const u32x2 hi = *(at_lds_u32x2*)(tile + tr_off(32 * t + 16 + 4 * grp, n));
-  return u32x4{lo.x, lo.y, hi.x, hi.y};
-}
 
-// 64 rows x 64 columns (row stride ld elements) from global into a row-major
-// swizzled tile and/or a transposed one; 256 threads, two 16-byte chunks each.
-template <bool RM, bool TR>
-__device__ __forceinline__ void stage(const bf16_t* src, int64_t ld, bf16_t* rm, bf16_t* tr) {
+
+__device__ __forceinline__ uint32_t pk(float a, float b) { return pack_bf16x2(a, b); }
+
+// 64 rows x 64 columns (row stride ld) from global into an sv-swizzled row-major
+// tile; 256 threads, two 16-byte chunks each.
+__device__ __forceinline__ void stage_v(const bf16_t* src, int64_t ld, bf16_t* tile) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int id = threadIdx.x + 256 * j;
     const int r = id >> 3, c = id & 7;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src + r * ld + 8 * c);
-    if (RM) *(at_lds_u32x4_w*)(rm + rm_off(r, c)) = v;
-    if (TR) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w = v[e >> 1];
-        tr[tr_off(r, 8 * c + e)] = static_cast<bf16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu));
-      }
-    }
+    *(at_lds_u32x4_w*)(tile + rv_off(r, c)) = *reinterpret_cast<const u32x4*>(src + r * ld + 8 * c);
   }
 }
-
-__device__ __forceinline__ uint32_t pk(float a, float b) { return pack_bf16x2(a, b); }
 
 // 2^x with v_exp_f32 alone: the softmax only takes it of x <= 0, where a result
 // below 2^-126 flushing to zero changes nothing the bf16 products can see.
@@ -316,9 +305,7 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dvec,
     int T, int H, int KV, float scale_log2, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv) {
   __shared__ __attribute__((aligned(16))) bf16_t Qs[kBlk * kBlk];
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[kBlk * kBlk];
   __shared__ __attribute__((aligned(16))) bf16_t Ds[kBlk * kBlk];
-  __shared__ __attribute__((aligned(16))) bf16_t Dt[kBlk * kBlk];
   __shared__ float Ls[kBlk], Dd[kBlk];
   const int kbk = blockIdx.x, gkv = blockIdx.y, b = blockIdx.z;
   const int grp = H / KV;
@@ -346,8 +333,8 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
     for (int qb = kbk; qb < T / kBlk; ++qb) {
       __syncthreads();
       const int64_t qrow0 = static_cast<int64_t>(b) * T + qb * kBlk;
-      stage<true, true>(q + qrow0 * ldq + h * kDh, ldq, Qs, Qt);
-      stage<true, true>(dO + qrow0 * ldq + h * kDh, ldq, Ds, Dt);
+      stage_v(q + qrow0 * ldq + h * kDh, ldq, Qs);
+      stage_v(dO + qrow0 * ldq + h * kDh, ldq, Ds);
       if (threadIdx.x < kBlk) {
         const int64_t si = (static_cast<int64_t>(b) * H + h) * T + qb * kBlk + threadIdx.x;
         Ls[threadIdx.x] = lse[si] * kLog2e;
@@ -358,10 +345,10 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) {  // 16-query blocks
         const int r0 = sb * 16 + li;
-        f32x4 sc = mma(rd16(Qs, r0, lg), kf0, f32x4{0.f, 0.f, 0.f, 0.f});
-        sc = mma(rd16(Qs, r0, 4 + lg), kf1, sc);
-        f32x4 dp = mma(rd16(Ds, r0, lg), vf0, f32x4{0.f, 0.f, 0.f, 0.f});
-        dp = mma(rd16(Ds, r0, 4 + lg), vf1, dp);
+        f32x4 sc = mma(rd16v(Qs, r0, lg), kf0, f32x4{0.f, 0.f, 0.f, 0.f});
+        sc = mma(rd16v(Qs, r0, 4 + lg), kf1, sc);
+        f32x4 dp = mma(rd16v(Ds, r0, lg), vf0, f32x4{0.f, 0.f, 0.f, 0.f});
+        dp = mma(rd16v(Ds, r0, 4 + lg), vf1, dp);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qq = sb * 16 + 4 * lg + r;  // query within the block
@@ -380,8 +367,8 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
                         pk(dS[2 * t + 1][2], dS[2 * t + 1][3])};
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          adv[db] = mma(rd_tr8(Dt, 16 * db + li, t, lg), pb, adv[db]);
-          adk[db] = mma(rd_tr8(Qt, 16 * db + li, t, lg), sbv, adk[db]);
+          adv[db] = mma(rd_rm_tr8(Ds, 16 * db, t, lg, li), pb, adv[db]);
+          adk[db] = mma(rd_rm_tr8(Qs, 16 * db, t, lg, li), sbv, adk[db]);
         }
       }
     }
@@ -404,7 +391,6 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dvec,
     int T, int H, int KV, float scale_log2, bf16_t* __restrict__ dq) {
   __shared__ __attribute__((aligned(16))) bf16_t Ks[kBlk * kBlk];
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[kBlk * kBlk];
   __shared__ __attribute__((aligned(16))) bf16_t Vs[kBlk * kBlk];
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int gkv = h / (H / KV);
@@ -428,17 +414,17 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
   for (int kt = 0; kt <= qb; ++kt) {
     __syncthreads();
     const int64_t krow0 = static_cast<int64_t>(b) * T + kt * kBlk;
-    stage<true, true>(k + krow0 * ldk + gkv * kDh, ldk, Ks, Kt);
-    stage<true, false>(v + krow0 * ldk + gkv * kDh, ldk, Vs, nullptr);
+    stage_v(k + krow0 * ldk + gkv * kDh, ldk, Ks);
+    stage_v(v + krow0 * ldk + gkv * kDh, ldk, Vs);
     __syncthreads();
     f32x4 dS[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int r0 = kb * 16 + li;
-      f32x4 st = mma(rd16(Ks, r0, lg), qf0, f32x4{0.f, 0.f, 0.f, 0.f});
-      st = mma(rd16(Ks, r0, 4 + lg), qf1, st);
-      f32x4 dp = mma(rd16(Vs, r0, lg), df0, f32x4{0.f, 0.f, 0.f, 0.f});
-      dp = mma(rd16(Vs, r0, 4 + lg), df1, dp);
+      f32x4 st = mma(rd16v(Ks, r0, lg), qf0, f32x4{0.f, 0.f, 0.f, 0.f});
+      st = mma(rd16v(Ks, r0, 4 + lg), qf1, st);
+      f32x4 dp = mma(rd16v(Vs, r0, lg), df0, f32x4{0.f, 0.f, 0.f, 0.f});
+      dp = mma(rd16v(Vs, r0, 4 + lg), df1, dp);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float p = ex2(st[r] * scale_log2 - lq);
@@ -451,7 +437,7 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
       const u32x4 sbv{pk(dS[2 * t][0], dS[2 * t][1]), pk(dS[2 * t][2], dS[2 * t][3]),
                       pk(dS[2 * t + 1][0], dS[2 * t + 1][1]), pk(dS[2 * t + 1][2], dS[2 * t + 1][3])};
 #pragma unroll
-      for (int db = 0; db < 4; ++db) adq[db] = mma(rd_tr8(Kt, 16 * db + li, t, lg), sbv, adq[db]);
+      for (int db = 0; db < 4; ++db) adq[db] = mma(rd_rm_tr8(Ks, 16 * db, t, lg, li), sbv, adq[db]);
     }
   }
   bf16_t* dqrow = dq + (static_cast<int64_t>(b) * T + tq) * ldq + h * kDh;
