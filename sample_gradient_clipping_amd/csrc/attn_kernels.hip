@@ -218,16 +218,21 @@ __global__ void __launch_bounds__(512) k_attn_fwd(const bf16_t* __restrict__ q,
       s[kb] = mma(rd16(Ks, r, lg), qf0, f32x4{0.f, 0.f, 0.f, 0.f});
       s[kb] = mma(rd16(Ks, r, 4 + lg), qf1, s[kb]);
     }
-    // raw scores; the scale (> 0) goes into the max and the exponent's fma
+    // raw scores; the scale (> 0) goes into the max and the exponent's fma.  The
+    // causal mask only on the tiles that reach past the wave's first query (a
+    // wave-uniform branch).
+    if ((kt + 1) * kBlk > qb * kFwdQ + w * 16) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (kt * kBlk + kb * 16 + 4 * lg + r > tq) s[kb][r] = -INFINITY;
+    }
     float mx = -INFINITY;
-    const bool diag = (kt + 1) * kBlk > qb * kFwdQ + w * 16;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (diag && kt * kBlk + kb * 16 + 4 * lg + r > tq) s[kb][r] = -INFINITY;
-        mx = fmaxf(mx, s[kb][r]);
-      }
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mn = fmaxf(m, mx * scale_log2);
@@ -245,8 +250,10 @@ __global__ void __launch_bounds__(512) k_attn_fwd(const bf16_t* __restrict__ q,
     sum += __shfl_xor(sum, 32, 64);
     l = l * alpha + sum;
     m = mn;
+    if (__any(alpha != 1.0f)) {  // skipped when no lane's running max moved
 #pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+      for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const u32x4 pb{pk(s[2 * t][0], s[2 * t][1]), pk(s[2 * t][2], s[2 * t][3]),
@@ -352,8 +359,8 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int qq = sb * 16 + 4 * lg + r;  // query within the block
-          float p = ex2(sc[r] * scale_log2 - Ls[qq]);
-          if (qb == kbk && kk > qq) p = 0.f;
+          float p = ex2(fmaf(sc[r], scale_log2, -Ls[qq]));
+          if (qb == kbk && kk > qq) p = 0.f;  // a select, no branch between the MFMAs
           P[sb][r] = p;
           dS[sb][r] = p * (dp[r] - Dd[qq]);
         }
@@ -427,8 +434,8 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
       dp = mma(rd16v(Vs, r0, 4 + lg), df1, dp);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float p = ex2(st[r] * scale_log2 - lq);
-        if (kt == qb && kb * 16 + 4 * lg + r > qq) p = 0.f;
+        float p = ex2(fmaf(st[r], scale_log2, -lq));
+        if (kt == qb && kb * 16 + 4 * lg + r > qq) p = 0.f;  // a select, no branch
         dS[kb][r] = p * (dp[r] - dd);
       }
     }
