@@ -25,7 +25,8 @@ Sources it follows (cited by page title and section throughout):
   that are not linear layers) in ``other_layers.py``; the forward pass and
   backward pass 1 of a Llama-shaped MLP block ([RC] アルゴリズム的フロー, steps
   1-2) and that block's whole step in ``mlp_block.py``; the attention half of
-  the decoder layer (grouped heads, RoPE, causal softmax) in ``attn_block.py``.
+  the decoder layer (grouped heads, RoPE, causal softmax) in ``attn_block.py``,
+  with the whole layer (attention block, then MLP block) and its step.
 * Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
   easy as 1, 2, 3", SC'11 (the published counter-based generator).
 
@@ -104,4 +105,7 @@ from .attn_block import (  # noqa: F401
     attn_per_sample_grads,
     attn_dp_step,
     ATTN_LAYERS,
+    layer_forward,
+    layer_backward,
+    layer_dp_step,
 )

@@ -174,3 +174,54 @@ def attn_dp_step(acts, gamma, weights, method, k, C, sigma, eta, seed_norm, seed
     new["gamma"] = noise_update(to_f64(gamma)[None, :], S_g[None, :], sigma, C, eta, B,
                                 seed_noise, ids["gamma"])[0]
     return n, c, new
+
+
+def layer_forward(x, attn_p, mlp_p, eps, n_heads, n_kv, head_dim, base):
+    """A Llama decoder layer: the attention block, then the MLP block on its output.
+    attn_p = (gamma, Wq, Wk, Wv, Wo), mlp_p = (gamma, W_gate, W_up, W_down)."""
+    from .mlp_block import mlp_forward
+    fa = attn_forward(x, *attn_p, eps, n_heads, n_kv, head_dim, base)
+    fm = mlp_forward(fa["out"], *mlp_p, eps)
+    return fa, fm
+
+
+def layer_backward(x, attn_p, mlp_p, eps, n_heads, n_kv, head_dim, base, dout, fwd=None):
+    """Backward pass 1 through the layer: the MLP block from R = dL/d(out), then the
+    attention block from the MLP block's dL/d(input)."""
+    from .mlp_block import mlp_backward
+    fa, fm = layer_forward(x, attn_p, mlp_p, eps, n_heads, n_kv, head_dim, base) if fwd is None \
+        else fwd
+    bm = mlp_backward(fa["out"], *mlp_p, eps, dout, fm)
+    ba = attn_backward(x, *attn_p, eps, n_heads, n_kv, head_dim, base, bm["dx"], fa)
+    return ba, bm
+
+
+def layer_dp_step(a_acts, m_acts, attn_p, mlp_p, method, k, C, sigma, eta, seed_norm,
+                  seed_noise):
+    """One DP-SGD-RC step of the whole layer: the squared norms of all eleven
+    parameters (seven linears, two gains) summed per sample, one clip factor per
+    sample, then every parameter's clipped sum, noise and update.  Layer ids: the
+    attention block's parameters 0..4, the MLP block's 5..8 (ATTN_LAYERS, then
+    MLP_LAYERS shifted by 5).  Returns (n, c, {name: updated})."""
+    from .mlp_block import MLP_LAYERS
+    lin = {"W_q": (a_acts, "y", "G_q", attn_p[1]), "W_k": (a_acts, "y", "G_k", attn_p[2]),
+           "W_v": (a_acts, "y", "G_v", attn_p[3]), "W_o": (a_acts, "o", "G_o", attn_p[4]),
+           "W_gate": (m_acts, "y", "G_gate", mlp_p[1]), "W_up": (m_acts, "y", "G_up", mlp_p[2]),
+           "W_down": (m_acts, "h", "G_down", mlp_p[3])}
+    ids = dict(ATTN_LAYERS)
+    ids.update({("mlp_" + n if n == "gamma" else n): 5 + i for n, i in MLP_LAYERS})
+    n = rmsnorm_norm_sq(a_acts["xhat"], a_acts["dy"]) + rmsnorm_norm_sq(m_acts["xhat"],
+                                                                          m_acts["dy"])
+    for name, (acts, a, g, _W) in lin.items():
+        n = n + norm_est(method, acts[a], acts[g], k=k, seed=seed_norm, layer=ids[name])
+    c, _flag = clip_factors(n, C)
+    B = len(n)
+    new = {}
+    for name, (acts, a, g, W) in lin.items():
+        new[name] = noise_update(to_f64(W), aggregate(acts[a], acts[g], c), sigma, C, eta, B,
+                                 seed_noise, ids[name])
+    for name, acts, gamma in (("gamma", a_acts, attn_p[0]), ("mlp_gamma", m_acts, mlp_p[0])):
+        S_g = rmsnorm_aggregate(acts["xhat"], acts["dy"], c)
+        new[name] = noise_update(to_f64(gamma)[None, :], S_g[None, :], sigma, C, eta, B,
+                                 seed_noise, ids[name])[0]
+    return n, c, new

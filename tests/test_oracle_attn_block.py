@@ -186,3 +186,72 @@ def test_step_without_clipping_or_noise_is_sgd_on_the_batch_loss():
             am = [x] + [params[o] if o != name else Pm for o in order]
             fd = sum(_loss(i, ap, R) - _loss(i, am, R) for i in range(B)) / (2 * h)
             assert np.isclose(new[name][idx], P[idx] - eta / B * fd, rtol=1e-8, atol=1e-10)
+
+
+def test_layer_backward_matches_finite_differences():
+    """The attention block feeding the MLP block: every parameter of both halves
+    and dL/dx against central differences of the layer's per-sample loss."""
+    from oracle import mlp_block as mb
+    x, gamma, Wq, Wk, Wv, Wo, R = _block(41)
+    r = np.random.default_rng(42)
+    d, f = x.shape[-1], 6
+    mlp_p = (1.0 + 0.3 * r.standard_normal(d), r.standard_normal((f, d)) / np.sqrt(d),
+             r.standard_normal((f, d)) / np.sqrt(d), r.standard_normal((d, f)) / np.sqrt(f))
+    attn_p = (gamma, Wq, Wk, Wv, Wo)
+    fa, fm = ab.layer_forward(x, attn_p, mlp_p, EPS, H, KV, DH, BASE)
+    ba, bm = ab.layer_backward(x, attn_p, mlp_p, EPS, H, KV, DH, BASE, R, (fa, fm))
+    ga = ab.attn_per_sample_grads(fa, ba)
+    gm = mb.mlp_per_sample_grads(fm, bm)
+
+    def loss(i, xx, ap, mp):
+        return float(np.sum(R[i] * ab.layer_forward(xx, ap, mp, EPS, H, KV, DH, BASE)[1]["out"][i]))
+
+    h = 1e-5
+    for i in range(x.shape[0]):
+        checks = [("x", None, None)] + [("attn", j, n) for j, n in enumerate(
+            ["gamma", "W_q", "W_k", "W_v", "W_o"])] + [("mlp", j, n) for j, n in enumerate(
+                ["gamma", "W_gate", "W_up", "W_down"])]
+        for part, j, name in checks:
+            P = x if part == "x" else (attn_p[j] if part == "attn" else mlp_p[j])
+            for _ in range(2):
+                idx = tuple(int(r.integers(0, s)) for s in P.shape)
+                if part == "x":
+                    idx = (i,) + idx[1:]
+                Pp, Pm = P.copy(), P.copy()
+                Pp[idx] += h
+                Pm[idx] -= h
+                if part == "x":
+                    fd = (loss(i, Pp, attn_p, mlp_p) - loss(i, Pm, attn_p, mlp_p)) / (2 * h)
+                    an = ba["dx"][idx]
+                elif part == "attn":
+                    ap_, am_ = list(attn_p), list(attn_p)
+                    ap_[j], am_[j] = Pp, Pm
+                    fd = (loss(i, x, ap_, mlp_p) - loss(i, x, am_, mlp_p)) / (2 * h)
+                    an = ga[name][i][idx]
+                else:
+                    mp_, mm_ = list(mlp_p), list(mlp_p)
+                    mp_[j], mm_[j] = Pp, Pm
+                    fd = (loss(i, x, attn_p, mp_) - loss(i, x, attn_p, mm_)) / (2 * h)
+                    an = gm[name][i][idx]
+                assert np.isclose(an, fd, rtol=1e-6, atol=1e-8), (part, name, idx, an, fd)
+
+
+def test_layer_step_clips_the_whole_layer_gradient():
+    """With a small C the one-sample update of all eleven parameters together has
+    norm exactly C (one clip factor for the whole layer)."""
+    x, gamma, Wq, Wk, Wv, Wo, R = _block(43, B=1)
+    r = np.random.default_rng(44)
+    d, f = x.shape[-1], 6
+    mlp_p = (1.0 + 0.3 * r.standard_normal(d), r.standard_normal((f, d)) / np.sqrt(d),
+             r.standard_normal((f, d)) / np.sqrt(d), r.standard_normal((d, f)) / np.sqrt(f))
+    attn_p = (gamma, Wq, Wk, Wv, Wo)
+    fa, fm = ab.layer_forward(x, attn_p, mlp_p, EPS, H, KV, DH, BASE)
+    ba, bm = ab.layer_backward(x, attn_p, mlp_p, EPS, H, KV, DH, BASE, R, (fa, fm))
+    C = 1e-3
+    n, c, new = ab.layer_dp_step({**fa, **ba}, {**fm, **bm}, attn_p, mlp_p, "fgc", 0, C, 0.0, 1.0,
+                                 1, 2)
+    assert c[0] < 1.0
+    old = {"W_q": Wq, "W_k": Wk, "W_v": Wv, "W_o": Wo, "gamma": gamma, "W_gate": mlp_p[1],
+           "W_up": mlp_p[2], "W_down": mlp_p[3], "mlp_gamma": mlp_p[0]}
+    delta = np.concatenate([(old[k_] - new[k_]).ravel() for k_ in old])
+    assert np.isclose(np.linalg.norm(delta), C, rtol=1e-10)
