@@ -29,6 +29,16 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", INCLUDE, "-I", CSRC]
 
+# Per-source additions.  The attention and ghost kernels keep their MFMA
+# accumulators in ordinary VGPRs: left to choose, the compiler puts them in the
+# accumulation registers and then copies values back and forth (about 1200
+# v_accvgpr moves in the attention kernels); in VGPR form there are none and the
+# attention backward runs 12% faster (measured; forward unchanged).
+SOURCE_FLAGS = {
+    "attn_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "mfma_ghost.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def hipcc():
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -39,7 +49,7 @@ def hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + HIP_FLAGS
+    cmd = [hipcc(), "-c", os.path.join(CSRC, src), "-o", obj] + HIP_FLAGS + SOURCE_FLAGS.get(src, [])
     if src.endswith(".cpp"):
         cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + HIP_FLAGS
     if verbose:

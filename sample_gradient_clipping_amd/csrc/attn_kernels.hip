@@ -25,6 +25,7 @@
 // the same row-major tiles through ds_read_b64_tr_b16, whose 16-lane groups read
 // 4 consecutive rows, also at distinct banks.
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -137,6 +138,28 @@ __device__ __forceinline__ void bar() {
   asm volatile("" ::: "memory");
 }
 
+// Max and sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes that
+// hold one query's scores) with the row-swapping permutes: permlane32_swap of a
+// value with itself leaves {x[l], x[l ^ 32]} in the two results at every lane,
+// permlane16_swap {x[l], x[l ^ 16]}.
+__device__ __forceinline__ float max_lanes_xor48(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum_lanes_xor48(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Forward: one workgroup = 128 queries of one head, wave w owns queries
 // 16 w .. + 15; 64-key tiles of K (row-major) and V (row-major, read with
@@ -188,13 +211,16 @@ __global__ void __launch_bounds__(512) k_attn_fwd(const bf16_t* __restrict__ q,
   if (nkt > 1) issue(1);
   if (nkt > 2) issue(2);
 
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // l: this lane's share of the normaliser
   f32x4 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int qlast = qb * kFwdQ + w * 16 + 15;  // the wave's last query
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  // One key tile in LDS stage S (a constant, so that every LDS address below is
+  // a per-lane register plus an immediate).
+  auto tile = [&](int kt, auto stage) {
+    constexpr int S = decltype(stage)::value;
     // this wave's loads of tile kt are done (those of kt + 1, kt + 2 may be in
     // flight); after the barrier every wave's are, and every wave is done with
     // the stage of tile kt - 1, which tile kt + 3 refills
@@ -207,8 +233,8 @@ __global__ void __launch_bounds__(512) k_attn_fwd(const bf16_t* __restrict__ q,
       wait_vm<0>();
     bar();
     if (kt + 3 < nkt) issue(kt + 3);
-    if (kt * kBlk > qlast) continue;  // every key of the tile is after the wave's queries
-    const bf16_t* Ks = &KVs[kt % kFwdStages][0][0];
+    if (kt * kBlk > qlast) return;  // every key of the tile is after the wave's queries
+    const bf16_t* Ks = &KVs[S][0][0];
     const bf16_t* Vs = Ks + kTileElems;
 
     f32x4 s[4];
@@ -233,8 +259,7 @@ __global__ void __launch_bounds__(512) k_attn_fwd(const bf16_t* __restrict__ q,
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_lanes_xor48(mx);  // over the four lanes of this query
     const float mn = fmaxf(m, mx * scale_log2);
     const float alpha = ex2(m - mn);
     float sum = 0.f;
@@ -246,9 +271,7 @@ __global__ void __launch_bounds__(512) k_attn_fwd(const bf16_t* __restrict__ q,
         s[kb][r] = p;
         sum += p;
       }
-    sum += __shfl_xor(sum, 16, 64);
-    sum += __shfl_xor(sum, 32, 64);
-    l = l * alpha + sum;
+    l = l * alpha + sum;  // alpha is the same in the query's four lanes
     m = mn;
     if (__any(alpha != 1.0f)) {  // skipped when no lane's running max moved
 #pragma unroll
@@ -261,7 +284,16 @@ __global__ void __launch_bounds__(512) k_attn_fwd(const bf16_t* __restrict__ q,
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[db] = mma(rd_rm_tr8(Vs, 16 * db, t, lg, li), pb, acc[db]);
     }
+  };
+
+  static_assert(kFwdStages == 4, "the loop below is unrolled over four stages");
+  for (int kt = 0; kt < nkt; kt += 4) {
+    tile(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < nkt) tile(kt + 2, std::integral_constant<int, 2>{});
+    if (kt + 3 < nkt) tile(kt + 3, std::integral_constant<int, 3>{});
   }
+  l = sum_lanes_xor48(l);
 
   const float inv = 1.0f / l;
   bf16_t* orow = o + (static_cast<int64_t>(b) * T + tq) * ldq + h * kDh;
