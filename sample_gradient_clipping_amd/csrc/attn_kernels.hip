@@ -125,6 +125,18 @@ __device__ __forceinline__ void dma16(const bf16_t* gp, uint32_t lds) {
       : "memory");
 }
 
+// One 256-byte global -> LDS DMA instruction: lane i's 4 global bytes land at
+// LDS m0 + 4 i (counted and ordered like dma16).
+__device__ __forceinline__ void dma4(const float* gp, uint32_t lds) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(gp), "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory");
+}
+
 // s_waitcnt with vmcnt = N (other counters unconstrained).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -338,17 +350,21 @@ __global__ void __launch_bounds__(256) k_attn_bwd_dot(const bf16_t* __restrict__
 // dK, dV of 64 keys of one key/value head: wave w owns keys 16 w .. + 15 (the
 // key in the lane, S = Q K^T), and the workgroup walks the group's query heads
 // and, causally, the query blocks from its own on.  The head sums stay in
-// registers: no atomics, a fixed order.
+// registers: no atomics, a fixed order.  Each step's Q and dO tiles (sv-swizzled
+// row-major) and its 64 lse and D values come into LDS by DMA, one step ahead.
+constexpr int kBkvLd = 4 * 64;  // floats per stage: per wave 16 lse, 16 D, 32 unused
+
 __global__ void __launch_bounds__(256) k_attn_bwd_kv(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dvec,
     int T, int H, int KV, float scale_log2, bf16_t* __restrict__ dk, bf16_t* __restrict__ dv) {
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[kBlk * kBlk];
-  __shared__ __attribute__((aligned(16))) bf16_t Ds[kBlk * kBlk];
-  __shared__ float Ls[kBlk], Dd[kBlk];
+  // stage s: Q tile at QDs[s][0], dO tile at QDs[s][1], lse / D at LDs[s]
+  __shared__ __attribute__((aligned(16))) bf16_t QDs[2][2][kTileElems];
+  __shared__ __attribute__((aligned(16))) float LDs[2][kBkvLd];
   const int kbk = blockIdx.x, gkv = blockIdx.y, b = blockIdx.z;
   const int grp = H / KV;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int li = lane & 15, lg = lane >> 4;
   const int64_t ldq = static_cast<int64_t>(H) * kDh, ldk = static_cast<int64_t>(KV) * kDh;
   const int tk = kbk * kBlk + w * 16 + li;  // this lane's key
@@ -358,7 +374,35 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
   const u32x4 kf1 = *reinterpret_cast<const u32x4*>(krow + 32 + 8 * lg);
   const u32x4 vf0 = *reinterpret_cast<const u32x4*>(vrow + 8 * lg);
   const u32x4 vf1 = *reinterpret_cast<const u32x4*>(vrow + 32 + 8 * lg);
+  // Use the per-lane operands before the first DMA, so that the compiler waits
+  // for them here and not, with counts the DMA loads would inflate, in the loop.
+  asm volatile("" ::"v"(kf0), "v"(kf1), "v"(vf0), "v"(vf1));
   constexpr float kLog2e = 1.4426950408889634f;
+
+  // DMA: wave w fills rows 16 w .. 16 w + 15 of the Q and dO tiles (two
+  // instructions each, as in the dQ kernel) and, with one 4-byte-per-lane
+  // instruction, the lse (lanes 0-15) and D (lanes 16-31) of queries
+  // 16 w .. + 15; lanes 32-63 repeat lanes 0-31 into the unused half.
+  const int dr = 16 * w + (lane >> 3), dp = lane & 7;
+  const int64_t qd0 = dr * ldq + 8 * (dp ^ sv(dr));
+  const int l32 = lane & 31;
+  const float* ldsrc = (l32 < 16 ? lse : Dvec) + 16 * w + (l32 & 15);
+  const int nq = T / kBlk - kbk;  // query blocks from the diagonal on
+  const int nit = grp * nq;
+  auto issue = [&](int it) {
+    const int j = it / nq;
+    const int qb = kbk + (it - j * nq);
+    const int h = gkv * grp + j;
+    const int64_t off = (static_cast<int64_t>(b) * T + qb * kBlk) * ldq + h * kDh + qd0;
+    const int st = it & 1;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      dma16(q + off + 8 * u * ldq, lds_addr(&QDs[st][0][(16 * w + 8 * u) * kBlk]));
+      dma16(dO + off + 8 * u * ldq, lds_addr(&QDs[st][1][(16 * w + 8 * u) * kBlk]));
+    }
+    dma4(ldsrc + (static_cast<int64_t>(b) * H + h) * T + qb * kBlk, lds_addr(&LDs[st][64 * w]));
+  };
+  issue(0);
 
   f32x4 adk[4], adv[4];
 #pragma unroll
@@ -367,51 +411,59 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
     adv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int kk = w * 16 + li;  // key within the block
-  for (int j = 0; j < grp; ++j) {
-    const int h = gkv * grp + j;
-    for (int qb = kbk; qb < T / kBlk; ++qb) {
-      __syncthreads();
-      const int64_t qrow0 = static_cast<int64_t>(b) * T + qb * kBlk;
-      stage_v(q + qrow0 * ldq + h * kDh, ldq, Qs);
-      stage_v(dO + qrow0 * ldq + h * kDh, ldq, Ds);
-      if (threadIdx.x < kBlk) {
-        const int64_t si = (static_cast<int64_t>(b) * H + h) * T + qb * kBlk + threadIdx.x;
-        Ls[threadIdx.x] = lse[si] * kLog2e;
-        Dd[threadIdx.x] = Dvec[si];
-      }
-      __syncthreads();
-      f32x4 P[4], dS[4];
+
+  auto step = [&](int it, auto stage) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    // this wave's loads of step it are done; after the barrier every wave's
+    // are, and every wave is done with the stage of step it - 1, which step
+    // it + 1 refills
+    wait_vm<0>();
+    bar();
+    if (it + 1 < nit) issue(it + 1);
+    const bool diag = it % nq == 0;  // the query block of the workgroup's own keys
+    const bf16_t* Qs = &QDs[S][0][0];
+    const bf16_t* Ds = &QDs[S][1][0];
+    f32x4 P[4], dS[4];
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {  // 16-query blocks
-        const int r0 = sb * 16 + li;
-        f32x4 sc = mma(rd16v(Qs, r0, lg), kf0, f32x4{0.f, 0.f, 0.f, 0.f});
-        sc = mma(rd16v(Qs, r0, 4 + lg), kf1, sc);
-        f32x4 dp = mma(rd16v(Ds, r0, lg), vf0, f32x4{0.f, 0.f, 0.f, 0.f});
-        dp = mma(rd16v(Ds, r0, 4 + lg), vf1, dp);
+    for (int sb = 0; sb < 4; ++sb) {  // 16-query blocks
+      const int r0 = sb * 16 + li;
+      f32x4 sc = mma(rd16v(Qs, r0, lg), kf0, f32x4{0.f, 0.f, 0.f, 0.f});
+      sc = mma(rd16v(Qs, r0, 4 + lg), kf1, sc);
+      f32x4 dpv = mma(rd16v(Ds, r0, lg), vf0, f32x4{0.f, 0.f, 0.f, 0.f});
+      dpv = mma(rd16v(Ds, r0, 4 + lg), vf1, dpv);
+      // lse and D of queries 16 sb + 4 lg .. + 3 (loaded by wave sb)
+      const f32x4 L4 = *(const __attribute__((address_space(3))) f32x4*)(&LDs[S][64 * sb + 4 * lg]);
+      const f32x4 D4 =
+          *(const __attribute__((address_space(3))) f32x4*)(&LDs[S][64 * sb + 16 + 4 * lg]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qq = sb * 16 + 4 * lg + r;  // query within the block
-          float p = ex2(fmaf(sc[r], scale_log2, -Ls[qq]));
-          if (qb == kbk && kk > qq) p = 0.f;  // a select, no branch between the MFMAs
-          P[sb][r] = p;
-          dS[sb][r] = p * (dp[r] - Dd[qq]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 pb{pk(P[2 * t][0], P[2 * t][1]), pk(P[2 * t][2], P[2 * t][3]),
-                       pk(P[2 * t + 1][0], P[2 * t + 1][1]), pk(P[2 * t + 1][2], P[2 * t + 1][3])};
-        const u32x4 sbv{pk(dS[2 * t][0], dS[2 * t][1]), pk(dS[2 * t][2], dS[2 * t][3]),
-                        pk(dS[2 * t + 1][0], dS[2 * t + 1][1]),
-                        pk(dS[2 * t + 1][2], dS[2 * t + 1][3])};
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          adv[db] = mma(rd_rm_tr8(Ds, 16 * db, t, lg, li), pb, adv[db]);
-          adk[db] = mma(rd_rm_tr8(Qs, 16 * db, t, lg, li), sbv, adk[db]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int qq = sb * 16 + 4 * lg + r;  // query within the block
+        float p = ex2(fmaf(sc[r], scale_log2, -L4[r] * kLog2e));
+        if (diag && kk > qq) p = 0.f;  // a select, no branch between the MFMAs
+        P[sb][r] = p;
+        dS[sb][r] = p * (dpv[r] - D4[r]);
       }
     }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 pb{pk(P[2 * t][0], P[2 * t][1]), pk(P[2 * t][2], P[2 * t][3]),
+                     pk(P[2 * t + 1][0], P[2 * t + 1][1]), pk(P[2 * t + 1][2], P[2 * t + 1][3])};
+      const u32x4 sbv{pk(dS[2 * t][0], dS[2 * t][1]), pk(dS[2 * t][2], dS[2 * t][3]),
+                      pk(dS[2 * t + 1][0], dS[2 * t + 1][1]),
+                      pk(dS[2 * t + 1][2], dS[2 * t + 1][3])};
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        adv[db] = mma(rd_rm_tr8(Ds, 16 * db, t, lg, li), pb, adv[db]);
+        adk[db] = mma(rd_rm_tr8(Qs, 16 * db, t, lg, li), sbv, adk[db]);
+      }
+    }
+  };
+
+  for (int it = 0; it < nit; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < nit) step(it + 1, std::integral_constant<int, 1>{});
   }
+
   bf16_t* dkrow = dk + (static_cast<int64_t>(b) * T + tk) * ldk + gkv * kDh;
   bf16_t* dvrow = dv + (static_cast<int64_t>(b) * T + tk) * ldk + gkv * kDh;
 #pragma unroll
@@ -424,16 +476,24 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
 }
 
 // dQ of 64 queries of one head: wave w owns queries 16 w .. + 15 (the query in
-// the lane, S^T = K Q^T as in the forward); key tiles 0 .. the diagonal.
+// the lane, S^T = K Q^T as in the forward); key tiles 0 .. the diagonal, K and V
+// (both sv-swizzled row-major) brought into LDS by DMA, kBqStages deep.
+#ifndef DPRC_BQ_STAGES
+#define DPRC_BQ_STAGES 2
+#endif
+constexpr int kBqStages = DPRC_BQ_STAGES;
+static_assert(kBqStages == 2 || kBqStages == 3, "two or three LDS stages");
+
 __global__ void __launch_bounds__(256) k_attn_bwd_q(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dvec,
     int T, int H, int KV, float scale_log2, bf16_t* __restrict__ dq) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kBlk * kBlk];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[kBlk * kBlk];
+  // stage s: K tile at KVs[s][0], V tile at KVs[s][1]
+  __shared__ __attribute__((aligned(16))) bf16_t KVs[kBqStages][2][kTileElems];
   const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int gkv = h / (H / KV);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int li = lane & 15, lg = lane >> 4;
   const int64_t ldq = static_cast<int64_t>(H) * kDh, ldk = static_cast<int64_t>(KV) * kDh;
   const int tq = qb * kBlk + w * 16 + li;
@@ -445,30 +505,61 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
   const u32x4 df1 = *reinterpret_cast<const u32x4*>(drow + 32 + 8 * lg);
   const int64_t si = (static_cast<int64_t>(b) * H + h) * T + tq;
   const float lq = lse[si] * 1.4426950408889634f, dd = Dvec[si];
+  // Use the per-lane operands before the first DMA, so that the compiler waits
+  // for them here and not, with counts the DMA loads would inflate, in the loop.
+  asm volatile("" ::"v"(qf0), "v"(qf1), "v"(df0), "v"(df1), "v"(lq), "v"(dd));
+
+  // DMA: wave w fills rows 16 w .. 16 w + 15 of the K and V tiles, two
+  // instructions each; lane i -> row 16 w + 8 u + i / 8, LDS chunk i % 8, which
+  // holds global chunk (i % 8) ^ sv(row) (sv depends on the row modulo 8 only).
+  const int dr = 16 * w + (lane >> 3), dp = lane & 7;
+  const int64_t kv0 = static_cast<int64_t>(b) * T * ldk + gkv * kDh + dr * ldk + 8 * (dp ^ sv(dr));
+  const bf16_t* kg = k + kv0;
+  const bf16_t* vg = v + kv0;
+  const int nkt = qb + 1;
+  auto issue = [&](int kt) {
+    const int64_t off = static_cast<int64_t>(kt) * kBlk * ldk;
+    bf16_t* st = &KVs[kt % kBqStages][0][0];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      dma16(kg + off + 8 * u * ldk, lds_addr(st + (16 * w + 8 * u) * kBlk));
+      dma16(vg + off + 8 * u * ldk, lds_addr(st + kTileElems + (16 * w + 8 * u) * kBlk));
+    }
+  };
+  issue(0);
+  if (kBqStages == 3 && nkt > 1) issue(1);
 
   f32x4 adq[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) adq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int qq = w * 16 + li;
-  for (int kt = 0; kt <= qb; ++kt) {
-    __syncthreads();
-    const int64_t krow0 = static_cast<int64_t>(b) * T + kt * kBlk;
-    stage_v(k + krow0 * ldk + gkv * kDh, ldk, Ks);
-    stage_v(v + krow0 * ldk + gkv * kDh, ldk, Vs);
-    __syncthreads();
+
+  auto tile = [&](int kt, auto stage) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    // this wave's loads of tile kt are done (those of kt + 1 may be in flight
+    // with three stages); after the barrier every wave's are, and every wave is
+    // done with the stage of tile kt - 1, which tile kt + kBqStages - 1 refills
+    if (kBqStages == 3 && kt + 1 < nkt)
+      wait_vm<4>();
+    else
+      wait_vm<0>();
+    bar();
+    if (kt + kBqStages - 1 < nkt) issue(kt + kBqStages - 1);
+    const bf16_t* Ks = &KVs[S][0][0];
+    const bf16_t* Vs = Ks + kTileElems;
     f32x4 dS[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int r0 = kb * 16 + li;
       f32x4 st = mma(rd16v(Ks, r0, lg), qf0, f32x4{0.f, 0.f, 0.f, 0.f});
       st = mma(rd16v(Ks, r0, 4 + lg), qf1, st);
-      f32x4 dp = mma(rd16v(Vs, r0, lg), df0, f32x4{0.f, 0.f, 0.f, 0.f});
-      dp = mma(rd16v(Vs, r0, 4 + lg), df1, dp);
+      f32x4 dpv = mma(rd16v(Vs, r0, lg), df0, f32x4{0.f, 0.f, 0.f, 0.f});
+      dpv = mma(rd16v(Vs, r0, 4 + lg), df1, dpv);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float p = ex2(fmaf(st[r], scale_log2, -lq));
         if (kt == qb && kb * 16 + 4 * lg + r > qq) p = 0.f;  // a select, no branch
-        dS[kb][r] = p * (dp[r] - dd);
+        dS[kb][r] = p * (dpv[r] - dd);
       }
     }
 #pragma unroll
@@ -478,7 +569,15 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
 #pragma unroll
       for (int db = 0; db < 4; ++db) adq[db] = mma(rd_rm_tr8(Ks, 16 * db, t, lg, li), sbv, adq[db]);
     }
+  };
+
+  for (int kt = 0; kt < nkt; kt += kBqStages) {
+    tile(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
+    if constexpr (kBqStages == 3)
+      if (kt + 2 < nkt) tile(kt + 2, std::integral_constant<int, 2>{});
   }
+
   bf16_t* dqrow = dq + (static_cast<int64_t>(b) * T + tq) * ldq + h * kDh;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
