@@ -150,6 +150,26 @@ __device__ __forceinline__ void bar() {
   asm volatile("" ::: "memory");
 }
 
+// Workgroup order.  Causal attention gives the workgroups of one launch very
+// different amounts of work; dispatching the largest first keeps the last
+// dispatched ones short, so the CUs run out of work nearly together.  Both map
+// the flat workgroup index (x fastest) to (block, head, sample).
+__device__ __forceinline__ void heavy_first_q(int nx, int ny, int nz, int& qb, int& h, int& b) {
+  const int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  h = id % ny;
+  const int rest = id / ny;
+  b = rest % nz;
+  qb = nx - 1 - rest / nz;
+}
+
+__device__ __forceinline__ void heavy_first_kv(int nx, int ny, int nz, int& kbk, int& g, int& b) {
+  const int id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  g = id % ny;
+  const int rest = id / ny;
+  b = rest % nz;
+  kbk = rest / nz;
+}
+
 // Max and sum over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes that
 // hold one query's scores) with the row-swapping permutes: permlane32_swap of a
 // value with itself leaves {x[l], x[l ^ 32]} in the two results at every lane,
@@ -190,7 +210,10 @@ __global__ void __launch_bounds__(512) k_attn_fwd(const bf16_t* __restrict__ q,
                                                   float* __restrict__ lse) {
   // stage s: K tile at KV_s[s][0], V tile at KV_s[s][1]
   __shared__ __attribute__((aligned(16))) bf16_t KVs[kFwdStages][2][kTileElems];
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Heaviest work first: the workgroups of the last query block (the most key
+  // tiles) of every (sample, head) are dispatched first, the first block's last.
+  int qb, h, b;
+  heavy_first_q(gridDim.x, gridDim.y, gridDim.z, qb, h, b);
   const int gkv = h / (H / KV);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -361,7 +384,10 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
   // stage s: Q tile at QDs[s][0], dO tile at QDs[s][1], lse / D at LDs[s]
   __shared__ __attribute__((aligned(16))) bf16_t QDs[2][2][kTileElems];
   __shared__ __attribute__((aligned(16))) float LDs[2][kBkvLd];
-  const int kbk = blockIdx.x, gkv = blockIdx.y, b = blockIdx.z;
+  // Heaviest work first: the key blocks at the start of the sequence (the most
+  // query blocks after them) of every (sample, head group) are dispatched first.
+  int kbk, gkv, b;
+  heavy_first_kv(gridDim.x, gridDim.y, gridDim.z, kbk, gkv, b);
   const int grp = H / KV;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
@@ -490,7 +516,10 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
     int T, int H, int KV, float scale_log2, bf16_t* __restrict__ dq) {
   // stage s: K tile at KVs[s][0], V tile at KVs[s][1]
   __shared__ __attribute__((aligned(16))) bf16_t KVs[kBqStages][2][kTileElems];
-  const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // Heaviest work first: the workgroups of the last query block (the most key
+  // tiles) of every (sample, head) are dispatched first, the first block's last.
+  int qb, h, b;
+  heavy_first_q(gridDim.x, gridDim.y, gridDim.z, qb, h, b);
   const int gkv = h / (H / KV);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
