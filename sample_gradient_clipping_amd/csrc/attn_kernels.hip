@@ -501,21 +501,18 @@ __global__ void __launch_bounds__(256) k_attn_bwd_kv(
   }
 }
 
-// dQ of 64 queries of one head: wave w owns queries 16 w .. + 15 (the query in
-// the lane, S^T = K Q^T as in the forward); key tiles 0 .. the diagonal, K and V
-// (both sv-swizzled row-major) brought into LDS by DMA, kBqStages deep.
-#ifndef DPRC_BQ_STAGES
-#define DPRC_BQ_STAGES 2
-#endif
-constexpr int kBqStages = DPRC_BQ_STAGES;
-static_assert(kBqStages == 2 || kBqStages == 3, "two or three LDS stages");
+// dQ of 128 queries of one head: wave w (of 8) owns queries 16 w .. + 15 (the
+// query in the lane, S^T = K Q^T as in the forward); key tiles 0 .. the
+// diagonal, K and V (both sv-swizzled row-major) brought into LDS by DMA, double
+// buffered; each tile serves the workgroup's 128 queries.
+constexpr int kBqQ = 128;  // queries per workgroup
 
-__global__ void __launch_bounds__(256) k_attn_bwd_q(
+__global__ void __launch_bounds__(512) k_attn_bwd_q(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const bf16_t* __restrict__ dO, const float* __restrict__ lse, const float* __restrict__ Dvec,
     int T, int H, int KV, float scale_log2, bf16_t* __restrict__ dq) {
   // stage s: K tile at KVs[s][0], V tile at KVs[s][1]
-  __shared__ __attribute__((aligned(16))) bf16_t KVs[kBqStages][2][kTileElems];
+  __shared__ __attribute__((aligned(16))) bf16_t KVs[2][2][kTileElems];
   // Heaviest work first: the workgroups of the last query block (the most key
   // tiles) of every (sample, head) are dispatched first, the first block's last.
   int qb, h, b;
@@ -525,7 +522,8 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int li = lane & 15, lg = lane >> 4;
   const int64_t ldq = static_cast<int64_t>(H) * kDh, ldk = static_cast<int64_t>(KV) * kDh;
-  const int tq = qb * kBlk + w * 16 + li;
+  const int qfirst = qb * kBqQ + w * 16;  // the wave's first query
+  const int tq = qfirst + li;
   const bf16_t* qrow = q + (static_cast<int64_t>(b) * T + tq) * ldq + h * kDh;
   const bf16_t* drow = dO + (static_cast<int64_t>(b) * T + tq) * ldq + h * kDh;
   const u32x4 qf0 = *reinterpret_cast<const u32x4*>(qrow + 8 * lg);
@@ -538,42 +536,37 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
   // for them here and not, with counts the DMA loads would inflate, in the loop.
   asm volatile("" ::"v"(qf0), "v"(qf1), "v"(df0), "v"(df1), "v"(lq), "v"(dd));
 
-  // DMA: wave w fills rows 16 w .. 16 w + 15 of the K and V tiles, two
-  // instructions each; lane i -> row 16 w + 8 u + i / 8, LDS chunk i % 8, which
-  // holds global chunk (i % 8) ^ sv(row) (sv depends on the row modulo 8 only).
-  const int dr = 16 * w + (lane >> 3), dp = lane & 7;
+  // DMA: wave w fills rows 8 w .. 8 w + 7 of the K and V tiles, one instruction
+  // each; lane i -> row 8 w + i / 8, LDS chunk i % 8, which holds global chunk
+  // (i % 8) ^ sv(row).
+  const int dr = 8 * w + (lane >> 3), dp = lane & 7;
   const int64_t kv0 = static_cast<int64_t>(b) * T * ldk + gkv * kDh + dr * ldk + 8 * (dp ^ sv(dr));
   const bf16_t* kg = k + kv0;
   const bf16_t* vg = v + kv0;
-  const int nkt = qb + 1;
+  const int nkt = (qb * kBqQ + kBqQ) / kBlk;  // key tiles up to the diagonal
   auto issue = [&](int kt) {
     const int64_t off = static_cast<int64_t>(kt) * kBlk * ldk;
-    bf16_t* st = &KVs[kt % kBqStages][0][0];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      dma16(kg + off + 8 * u * ldk, lds_addr(st + (16 * w + 8 * u) * kBlk));
-      dma16(vg + off + 8 * u * ldk, lds_addr(st + kTileElems + (16 * w + 8 * u) * kBlk));
-    }
+    bf16_t* st = &KVs[kt & 1][0][0];
+    dma16(kg + off, lds_addr(st + 8 * w * kBlk));
+    dma16(vg + off, lds_addr(st + kTileElems + 8 * w * kBlk));
   };
   issue(0);
-  if (kBqStages == 3 && nkt > 1) issue(1);
 
   f32x4 adq[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) adq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int qq = w * 16 + li;
+  const int qlast = qfirst + 15;
 
   auto tile = [&](int kt, auto stage) __attribute__((always_inline)) {
     constexpr int S = decltype(stage)::value;
-    // this wave's loads of tile kt are done (those of kt + 1 may be in flight
-    // with three stages); after the barrier every wave's are, and every wave is
-    // done with the stage of tile kt - 1, which tile kt + kBqStages - 1 refills
-    if (kBqStages == 3 && kt + 1 < nkt)
-      wait_vm<4>();
-    else
-      wait_vm<0>();
+    // this wave's loads of tile kt are done; after the barrier every wave's are,
+    // and every wave is done with the stage of tile kt - 1, which tile kt + 1
+    // refills
+    wait_vm<0>();
     bar();
-    if (kt + kBqStages - 1 < nkt) issue(kt + kBqStages - 1);
+    if (kt + 1 < nkt) issue(kt + 1);
+    if (kt * kBlk > qlast) return;  // every key of the tile is after the wave's queries
+    const bool diag = (kt + 1) * kBlk > qfirst;  // some key after the wave's first query
     const bf16_t* Ks = &KVs[S][0][0];
     const bf16_t* Vs = Ks + kTileElems;
     f32x4 dS[4];
@@ -587,7 +580,7 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float p = ex2(fmaf(st[r], scale_log2, -lq));
-        if (kt == qb && kb * 16 + 4 * lg + r > qq) p = 0.f;  // a select, no branch
+        if (diag && kt * kBlk + kb * 16 + 4 * lg + r > tq) p = 0.f;  // a select, no branch
         dS[kb][r] = p * (dpv[r] - dd);
       }
     }
@@ -600,11 +593,9 @@ __global__ void __launch_bounds__(256) k_attn_bwd_q(
     }
   };
 
-  for (int kt = 0; kt < nkt; kt += kBqStages) {
+  for (int kt = 0; kt < nkt; kt += 2) {  // nkt is even
     tile(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < nkt) tile(kt + 1, std::integral_constant<int, 1>{});
-    if constexpr (kBqStages == 3)
-      if (kt + 2 < nkt) tile(kt + 2, std::integral_constant<int, 2>{});
+    tile(kt + 1, std::integral_constant<int, 1>{});
   }
 
   bf16_t* dqrow = dq + (static_cast<int64_t>(b) * T + tq) * ldq + h * kDh;
@@ -700,7 +691,7 @@ hipError_t launch_attn_bwd(const bf16_t* q, const bf16_t* k, const bf16_t* v, co
   const float scale_log2 = 1.4426950408889634f / 8.0f;
   hipLaunchKernelGGL(k_attn_bwd_kv, dim3(T / kBlk, KV, B), dim3(256), 0, s, q, k, v, dO, lse,
                      Dvec, T, H, KV, scale_log2, dk, dv);
-  hipLaunchKernelGGL(k_attn_bwd_q, dim3(T / kBlk, H, B), dim3(256), 0, s, q, k, v, dO, lse, Dvec,
+  hipLaunchKernelGGL(k_attn_bwd_q, dim3(T / kBqQ, H, B), dim3(512), 0, s, q, k, v, dO, lse, Dvec,
                      T, H, KV, scale_log2, dq);
   return hipGetLastError();
 }
