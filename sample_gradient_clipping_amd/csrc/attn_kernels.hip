@@ -195,8 +195,9 @@ __device__ __forceinline__ float sum_lanes_xor48(float x) {
 // ---------------------------------------------------------------------------
 // Forward: one workgroup = 128 queries of one head, wave w owns queries
 // 16 w .. + 15; 64-key tiles of K (row-major) and V (row-major, read with
-// transposing reads), the next tile's loads issued before the current tile's
-// MFMAs.  Online softmax in the log2 domain.
+// transposing reads) come into LDS by DMA three tiles ahead of the one in use.
+// Online softmax in the log2 domain; each lane keeps its own share of a
+// query's normaliser, summed over the query's four lanes after the loop.
 // ---------------------------------------------------------------------------
 constexpr int kFwdQ = 128;
 constexpr int kFwdStages = 4;
