@@ -610,41 +610,61 @@ __global__ void __launch_bounds__(512) k_attn_bwd_q(
 // ---------------------------------------------------------------------------
 // RoPE in place on x [B T][nh * 64]: in each head the pair (i, i + 32) is
 // rotated by pos * base^(-i / 32), pos = row % T; the angle and its sine and
-// cosine are taken in fp64.  One thread per (row, head, 8 pairs).
+// cosine are taken in fp64.  A block takes 8 rows: first one thread per (row,
+// pair) forms the row's 32 cosines and sines (shared by all heads) in LDS, then
+// one thread per (row, head, 8 pairs) rotates.
 // ---------------------------------------------------------------------------
+constexpr int kRopeRows = 8;  // rows per block step; 8 x 32 angles = one per thread
+
 __global__ void __launch_bounds__(256) k_rope(bf16_t* __restrict__ x, int64_t M, int T, int nh,
                                               double log_base, int inverse) {
-  const int64_t n = M * nh * 4;
-  for (int64_t id = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; id < n;
-       id += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t row = id / (nh * 4);
-    const int rem = static_cast<int>(id - row * nh * 4);
-    const int hd = rem >> 2, i0 = (rem & 3) * 8;
-    const double pos = static_cast<double>(row % T);
-    bf16_t* p = x + row * nh * kDh + hd * kDh;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p + i0);
-    const u32x4 c = *reinterpret_cast<const u32x4*>(p + 32 + i0);
-    float x1[8], x2[8], y1[8], y2[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x1[2 * e] = __uint_as_float(a[e] << 16);
-      x1[2 * e + 1] = __uint_as_float(a[e] & 0xFFFF0000u);
-      x2[2 * e] = __uint_as_float(c[e] << 16);
-      x2[2 * e + 1] = __uint_as_float(c[e] & 0xFFFF0000u);
+  __shared__ float cs_l[kRopeRows][32], sn_l[kRopeRows][32];
+  const int64_t ngroups = (M + kRopeRows - 1) / kRopeRows;
+  const int items = kRopeRows * nh * 4;
+  for (int64_t rg = blockIdx.x; rg < ngroups; rg += gridDim.x) {
+    const int64_t row0 = rg * kRopeRows;
+    {
+      const int r = threadIdx.x >> 5, i = threadIdx.x & 31;
+      const int64_t row = row0 + r;
+      if (row < M) {
+        const double pos = static_cast<double>(row % T);
+        const double ang = pos * exp(-static_cast<double>(i) / 32.0 * log_base);
+        double sd, cd;
+        sincos(ang, &sd, &cd);
+        cs_l[r][i] = static_cast<float>(cd);
+        sn_l[r][i] = static_cast<float>(inverse ? -sd : sd);
+      }
     }
+    __syncthreads();
+    for (int it = threadIdx.x; it < items; it += blockDim.x) {
+      const int r = it / (nh * 4);
+      const int rem = it - r * nh * 4;
+      const int64_t row = row0 + r;
+      if (row >= M) continue;
+      const int hd = rem >> 2, i0 = (rem & 3) * 8;
+      bf16_t* p = x + row * nh * kDh + hd * kDh;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(p + i0);
+      const u32x4 c = *reinterpret_cast<const u32x4*>(p + 32 + i0);
+      float x1[8], x2[8], y1[8], y2[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double ang = pos * exp(-static_cast<double>(i0 + e) / 32.0 * log_base);
-      double sd, cd;
-      sincos(ang, &sd, &cd);
-      const float cs = static_cast<float>(cd), sn = static_cast<float>(inverse ? -sd : sd);
-      y1[e] = x1[e] * cs - x2[e] * sn;
-      y2[e] = x2[e] * cs + x1[e] * sn;
+      for (int e2 = 0; e2 < 4; ++e2) {
+        x1[2 * e2] = __uint_as_float(a[e2] << 16);
+        x1[2 * e2 + 1] = __uint_as_float(a[e2] & 0xFFFF0000u);
+        x2[2 * e2] = __uint_as_float(c[e2] << 16);
+        x2[2 * e2 + 1] = __uint_as_float(c[e2] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {
+        const float cs = cs_l[r][i0 + e2], sn = sn_l[r][i0 + e2];
+        y1[e2] = x1[e2] * cs - x2[e2] * sn;
+        y2[e2] = x2[e2] * cs + x1[e2] * sn;
+      }
+      *reinterpret_cast<u32x4*>(p + i0) =
+          u32x4{pk(y1[0], y1[1]), pk(y1[2], y1[3]), pk(y1[4], y1[5]), pk(y1[6], y1[7])};
+      *reinterpret_cast<u32x4*>(p + 32 + i0) =
+          u32x4{pk(y2[0], y2[1]), pk(y2[2], y2[3]), pk(y2[4], y2[5]), pk(y2[6], y2[7])};
     }
-    *reinterpret_cast<u32x4*>(p + i0) =
-        u32x4{pk(y1[0], y1[1]), pk(y1[2], y1[3]), pk(y1[4], y1[5]), pk(y1[6], y1[7])};
-    *reinterpret_cast<u32x4*>(p + 32 + i0) =
-        u32x4{pk(y2[0], y2[1]), pk(y2[2], y2[3]), pk(y2[4], y2[5]), pk(y2[6], y2[7])};
+    __syncthreads();  // the angles of this step are read before the next step writes
   }
 }
 
@@ -658,8 +678,8 @@ hipError_t launch_rope(bf16_t* x, int64_t M, int T, int nh, double base, bool in
                        hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (T <= 0 || nh <= 0 || !(base > 1.0)) return hipErrorInvalidValue;
-  const int64_t n = M * nh * 4;
-  const int64_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+  const int64_t groups = (M + kRopeRows - 1) / kRopeRows;
+  const int64_t blocks = groups < 8192 ? groups : 8192;
   hipLaunchKernelGGL(k_rope, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, x, M, T, nh,
                      std::log(base), inverse ? 1 : 0);
   return hipGetLastError();
