@@ -437,6 +437,75 @@ def attn_block_timing(dp, wl, dev, d=2048, H=32, KV=8, k=32, reps=5):
             "block_step_tokens_per_s": M / (t[5] * 1e-3)}
 
 
+def layer_timing(dp, wl, dev, d=2048, f=8192, H=32, KV=8, k=32, reps=3):
+    """One DP-SGD-RC step of a whole Llama-3.2-1B-shaped decoder layer at the
+    workload's B and T: the attention block's forward pass feeding the MLP
+    block's, backward pass 1 through both (the MLP block's dL/d(input) is the
+    attention block's output gradient), then Hutch norms of the seven linears and
+    the two gains' exact norms summed per sample, one clip factor per sample,
+    and the clipped sums, noise and updates of all eleven parameters."""
+    import torch
+    from sample_gradient_clipping_amd.inputs import mlp_block_inputs_device
+    B, T = wl.B, wl.T
+    M = B * T
+    x, g_mlp, th_mlp, R = mlp_block_inputs_device(B, T, d, f, 7171, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7272)
+
+    def randn(*shape):
+        return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+
+    g_attn = 1.0 + 0.1 * randn(d)
+    thetas = {"W_q": 0.02 * randn(64 * H, d), "W_k": 0.02 * randn(64 * KV, d),
+              "W_v": 0.02 * randn(64 * KV, d), "W_o": 0.02 * randn(d, 64 * H), **th_mlp}
+    Wb = {name: dp.dp_weights_bf16(t) for name, t in thetas.items()}
+    a_acts, a_grads, m_acts, m_grads = {}, {}, {}, {}
+    ws = torch.empty(dp.load_library().dp_attn_backward_workspace(B, T, H), dtype=torch.uint8,
+                     device=dev)
+    n = torch.zeros(B, dtype=torch.float32, device=dev)
+    va = torch.empty(B, d, dtype=torch.float32, device=dev)
+    vm = torch.empty(B, d, dtype=torch.float32, device=dev)
+    ids = {"W_q": 0, "W_k": 1, "W_v": 2, "W_o": 3, "gamma": 4, "W_gate": 5, "W_up": 6,
+           "W_down": 7, "mlp_gamma": 8}
+
+    def step(it):
+        dp.dp_attn_forward(x, g_attn, Wb["W_q"][0], Wb["W_k"][0], Wb["W_v"][0], Wb["W_o"][0], H,
+                           KV, acts=a_acts)
+        h1 = a_acts["out"]
+        dp.dp_mlp_forward(h1, g_mlp, Wb["W_gate"][0], Wb["W_up"][0], Wb["W_down"][0], acts=m_acts)
+        dp.dp_mlp_backward(h1, m_acts["rstd"], g_mlp, m_acts["g"], m_acts["u"], Wb["W_gate"][1],
+                           Wb["W_up"][1], Wb["W_down"][1], R, grads=m_grads)
+        dp.dp_attn_backward(x, a_acts, g_attn, Wb["W_q"][1], Wb["W_k"][1], Wb["W_v"][1],
+                            Wb["W_o"][1], m_grads["dx"], H, KV, grads=a_grads, ws=ws)
+        lin = {"W_q": (a_acts["y"], a_grads["G_q"]), "W_k": (a_acts["y"], a_grads["G_k"]),
+               "W_v": (a_acts["y"], a_grads["G_v"]), "W_o": (a_acts["o"], m_grads["dx"]),
+               "W_gate": (m_acts["y"], m_grads["G_gate"]), "W_up": (m_acts["y"], m_grads["G_up"]),
+               "W_down": (m_acts["h"], R)}
+        dp.dp_rmsnorm_norm(a_acts["xhat"], a_grads["dy"], n, v=va)
+        dp.dp_rmsnorm_norm(m_acts["xhat"], m_grads["dy"], n, v=vm, flags=dp.DP_ACCUMULATE)
+        for name, (A, G) in lin.items():
+            dp.dp_norm_est("hutch", A, G, k, 1100 + it, ids[name], n, flags=dp.DP_ACCUMULATE)
+        for name, (A, G) in lin.items():
+            dp.dp_clip_aggregate_update(A, G, n, 1.0, 1.0, 1e-4, 2100 + it, ids[name],
+                                        thetas[name])
+        dp.dp_rmsnorm_clip_aggregate_update(va, n, 1.0, 1.0, 1e-4, 2100 + it, ids["gamma"], g_attn)
+        dp.dp_rmsnorm_clip_aggregate_update(vm, n, 1.0, 1.0, 1e-4, 2100 + it, ids["mlp_gamma"],
+                                            g_mlp)
+
+    step(0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for it in range(reps):
+        step(it + 1)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps
+    del a_acts, a_grads, m_acts, m_grads
+    return {"B": B, "T": T, "d": d, "f": f, "H": H, "KV": KV, "k": k, "method": "hutch",
+            "parameters": 11, "layer_step_ms": t, "layer_step_tokens_per_s": M / (t * 1e-3)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -619,7 +688,7 @@ def main():
             f"{kv['GBps']:8.1f} GB/s  {kv.get('TFLOPs', 0):8.1f} TF/s  frac {kv['frac']:.3f}  "
             f"share {kv['share_of_step']:.2f}")
 
-    accuracy = sampler = rms = emb = mlp = attn = None
+    accuracy = sampler = rms = emb = mlp = attn = layer = None
     if not args.only_step:
         accuracy = estimator_accuracy(dp, wl, inputs[0][0], dev, rademacher=args.rademacher)
         log(f"[bench] estimator accuracy {accuracy}")
@@ -636,6 +705,9 @@ def main():
         torch.cuda.empty_cache()
         attn = attn_block_timing(dp, wl, dev) if wl.dtype == "bf16" and wl.T % 128 == 0 else None
         log(f"[bench] attention block {attn}")
+        torch.cuda.empty_cache()
+        layer = layer_timing(dp, wl, dev) if wl.dtype == "bf16" and wl.T % 128 == 0 else None
+        log(f"[bench] decoder layer {layer}")
 
     cpu = None
     if not args.no_cpu_baseline and not args.only_step:
@@ -660,6 +732,7 @@ def main():
         "embedding": emb,
         "mlp_block": mlp,
         "attn_block": attn,
+        "decoder_layer": layer,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
