@@ -263,31 +263,49 @@ __global__ void __launch_bounds__(256) k_frob_finish(const float* __restrict__ Z
   const int E4 = kMfmaProbeCols * W / 4;
   const float4* zb = reinterpret_cast<const float4*>(Zp) + static_cast<int64_t>(b) * nsplit * E4;
   const int u1 = (chunk + 1) * kFrobPer < E4 ? (chunk + 1) * kFrobPer : E4;
-  double acc = 0.0;
-  for (int u = chunk * kFrobPer + threadIdx.x; u < u1; u += blockDim.x) {
-    const int j = (4 * u) / W;
-    const float w = j < n0 ? w0 : (j < n0 + n1 ? w1 : 0.f);
-    if (w == 0.f) continue;
-    float4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
-      float4 v[8];
+  // The thread's kFrobPer / 256 = 2 positions, every split's loads of both in
+  // flight together (positions past the end read the last one, in bounds, and
+  // count zero).
+  static_assert(kFrobPer == 2 * 256, "two positions per thread of a 256-thread block");
+  int u[2];
+  bool in[2];
+  float4 z[2];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int sp = s0 + i < nsplit ? s0 + i : nsplit - 1;
-        v[i] = zb[static_cast<int64_t>(sp) * E4 + u];
-      }
+  for (int q = 0; q < 2; ++q) {
+    const int uq = chunk * kFrobPer + threadIdx.x + 256 * q;
+    in[q] = uq < u1;
+    u[q] = in[q] ? uq : u1 - 1;
+    z[q] = float4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int s0 = 0; s0 < nsplit; s0 += 4) {
+    float4 v[2][4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (s0 + i < nsplit) {
-          z.x += v[i].x;
-          z.y += v[i].y;
-          z.z += v[i].z;
-          z.w += v[i].w;
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int sp = s0 + i < nsplit ? s0 + i : nsplit - 1;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) v[q][i] = zb[static_cast<int64_t>(sp) * E4 + u[q]];
     }
-    acc += static_cast<double>(w) *
-           (static_cast<double>(z.x) * z.x + static_cast<double>(z.y) * z.y +
-            static_cast<double>(z.z) * z.z + static_cast<double>(z.w) * z.w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (s0 + i < nsplit) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          z[q].x += v[q][i].x;
+          z[q].y += v[q][i].y;
+          z[q].z += v[q][i].z;
+          z[q].w += v[q][i].w;
+        }
+      }
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int j = (4 * u[q]) / W;
+    const float w = j < n0 ? w0 : (j < n0 + n1 ? w1 : 0.f);
+    if (in[q] && w != 0.f)
+      acc += static_cast<double>(w) *
+             (static_cast<double>(z[q].x) * z[q].x + static_cast<double>(z[q].y) * z[q].y +
+              static_cast<double>(z[q].z) * z[q].z + static_cast<double>(z[q].w) * z[q].w);
   }
   acc = block_sum_d(acc, red);
   double* pb = part + static_cast<int64_t>(b) * nchunk;
