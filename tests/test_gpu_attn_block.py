@@ -78,7 +78,7 @@ def _attn_ref_bound(q, k, v, H, KV, o_ref, lse_ref):
     return pv.reshape(T, H * 64)
 
 
-@pytest.mark.parametrize("B,T,H,KV", [(2, 128, 8, 2), (1, 128, 4, 4), (2, 384, 4, 1)])
+@pytest.mark.parametrize("B,T,H,KV", [(2, 128, 8, 2), (1, 128, 4, 4), (2, 384, 4, 1), (1, 640, 32, 8)])
 def test_attention_forward(dev, B, T, H, KV):
     r = np.random.default_rng(T * 3 + H)
     q = _rand_bf16(r, (B, T, 64 * H), 0.5)
@@ -143,7 +143,7 @@ def test_attn_block_forward(dev, B, T, d, H, KV):
     assert np.all(np.abs(got["lse"] - ref["lse"]) <= 2e-2 * (1 + np.abs(ref["lse"])))
 
 
-@pytest.mark.parametrize("B,T,H,KV", [(2, 128, 8, 2), (1, 128, 4, 4), (2, 384, 4, 1)])
+@pytest.mark.parametrize("B,T,H,KV", [(2, 128, 8, 2), (1, 128, 4, 4), (2, 384, 4, 1), (1, 640, 32, 8)])
 def test_attention_backward(dev, B, T, H, KV):
     r = np.random.default_rng(T * 5 + H)
     q = _rand_bf16(r, (B, T, 64 * H), 0.5).to(dev)
