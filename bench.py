@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="attn_proj_b8_t4096_d2048")
+    ap.add_argument("--workload", default="llama1b_stack_b8_t4096")
     ap.add_argument("--method", default=None, help="override the workload's estimator")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -184,6 +184,75 @@ def estimator_accuracy(dp, wl, layer_inputs, dev, nseeds=8, rademacher=False):
         e = torch.stack(errs)
         out[f"{m}_rel_rms"] = float(torch.sqrt(torch.mean(e * e)))
         out[f"{m}_us_per_call"] = ms / nseeds * 1e3
+    return out
+
+
+def estimator_costs(dp, dev, reps=5):
+    """Time and device memory of every estimator on one layer, outside the timed
+    steps: the long-context layer (B 2, T 16384, d 2048, p 8192) for ghost-exact,
+    Hutch (k 32), Hutch++ (k 32) and FGC, and the MLP up projection (B 8,
+    T 4096, d 2048, p 8192) for the Hutch / Hutch++ latency ratio.
+
+    Memory per estimator: the library allocates nothing, so a call's device
+    memory beyond its inputs and n is its workspace (the *_workspace query);
+    ``peak_bytes_measured`` is torch's peak-allocation increase over a call
+    with that workspace allocated inside the measured window.  Beside them the
+    summary's memory accounting (section 主要な貢献, 1. 複雑性の削減):
+    O(B k T + k p) for randomized clipping, O(B min(d^2, T^2)) for the exact
+    methods, here as fp32 bytes: B k T + k p for Hutch, B T^2 for materialised
+    ghost Grams (two per sample), B d p for FGC's per-sample gradients."""
+    import torch
+    from sample_gradient_clipping_amd import roofline as rf
+    from sample_gradient_clipping_amd.configs import workloads
+    from sample_gradient_clipping_amd.inputs import linear_inputs_device
+    W = workloads()
+    out = {}
+    for wname, methods in (("long_ctx_b2_t16384_d2048_p8192", ("ghost", "hutch", "hutchpp", "fgc")),
+                           ("mlp_up_b8_t4096_d2048_p8192", ("hutch", "hutchpp"))):
+        wl = W[wname]
+        l = wl.layers[0]
+        B, T, d, p, k = wl.B, wl.T, l.d, l.p, wl.k
+        A, G = linear_inputs_device(B, T, d, p, wl.dtype, wl.recipe, wl.data_seed, l.layer_id, dev)
+        n = torch.zeros(B, dtype=torch.float32, device=dev)
+        res = {"B": B, "T": T, "d": d, "p": p, "k": k}
+        for m in methods:
+            torch.cuda.synchronize()
+            torch.cuda.reset_peak_memory_stats(dev)
+            base = torch.cuda.memory_allocated(dev)
+            wsb = dp.dp_norm_est_workspace(m, wl.dtype, B, T, d, p, k)
+            ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+            dp.dp_norm_est(m, A, G, k, 11, l.layer_id, n, ws=ws)
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated(dev) - base
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for r in range(reps):
+                dp.dp_norm_est(m, A, G, k, 12 + r, l.layer_id, n, ws=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / reps * 1e3
+            del ws
+            if m == "ghost":
+                pages = 4 * B * T * T * 2
+            elif m == "fgc":
+                pages = 4 * B * d * p
+            else:
+                pages = 4 * (B * k * T + k * p)
+            flops = (rf.ghost_flops(B, T, d, p) if m == "ghost" else
+                     rf.gemm_flops(B, T, d, p) if m == "fgc" else
+                     rf.hutch_flops(B, T, d, p, k) if m == "hutch" else
+                     rf.hutchpp_flops(B, T, d, p, k))
+            res[m] = {"us_per_call": us, "workspace_bytes": int(wsb),
+                      "peak_bytes_measured": int(peak), "pages_accounting_bytes": int(pages),
+                      "flops": flops, "big_o_flops": rf.big_o_flops(m, B, T, d, p, k)}
+        if "hutchpp" in res and "hutch" in res:
+            res["hutchpp_over_hutch_time"] = res["hutchpp"]["us_per_call"] / res["hutch"]["us_per_call"]
+        if "fgc" in res:
+            res["hutch_workspace_over_fgc"] = res["hutch"]["workspace_bytes"] / res["fgc"]["workspace_bytes"]
+            res["ghost_over_hutch_time"] = res["ghost"]["us_per_call"] / res["hutch"]["us_per_call"]
+        out[wname] = res
+        del A, G
+        torch.cuda.empty_cache()
     return out
 
 
@@ -548,7 +617,7 @@ def main():
     ws_a = max(dp.dp_clip_aggregate_update_workspace(wl.dtype, wl.B, wl.T, l.d, l.p)
                for l in wl.layers)
     ws_norm = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
-    ws_agg = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev)
+    ws_agg = dp.clip_workspace(ws_a, dev)
 
     K, W = args.steps, args.warmup
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(L)]
@@ -688,7 +757,7 @@ def main():
             f"{kv['GBps']:8.1f} GB/s  {kv.get('TFLOPs', 0):8.1f} TF/s  frac {kv['frac']:.3f}  "
             f"share {kv['share_of_step']:.2f}")
 
-    accuracy = sampler = rms = emb = mlp = attn = layer = None
+    accuracy = sampler = rms = emb = mlp = attn = layer = costs = None
     if not args.only_step:
         accuracy = estimator_accuracy(dp, wl, inputs[0][0], dev, rademacher=args.rademacher)
         log(f"[bench] estimator accuracy {accuracy}")
@@ -699,6 +768,9 @@ def main():
         emb = embedding_timing(dp, wl, dev) if wl.dtype == "bf16" else None
         log(f"[bench] embedding {emb}")
         del inputs
+        torch.cuda.empty_cache()
+        costs = estimator_costs(dp, dev)
+        log(f"[bench] estimator costs {costs}")
         torch.cuda.empty_cache()
         mlp = mlp_block_timing(dp, wl, dev) if wl.dtype == "bf16" else None
         log(f"[bench] mlp block {mlp}")
@@ -727,6 +799,7 @@ def main():
         "roofline": roof,
         "kernels": kernels,
         "estimator_accuracy": accuracy,
+        "estimator_costs": costs,
         "poisson_sampler": sampler,
         "rmsnorm_gain_norms": rms,
         "embedding": emb,

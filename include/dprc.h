@@ -20,8 +20,9 @@
  *
  * Conventions for every entry point:
  *  - Tensors are caller-owned DEVICE memory, dense row-major, and 16-byte
- *    aligned (A, G, S, theta, workspace) or 4-byte aligned (n_sq, c_out,
- *    status).  The library never allocates, frees, prints or synchronises.
+ *    aligned (A, G, S, theta, workspace) or 4-byte aligned (n_sq, c_out).
+ *    The library never allocates, frees or prints, and never synchronises
+ *    except in dp_read_device_status.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    runs asynchronously.  A DP_OK return means "validated and enqueued".
  *  - Arguments are validated on the host before anything is enqueued; on an
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DPRC_ABI_VERSION 1
+#define DPRC_ABI_VERSION 2
 
 typedef void *dp_stream_t; /* a hipStream_t */
 
@@ -72,7 +73,15 @@ typedef enum {
  * 32-bit word's top bit is 0.  The estimate keeps the 1/k (E[P P^T] = k I). */
 #define DP_PROBE_RADEMACHER 4u
 
-/* dp_clip_aggregate status bits (ORed into *status) */
+/*
+ * Device status flags.  Every call that forms clip factors (dp_clip_aggregate,
+ * dp_clip_aggregate_update, dp_rmsnorm_clip_aggregate_update,
+ * dp_embedding_clip_aggregate_update) ORs them into a sticky status word kept
+ * in the first 8 bytes of its workspace; the word stays set over any number of
+ * calls that reuse the workspace until dp_read_device_status reads and clears
+ * it.  A newly allocated workspace must start with that word at zero: allocate
+ * it zeroed, or call dp_read_device_status on it once and discard the result.
+ */
 #define DP_STATUS_NONFINITE_NORM 1u /* some n_sq[i] was NaN/Inf: its c_i was set to 0 */
 
 int dp_abi_version(void);
@@ -121,7 +130,7 @@ size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p);
  *
  *  c_i = 1 if n_sq[i] <= C^2 (0 and negative values included), C / sqrt(n_sq[i])
  *  otherwise, 0 if n_sq[i] is not finite (the sample is dropped and
- *  DP_STATUS_NONFINITE_NORM is ORed into *status); then
+ *  DP_STATUS_NONFINITE_NORM is ORed into the workspace's status word); then
  *      S[o][q] = sum_i c_i sum_t G_i[t][o] A_i[t][q]          (S = sum_i c_i G_i^T A_i)
  *  which is the second backward pass on the loss rescaled by c_i (glossary
  *  step 3-4 without the noise; summary step 4-5).
@@ -129,15 +138,13 @@ size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p);
  *  A [B][T][d], G [B][T][p] device (dtype); n_sq [B] fp32 device (squared norms
  *  summed over all layers); C > 0 finite.
  *  c_out   [B] fp32 device output, or NULL.
- *  status  one uint32 device word the kernel ORs flags into (the caller clears
- *          it), or NULL.
  *  S       [p][d] fp32 device output (the (p, d) weight layout), overwritten.
- *  ws      device workspace of ws_bytes >= dp_clip_aggregate_workspace(...).
+ *  ws      device workspace of ws_bytes >= dp_clip_aggregate_workspace(...);
+ *          its first 8 bytes hold the sticky status word (see above).
  */
 dp_status_t dp_clip_aggregate(int dtype, int B, int T, int d, int p, const void *A,
-                              const void *G, const float *n_sq, float C, float *c_out,
-                              uint32_t *status, float *S, void *ws, size_t ws_bytes,
-                              dp_stream_t stream);
+                              const void *G, const float *n_sq, float C, float *c_out, float *S,
+                              void *ws, size_t ws_bytes, dp_stream_t stream);
 
 /*
  * Noise and SGD update of one (p, d) fp32 parameter block, in place:
@@ -173,8 +180,24 @@ size_t dp_clip_aggregate_update_workspace(int dtype, int B, int T, int d, int p)
 dp_status_t dp_clip_aggregate_update(int dtype, int B, int T, int d, int p, const void *A,
                                      const void *G, const float *n_sq, float C, float sigma,
                                      float eta, uint64_t seed, uint32_t layer, float *theta,
-                                     float *S, float *c_out, uint32_t *status, void *ws,
-                                     size_t ws_bytes, dp_stream_t stream);
+                                     float *S, float *c_out, void *ws, size_t ws_bytes,
+                                     dp_stream_t stream);
+
+/*
+ * The sticky device status flags of a workspace (DP_STATUS_* bits ORed by the
+ * clip-factor calls above and below since the previous read), e.g.
+ * DP_STATUS_NONFINITE_NORM when some sample's summed squared norm was NaN or
+ * Inf and the sample was dropped (its c_i = 0; the randomized-clipping
+ * summary, section アルゴリズム的フロー, step 4, leaves such values open).
+ *  ws         the workspace passed to those calls (16-byte aligned device).
+ *  flags_out  host pointer receiving the flags.
+ * Enqueues an atomic read-and-clear of the word on `stream`, copies the value
+ * to the host and synchronises `stream`: the only call of the library that
+ * blocks the host.  Not for use under stream capture.  DP_ERR_INVALID_ARG for
+ * a NULL or misaligned pointer; DP_ERR_HIP if a HIP call fails (then
+ * *flags_out is unchanged).
+ */
+dp_status_t dp_read_device_status(void *ws, uint32_t *flags_out, dp_stream_t stream);
 
 /* ---- timed variants: the same calls, plus live kernel timing ----
  * Identical to the call without "_timed", and additionally record the two
@@ -192,8 +215,8 @@ dp_status_t dp_norm_est_timed(int method, int dtype, int B, int T, int d, int p,
                               dp_stream_t stream, void *ev_begin, void *ev_end);
 dp_status_t dp_clip_aggregate_timed(int dtype, int B, int T, int d, int p, const void *A,
                                     const void *G, const float *n_sq, float C, float *c_out,
-                                    uint32_t *status, float *S, void *ws, size_t ws_bytes,
-                                    dp_stream_t stream, void *ev_begin, void *ev_end);
+                                    float *S, void *ws, size_t ws_bytes, dp_stream_t stream,
+                                    void *ev_begin, void *ev_end);
 dp_status_t dp_noise_update_timed(int d, int p, float *theta, const float *S, float sigma,
                                   float C, float eta, int B, uint64_t seed, uint32_t layer,
                                   dp_stream_t stream, void *ev_begin, void *ev_end);
@@ -202,11 +225,10 @@ dp_status_t dp_noise_update_timed(int d, int p, float *theta, const float *S, fl
 dp_status_t dp_clip_aggregate_update_timed(int dtype, int B, int T, int d, int p, const void *A,
                                            const void *G, const float *n_sq, float C,
                                            float sigma, float eta, uint64_t seed, uint32_t layer,
-                                           float *theta, float *S, float *c_out,
-                                           uint32_t *status, void *ws, size_t ws_bytes,
-                                           dp_stream_t stream, void *ev_agg_begin,
-                                           void *ev_agg_end, void *ev_upd_begin,
-                                           void *ev_upd_end);
+                                           float *theta, float *S, float *c_out, void *ws,
+                                           size_t ws_bytes, dp_stream_t stream,
+                                           void *ev_agg_begin, void *ev_agg_end,
+                                           void *ev_upd_begin, void *ev_upd_end);
 
 /* ---- RMSNorm gains (a parameter that is not a linear layer) ----
  *
@@ -220,10 +242,11 @@ dp_status_t dp_clip_aggregate_update_timed(int dtype, int B, int T, int d, int p
  *  ws           device workspace, ws_bytes >= dp_rmsnorm_norm_workspace(...).
  * dp_rmsnorm_clip_aggregate_update then takes the clip factors
  * c_i = min(1, C / sqrt(n_i)) of the summed norms (the same rule as
- * dp_clip_aggregate: non-finite n_i gives c_i = 0 and the status bit) and
+ * dp_clip_aggregate: non-finite n_i gives c_i = 0 and the status bit in the
+ * workspace's status word) and
  * updates gamma [d] fp32: gamma <- gamma - (eta / B) (sum_i c_i v_i + sigma C xi),
  * xi from the noise stream of `layer` (give each parameter its own layer id).
- * S [d] (optional) receives the clipped sum; c_out [B] and status optional.
+ * S [d] (optional) receives the clipped sum; c_out [B] optional.
  */
 size_t dp_rmsnorm_norm_workspace(int dtype, int B, int T, int d);
 dp_status_t dp_rmsnorm_norm(int dtype, int B, int T, int d, const void *xhat, const void *delta,
@@ -233,8 +256,8 @@ size_t dp_rmsnorm_update_workspace(int B, int d);
 dp_status_t dp_rmsnorm_clip_aggregate_update(int B, int d, const float *v, const float *n_sq,
                                              float C, float sigma, float eta, uint64_t seed,
                                              uint32_t layer, float *gamma, float *S,
-                                             float *c_out, uint32_t *status, void *ws,
-                                             size_t ws_bytes, dp_stream_t stream);
+                                             float *c_out, void *ws, size_t ws_bytes,
+                                             dp_stream_t stream);
 
 /* ---- embedding tables (a parameter that is not a linear layer) ----
  *
@@ -259,8 +282,8 @@ dp_status_t dp_embedding_clip_aggregate_update(int dtype, int B, int T, int d, i
                                                const int32_t *ids, const void *delta,
                                                const float *n_sq, float C, float sigma,
                                                float eta, uint64_t seed, uint32_t layer, float *E,
-                                               float *c_out, uint32_t *status, void *ws,
-                                               size_t ws_bytes, dp_stream_t stream);
+                                               float *c_out, void *ws, size_t ws_bytes,
+                                               dp_stream_t stream);
 
 /* ---- Poisson subsampling of the minibatch ----
  *

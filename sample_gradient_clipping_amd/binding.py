@@ -59,7 +59,7 @@ def load_library():
     L.dp_norm_est.restype = c_int
     L.dp_clip_aggregate_workspace.argtypes = [c_int] * 5
     L.dp_clip_aggregate_workspace.restype = c_sz
-    L.dp_clip_aggregate.argtypes = [c_int] * 5 + [c_p, c_p, c_p, c_f, c_p, c_p, c_p, c_p, c_sz, c_p]
+    L.dp_clip_aggregate.argtypes = [c_int] * 5 + [c_p, c_p, c_p, c_f, c_p, c_p, c_p, c_sz, c_p]
     L.dp_clip_aggregate.restype = c_int
     L.dp_noise_update.argtypes = [c_int, c_int, c_p, c_p, c_f, c_f, c_f, c_int, c_u64, c_u32, c_p]
     L.dp_noise_update.restype = c_int
@@ -72,8 +72,10 @@ def load_library():
     L.dp_clip_aggregate_update_workspace.argtypes = [c_int] * 5
     L.dp_clip_aggregate_update_workspace.restype = c_sz
     L.dp_clip_aggregate_update.argtypes = ([c_int] * 5 + [c_p, c_p, c_p, c_f, c_f, c_f, c_u64, c_u32]
-                                           + [c_p, c_p, c_p, c_p, c_p, c_sz, c_p])
+                                           + [c_p, c_p, c_p, c_p, c_sz, c_p])
     L.dp_clip_aggregate_update.restype = c_int
+    L.dp_read_device_status.argtypes = [c_p, ctypes.POINTER(c_u32), c_p]
+    L.dp_read_device_status.restype = c_int
     L.dp_clip_aggregate_update_timed.argtypes = L.dp_clip_aggregate_update.argtypes + [c_p] * 4
     L.dp_clip_aggregate_update_timed.restype = c_int
     L.dp_philox_u32.argtypes = [c_u64, c_p, c_p, c_sz, c_p]
@@ -96,7 +98,7 @@ def load_library():
     L.dp_rmsnorm_update_workspace.argtypes = [c_int, c_int]
     L.dp_rmsnorm_update_workspace.restype = c_sz
     L.dp_rmsnorm_clip_aggregate_update.argtypes = [c_int, c_int, c_p, c_p, c_f, c_f, c_f, c_u64,
-                                                   c_u32, c_p, c_p, c_p, c_p, c_p, c_sz, c_p]
+                                                   c_u32, c_p, c_p, c_p, c_p, c_sz, c_p]
     L.dp_rmsnorm_clip_aggregate_update.restype = c_int
     L.dp_embedding_norm_workspace.argtypes = [c_int] * 4
     L.dp_embedding_norm_workspace.restype = c_sz
@@ -106,7 +108,7 @@ def load_library():
     L.dp_embedding_update_workspace.restype = c_sz
     L.dp_embedding_clip_aggregate_update.argtypes = ([c_int] * 5 + [c_p, c_p, c_p, c_f, c_f, c_f,
                                                                     c_u64, c_u32, c_p, c_p, c_p,
-                                                                    c_p, c_sz, c_p])
+                                                                    c_sz, c_p])
     L.dp_embedding_clip_aggregate_update.restype = c_int
     L.dp_weights_bf16.argtypes = [c_int, c_int, c_p, c_p, c_p, c_p]
     L.dp_weights_bf16.restype = c_int
@@ -180,12 +182,30 @@ def _method_code(method):
     return METHODS[method] if isinstance(method, str) else int(method)
 
 
-def _workspace(nbytes, device, ws):
+def _workspace(nbytes, device, ws, zeroed=False):
+    """The caller's workspace, or a new one of nbytes (zeroed for the calls that
+    keep a status word in it)."""
     if nbytes == _SIZE_INVALID:
         return None
     if ws is not None:
         return ws
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    alloc = torch.zeros if zeroed else torch.empty
+    return alloc(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def clip_workspace(nbytes, device):
+    """A zeroed workspace for the calls that form clip factors (its first word is
+    the sticky status word read by dp_read_device_status)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def dp_read_device_status(ws, stream=None):
+    """The DP_STATUS_* flags ORed into ``ws`` by the clip-factor calls since the
+    last read; clears them.  Synchronises the stream."""
+    flags = ctypes.c_uint32(0)
+    _check(load_library().dp_read_device_status(_ptr(ws), ctypes.byref(flags), _stream(stream)),
+           "dp_read_device_status")
+    return int(flags.value)
 
 
 def dp_norm_est_workspace(method, dtype, B, T, d, p, k):
@@ -227,17 +247,16 @@ def dp_clip_aggregate_workspace(dtype, B, T, d, p):
     return None if n == _SIZE_INVALID else n
 
 
-def dp_clip_aggregate(A, G, n_sq, C, S, c_out=None, status=None, ws=None, stream=None,
-                      events=None):
+def dp_clip_aggregate(A, G, n_sq, C, S, c_out=None, ws=None, stream=None, events=None):
     """Clip factors from n_sq and S[o][q] = sum_i c_i sum_t G_i[t][o] A_i[t][q]."""
     L = load_library()
     B, T, d = A.shape
     p = G.shape[2]
     dt = _dtype_code(A)
     nbytes = L.dp_clip_aggregate_workspace(dt, B, T, d, p)
-    ws_t = _workspace(nbytes, A.device, ws)
-    args = [dt, B, T, d, p, _ptr(A), _ptr(G), _ptr(n_sq), float(C), _ptr(c_out), _ptr(status),
-            _ptr(S), _ptr(ws_t), 0 if ws_t is None else ws_t.numel(), _stream(stream)]
+    ws_t = _workspace(nbytes, A.device, ws, zeroed=True)
+    args = [dt, B, T, d, p, _ptr(A), _ptr(G), _ptr(n_sq), float(C), _ptr(c_out), _ptr(S),
+            _ptr(ws_t), 0 if ws_t is None else ws_t.numel(), _stream(stream)]
     if events is None:
         st = L.dp_clip_aggregate(*args)
     else:
@@ -253,7 +272,7 @@ def dp_clip_aggregate_update_workspace(dtype, B, T, d, p):
 
 
 def dp_clip_aggregate_update(A, G, n_sq, C, sigma, eta, seed, layer, theta, S=None, c_out=None,
-                             status=None, ws=None, stream=None, events=None):
+                             ws=None, stream=None, events=None):
     """Clip factors, clipped sum, noise and update of theta [p][d] in one call
     (|B| = A.shape[0]); S, if given, receives the clipped sum.  ``events``: optional
     ((agg_begin, agg_end), (upd_begin, upd_end)) torch.cuda.Event pairs."""
@@ -262,9 +281,9 @@ def dp_clip_aggregate_update(A, G, n_sq, C, sigma, eta, seed, layer, theta, S=No
     p = G.shape[2]
     dt = _dtype_code(A)
     nbytes = L.dp_clip_aggregate_update_workspace(dt, B, T, d, p)
-    ws_t = _workspace(nbytes, A.device, ws)
+    ws_t = _workspace(nbytes, A.device, ws, zeroed=True)
     args = [dt, B, T, d, p, _ptr(A), _ptr(G), _ptr(n_sq), float(C), float(sigma), float(eta),
-            int(seed) & (2**64 - 1), int(layer), _ptr(theta), _ptr(S), _ptr(c_out), _ptr(status),
+            int(seed) & (2**64 - 1), int(layer), _ptr(theta), _ptr(S), _ptr(c_out),
             _ptr(ws_t), 0 if ws_t is None else ws_t.numel(), _stream(stream)]
     if events is None:
         st = L.dp_clip_aggregate_update(*args)
@@ -363,15 +382,14 @@ def dp_rmsnorm_norm(xhat, delta, n_sq, v=None, flags=0, ws=None, stream=None):
 
 
 def dp_rmsnorm_clip_aggregate_update(v, n_sq, C, sigma, eta, seed, layer, gamma, S=None,
-                                     c_out=None, status=None, ws=None, stream=None):
+                                     c_out=None, ws=None, stream=None):
     """gamma[d] <- gamma - (eta / B) (sum_i c_i v_i + sigma C xi), c_i = min(1, C / sqrt(n_i))."""
     L = load_library()
     B, d = v.shape
-    ws_t = _workspace(L.dp_rmsnorm_update_workspace(B, d), v.device, ws)
+    ws_t = _workspace(L.dp_rmsnorm_update_workspace(B, d), v.device, ws, zeroed=True)
     st = L.dp_rmsnorm_clip_aggregate_update(B, d, _ptr(v), _ptr(n_sq), float(C), float(sigma),
                                             float(eta), int(seed) & (2**64 - 1), int(layer),
-                                            _ptr(gamma), _ptr(S), _ptr(c_out), _ptr(status),
-                                            _ptr(ws_t), 0 if ws_t is None else ws_t.numel(),
+                                            _ptr(gamma), _ptr(S), _ptr(c_out), _ptr(ws_t), 0 if ws_t is None else ws_t.numel(),
                                             _stream(stream))
     _check(st, "dp_rmsnorm_clip_aggregate_update")
     return gamma
@@ -391,17 +409,18 @@ def dp_embedding_norm(ids, delta, n_sq, flags=0, ws=None, stream=None):
 
 
 def dp_embedding_clip_aggregate_update(ids, delta, n_sq, C, sigma, eta, seed, layer, E,
-                                       c_out=None, status=None, ws=None, stream=None):
+                                       c_out=None, ws=None, stream=None):
     """E [V][d] <- E - (eta / B) (sum_i c_i grad_i + sigma C xi) over every row of E."""
     L = load_library()
     B, T, d = delta.shape
     V = E.shape[0]
     dt = _dtype_code(delta)
-    ws_t = _workspace(L.dp_embedding_update_workspace(dt, B, T, d, V), delta.device, ws)
+    ws_t = _workspace(L.dp_embedding_update_workspace(dt, B, T, d, V), delta.device, ws,
+                      zeroed=True)
     st = L.dp_embedding_clip_aggregate_update(dt, B, T, d, V, _ptr(ids), _ptr(delta), _ptr(n_sq),
                                               float(C), float(sigma), float(eta),
                                               int(seed) & (2**64 - 1), int(layer), _ptr(E),
-                                              _ptr(c_out), _ptr(status), _ptr(ws_t),
+                                              _ptr(c_out), _ptr(ws_t),
                                               0 if ws_t is None else ws_t.numel(),
                                               _stream(stream))
     _check(st, "dp_embedding_clip_aggregate_update")

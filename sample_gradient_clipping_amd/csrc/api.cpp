@@ -19,6 +19,10 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr size_t kInvalid = static_cast<size_t>(-1);
+// Every call that forms clip factors keeps its sticky status word at byte 0 of
+// its workspace (read and cleared by dp_read_device_status); the word after it
+// receives the value being read.
+constexpr size_t kStatusBytes = 8;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -309,7 +313,7 @@ dp_status_t run_norm_exact(int method, const NormPlan& P, int B, int T, int d, i
 struct AggPlan {
   bool mfma = false;
   int nsplit = 1;
-  size_t c = 0, order = 0, count = 0, part = 0, sbuf = 0, total = 0;
+  size_t status = 0, c = 0, order = 0, count = 0, part = 0, sbuf = 0, total = 0;
 };
 
 // with_sbuf: also a [p][d] buffer for the clipped sum when the caller of the
@@ -318,6 +322,7 @@ AggPlan plan_agg(int dtype, int B, int T, int d, int p, bool with_sbuf = false) 
   AggPlan P;
   Carver cv;
   const size_t Bz = static_cast<size_t>(B > 0 ? B : 1);
+  P.status = cv.take(kStatusBytes);
   P.c = cv.take(Bz * 4);
   P.order = cv.take(Bz * 4);
   P.count = cv.take(4);
@@ -418,12 +423,12 @@ size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p) {
 }
 
 bool agg_ptrs_ok(int B, int T, const void* A, const void* G, const float* n_sq, float C,
-                 float* c_out, uint32_t* status) {
+                 float* c_out) {
   if (!(C > 0.f) || !std::isfinite(C)) return false;
   if (B > 0 && (n_sq == nullptr || !aligned(n_sq, 4))) return false;
   if (B > 0 && T > 0 && (A == nullptr || G == nullptr || !aligned(A, 16) || !aligned(G, 16)))
     return false;
-  if ((c_out && !aligned(c_out, 4)) || (status && !aligned(status, 4))) return false;
+  if (c_out && !aligned(c_out, 4)) return false;
   return true;
 }
 
@@ -431,13 +436,13 @@ bool agg_ptrs_ok(int B, int T, const void* A, const void* G, const float* n_sq, 
 // generic kernel), or as *nsplit planes at *planes (the workspace).  Returns
 // where the sum is and how many planes make it up.
 dp_status_t clip_and_sum(const AggPlan& P, int dtype, int B, int T, int d, int p, const void* A,
-                         const void* G, const float* n_sq, float C, float* c_out,
-                         uint32_t* status, float* S, void* ws, hipStream_t s, const Marks& mk,
-                         const float** planes, int* nplanes) {
+                         const void* G, const float* n_sq, float C, float* c_out, float* S,
+                         void* ws, hipStream_t s, const Marks& mk, const float** planes,
+                         int* nplanes) {
   float* c = at<float>(ws, P.c);
   int* order = at<int>(ws, P.order);
   int* count = at<int>(ws, P.count);
-  DP_TRY(launch_clip(n_sq, B, C, c, c_out, status, order, count, s));
+  DP_TRY(launch_clip(n_sq, B, C, c, c_out, at<uint32_t>(ws, P.status), order, count, s));
   *planes = S;
   *nplanes = 1;
   if (P.mfma) {
@@ -465,10 +470,10 @@ dp_status_t clip_and_sum(const AggPlan& P, int dtype, int B, int T, int d, int p
 
 static dp_status_t clip_aggregate_impl(int dtype, int B, int T, int d, int p, const void* A,
                                        const void* G, const float* n_sq, float C, float* c_out,
-                                       uint32_t* status, float* S, void* ws, size_t ws_bytes,
-                                       dp_stream_t stream, const Marks& mk) {
+                                       float* S, void* ws, size_t ws_bytes, dp_stream_t stream,
+                                       const Marks& mk) {
   if (!agg_args_ok(dtype, B, T, d, p)) return DP_ERR_INVALID_ARG;
-  if (!agg_ptrs_ok(B, T, A, G, n_sq, C, c_out, status)) return DP_ERR_INVALID_ARG;
+  if (!agg_ptrs_ok(B, T, A, G, n_sq, C, c_out)) return DP_ERR_INVALID_ARG;
   if (S == nullptr || !aligned(S, 16)) return DP_ERR_INVALID_ARG;
   const AggPlan P = plan_agg(dtype, B, T, d, p);
   if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
@@ -477,8 +482,7 @@ static dp_status_t clip_aggregate_impl(int dtype, int B, int T, int d, int p, co
   const float* planes = nullptr;
   int nplanes = 1;
   const dp_status_t st =
-      clip_and_sum(P, dtype, B, T, d, p, A, G, n_sq, C, c_out, status, S, ws, s, mk, &planes,
-                   &nplanes);
+      clip_and_sum(P, dtype, B, T, d, p, A, G, n_sq, C, c_out, S, ws, s, mk, &planes, &nplanes);
   if (st != DP_OK) return st;
   if (planes != S) DP_TRY(launch_reduce_splits(planes, nplanes, static_cast<int64_t>(p) * d, S, s));
   return DP_OK;
@@ -499,12 +503,12 @@ static dp_status_t clip_aggregate_update_impl(int dtype, int B, int T, int d, in
                                               const void* A, const void* G, const float* n_sq,
                                               float C, float sigma, float eta, uint64_t seed,
                                               uint32_t layer, float* theta, float* S,
-                                              float* c_out, uint32_t* status, void* ws,
-                                              size_t ws_bytes, dp_stream_t stream,
-                                              const Marks& mk_agg, const Marks& mk_upd) {
+                                              float* c_out, void* ws, size_t ws_bytes,
+                                              dp_stream_t stream, const Marks& mk_agg,
+                                              const Marks& mk_upd) {
   if (!agg_args_ok(dtype, B, T, d, p)) return DP_ERR_INVALID_ARG;
   if (!update_args_ok(d, p, B, sigma, C, eta)) return DP_ERR_INVALID_ARG;
-  if (!agg_ptrs_ok(B, T, A, G, n_sq, C, c_out, status)) return DP_ERR_INVALID_ARG;
+  if (!agg_ptrs_ok(B, T, A, G, n_sq, C, c_out)) return DP_ERR_INVALID_ARG;
   if (theta == nullptr || !aligned(theta, 16)) return DP_ERR_INVALID_ARG;
   if (S != nullptr && !aligned(S, 16)) return DP_ERR_INVALID_ARG;
   const size_t bytes = static_cast<size_t>(p) * d * 4;
@@ -518,8 +522,8 @@ static dp_status_t clip_aggregate_update_impl(int dtype, int B, int T, int d, in
   float* sum = S != nullptr ? S : at<float>(ws, P.sbuf);
   const float* planes = nullptr;
   int nplanes = 1;
-  const dp_status_t st = clip_and_sum(P, dtype, B, T, d, p, A, G, n_sq, C, c_out, status, sum,
-                                      ws, s, mk_agg, &planes, &nplanes);
+  const dp_status_t st = clip_and_sum(P, dtype, B, T, d, p, A, G, n_sq, C, c_out, sum, ws, s,
+                                      mk_agg, &planes, &nplanes);
   if (st != DP_OK) return st;
   const float sigmaC = sigma * C;
   const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
@@ -535,18 +539,17 @@ static dp_status_t clip_aggregate_update_impl(int dtype, int B, int T, int d, in
 }
 
 dp_status_t dp_clip_aggregate(int dtype, int B, int T, int d, int p, const void* A, const void* G,
-                              const float* n_sq, float C, float* c_out, uint32_t* status, float* S,
-                              void* ws, size_t ws_bytes, dp_stream_t stream) {
-  return clip_aggregate_impl(dtype, B, T, d, p, A, G, n_sq, C, c_out, status, S, ws, ws_bytes,
-                             stream, Marks{});
+                              const float* n_sq, float C, float* c_out, float* S, void* ws,
+                              size_t ws_bytes, dp_stream_t stream) {
+  return clip_aggregate_impl(dtype, B, T, d, p, A, G, n_sq, C, c_out, S, ws, ws_bytes, stream,
+                             Marks{});
 }
 
 dp_status_t dp_clip_aggregate_timed(int dtype, int B, int T, int d, int p, const void* A,
                                     const void* G, const float* n_sq, float C, float* c_out,
-                                    uint32_t* status, float* S, void* ws, size_t ws_bytes,
-                                    dp_stream_t stream, void* ev_begin, void* ev_end) {
-  return clip_aggregate_impl(dtype, B, T, d, p, A, G, n_sq, C, c_out, status, S, ws, ws_bytes,
-                             stream,
+                                    float* S, void* ws, size_t ws_bytes, dp_stream_t stream,
+                                    void* ev_begin, void* ev_end) {
+  return clip_aggregate_impl(dtype, B, T, d, p, A, G, n_sq, C, c_out, S, ws, ws_bytes, stream,
                              Marks{static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)});
 }
 
@@ -576,24 +579,22 @@ size_t dp_clip_aggregate_update_workspace(int dtype, int B, int T, int d, int p)
 dp_status_t dp_clip_aggregate_update(int dtype, int B, int T, int d, int p, const void* A,
                                      const void* G, const float* n_sq, float C, float sigma,
                                      float eta, uint64_t seed, uint32_t layer, float* theta,
-                                     float* S, float* c_out, uint32_t* status, void* ws,
-                                     size_t ws_bytes, dp_stream_t stream) {
+                                     float* S, float* c_out, void* ws, size_t ws_bytes,
+                                     dp_stream_t stream) {
   return clip_aggregate_update_impl(dtype, B, T, d, p, A, G, n_sq, C, sigma, eta, seed, layer,
-                                    theta, S, c_out, status, ws, ws_bytes, stream, Marks{},
-                                    Marks{});
+                                    theta, S, c_out, ws, ws_bytes, stream, Marks{}, Marks{});
 }
 
 dp_status_t dp_clip_aggregate_update_timed(int dtype, int B, int T, int d, int p, const void* A,
                                            const void* G, const float* n_sq, float C,
                                            float sigma, float eta, uint64_t seed, uint32_t layer,
-                                           float* theta, float* S, float* c_out,
-                                           uint32_t* status, void* ws, size_t ws_bytes,
-                                           dp_stream_t stream, void* ev_agg_begin,
-                                           void* ev_agg_end, void* ev_upd_begin,
-                                           void* ev_upd_end) {
+                                           float* theta, float* S, float* c_out, void* ws,
+                                           size_t ws_bytes, dp_stream_t stream,
+                                           void* ev_agg_begin, void* ev_agg_end,
+                                           void* ev_upd_begin, void* ev_upd_end) {
   return clip_aggregate_update_impl(
-      dtype, B, T, d, p, A, G, n_sq, C, sigma, eta, seed, layer, theta, S, c_out, status, ws,
-      ws_bytes, stream,
+      dtype, B, T, d, p, A, G, n_sq, C, sigma, eta, seed, layer, theta, S, c_out, ws, ws_bytes,
+      stream,
       Marks{static_cast<hipEvent_t>(ev_agg_begin), static_cast<hipEvent_t>(ev_agg_end)},
       Marks{static_cast<hipEvent_t>(ev_upd_begin), static_cast<hipEvent_t>(ev_upd_end)});
 }
@@ -608,6 +609,18 @@ dp_status_t dp_noise_update_timed(int d, int p, float* theta, const float* S, fl
                                   dp_stream_t stream, void* ev_begin, void* ev_end) {
   return noise_update_impl(d, p, theta, S, sigma, C, eta, B, seed, layer, stream,
                            Marks{static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)});
+}
+
+dp_status_t dp_read_device_status(void* ws, uint32_t* flags_out, dp_stream_t stream) {
+  if (ws == nullptr || flags_out == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t* w = static_cast<uint32_t*>(ws);
+  uint32_t v = 0;
+  DP_TRY(launch_take_status(w, s));
+  DP_TRY(hipMemcpyAsync(&v, w + 1, sizeof(v), hipMemcpyDeviceToHost, s));
+  DP_TRY(hipStreamSynchronize(s));
+  *flags_out = v;
+  return DP_OK;
 }
 
 dp_status_t dp_philox_u32(uint64_t seed, const uint32_t* ctr, uint32_t* out, size_t n,
@@ -706,13 +719,14 @@ dp_status_t dp_rmsnorm_norm(int dtype, int B, int T, int d, const void* xhat, co
 }
 
 struct GainPlan {
-  size_t c = 0, order = 0, count = 0, sbuf = 0, total = 0;
+  size_t status = 0, c = 0, order = 0, count = 0, sbuf = 0, total = 0;
 };
 
 static GainPlan plan_gain(int B, int d) {
   GainPlan P;
   Carver cv;
   const size_t Bz = static_cast<size_t>(B > 0 ? B : 1);
+  P.status = cv.take(kStatusBytes);
   P.c = cv.take(Bz * sizeof(float));
   P.order = cv.take(Bz * sizeof(int));
   P.count = cv.take(sizeof(int));
@@ -729,15 +743,13 @@ size_t dp_rmsnorm_update_workspace(int B, int d) {
 dp_status_t dp_rmsnorm_clip_aggregate_update(int B, int d, const float* v, const float* n_sq,
                                              float C, float sigma, float eta, uint64_t seed,
                                              uint32_t layer, float* gamma, float* S,
-                                             float* c_out, uint32_t* status, void* ws,
-                                             size_t ws_bytes, dp_stream_t stream) {
+                                             float* c_out, void* ws, size_t ws_bytes,
+                                             dp_stream_t stream) {
   if (!update_args_ok(d, 1, B, sigma, C, eta)) return DP_ERR_INVALID_ARG;
   if (v == nullptr || n_sq == nullptr || gamma == nullptr || !aligned(v, 4) ||
       !aligned(n_sq, 4) || !aligned(gamma, 16))
     return DP_ERR_INVALID_ARG;
-  if ((S != nullptr && !aligned(S, 16)) || (c_out && !aligned(c_out, 4)) ||
-      (status && !aligned(status, 4)))
-    return DP_ERR_INVALID_ARG;
+  if ((S != nullptr && !aligned(S, 16)) || (c_out && !aligned(c_out, 4))) return DP_ERR_INVALID_ARG;
   const size_t bytes = static_cast<size_t>(d) * 4;
   if (S != nullptr && overlaps(gamma, bytes, S, bytes)) return DP_ERR_INVALID_ARG;
   const GainPlan P = plan_gain(B, d);
@@ -747,7 +759,8 @@ dp_status_t dp_rmsnorm_clip_aggregate_update(int B, int d, const float* v, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* c = at<float>(ws, P.c);
   float* sum = S != nullptr ? S : at<float>(ws, P.sbuf);
-  DP_TRY(launch_clip(n_sq, B, C, c, c_out, status, at<int>(ws, P.order), at<int>(ws, P.count), s));
+  DP_TRY(launch_clip(n_sq, B, C, c, c_out, at<uint32_t>(ws, P.status), at<int>(ws, P.order),
+                     at<int>(ws, P.count), s));
   DP_TRY(launch_weighted_rows(v, c, B, d, sum, s));
   const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
   DP_TRY(launch_noise_update(gamma, sum, d, sigma * C, eta_over_B, seed, layer, s));
@@ -759,7 +772,7 @@ constexpr int kEmbMaxTokens = 16384;
 
 struct EmbPlan {
   int nsplit = 1, nchunk = 1;
-  size_t spos = 0, sid = 0, gidp = 0, ustart = 0, uid = 0, ng = 0, head = 0, tail = 0, part = 0,
+  size_t status = 0, spos = 0, sid = 0, gidp = 0, ustart = 0, uid = 0, ng = 0, head = 0, tail = 0, part = 0,
          cpart = 0, gsum = 0, rowmap = 0, c = 0, order = 0, count = 0, total = 0;
 };
 
@@ -769,6 +782,7 @@ static EmbPlan plan_emb(int B, int T, int d, int V) {
   const size_t Bz = static_cast<size_t>(B > 0 ? B : 1), Tz = static_cast<size_t>(T > 0 ? T : 1);
   P.nsplit = emb_splits(B, T, d);
   P.nchunk = (d + 2047) / 2048;
+  if (V > 0) P.status = cv.take(kStatusBytes);  // the update forms clip factors
   P.spos = cv.take(Bz * Tz * 4);
   P.sid = cv.take(Bz * Tz * 4);
   P.gidp = cv.take(Bz * Tz * 4);
@@ -844,22 +858,23 @@ dp_status_t dp_embedding_clip_aggregate_update(int dtype, int B, int T, int d, i
                                                const int32_t* ids, const void* delta,
                                                const float* n_sq, float C, float sigma,
                                                float eta, uint64_t seed, uint32_t layer, float* E,
-                                               float* c_out, uint32_t* status, void* ws,
-                                               size_t ws_bytes, dp_stream_t stream) {
+                                               float* c_out, void* ws, size_t ws_bytes,
+                                               dp_stream_t stream) {
   if (!emb_args_ok(dtype, B, T, d) || V < 1) return DP_ERR_INVALID_ARG;
   if (!update_args_ok(d, V, B, sigma, C, eta)) return DP_ERR_INVALID_ARG;
   if (n_sq == nullptr || E == nullptr || !aligned(n_sq, 4) || !aligned(E, 16))
     return DP_ERR_INVALID_ARG;
   if (T > 0 && (ids == nullptr || delta == nullptr || !aligned(ids, 4) || !aligned(delta, 16)))
     return DP_ERR_INVALID_ARG;
-  if ((c_out && !aligned(c_out, 4)) || (status && !aligned(status, 4))) return DP_ERR_INVALID_ARG;
+  if (c_out && !aligned(c_out, 4)) return DP_ERR_INVALID_ARG;
   const EmbPlan P = plan_emb(B, T, d, V);
   if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
   if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
   if (overlaps(E, static_cast<size_t>(V) * d * 4, ws, P.total)) return DP_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* c = at<float>(ws, P.c);
-  DP_TRY(launch_clip(n_sq, B, C, c, c_out, status, at<int>(ws, P.order), at<int>(ws, P.count), s));
+  DP_TRY(launch_clip(n_sq, B, C, c, c_out, at<uint32_t>(ws, P.status), at<int>(ws, P.order),
+                     at<int>(ws, P.count), s));
   int32_t* spos = at<int32_t>(ws, P.spos);
   int32_t* sid = at<int32_t>(ws, P.sid);
   int32_t* gidp = at<int32_t>(ws, P.gidp);

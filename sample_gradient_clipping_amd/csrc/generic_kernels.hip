@@ -284,6 +284,17 @@ hipError_t launch_clip(const float* n, int B, float C, float* c, float* c_out, u
   return hipGetLastError();
 }
 
+// Sticky status word: w[1] receives w[0], and w[0] is cleared, in one atomic
+// exchange (stream-ordered after every clip kernel that ORed into w[0]).
+__global__ void k_take_status(uint32_t* w) {
+  if (threadIdx.x == 0) w[1] = atomicExch(w, 0u);
+}
+
+hipError_t launch_take_status(uint32_t* w, hipStream_t s) {
+  hipLaunchKernelGGL(k_take_status, dim3(1), dim3(64), 0, s, w);
+  return hipGetLastError();
+}
+
 // out[e] = sum over splits of part[split][e], fixed order.
 __global__ void k_reduce_splits(const float* __restrict__ part, int nsplit, int64_t n,
                                 float* __restrict__ out) {

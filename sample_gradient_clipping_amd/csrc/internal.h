@@ -70,6 +70,8 @@ hipError_t launch_aggregate_generic(const TIn* A, const TIn* G, int B, int T, in
 // c[i], optional c_out, status bit, and the active samples in ascending c order.
 hipError_t launch_clip(const float* n, int B, float C, float* c, float* c_out, uint32_t* status,
                        int* order, int* count, hipStream_t s);
+// w[1] = w[0], w[0] = 0 (one atomic exchange).
+hipError_t launch_take_status(uint32_t* w, hipStream_t s);
 // out[e] = sum_{sp < nsplit} part[sp][e].
 hipError_t launch_reduce_splits(const float* part, int nsplit, int64_t n, float* out, hipStream_t s);
 // Hutch++ probe for the last pass: rows 0..s-1 = orthonormal basis of the s

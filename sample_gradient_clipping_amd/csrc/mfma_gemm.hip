@@ -64,6 +64,12 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt lgkmcnt(0): the wave's LDS reads (and scalar loads) have returned;
+// vmcnt and expcnt unconstrained.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((0x3 << 14) | 0xF | (0x7 << 4));
+}
+
 __device__ __forceinline__ v4i16 tr_read(const unsigned char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
 }
@@ -216,7 +222,9 @@ __global__ void __launch_bounds__(512, 1) k_gemm_tokens(
   if (nstage > 2) issue(L2);
 
   // Stage s: wait for this wave's loads of s (loads of s+1, s+2 may stay in
-  // flight), barrier, refill the slot freed by stage s-1 with s+3, compute.
+  // flight) and for its own LDS reads of stage s-1 (lgkmcnt: every wave's
+  // reads of the slot that is refilled next have returned once all waves pass
+  // the barrier), barrier, refill the slot freed by stage s-1 with s+3, compute.
   auto stage = [&](int s, const unsigned char* cur, unsigned char* refill) {
     const int ahead = nstage - 1 - s;
     if (ahead >= 2)
@@ -225,6 +233,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_tokens(
       wait_vm<4>();
     else
       wait_vm<0>();
+    wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     if (s + 3 < nstage) issue(refill);
     compute(cur);

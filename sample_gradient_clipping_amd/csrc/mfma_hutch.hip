@@ -248,8 +248,9 @@ __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__
 // rows, summing the splits in order (eight loads in flight per thread), and
 // writes its fp64 partial; the last block of the sample to finish adds the
 // partials (a fixed-shape block reduction).  part and ctr are shared between blocks that may
-// sit on different XCDs (separate L2s): they are accessed with device-scope
-// atomics, and a vmcnt wait orders the partial before the counter.
+// sit on different XCDs (separate L2s): each block publishes its partial with
+// an agent-scope release (the counter's acq_rel increment), and the last
+// block's threads take an agent-scope acquire before they load the partials.
 // ---------------------------------------------------------------------------
 constexpr int kFrobPer = 512;
 
@@ -311,12 +312,12 @@ __global__ void __launch_bounds__(256) k_frob_finish(const float* __restrict__ Z
   double* pb = part + static_cast<int64_t>(b) * nchunk;
   if (threadIdx.x == 0) {
     __hip_atomic_store(pb + chunk, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    s_last = __hip_atomic_fetch_add(ctr + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+    s_last = __hip_atomic_fetch_add(ctr + b, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
              static_cast<uint32_t>(nchunk - 1);
   }
   __syncthreads();
   if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   // the last block: all threads load the chunk partials at once, then a
   // fixed-shape block reduction
   double t = 0.0;

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dp.dp_abi_version() == 1
+    assert dp.dp_abi_version() == 2
     for s in range(5):
         assert dp.dp_status_string(s).startswith("DP_")
     assert "unknown" in dp.dp_status_string(99)
@@ -89,9 +89,8 @@ def test_norm_est_rejects_bad_arguments(lib):
 
 
 def _agg(lib, dtype=0, B=2, T=8, d=8, p=8, A=FAKE, G=FAKE, n=FAKE, C=1.0, S=FAKE, ws=FAKE,
-         ws_bytes=1 << 30, c_out=NULL, status=NULL):
-    return lib.dp_clip_aggregate(dtype, B, T, d, p, A, G, n, C, c_out, status, S, ws, ws_bytes,
-                                 NULL)
+         ws_bytes=1 << 30, c_out=NULL):
+    return lib.dp_clip_aggregate(dtype, B, T, d, p, A, G, n, C, c_out, S, ws, ws_bytes, NULL)
 
 
 def test_clip_aggregate_rejects_bad_arguments(lib):
@@ -130,7 +129,7 @@ def test_noise_update_rejects_bad_arguments(lib):
 def _aggu(lib, dtype=0, B=2, T=8, d=8, p=8, A=FAKE, G=FAKE, n=FAKE, C=1.0, sigma=1.0, eta=0.1,
           th=ctypes.c_void_p(0x400000), S=NULL, ws=ctypes.c_void_p(0x800000), ws_bytes=1 << 20):
     return lib.dp_clip_aggregate_update(dtype, B, T, d, p, A, G, n, C, sigma, eta, 1, 0, th, S,
-                                        NULL, NULL, ws, ws_bytes, NULL)
+                                        NULL, ws, ws_bytes, NULL)
 
 
 def test_clip_aggregate_update_rejects_bad_arguments(lib):
@@ -149,6 +148,23 @@ def test_clip_aggregate_update_rejects_bad_arguments(lib):
     need = dp.dp_clip_aggregate_update_workspace("f32", 2, 8, 8, 8)
     assert need >= dp.dp_clip_aggregate_workspace("f32", 2, 8, 8, 8) + 8 * 8 * 4
     assert dp.dp_clip_aggregate_update_workspace("f32", 2, 8, 0, 8) is None
+
+
+def test_read_device_status_rejects_bad_arguments(lib):
+    E = dp.DP_ERR_INVALID_ARG
+    flags = ctypes.c_uint32(77)
+    assert lib.dp_read_device_status(NULL, ctypes.byref(flags), NULL) == E
+    assert lib.dp_read_device_status(FAKE, None, NULL) == E
+    assert lib.dp_read_device_status(FAKE_MIS, ctypes.byref(flags), NULL) == E
+    assert flags.value == 77  # untouched on an argument error
+
+
+def test_clip_workspaces_hold_the_status_word(lib):
+    # the status word sits in the first 8 bytes, so every clip workspace has them
+    assert dp.dp_clip_aggregate_workspace("f32", 1, 1, 1, 1) >= 8
+    assert dp.dp_clip_aggregate_update_workspace("f32", 1, 1, 1, 1) >= 8
+    assert lib.dp_rmsnorm_update_workspace(1, 1) >= 8
+    assert lib.dp_embedding_update_workspace(0, 1, 0, 1, 1) >= 8
 
 
 def test_test_hooks_reject_bad_arguments(lib):
@@ -207,7 +223,7 @@ def test_rmsnorm_entry_points_reject_bad_arguments(lib):
     def upd(B=2, d=8, v=FAKE, n=FAKE, C=1.0, sigma=1.0, eta=0.1, gamma=FAKE, ws=FAKE,
             ws_bytes=1 << 20):
         return lib.dp_rmsnorm_clip_aggregate_update(B, d, v, n, C, sigma, eta, 1, 0, gamma, NULL,
-                                                    NULL, NULL, ws, ws_bytes, NULL)
+                                                    NULL, ws, ws_bytes, NULL)
 
     assert upd(B=0) == E
     assert upd(C=0.0) == E
@@ -236,7 +252,7 @@ def test_embedding_entry_points_reject_bad_arguments(lib):
 
     def upd(B=2, T=8, d=8, V=16, C=1.0, Ep=FAKE, ws_bytes=1 << 20):
         return lib.dp_embedding_clip_aggregate_update(0, B, T, d, V, FAKE, FAKE, FAKE, C, 1.0, 0.1,
-                                                      1, 0, Ep, NULL, NULL, FAKE, ws_bytes, NULL)
+                                                      1, 0, Ep, NULL, FAKE, ws_bytes, NULL)
 
     assert upd(V=0) == E
     assert upd(B=0) == E

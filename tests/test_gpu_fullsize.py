@@ -1,10 +1,13 @@
 """GPU parity at the workloads' full sizes (the shapes and calls bench.py times).
 
-Per-sample norms are compared for every sample; the clipped sum and the update
-are compared on seeded sampled rows of the (p, d) outputs, which the oracle
-computes row by row.  The 112-layer stack is covered per layer shape (one
-layer of each distinct (d, p), norms accumulated over them), since its inputs
-(46 GB) cannot be drawn on the host in a test.
+Per-sample norms are compared for every sample, for the workload's estimator,
+for the other estimators its configuration compares it with, and for the exact
+ghost and FGC baselines (against the oracle's materialised ||A_i^T G_i||^2 of
+every sample); the clipped sum and the update are compared on seeded sampled
+rows of the (p, d) outputs, which the oracle computes row by row.  The
+112-layer stack is covered per layer shape (one layer of each distinct (d, p),
+norms accumulated over them), since its inputs (46 GB) cannot be drawn on the
+host in a test.
 Tolerances: bf16-input norms 2e-2 relative per sample; S within 1e-4 of its
 max (fp32 accumulation of exact bf16 products); theta' within 1e-5.
 """
@@ -31,9 +34,11 @@ def dev():
     return d
 
 
-def _step_and_check(dev, wl, layers, method, rows_per_layer=24, baselines=()):
+def _step_and_check(dev, wl, layers, method, rows_per_layer=24, baselines=(), estimators=()):
     """Norms over `layers` (accumulated), clip + aggregate + update per layer;
-    compare to the oracle on all norms and on sampled rows."""
+    compare to the oracle on all norms and on sampled rows.  Then, on the first
+    layer, the other `estimators` (same probes as the oracle's) and the exact
+    `baselines` on every sample."""
     B, T, k = wl.B, wl.T, wl.k
     host = []
     n = torch.zeros(B, dtype=torch.float32, device=dev)
@@ -73,15 +78,24 @@ def _step_and_check(dev, wl, layers, method, rows_per_layer=24, baselines=()):
         assert es <= 1e-4
         assert et <= 1e-5
         del Ad, Gd, S, theta
-    for bl in baselines:  # exact baselines on the GPU against the oracle, samples 0 and B-1
-        l, A, G = host[0]
-        nb = torch.zeros(B, dtype=torch.float32, device=dev)
-        dp.dp_norm_est(bl, A.to(dev), G.to(dev), 0, 0, 0, nb)
+    l, A, G = host[0]
+    for est in estimators:  # another estimator, same seeded probes as the oracle's
+        ne = torch.zeros(B, dtype=torch.float32, device=dev)
+        dp.dp_norm_est(est, A.to(dev), G.to(dev), k, wl.method_seed, l.layer_id, ne)
         torch.cuda.synchronize()
-        for i in (0, B - 1):
-            ref = oracle.fgc_norm_sq(oracle.to_f64(A[i]), oracle.to_f64(G[i]))
-            e = abs(float(nb[i]) - ref) / ref
-            report(f"{wl.name} {bl} sample {i}", rel=e)
+        ref = oracle.norm_est(est, A, G, k=k, seed=wl.method_seed, layer=l.layer_id)
+        e = max_rel_elementwise(f64(ne), ref)
+        report(f"{wl.name} layer {l.name} {est} every sample", max_rel=e)
+        assert e <= 2e-2
+    if baselines:  # exact baselines against the materialised ||A_i^T G_i||^2 of every sample
+        exact = np.array([oracle.fgc_norm_sq(oracle.to_f64(A[i]), oracle.to_f64(G[i]))
+                          for i in range(B)])
+        for bl in baselines:
+            nb = torch.zeros(B, dtype=torch.float32, device=dev)
+            dp.dp_norm_est(bl, A.to(dev), G.to(dev), 0, 0, 0, nb)
+            torch.cuda.synchronize()
+            e = max_rel_elementwise(f64(nb), exact)
+            report(f"{wl.name} layer {l.name} {bl} every sample", max_rel=e)
             assert e <= 2e-2
 
 
@@ -93,12 +107,14 @@ def test_attention_projection(dev):
 @pytest.mark.parametrize("name", ["mlp_up_b8_t4096_d2048_p8192", "mlp_down_b8_t4096_d8192_p2048"])
 def test_mlp_hutchpp(dev, name):
     wl = WL[name]
-    _step_and_check(dev, wl, wl.layers, "hutchpp")
+    _step_and_check(dev, wl, wl.layers, "hutchpp", baselines=("ghost", "fgc"),
+                    estimators=("hutch",))
 
 
 def test_long_context(dev):
     wl = WL["long_ctx_b2_t16384_d2048_p8192"]
-    _step_and_check(dev, wl, wl.layers, "hutch", rows_per_layer=8, baselines=("ghost",))
+    _step_and_check(dev, wl, wl.layers, "hutch", rows_per_layer=8, baselines=("ghost", "fgc"),
+                    estimators=("hutchpp",))
 
 
 def test_llama_stack_layer_shapes(dev):

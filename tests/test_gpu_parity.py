@@ -82,6 +82,15 @@ NORM_CASES = [
     ("tiles_bf16_k7", "bf16", 2, 128, 128, 256, 7),
     ("wide_sketch_f32", "f32", 2, 64, 48, 300, 60),   # s = 20 > 16 sketch columns, ragged p
     ("rank_deficient_f32", "f32", 2, 4, 30, 40, 24),  # T = 4 < s = 8: dead pivots in the QR
+    # probe-count edge cases.  Generic kernels: fp32 or shapes off the MFMA tiles;
+    # MFMA kernels: bf16 with T % 128 == 0, p % 256 == 0, d % 256 == 0, k <= 32
+    # (Hutch++: s + r <= 32), where the probe block is padded to 32 columns.
+    ("k1_f32", "f32", 3, 40, 24, 20, 1),              # one probe, generic
+    ("k1_bf16_mfma", "bf16", 2, 256, 256, 512, 1),    # one probe, 31 padded columns
+    ("kp_f32", "f32", 2, 30, 20, 12, 12),             # k = p, generic (Hutch++: s = r = 4)
+    ("kp_bf16", "bf16", 2, 37, 50, 24, 24),           # k = p, generic bf16 kernels
+    ("k3_f32", "f32", 2, 64, 48, 40, 3),              # Hutch++ s = r = 1 with T > s, generic
+    ("k3_bf16_mfma", "bf16", 2, 256, 256, 512, 3),    # Hutch++ s = r = 1 with T > s, MFMA
 ]
 
 
@@ -165,6 +174,8 @@ def test_rademacher_probe_bit_exact(dev, seed, layer, sample, p, k):
 @pytest.mark.parametrize("case", NORM_CASES, ids=[c[0] for c in NORM_CASES])
 def test_norm_parity_rademacher(dev, method, case):
     name, dtype, B, T, d, p, k = case
+    if method == "hutchpp" and k < 3:
+        pytest.skip("Hutch++ needs k >= 3")
     recipe = "unit_u0.1_3" if dtype == "f32" else "llama_logu"
     A, G = linear_inputs(B, T, d, p, dtype, recipe, seed=13 + T)
     n = torch.full((B,), -1.0, dtype=torch.float32, device=dev)
@@ -258,15 +269,15 @@ def test_clip_aggregate_parity(dev, case):
     C = float(np.median(np.sqrt(exact)))  # both branches of the clip
     c = torch.zeros(B, dtype=torch.float32, device=dev)
     S = torch.full((p, d), float("nan"), dtype=torch.float32, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-    dp.dp_clip_aggregate(A.to(dev), G.to(dev), n32.to(dev), C, S, c_out=c, status=status)
-    torch.cuda.synchronize()
+    ws = dp.clip_workspace(dp.dp_clip_aggregate_workspace(dtype, B, T, d, p), dev)
+    dp.dp_clip_aggregate(A.to(dev), G.to(dev), n32.to(dev), C, S, c_out=c, ws=ws)
+    status = dp.dp_read_device_status(ws)
     c_ref, flag = oracle.clip_factors(n32.double().numpy(), C)
     S_ref = oracle.aggregate(A, G, c_ref)
     ec = max_rel_elementwise(f64(c), c_ref)
     es = max_rel_normwise(f64(S), S_ref)
     report(f"aggregate {name}", c_err=ec, S_err=es)
-    assert int(status.item()) == 0 and not flag
+    assert status == 0 and not flag
     assert np.any(c_ref < 1) and np.any(c_ref == 1)
     assert ec <= TOL_F32
     assert es <= (TOL_F32 if dtype == "f32" else 1e-4)
@@ -280,14 +291,43 @@ def test_clip_nonfinite_dropped_and_flagged(dev, dtype, shape):
     n = torch.tensor([4.0, float("nan"), 0.25, float("inf")], dtype=torch.float32)
     c = torch.zeros(B, dtype=torch.float32, device=dev)
     S = torch.empty(p, d, dtype=torch.float32, device=dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-    dp.dp_clip_aggregate(A.to(dev), G.to(dev), n.to(dev), 1.0, S, c_out=c, status=status)
-    torch.cuda.synchronize()
+    ws = dp.clip_workspace(dp.dp_clip_aggregate_workspace(dtype, B, T, d, p), dev)
+    dp.dp_clip_aggregate(A.to(dev), G.to(dev), n.to(dev), 1.0, S, c_out=c, ws=ws)
+    status = dp.dp_read_device_status(ws)
     c_ref, flag = oracle.clip_factors(n.double().numpy(), 1.0)
-    assert flag and int(status.item()) == dp.DP_STATUS_NONFINITE_NORM
+    assert flag and status == dp.DP_STATUS_NONFINITE_NORM
     assert np.array_equal(f64(c), c_ref)
     S_ref = oracle.aggregate(A, G, c_ref)
     assert max_rel_normwise(f64(S), S_ref) <= (TOL_F32 if dtype == "f32" else 1e-4)
+
+
+def test_device_status_sticky_until_read(dev):
+    """A NaN norm sets the workspace's status flag; calls with finite norms that
+    reuse the workspace leave it set; dp_read_device_status reports it once and
+    clears it.  The same word serves the fused call and the gain update."""
+    B, T, d, p = 4, 64, 256, 256
+    A, G = linear_inputs(B, T, d, p, "bf16", "llama_logu", seed=12)
+    Ad, Gd = A.to(dev), G.to(dev)
+    good = torch.tensor([4.0, 0.5, 2.0, 9.0], dtype=torch.float32, device=dev)
+    bad = torch.tensor([4.0, float("nan"), 2.0, 9.0], dtype=torch.float32, device=dev)
+    S = torch.empty(p, d, dtype=torch.float32, device=dev)
+    ws = dp.clip_workspace(dp.dp_clip_aggregate_update_workspace("bf16", B, T, d, p), dev)
+    dp.dp_clip_aggregate(Ad, Gd, good, 1.0, S, ws=ws)
+    assert dp.dp_read_device_status(ws) == 0
+    dp.dp_clip_aggregate(Ad, Gd, bad, 1.0, S, ws=ws)
+    dp.dp_clip_aggregate(Ad, Gd, good, 1.0, S, ws=ws)  # a later clean call keeps the flag
+    assert dp.dp_read_device_status(ws) == dp.DP_STATUS_NONFINITE_NORM
+    assert dp.dp_read_device_status(ws) == 0          # cleared by the read
+    theta = torch.zeros(p, d, dtype=torch.float32, device=dev)
+    dp.dp_clip_aggregate_update(Ad, Gd, bad, 1.0, 1.0, 1e-4, 5, 0, theta, ws=ws)
+    assert dp.dp_read_device_status(ws) == dp.DP_STATUS_NONFINITE_NORM
+    v = torch.ones(B, d, dtype=torch.float32, device=dev)
+    gamma = torch.zeros(d, dtype=torch.float32, device=dev)
+    wg = dp.clip_workspace(dp.load_library().dp_rmsnorm_update_workspace(B, d), dev)
+    dp.dp_rmsnorm_clip_aggregate_update(v, good, 1.0, 1.0, 1e-4, 5, 1, gamma, ws=wg)
+    assert dp.dp_read_device_status(wg) == 0
+    dp.dp_rmsnorm_clip_aggregate_update(v, bad, 1.0, 1.0, 1e-4, 5, 1, gamma, ws=wg)
+    assert dp.dp_read_device_status(wg) == dp.DP_STATUS_NONFINITE_NORM
 
 
 def test_clip_all_dropped_gives_zero_sum(dev):
