@@ -28,7 +28,8 @@
  *  - Arguments are validated on the host before anything is enqueued; on an
  *    error nothing is enqueued and no output is touched.  DP_ERR_HIP means a
  *    launch failed (hipGetLastError); outputs are then undefined.
- *  - Calls are thread-safe (no mutable global state).  Concurrent calls that
+ *  - Calls are thread-safe (the only mutable global state is the lock-guarded
+ *    per-device address table of dp_norm_est_noalloc).  Concurrent calls that
  *    share a workspace or an output buffer race, as any stream work would.
  *  - Results are deterministic: no floating-point atomics; the same inputs and
  *    seeds give the same bits on the same device.
@@ -121,6 +122,32 @@ dp_status_t dp_norm_est(int method, int dtype, int B, int T, int d, int p, int k
                         const void *A, const void *G, uint64_t seed, uint32_t layer,
                         uint32_t flags, float *n_sq, void *ws, size_t ws_bytes,
                         dp_stream_t stream);
+
+/*
+ * dp_norm_est without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The arguments, results and errors are those of
+ * dp_norm_est (the same kernels); the workspace is instead a library-owned
+ * scratch array of DP_NOALLOC_SCRATCH_BYTES in device memory, one per GPU,
+ * held from the first call on that GPU until the process ends.  No call
+ * allocates or frees anything.
+ *  - Returns DP_ERR_WORKSPACE, with nothing enqueued, when
+ *    dp_norm_est_workspace(...) of the arguments exceeds
+ *    DP_NOALLOC_SCRATCH_BYTES (it covers Hutch and Hutch++ with k <= 32 on
+ *    every layer of a Llama-3.2-1B-sized model at B = 8, T = 4096, and the
+ *    ghost baseline; FGC's per-sample d x p matrices mostly do not fit).
+ *  - Every call on one GPU shares that GPU's array: calls that may overlap
+ *    (different streams, or different host threads, on the same GPU) race and
+ *    must be ordered by the caller.  Calls on one stream are ordered.
+ *  - The array keeps the last call's contents; the kernels need no part of it
+ *    to start at zero.
+ *  - The first call on a GPU looks up the array's device address (a host-side
+ *    runtime query, guarded by a lock); DP_ERR_HIP if that fails.
+ */
+#define DP_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+dp_status_t dp_norm_est_noalloc(int method, int dtype, int B, int T, int d, int p, int k,
+                                const void *A, const void *G, uint64_t seed, uint32_t layer,
+                                uint32_t flags, float *n_sq, dp_stream_t stream);
 
 /* Bytes of workspace dp_clip_aggregate needs, or (size_t)-1 if invalid. */
 size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p);

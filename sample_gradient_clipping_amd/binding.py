@@ -57,6 +57,8 @@ def load_library():
     L.dp_norm_est_workspace.restype = c_sz
     L.dp_norm_est.argtypes = [c_int] * 7 + [c_p, c_p, c_u64, c_u32, c_u32, c_p, c_p, c_sz, c_p]
     L.dp_norm_est.restype = c_int
+    L.dp_norm_est_noalloc.argtypes = [c_int] * 7 + [c_p, c_p, c_u64, c_u32, c_u32, c_p, c_p]
+    L.dp_norm_est_noalloc.restype = c_int
     L.dp_clip_aggregate_workspace.argtypes = [c_int] * 5
     L.dp_clip_aggregate_workspace.restype = c_sz
     L.dp_clip_aggregate.argtypes = [c_int] * 5 + [c_p, c_p, c_p, c_f, c_p, c_p, c_p, c_sz, c_p]
@@ -238,6 +240,23 @@ def dp_norm_est(method, A, G, k, seed, layer, n_sq, flags=0, ws=None, stream=Non
     else:
         st = L.dp_norm_est_timed(*args, _event(events[0]), _event(events[1]))
     _check(st, "dp_norm_est")
+    return n_sq
+
+
+DP_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def dp_norm_est_noalloc(method, A, G, k, seed, layer, n_sq, flags=0, stream=None):
+    """dp_norm_est on the library's own per-GPU scratch array (no workspace, no
+    allocation); raises DprcError(DP_ERR_WORKSPACE) when the call needs more
+    than DP_NOALLOC_SCRATCH_BYTES."""
+    L = load_library()
+    B, T, d = A.shape
+    p = G.shape[2]
+    st = L.dp_norm_est_noalloc(_method_code(method), _dtype_code(A), B, T, d, p, int(k or 0),
+                               _ptr(A), _ptr(G), int(seed) & (2**64 - 1), int(layer), int(flags),
+                               _ptr(n_sq), _stream(stream))
+    _check(st, "dp_norm_est_noalloc")
     return n_sq
 
 

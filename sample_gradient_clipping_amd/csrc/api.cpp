@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 
 #include "dprc.h"
 #include "internal.h"
@@ -23,6 +24,7 @@ constexpr size_t kInvalid = static_cast<size_t>(-1);
 // its workspace (read and cleared by dp_read_device_status); the word after it
 // receives the value being read.
 constexpr size_t kStatusBytes = 8;
+constexpr int kMaxDevices = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -415,6 +417,43 @@ dp_status_t dp_norm_est_timed(int method, int dtype, int B, int T, int d, int p,
   return norm_est_impl(method, dtype, B, T, d, p, k, A, G, seed, layer, flags, n_sq, ws, ws_bytes,
                        stream,
                        Marks{static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)});
+}
+
+// ---- dp_norm_est_noalloc: the same call on a library-owned scratch array ----
+// Each GPU the library runs on holds its own copy of `scratch` until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol): the device address is looked up
+// once per device with hipGetSymbolAddress and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[DP_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex scratch_mu;
+static void* scratch_ptr[kMaxDevices];  // per-device address of `scratch`, set once
+
+static dp_status_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return DP_ERR_HIP;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return DP_OK;
+}
+
+dp_status_t dp_norm_est_noalloc(int method, int dtype, int B, int T, int d, int p, int k,
+                                const void* A, const void* G, uint64_t seed, uint32_t layer,
+                                uint32_t flags, float* n_sq, dp_stream_t stream) {
+  if (!norm_args_ok(method, dtype, B, T, d, p, k)) return DP_ERR_INVALID_ARG;
+  if (plan_norm(method, dtype, B, T, d, p, k).total > DP_NOALLOC_SCRATCH_BYTES)
+    return DP_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const dp_status_t st = scratch_address(&ws);
+  if (st != DP_OK) return st;
+  return norm_est_impl(method, dtype, B, T, d, p, k, A, G, seed, layer, flags, n_sq, ws,
+                       DP_NOALLOC_SCRATCH_BYTES, stream, Marks{});
 }
 
 size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p) {

@@ -88,6 +88,20 @@ def test_norm_est_rejects_bad_arguments(lib):
     assert _norm(lib, B=0) == dp.DP_OK    # empty batch: nothing to do
 
 
+def test_norm_est_noalloc_rejects_before_any_hip_call(lib):
+    # invalid sizes, and calls whose workspace exceeds the scratch array, return
+    # before the array's address is looked up
+    f = lambda method=0, dtype=1, B=8, T=128, d=2048, p=2048, k=32: lib.dp_norm_est_noalloc(
+        method, dtype, B, T, d, p, k, FAKE, FAKE, 1, 0, 0, FAKE, NULL)
+    assert f(method=7) == dp.DP_ERR_INVALID_ARG
+    assert f(k=0) == dp.DP_ERR_INVALID_ARG
+    assert f(d=0) == dp.DP_ERR_INVALID_ARG
+    assert dp.dp_norm_est_workspace("fgc", "bf16", 8, 128, 2048, 2048, 0) > dp.DP_NOALLOC_SCRATCH_BYTES
+    assert f(method=dp.DP_NORM_FGC, k=0) == dp.DP_ERR_WORKSPACE
+    assert dp.DP_NOALLOC_SCRATCH_BYTES == 64 << 20  # the header's DP_NOALLOC_SCRATCH_BYTES
+    assert "((size_t)64 << 20)" in open(HEADER).read()
+
+
 def _agg(lib, dtype=0, B=2, T=8, d=8, p=8, A=FAKE, G=FAKE, n=FAKE, C=1.0, S=FAKE, ws=FAKE,
          ws_bytes=1 << 30, c_out=NULL):
     return lib.dp_clip_aggregate(dtype, B, T, d, p, A, G, n, C, c_out, S, ws, ws_bytes, NULL)
