@@ -24,8 +24,11 @@
 // Pipeline.  Workgroup tile 256 x 256, eight waves of 128 (M) x 64 (N), four
 // LDS stages of 32 tokens.  Each stage lives in its own __shared__ array so
 // that the compiler can see the in-flight LDS DMA does not alias the stage
-// being read; the loop is unrolled over the four arrays.  Synchronisation is
-// an explicit vmcnt wait for this wave's loads of the stage plus a bare
+// being read; the loop is unrolled over the four arrays.  A stage's operands
+// are read from LDS into registers one step ahead of its products, so the
+// transposing reads of stage s+1 run under the MFMAs of stage s, and the slot
+// of stage s is refilled (stage s+4) as soon as every wave has read it.
+// Synchronisation is an explicit vmcnt wait for this wave's loads plus a bare
 // s_barrier (no fence that would drain the loads of later stages).
 //
 // Per-sample clip factors without a second accumulator: the active samples are
@@ -166,18 +169,23 @@ __global__ void __launch_bounds__(512, 1) k_gemm_tokens(
   const uint32_t pair_step = static_cast<uint32_t>(2 * ld * 2);
   const int dst_off = side * kSideBytes + pair0 * kPairBytes;
 
+  // The sample being loaded is looked up once per sample (its entry of the
+  // visiting order is read when the previous sample's last tile is issued), so
+  // that no stage waits on a scalar load after its barrier.
   int64_t ld_seg = kv0 / T;
   int ld_off = static_cast<int>(kv0 - ld_seg * T);
+  const int64_t nseg = MODE == 0 ? static_cast<int64_t>(*count) : 1;
+  int64_t ld_sample = MODE == 0 ? (nstage > 0 ? static_cast<int64_t>(order[ld_seg]) : 0)
+                                : static_cast<int64_t>(z);
   auto issue = [&](unsigned char* stage_lds) {
-    const int64_t sample =
-        MODE == 0 ? static_cast<int64_t>(order[ld_seg]) : static_cast<int64_t>(z);
     const unsigned char* base =
-        reinterpret_cast<const unsigned char*>(src + (sample * T + ld_off) * ld) + lane_src;
+        reinterpret_cast<const unsigned char*>(src + (ld_sample * T + ld_off) * ld) + lane_src;
     dma_pairs(base, pair_step, lds_addr_of(stage_lds) + dst_off);
     ld_off += kGK;
     if (ld_off == T) {
       ld_off = 0;
       ++ld_seg;
+      if (MODE == 0 && ld_seg < nseg) ld_sample = order[ld_seg];
     }
   };
 
@@ -196,37 +204,58 @@ __global__ void __launch_bounds__(512, 1) k_gemm_tokens(
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const unsigned char* st) {
-    v4i16 a[8][2];
+  // A stage's MFMA operands, read from LDS into registers one stage ahead of
+  // the products that use them.
+  struct Frag {
+    v4i16 a[8][2], b[4][2];
+  };
+  auto read_frags = [&](const unsigned char* st, Frag& f) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) a[i][h] = tr_read(st + rd_a + h * kRowBytes + i * 32);
+      for (int h = 0; h < 2; ++h) f.a[i][h] = tr_read(st + rd_a + h * kRowBytes + i * 32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i16 b0 = tr_read(st + rd_b + j * 32);
-      const v4i16 b1 = tr_read(st + rd_b + kRowBytes + j * 32);
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][j] = mfma_tr(a[i][0], a[i][1], b0, b1, acc[i][j]);
-    }
+      for (int h = 0; h < 2; ++h) f.b[j][h] = tr_read(st + rd_b + h * kRowBytes + j * 32);
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        acc[i][j] = mfma_tr(f.a[i][0], f.a[i][1], f.b[j][0], f.b[j][1], acc[i][j]);
   };
 
   unsigned char* L0 = g_lds0;
   unsigned char* L1 = g_lds1;
   unsigned char* L2 = g_lds2;
   unsigned char* L3 = g_lds3;
+  Frag F0, F1;
 
-  // Prologue: stages 0..2 in flight.
+  // Prologue: stages 0..2 in flight; once stage 0 has landed everywhere, its
+  // operands go to registers and stage 3 fills the fourth slot.
   if (nstage > 0) issue(L0);
   if (nstage > 1) issue(L1);
   if (nstage > 2) issue(L2);
+  if (nstage > 2)
+    wait_vm<8>();
+  else if (nstage > 1)
+    wait_vm<4>();
+  else
+    wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  if (nstage > 0) read_frags(L0, F0);
+  if (nstage > 3) issue(L3);
 
-  // Stage s: wait for this wave's loads of s (loads of s+1, s+2 may stay in
-  // flight) and for its own LDS reads of stage s-1 (lgkmcnt: every wave's
-  // reads of the slot that is refilled next have returned once all waves pass
-  // the barrier), barrier, refill the slot freed by stage s-1 with s+3, compute.
-  auto stage = [&](int s, const unsigned char* cur, unsigned char* refill) {
-    const int ahead = nstage - 1 - s;
+  // Step s (stage s's operands are in `cur`): wait for this wave's loads of
+  // stage s+1 (those of s+2 and s+3 may stay in flight) and for its LDS reads
+  // of stage s; the barrier then certifies that stage s+1 has landed for every
+  // wave and that no wave still reads stage s's slot, which is refilled with
+  // stage s+4; stage s+1's operands are read while stage s's products run.
+  auto step = [&](int s, const Frag& cur, Frag& next, const unsigned char* next_lds,
+                  unsigned char* refill) {
+    const int ahead = nstage - 2 - s;  // stages issued beyond s+1
     if (ahead >= 2)
       wait_vm<8>();
     else if (ahead == 1)
@@ -235,8 +264,9 @@ __global__ void __launch_bounds__(512, 1) k_gemm_tokens(
       wait_vm<0>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
-    if (s + 3 < nstage) issue(refill);
-    compute(cur);
+    if (s + 4 < nstage) issue(refill);
+    if (s + 1 < nstage) read_frags(next_lds, next);
+    mma(cur);
   };
 
   float cur_c = 1.f;
@@ -258,10 +288,10 @@ __global__ void __launch_bounds__(512, 1) k_gemm_tokens(
         cur_seg = seg;
       }
     }
-    stage(s, L0, L3);
-    if (s + 1 < nstage) stage(s + 1, L1, L0);
-    if (s + 2 < nstage) stage(s + 2, L2, L1);
-    if (s + 3 < nstage) stage(s + 3, L3, L2);
+    step(s, F0, F1, L1, L0);
+    if (s + 1 < nstage) step(s + 1, F1, F0, L2, L1);
+    if (s + 2 < nstage) step(s + 2, F0, F1, L3, L2);
+    if (s + 3 < nstage) step(s + 3, F1, F0, L0, L3);
   }
   const float fin = (MODE == 0 && cur_seg >= 0) ? cur_c : 1.f;
 
