@@ -106,50 +106,99 @@ def make_inputs(wl, copies, dev):
     return out
 
 
-def cpu_baseline(wl, method, target_s=12.0, rademacher=False):
-    """The oracle (plain fp64 numpy) on a bounded sample of the workload."""
-    import numpy as np
-    import oracle
-    from sample_gradient_clipping_amd.inputs import linear_inputs
+def _cpu_threads():
+    """Host threads this process may use: its CPU affinity, capped by OMP_NUM_THREADS."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(cap))) if cap.isdigit() and int(cap) > 0 else max(1, n)
+
+
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS default
-        cores = os.cpu_count() or 1
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, method, target_s=15.0, rademacher=False):
+    """The CPU oracle on a bounded sample of the workload: the plain C++ fp64
+    oracle (std::thread, no BLAS) for Hutch with Gaussian probes, else the numpy
+    fp64 oracle.  One sampled step = Bs samples of the first block's linear
+    layers (all of them for a single layer) through norms, clip factors,
+    clipped sums, noise and update; a layer stack's time is scaled to all of
+    its blocks."""
+    import numpy as np
+    from sample_gradient_clipping_amd.inputs import linear_inputs
     layers = wl.layers
     scale_blocks = 1
     if len(layers) > 7:  # a layer stack: time block 0, extrapolate to all blocks
         scale_blocks = len(layers) // 7
         layers = layers[:7]
+    use_cpp = method == "hutch" and not rademacher
+    threads = _cpu_threads()
+    if use_cpp:
+        from oracle import cpp_oracle as co
+        co.load()
+        kind = "oracle (plain C++17 fp64, std::thread, no BLAS)"
+    else:
+        import oracle
+        kind = "oracle (numpy fp64)"
 
-    def run(Bs, reps=1):
+    def run(Bs):
         data = []
         for l in layers:
             A, G = linear_inputs(Bs, wl.T, l.d, l.p, wl.dtype, wl.recipe, wl.data_seed, l.layer_id)
-            data.append((l.layer_id, A, G, np.zeros((l.p, l.d))))
+            data.append((l, A, G))
+        t = {"norms": 0.0, "clip": 0.0, "aggregate": 0.0, "noise_update": 0.0}
+        if not use_cpp:
+            t0 = time.perf_counter()
+            oracle.dp_step([(l.layer_id, A, G, np.zeros((l.p, l.d))) for l, A, G in data], method,
+                           wl.k, wl.C, wl.sigma, wl.eta, wl.method_seed, wl.noise_seed,
+                           rademacher=rademacher)
+            return time.perf_counter() - t0, None
+        n = None
         t0 = time.perf_counter()
-        for _ in range(reps):
-            oracle.dp_step(data, method, wl.k, wl.C, wl.sigma, wl.eta, wl.method_seed,
-                           wl.noise_seed, rademacher=rademacher)
-        return time.perf_counter() - t0
+        for l, A, G in data:
+            n = co.hutch_norms(A, G, wl.k, wl.method_seed, l.layer_id, n=n, threads=threads)
+        t1 = time.perf_counter()
+        c, _ = co.clip_factors(n, wl.C)
+        t2 = time.perf_counter()
+        t["norms"], t["clip"] = t1 - t0, t2 - t1
+        for l, A, G in data:
+            t3 = time.perf_counter()
+            S = co.aggregate(A, G, c, threads=threads)
+            t4 = time.perf_counter()
+            co.noise_update(np.zeros((l.p, l.d)), S, wl.sigma, wl.C, wl.eta, Bs, wl.noise_seed,
+                            l.layer_id, threads=threads)
+            t["aggregate"] += t4 - t3
+            t["noise_update"] += time.perf_counter() - t4
+        return sum(t.values()), t
 
-    # one sample first; then as many samples (and, if the whole batch is quicker
-    # than that, repeated steps) as fill about `target_s` of CPU work
-    Bs, reps, t = 1, 1, run(1)
+    # one sample first, then as many samples as fill about `target_s`
+    Bs = 1
+    t, stages = run(1)
     if t < target_s and wl.B > 1:
         Bs = int(min(wl.B, max(2, target_s // max(t, 1e-3))))
-        t = run(Bs)
-        if t < 0.5 * target_s:
-            reps = int(min(20, -(-target_s // t)))
-            t = run(Bs, reps)
-    t_step = t * scale_blocks / reps
+        t, stages = run(Bs)
+    t_step = t * scale_blocks
     sample = (f"{Bs} of {wl.B} samples x {wl.T} tokens, {len(layers)} of {len(wl.layers)} linear "
-              f"layers" + (f", time x{scale_blocks} (extrapolated to all blocks)"
-                           if scale_blocks > 1 else "")
-              + f"; {reps} full oracle step(s) (norms, clip, aggregation, noise+update) "
-                f"in {t:.2f} s")
-    return {"value": Bs * wl.T / t_step, "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle", "sample": sample}
+              f"layers, one step (norms, clip, clipped sums, noise + update) in {t:.2f} s"
+              + (f"; time x{scale_blocks} (extrapolated to all blocks)" if scale_blocks > 1 else ""))
+    out = {"value": Bs * wl.T / t_step, "unit": "tokens/s", "cores": threads if use_cpp else None,
+           "kind": "oracle", "implementation": kind, "sample": sample, "cpu_model": _cpu_model()}
+    if use_cpp:
+        out["stage_seconds"] = stages
+        out["hardware_concurrency"] = co.hardware_concurrency()
+    else:
+        try:
+            from threadpoolctl import threadpool_info
+            out["cores"] = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # threadpoolctl missing: numpy's BLAS default
+            out["cores"] = os.cpu_count() or 1
+    return out
 
 
 def estimator_accuracy(dp, wl, layer_inputs, dev, nseeds=8, rademacher=False):
