@@ -56,7 +56,7 @@ struct NormPlan {
   int nsplit_d = 1, nsplit_p = 1, nchunk = 1, nparts = 0;
   // offsets (bytes) into the workspace; unused ones stay 0
   size_t pf = 0, pb = 0, y = 0, yb = 0, z = 0, zp = 0, z1b = 0, v = 0, xp = 0, x = 0, p3 = 0,
-         p3b = 0, m = 0, part = 0, orth = 0, ctr = 0;
+         p3b = 0, m = 0, part = 0, orth = 0;
   size_t total = 0;
 };
 
@@ -86,8 +86,6 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
       P.pb = cv.take(Bz * kMfmaProbeCols * p * h2);
       P.yb = cv.take(Bz * kMfmaProbeCols * T * h2);
       P.zp = cv.take(Bz * P.nsplit_d * kMfmaProbeCols * d * f4);
-      P.ctr = cv.take(Bz * 4);
-      P.nchunk = frob_finish_chunks(d);
     } else {
       P.pf = cv.take(Bz * k * p * f4);
       P.y = cv.take(Bz * k * T * f4);
@@ -112,8 +110,6 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
       P.z1b = cv.take(Bz * kMfmaProbeCols * d * h2);
       P.xp = cv.take(Bz * P.nsplit_p * kMfmaProbeCols * p * f4);
       P.p3b = cv.take(Bz * kMfmaProbeCols * p * h2);
-      P.ctr = cv.take(Bz * 4);
-      P.nchunk = frob_finish_chunks(d);
     } else {
       P.y = cv.take(Bz * P.k3 * (T > 0 ? T : 1) * f4);
       P.z = cv.take(Bz * P.k3 * d * f4);
@@ -131,7 +127,8 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
     P.nchunk = frob_chunks(static_cast<int64_t>(p) * d);
   }
   const int nparts = method == DP_NORM_GHOST ? P.nparts : P.nchunk;
-  P.part = cv.take(Bz * (nparts > 0 ? nparts : 1) * sizeof(double));
+  if (!P.mfma || method == DP_NORM_GHOST || method == DP_NORM_FGC)  // the MFMA Hutch finish needs none
+    P.part = cv.take(Bz * (nparts > 0 ? nparts : 1) * sizeof(double));
   P.total = cv.off;
   return P;
 }
@@ -182,17 +179,14 @@ dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, i
   bf16_t* Pb = at<bf16_t>(ws, P.pb);
   bf16_t* Yb = at<bf16_t>(ws, P.yb);
   float* Zp = at<float>(ws, P.zp);
-  double* part = at<double>(ws, P.part);
   const int nS = shared ? 1 : B;
   const int64_t pbs = shared ? 0 : static_cast<int64_t>(kMfmaProbeCols) * p;
-  uint32_t* ctr = at<uint32_t>(ws, P.ctr);
-  DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, k, kMfmaProbeCols, Pb, s, signs, ctr, B));
+  DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, k, kMfmaProbeCols, Pb, s, signs));
   DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_mfma(G, B, T, p, Pb, pbs, Yb, s));
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
   DP_TRY(mk.close(s));
-  DP_TRY(launch_frob_finish(Zp, B, P.nsplit_d, d, k, 1.0f / k, 0, 0.f, part, ctr, n_sq,
-                            accum ? 1 : 0, s));
+  DP_TRY(launch_frob_finish(Zp, B, P.nsplit_d, d, k, 1.0f / k, 0, 0.f, n_sq, accum ? 1 : 0, s));
   return DP_OK;
 }
 
@@ -243,15 +237,13 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
   bf16_t* Z1b = at<bf16_t>(ws, P.z1b);
   float* Xp = at<float>(ws, P.xp);
   bf16_t* P3b = at<bf16_t>(ws, P.p3b);
-  double* part = at<double>(ws, P.part);
   const int nS = shared ? 1 : B;
   const int64_t pfs = shared ? 0 : static_cast<int64_t>(K3) * p;
   const int64_t pbs = shared ? 0 : static_cast<int64_t>(kMfmaProbeCols) * p;
   const int64_t pad_d = static_cast<int64_t>(kMfmaProbeCols) * d;
   const int64_t pad_p = static_cast<int64_t>(kMfmaProbeCols) * p;
-  uint32_t* ctr = at<uint32_t>(ws, P.ctr);
   DP_TRY(launch_probe_fill_f32(seed, layer, 0, nS, p, K3, K3, Pf, s, signs));
-  DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, S_, kMfmaProbeCols, Pb, s, signs, ctr, B));
+  DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, S_, kMfmaProbeCols, Pb, s, signs));
   // pass 1: Z1 = A^T (G S)
   DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_mfma(G, B, T, p, Pb, pbs, Yb, s));
@@ -267,8 +259,8 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
   DP_TRY(launch_sketch_mfma(G, B, T, p, P3b, pad_p, Yb, s));
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
   DP_TRY(mk.close(s));
-  DP_TRY(launch_frob_finish(Zp, B, P.nsplit_d, d, S_, 1.0f, R_, 1.0f / R_, part, ctr, n_sq,
-                            accum ? 1 : 0, s));
+  DP_TRY(launch_frob_finish(Zp, B, P.nsplit_d, d, S_, 1.0f, R_, 1.0f / R_, n_sq, accum ? 1 : 0,
+                            s));
   return DP_OK;
 }
 

@@ -26,7 +26,7 @@ hipError_t launch_probe_fill_f32(uint64_t seed, uint32_t layer, uint32_t sample0
 // of the same call), saving a launch.
 hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
                                   int p, int kfill, int kpad, bf16_t* out, hipStream_t s,
-                                  bool signs = false, uint32_t* zero = nullptr, int nzero = 0);
+                                  bool signs = false);
 hipError_t launch_noise_fill(uint64_t seed, uint32_t layer, uint64_t offset, size_t n, float* xi,
                              hipStream_t s);
 hipError_t launch_noise_update(float* theta, const float* S, int64_t n, float sigmaC,
@@ -145,13 +145,10 @@ hipError_t launch_sketch_mfma(const bf16_t* X, int B, int T, int W, const bf16_t
 hipError_t launch_project_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* Y, int nsplit,
                                float* Zp, hipStream_t s);
 // n_sq[b] (= or +=) sum_j w_j ||sum_split Zp[b][split][j][:]||^2 with w_j = w0
-// for j < n0, w1 for n0 <= j < n0 + n1, else 0 (W % 4 == 0).  One launch:
-// part[b][chunk] (fp64) per block, then the last block of a sample sums them
-// in order.  ctr: B counters, zero on entry.
-int frob_finish_chunks(int W);
+// for j < n0, w1 for n0 <= j < n0 + n1, else 0 (W % 4 == 0).  One block per
+// sample, fixed-order fp64 sums.
 hipError_t launch_frob_finish(const float* Zp, int B, int nsplit, int W, int n0, float w0, int n1,
-                              float w1, double* part, uint32_t* ctr, float* n_sq, int accumulate,
-                              hipStream_t s);
+                              float w1, float* n_sq, int accumulate, hipStream_t s);
 
 // Ghost norm per sample from 128 x 128 Gram tile pairs: part[b][pair] (fp64).
 bool mfma_ghost_ok(int T, int d, int p);

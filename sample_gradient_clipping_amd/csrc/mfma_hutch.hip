@@ -244,99 +244,70 @@ __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__
 // ---------------------------------------------------------------------------
 // Finish (randomized-clipping summary, section 中核メカニズム, item 1: the
 // estimate is the weighted squared Frobenius norm of Z = sum of the token
-// splits).  Block (chunk, b) streams kFrobPer float4 of sample b's [32][W]
-// rows, summing the splits in order (eight loads in flight per thread), and
-// writes its fp64 partial; the last block of the sample to finish adds the
-// partials (a fixed-shape block reduction).  part and ctr are shared between blocks that may
-// sit on different XCDs (separate L2s): each block publishes its partial with
-// an agent-scope release (the counter's acq_rel increment), and the last
-// block's threads take an agent-scope acquire before they load the partials.
+// splits).  One block of 1024 threads per sample: each thread takes float4
+// positions u = tid + 1024 m of the sample's [32][W] rows, kFrobU of them with
+// every split's loads in flight together, sums the splits in order, and adds
+// the weighted squares in fp64; a block reduction in a fixed shape gives n_i.
+// Positions past the end load the last element (in bounds) and count zero, so
+// no load sits under a branch (the compiler would wait for it before the join).
+// No block communicates with another, so no atomics or fences are needed and
+// the result is deterministic.
 // ---------------------------------------------------------------------------
-constexpr int kFrobPer = 512;
+constexpr int kFrobThreads = 1024, kFrobU = 8;
 
-__global__ void __launch_bounds__(256) k_frob_finish(const float* __restrict__ Zp, int nsplit, int W,
-                                                     int n0, float w0, int n1, float w1,
-                                                     double* part, uint32_t* ctr,
-                                                     float* __restrict__ n_sq, int accumulate) {
+__global__ void __launch_bounds__(kFrobThreads) k_frob_finish(const float* __restrict__ Zp,
+                                                              int nsplit, int W, int n0, float w0,
+                                                              int n1, float w1,
+                                                              float* __restrict__ n_sq,
+                                                              int accumulate) {
   __shared__ double red[16];
-  __shared__ int s_last;
-  const int b = blockIdx.y, chunk = blockIdx.x, nchunk = gridDim.x;
+  const int b = blockIdx.x;
   const int E4 = kMfmaProbeCols * W / 4;
   const float4* zb = reinterpret_cast<const float4*>(Zp) + static_cast<int64_t>(b) * nsplit * E4;
-  const int u1 = (chunk + 1) * kFrobPer < E4 ? (chunk + 1) * kFrobPer : E4;
-  // The thread's kFrobPer / 256 = 2 positions, every split's loads of both in
-  // flight together (positions past the end read the last one, in bounds, and
-  // count zero).
-  static_assert(kFrobPer == 2 * 256, "two positions per thread of a 256-thread block");
-  int u[2];
-  bool in[2];
-  float4 z[2];
+  double acc = 0.0;
+  for (int u0 = 0; u0 < E4; u0 += kFrobThreads * kFrobU) {
+    int uc[kFrobU];
+    float4 z[kFrobU];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int uq = chunk * kFrobPer + threadIdx.x + 256 * q;
-    in[q] = uq < u1;
-    u[q] = in[q] ? uq : u1 - 1;
-    z[q] = float4{0.f, 0.f, 0.f, 0.f};
-  }
-  for (int s0 = 0; s0 < nsplit; s0 += 4) {
-    float4 v[2][4];
+    for (int q = 0; q < kFrobU; ++q) {
+      const int u = u0 + threadIdx.x + kFrobThreads * q;
+      uc[q] = u < E4 ? u : E4 - 1;
+      z[q] = zb[uc[q]];
+    }
+    for (int sp = 1; sp < nsplit; ++sp) {
+      float4 v[kFrobU];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sp = s0 + i < nsplit ? s0 + i : nsplit - 1;
+      for (int q = 0; q < kFrobU; ++q) v[q] = zb[static_cast<int64_t>(sp) * E4 + uc[q]];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) v[q][i] = zb[static_cast<int64_t>(sp) * E4 + u[q]];
+      for (int q = 0; q < kFrobU; ++q) {
+        z[q].x += v[q].x;
+        z[q].y += v[q].y;
+        z[q].z += v[q].z;
+        z[q].w += v[q].w;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (s0 + i < nsplit) {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          z[q].x += v[q][i].x;
-          z[q].y += v[q][i].y;
-          z[q].z += v[q][i].z;
-          z[q].w += v[q][i].w;
-        }
-      }
-  }
-  double acc = 0.0;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int j = (4 * u[q]) / W;
-    const float w = j < n0 ? w0 : (j < n0 + n1 ? w1 : 0.f);
-    if (in[q] && w != 0.f)
-      acc += static_cast<double>(w) *
-             (static_cast<double>(z[q].x) * z[q].x + static_cast<double>(z[q].y) * z[q].y +
-              static_cast<double>(z[q].z) * z[q].z + static_cast<double>(z[q].w) * z[q].w);
+    for (int q = 0; q < kFrobU; ++q) {
+      const int u = u0 + threadIdx.x + kFrobThreads * q;
+      const int j = (4 * u) / W;  // probe column of this float4 (W % 4 == 0)
+      const float w = j < n0 ? w0 : (j < n0 + n1 ? w1 : 0.f);
+      if (u < E4 && w != 0.f)
+        acc += static_cast<double>(w) *
+               (static_cast<double>(z[q].x) * z[q].x + static_cast<double>(z[q].y) * z[q].y +
+                static_cast<double>(z[q].z) * z[q].z + static_cast<double>(z[q].w) * z[q].w);
+    }
   }
   acc = block_sum_d(acc, red);
-  double* pb = part + static_cast<int64_t>(b) * nchunk;
-  if (threadIdx.x == 0) {
-    __hip_atomic_store(pb + chunk, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = __hip_atomic_fetch_add(ctr + b, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-             static_cast<uint32_t>(nchunk - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  // the last block: all threads load the chunk partials at once, then a
-  // fixed-shape block reduction
-  double t = 0.0;
-  for (int i = threadIdx.x; i < nchunk; i += blockDim.x)
-    t += __hip_atomic_load(pb + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  t = block_sum_d(t, red);
   if (threadIdx.x == 0)
-    n_sq[b] = static_cast<float>(accumulate ? static_cast<double>(n_sq[b]) + t : t);
+    n_sq[b] = static_cast<float>(accumulate ? static_cast<double>(n_sq[b]) + acc : acc);
 }
 
-int frob_finish_chunks(int W) { return (kMfmaProbeCols * W / 4 + kFrobPer - 1) / kFrobPer; }
-
 hipError_t launch_frob_finish(const float* Zp, int B, int nsplit, int W, int n0, float w0, int n1,
-                              float w1, double* part, uint32_t* ctr, float* n_sq, int accumulate,
-                              hipStream_t s) {
+                              float w1, float* n_sq, int accumulate, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (W % 4 != 0 || nsplit < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_frob_finish, dim3(frob_finish_chunks(W), B), dim3(256), 0, s, Zp, nsplit,
-                     W, n0, w0, n1, w1, part, ctr, n_sq, accumulate);
+  hipLaunchKernelGGL(k_frob_finish, dim3(B), dim3(kFrobThreads), 0, s, Zp, nsplit, W, n0, w0, n1,
+                     w1, n_sq, accumulate);
   return hipGetLastError();
 }
 

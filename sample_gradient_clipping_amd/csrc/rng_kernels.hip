@@ -42,13 +42,11 @@ hipError_t launch_philox_u32(uint64_t seed, const uint32_t* ctr, uint32_t* out, 
 template <typename TOut>
 __global__ void k_probe_fill(uint32_t k0, uint32_t k1, uint32_t layer, uint32_t sample0, int p,
                              int kfill, int kpad, TOut* __restrict__ out,
-                             uint32_t* __restrict__ zero, int nzero, int signs) {
+                             int signs) {
   const int ngroups = (p + 3) >> 2;
   const int g = blockIdx.x * blockDim.x + threadIdx.x;
   const int j = blockIdx.y;
   const int i = blockIdx.z;
-  if (zero != nullptr && blockIdx.x == 0 && j == 0 && i == 0)
-    for (int t = threadIdx.x; t < nzero; t += blockDim.x) zero[t] = 0u;
   if (g >= ngroups) return;
   float z[4] = {0.f, 0.f, 0.f, 0.f};
   if (j < kfill) {
@@ -80,29 +78,26 @@ __global__ void k_probe_fill(uint32_t k0, uint32_t k1, uint32_t layer, uint32_t 
 
 template <typename TOut>
 static hipError_t probe_fill(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp, int p,
-                             int kfill, int kpad, TOut* out, hipStream_t s, bool signs,
-                             uint32_t* zero, int nzero) {
+                             int kfill, int kpad, TOut* out, hipStream_t s, bool signs) {
   if (nsamp <= 0 || p <= 0 || kpad <= 0) return hipSuccess;
   const int ngroups = (p + 3) >> 2;
   dim3 grid((ngroups + 255) / 256, kpad, nsamp);
   hipLaunchKernelGGL(k_probe_fill<TOut>, grid, dim3(256), 0, s, static_cast<uint32_t>(seed),
-                     static_cast<uint32_t>(seed >> 32), layer, sample0, p, kfill, kpad, out, zero,
-                     nzero, signs ? 1 : 0);
+                     static_cast<uint32_t>(seed >> 32), layer, sample0, p, kfill, kpad, out,
+                     signs ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_probe_fill_f32(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
                                  int p, int kfill, int kpad, float* out, hipStream_t s,
                                  bool signs) {
-  return probe_fill<float>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s, signs, nullptr,
-                           0);
+  return probe_fill<float>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s, signs);
 }
 
 hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
                                   int p, int kfill, int kpad, bf16_t* out, hipStream_t s,
-                                  bool signs, uint32_t* zero, int nzero) {
-  return probe_fill<bf16_t>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s, signs, zero,
-                            nzero);
+                                  bool signs) {
+  return probe_fill<bf16_t>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s, signs);
 }
 
 // xi[e - offset] for e in [offset, offset + n); one thread per counter group.
