@@ -14,6 +14,9 @@
 // (features) contiguous, which is the MFMA operand layout as stored: 64-feature
 // slabs of the two token blocks are staged in LDS and read with 16-byte reads.
 // Four waves of 64 x 64 (2 x 2 blocks of v_mfma_f32_32x32x16_bf16) per tile.
+// The tile pairs are dealt to the eight XCDs in contiguous runs of an order
+// that walks 8 x 8 super-tiles of token blocks, so that the 64 workgroups an
+// XCD holds at a time share 16 token blocks in its L2.
 #include "common.h"
 #include "internal.h"
 
@@ -89,6 +92,48 @@ __device__ __forceinline__ void gram_tile(const bf16_t* __restrict__ xs,
   }
 }
 
+// Upper-triangle pair index -> token blocks (sb, tb), sb <= tb.  With nb a
+// multiple of 8 the pairs are ordered in 8 x 8 super-tiles (I <= J, row by
+// row; a diagonal super-tile holds its 36 pairs a <= c), so that a run of 64
+// consecutive pairs needs only 16 token blocks; otherwise row by row.
+__device__ __forceinline__ void pair_blocks(int pair, int nb, int& sb, int& tb) {
+  int rem = pair;
+  if (nb % 8 == 0) {
+    const int nsup = nb / 8;
+    int I = 0, J = 0;
+    for (;;) {
+      const int size = I == J ? 36 : 64;
+      if (rem < size) break;
+      rem -= size;
+      if (++J == nsup) {
+        ++I;
+        J = I;
+      }
+    }
+    int a, c;
+    if (I == J) {
+      a = 0;
+      while (rem >= 8 - a) {
+        rem -= 8 - a;
+        ++a;
+      }
+      c = a + rem;
+    } else {
+      a = rem >> 3;
+      c = rem & 7;
+    }
+    sb = 8 * I + a;
+    tb = 8 * J + c;
+    return;
+  }
+  sb = 0;
+  while (rem >= nb - sb) {
+    rem -= nb - sb;
+    ++sb;
+  }
+  tb = sb + rem;
+}
+
 __global__ void __launch_bounds__(256) k_ghost_mfma(const bf16_t* __restrict__ A,
                                                     const bf16_t* __restrict__ G, int T, int d,
                                                     int p, double* __restrict__ part) {
@@ -96,13 +141,11 @@ __global__ void __launch_bounds__(256) k_ghost_mfma(const bf16_t* __restrict__ A
   __shared__ double red[4];
   const int b = blockIdx.y;
   const int nb = T / kTB;
-  // upper-triangle pair index -> (sb, tb), sb <= tb
-  int rem = blockIdx.x, sb = 0;
-  while (rem >= nb - sb) {
-    rem -= nb - sb;
-    ++sb;
-  }
-  const int tb = sb + rem;
+  const int npair = gridDim.x;
+  const int w = blockIdx.x;  // consecutive workgroups go to the eight XCDs in turn
+  const int pair = (npair % 8 == 0) ? (w % 8) * (npair / 8) + w / 8 : w;
+  int sb, tb;
+  pair_blocks(pair, nb, sb, tb);
   const bf16_t* as = A + (static_cast<int64_t>(b) * T + sb * kTB) * d;
   const bf16_t* at = A + (static_cast<int64_t>(b) * T + tb * kTB) * d;
   const bf16_t* gs = G + (static_cast<int64_t>(b) * T + sb * kTB) * p;
@@ -123,7 +166,7 @@ __global__ void __launch_bounds__(256) k_ghost_mfma(const bf16_t* __restrict__ A
   __syncthreads();
   if (threadIdx.x == 0) {
     const double w = sb == tb ? 1.0 : 2.0;
-    part[static_cast<int64_t>(b) * gridDim.x + blockIdx.x] = w * (red[0] + red[1] + red[2] + red[3]);
+    part[static_cast<int64_t>(b) * gridDim.x + pair] = w * (red[0] + red[1] + red[2] + red[3]);
   }
 }
 
