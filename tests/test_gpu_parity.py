@@ -330,6 +330,24 @@ def test_device_status_sticky_until_read(dev):
     assert dp.dp_read_device_status(wg) == dp.DP_STATUS_NONFINITE_NORM
 
 
+@pytest.mark.parametrize("dtype,shape", [("f32", (3, 40, 24, 20)), ("bf16", (3, 256, 256, 512))])
+def test_clip_none_clipped_gives_batch_gradient(dev, dtype, shape):
+    # C above every sample's norm: c = 1 for all, and S is the batch gradient G^T A
+    B, T, d, p = shape
+    A, G = linear_inputs(B, T, d, p, dtype, "llama_logu", seed=14)
+    exact = oracle.norm_est("fgc", A, G)
+    C = 2.0 * float(np.sqrt(exact.max()))
+    c = torch.zeros(B, dtype=torch.float32, device=dev)
+    S = torch.empty(p, d, dtype=torch.float32, device=dev)
+    dp.dp_clip_aggregate(A.to(dev), G.to(dev), torch.tensor(exact, dtype=torch.float32).to(dev), C, S,
+                         c_out=c)
+    torch.cuda.synchronize()
+    assert torch.all(c == 1.0).item()
+    Af, Gf = oracle.to_f64(A), oracle.to_f64(G)
+    batch = Gf.reshape(-1, p).T @ Af.reshape(-1, d)
+    assert max_rel_normwise(f64(S), batch) <= (TOL_F32 if dtype == "f32" else 1e-4)
+
+
 def test_clip_all_dropped_gives_zero_sum(dev):
     A, G = linear_inputs(2, 128, 256, 256, "bf16", "llama_logu", seed=9)
     n = torch.tensor([float("nan"), float("nan")], dtype=torch.float32, device=dev)
