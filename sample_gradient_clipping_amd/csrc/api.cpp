@@ -54,6 +54,7 @@ struct NormPlan {
   bool mfma = false;
   int s = 0, r = 0, k3 = 0;  // Hutch++ split
   int nsplit_d = 1, nsplit_p = 1, nchunk = 1, nparts = 0;
+  int sq_cols = 0;  // MFMA Hutch final pass: fused projection-and-square column block, 0 = split + finish
   // offsets (bytes) into the workspace; unused ones stay 0
   size_t pf = 0, pb = 0, y = 0, yb = 0, z = 0, zp = 0, z1b = 0, v = 0, xp = 0, x = 0, p3 = 0,
          p3b = 0, m = 0, part = 0, orth = 0;
@@ -82,10 +83,15 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
   if (method == DP_NORM_HUTCH) {
     P.mfma = bf && k <= kMfmaProbeCols && mfma_sketch_ok(T, p) && mfma_project_ok(T, d);
     if (P.mfma) {
-      P.nsplit_d = mfma_project_splits(B, T, d);
+      P.sq_cols = mfma_project_sq_cols(B, T, d);
       P.pb = cv.take(Bz * kMfmaProbeCols * p * h2);
       P.yb = cv.take(Bz * kMfmaProbeCols * T * h2);
-      P.zp = cv.take(Bz * P.nsplit_d * kMfmaProbeCols * d * f4);
+      if (P.sq_cols > 0) {
+        P.part = cv.take(Bz * (d / P.sq_cols) * sizeof(double));
+      } else {
+        P.nsplit_d = mfma_project_splits(B, T, d);
+        P.zp = cv.take(Bz * P.nsplit_d * kMfmaProbeCols * d * f4);
+      }
     } else {
       P.pf = cv.take(Bz * k * p * f4);
       P.y = cv.take(Bz * k * T * f4);
@@ -110,6 +116,8 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
       P.z1b = cv.take(Bz * kMfmaProbeCols * d * h2);
       P.xp = cv.take(Bz * P.nsplit_p * kMfmaProbeCols * p * f4);
       P.p3b = cv.take(Bz * kMfmaProbeCols * p * h2);
+      P.sq_cols = mfma_project_sq_cols(B, T, d);
+      if (P.sq_cols > 0) P.part = cv.take(Bz * (d / P.sq_cols) * sizeof(double));
     } else {
       P.y = cv.take(Bz * P.k3 * (T > 0 ? T : 1) * f4);
       P.z = cv.take(Bz * P.k3 * d * f4);
@@ -127,7 +135,7 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
     P.nchunk = frob_chunks(static_cast<int64_t>(p) * d);
   }
   const int nparts = method == DP_NORM_GHOST ? P.nparts : P.nchunk;
-  if (!P.mfma || method == DP_NORM_GHOST || method == DP_NORM_FGC)  // the MFMA Hutch finish needs none
+  if (!P.mfma || method == DP_NORM_GHOST || method == DP_NORM_FGC)  // MFMA Hutch: taken above
     P.part = cv.take(Bz * (nparts > 0 ? nparts : 1) * sizeof(double));
   P.total = cv.off;
   return P;
@@ -184,6 +192,13 @@ dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, i
   DP_TRY(launch_probe_fill_bf16(seed, layer, 0, nS, p, k, kMfmaProbeCols, Pb, s, signs));
   DP_TRY(mk.open(s));
   DP_TRY(launch_sketch_mfma(G, B, T, p, Pb, pbs, Yb, s));
+  if (P.sq_cols > 0) {
+    double* part = at<double>(ws, P.part);
+    DP_TRY(launch_project_sq_mfma(A, B, T, d, Yb, P.sq_cols, k, 1.0f / k, 0, 0.f, part, s));
+    DP_TRY(mk.close(s));
+    DP_TRY(launch_sum_parts(part, B, d / P.sq_cols, n_sq, accum ? 1 : 0, s));
+    return DP_OK;
+  }
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
   DP_TRY(mk.close(s));
   DP_TRY(launch_frob_finish(Zp, B, P.nsplit_d, d, k, 1.0f / k, 0, 0.f, n_sq, accum ? 1 : 0, s));
@@ -257,6 +272,13 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
                          pfs, B, p, S_, R_, P3, P3b, kMfmaProbeCols, at<double>(ws, P.orth), s));
   // pass 3
   DP_TRY(launch_sketch_mfma(G, B, T, p, P3b, pad_p, Yb, s));
+  if (P.sq_cols > 0) {
+    double* part = at<double>(ws, P.part);
+    DP_TRY(launch_project_sq_mfma(A, B, T, d, Yb, P.sq_cols, S_, 1.0f, R_, 1.0f / R_, part, s));
+    DP_TRY(mk.close(s));
+    DP_TRY(launch_sum_parts(part, B, d / P.sq_cols, n_sq, accum ? 1 : 0, s));
+    return DP_OK;
+  }
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
   DP_TRY(mk.close(s));
   DP_TRY(launch_frob_finish(Zp, B, P.nsplit_d, d, S_, 1.0f, R_, 1.0f / R_, n_sq, accum ? 1 : 0,

@@ -144,6 +144,13 @@ hipError_t launch_sketch_mfma(const bf16_t* X, int B, int T, int W, const bf16_t
 // Zp[b][split][j][q] (fp32, j < 32) = sum_{t in split} X[b][t][q] Y[b][j][t].
 hipError_t launch_project_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* Y, int nsplit,
                                float* Zp, hipStream_t s);
+// Column block (128 or 64) of the fused projection-and-square, 0 if it would
+// give fewer than 256 workgroups.
+int mfma_project_sq_cols(int B, int T, int W);
+// part[b][W / cols] (fp64) = sum_j w_j sum_{q in block} (sum_t X[b][t][q] Y[b][j][t])^2,
+// w_j as in launch_frob_finish; whole token range in one workgroup per block.
+hipError_t launch_project_sq_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* Y, int cols,
+                                  int n0, float w0, int n1, float w1, double* part, hipStream_t s);
 // n_sq[b] (= or +=) sum_j w_j ||sum_split Zp[b][split][j][:]||^2 with w_j = w0
 // for j < n0, w1 for n0 <= j < n0 + n1, else 0 (W % 4 == 0).  One block per
 // sample, fixed-order fp64 sums.

@@ -29,7 +29,9 @@
 // transposing reads of stage s+1 run under the MFMAs of stage s, and the slot
 // of stage s is refilled (stage s+4) as soon as every wave has read it.
 // Synchronisation is an explicit vmcnt wait for this wave's loads plus a bare
-// s_barrier (no fence that would drain the loads of later stages).
+// s_barrier (no fence that would drain the loads of later stages).  Inside a
+// step the 24 transposing reads are interleaved one by one with the first 24
+// of its 32 MFMAs.
 //
 // Per-sample clip factors without a second accumulator: the active samples are
 // visited in ascending c, and the accumulator holds sum_{seen} (c_seg / c_cur)
@@ -265,8 +267,19 @@ __global__ void __launch_bounds__(512, 1) k_gemm_tokens(
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     if (s + 4 < nstage) issue(refill);
-    if (s + 1 < nstage) read_frags(next_lds, next);
+    // Unconditional, so that the reads and the products share one basic block
+    // and can be interleaved: after the last stage this reads a slot that no
+    // later stage fills, and those operands are never used.
+    read_frags(next_lds, next);
     mma(cur);
+    // One transposing read after each of the first 24 products: the LDS reads
+    // then issue under the MFMA pipe instead of ahead of it.
+#pragma unroll
+    for (int k = 0; k < 24; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   float cur_c = 1.f;

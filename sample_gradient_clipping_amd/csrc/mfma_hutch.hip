@@ -26,27 +26,30 @@ __device__ __forceinline__ u32x4 ld16(const bf16_t* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Sketch.  A workgroup (4 waves) owns 16*MB tokens of one sample; wave w
-// reduces the quarter r in [w W/4, (w+1) W/4) in steps of 64.  In a step, lane
+// Sketch.  A workgroup (NW waves) owns 16*MB tokens of one sample; wave w
+// reduces the slice r in [w W/NW, (w+1) W/NW) in steps of 64.  In a step, lane
 // (m = l % 16, g = l / 16) loads 32 contiguous bytes of token row m at offset
 // 16 g; contraction slot (h, g, e) is r = r0 + 16 g + 8 h + e for both the
-// token rows (A operand) and the probe rows P^T[j] (B operand).  The four
-// waves' partial Y tiles are summed in LDS in a fixed order and stored as bf16
-// Y^T[b][j][t].
+// token rows (A operand) and the probe rows P^T[j] (B operand).  The waves'
+// partial Y tiles are summed in LDS in a fixed order and stored as bf16
+// Y^T[b][j][t].  Every workgroup re-reads its sample's probe rows (32 x W)
+// from L2: 64-token workgroups read half a byte of P per byte of X, 128-token
+// ones a quarter, which is what wide rows (W >= 4096) need; narrower rows keep
+// 64 tokens and four waves, whose loops would otherwise be too short.
 // ---------------------------------------------------------------------------
 constexpr int kSketchK = 64;
 
-template <int MB>
-__global__ void __launch_bounds__(256) k_sketch_mfma(const bf16_t* __restrict__ X, int T, int W,
+template <int MB, int NW>
+__global__ void __launch_bounds__(64 * NW) k_sketch_mfma(const bf16_t* __restrict__ X, int T, int W,
                                                      const bf16_t* __restrict__ P,
                                                      int64_t p_bstride, bf16_t* __restrict__ Y) {
   constexpr int TM = 16 * MB;
-  __shared__ float red[4][32][TM + 1];
+  __shared__ float red[NW][32][TM + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, g = lane >> 4;
   const int b = blockIdx.y;
   const int t0 = blockIdx.x * TM;
-  const int Wq = W >> 2;
+  const int Wq = W / NW;
   const int rbeg = wave * Wq + 16 * g;
 
   const bf16_t* xr[MB];
@@ -103,8 +106,9 @@ __global__ void __launch_bounds__(256) k_sketch_mfma(const bf16_t* __restrict__ 
       for (int i = 0; i < 4; ++i) red[wave][nb * 16 + m][mb * 16 + 4 * g + i] = acc[mb][nb][i];
   __syncthreads();
 
-  // 32 x TM outputs, TM / 8 consecutive tokens per thread.
+  // 32 x TM outputs over the first 256 threads, TM / 8 consecutive tokens each.
   constexpr int PER = TM / 8;
+  if (threadIdx.x >= 256) return;
   const int j = threadIdx.x >> 3;
   const int tc = (threadIdx.x & 7) * PER;
   uint32_t packed[PER / 2];
@@ -112,16 +116,19 @@ __global__ void __launch_bounds__(256) k_sketch_mfma(const bf16_t* __restrict__ 
   for (int u = 0; u < PER; u += 2) {
     float v0 = 0.f, v1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       v0 += red[w][j][tc + u];
       v1 += red[w][j][tc + u + 1];
     }
     packed[u / 2] = pack_bf16x2(v0, v1);
   }
   bf16_t* dst = Y + (static_cast<int64_t>(b) * kMfmaProbeCols + j) * T + t0 + tc;
-  if constexpr (PER == 8) {
-    u32x4 v{packed[0], packed[1], packed[2], packed[3]};
-    *reinterpret_cast<u32x4*>(dst) = v;
+  if constexpr (PER >= 8) {
+#pragma unroll
+    for (int c = 0; c < PER / 8; ++c) {
+      u32x4 v{packed[4 * c], packed[4 * c + 1], packed[4 * c + 2], packed[4 * c + 3]};
+      *reinterpret_cast<u32x4*>(dst + 8 * c) = v;
+    }
   } else {
     uint2 v{packed[0], packed[1]};
     *reinterpret_cast<uint2*>(dst) = v;
@@ -134,27 +141,49 @@ hipError_t launch_sketch_mfma(const bf16_t* X, int B, int T, int W, const bf16_t
                               int64_t p_bstride, bf16_t* Y, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (!mfma_sketch_ok(T, W)) return hipErrorInvalidValue;
-  if (T % 64 == 0 && static_cast<int64_t>(B) * (T / 64) >= 512) {
-    hipLaunchKernelGGL(k_sketch_mfma<4>, dim3(T / 64, B), dim3(256), 0, s, X, T, W, P, p_bstride, Y);
+  if (T % 128 == 0 && W >= 4096 && W % (8 * kSketchK) == 0 &&
+      static_cast<int64_t>(B) * (T / 128) >= 256) {
+    hipLaunchKernelGGL((k_sketch_mfma<8, 8>), dim3(T / 128, B), dim3(512), 0, s, X, T, W, P,
+                       p_bstride, Y);
+  } else if (T % 64 == 0 && static_cast<int64_t>(B) * (T / 64) >= 512) {
+    hipLaunchKernelGGL((k_sketch_mfma<4, 4>), dim3(T / 64, B), dim3(256), 0, s, X, T, W, P,
+                       p_bstride, Y);
   } else {
-    hipLaunchKernelGGL(k_sketch_mfma<2>, dim3(T / 32, B), dim3(256), 0, s, X, T, W, P, p_bstride, Y);
+    hipLaunchKernelGGL((k_sketch_mfma<2, 4>), dim3(T / 32, B), dim3(256), 0, s, X, T, W, P,
+                       p_bstride, Y);
   }
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Project.  A workgroup owns 128 columns q of one sample and one token split;
-// wave w takes a contiguous quarter of the split in steps of 32 tokens.  In a
-// step, lane (m, g) loads tokens t0 + 8 g + e (e = 0..7) of the 16-byte column
-// group q0 + 8 m; an in-register 8 x 8 transpose of those 16-bit values gives
-// the A operand of eight MFMA blocks, block c holding rows q = q0 + 8 m + c.
-// The B operand is Y^T[j][t0 + 8 g .. + 7], one 16-byte load.  Contraction
-// slot (g, e) is token t0 + 8 g + e for both operands.
+// Project.  A workgroup owns 16 CW columns q of one sample (CW = 8: 128
+// columns, CW = 4: 64) and one token split; wave w takes a contiguous quarter
+// of the split in steps of 32 tokens.  In a step, lane (m, g) loads tokens
+// t0 + 8 g + e (e = 0..7) of the CW-column group q0 + CW m (16 or 8 bytes);
+// an in-register transpose of those 16-bit values gives the A operand of CW
+// MFMA blocks, block c holding rows q = q0 + CW m + c.  The B operand is
+// Y^T[j][t0 + 8 g .. + 7], one 16-byte load.  Contraction slot (g, e) is token
+// t0 + 8 g + e for both operands.
+//
+// SQ = false: the workgroup's 32 x 16 CW tile of Z (one split) is stored to
+// the fp32 partials Zp[b][split].  SQ = true (one split, so the tile is final):
+// the workgroup reduces it at once to sum_j w_j sum_q Z[j][q]^2 in fp64 (the
+// weighted squared Frobenius norm restricted to its columns; w_j = w0 for
+// j < n0, w1 for the next n1, 0 for padding) and stores that one double to
+// part[b][column block], so no Z partials are written or read back.
 // ---------------------------------------------------------------------------
-constexpr int kProjQ = 128;
 constexpr int kProjK = 32;
 
-__device__ __forceinline__ u32x4 transpose_col(const u32x4 (&rows)[8], int c) {
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int CW> struct ProjRow;
+template <> struct ProjRow<8> { typedef u32x4 type; };
+template <> struct ProjRow<4> { typedef u32x2 type; };
+
+// Column c of eight rows of 16-bit values (rows[e] holds 2 per dword), as the
+// MFMA's 8 contraction values (4 dwords, row e in slot e).
+template <typename R>
+__device__ __forceinline__ u32x4 transpose_col(const R (&rows)[8], int c) {
   u32x4 a;
   const int w = c >> 1;
   if ((c & 1) == 0) {
@@ -167,40 +196,48 @@ __device__ __forceinline__ u32x4 transpose_col(const u32x4 (&rows)[8], int c) {
   return a;
 }
 
+template <int CW, bool SQ>
 __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__ X, int T, int W,
                                                       const bf16_t* __restrict__ Y,
                                                       int split_tokens, int nsplit,
-                                                      float* __restrict__ Zp) {
-  __shared__ float red[4][32][kProjQ + 4];
+                                                      float* __restrict__ Zp, int n0, float w0,
+                                                      int n1, float w1,
+                                                      double* __restrict__ part) {
+  constexpr int kQ = 16 * CW;
+  typedef typename ProjRow<CW>::type RowT;
+  __shared__ float red[4][32][kQ + 4];
+  __shared__ double dred[16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, g = lane >> 4;
-  const int q0 = blockIdx.x * kProjQ;
+  const int q0 = blockIdx.x * kQ;
   const int split = blockIdx.y;
   const int b = blockIdx.z;
   const int tw = split_tokens >> 2;
   const int tbeg = split * split_tokens + wave * tw;
 
-  const bf16_t* xbase = X + (static_cast<int64_t>(b) * T + tbeg + 8 * g) * W + q0 + 8 * m;
+  const bf16_t* xbase = X + (static_cast<int64_t>(b) * T + tbeg + 8 * g) * W + q0 + CW * m;
   const bf16_t* yb0 = Y + (static_cast<int64_t>(b) * kMfmaProbeCols + m) * T + tbeg + 8 * g;
   const bf16_t* yb1 = yb0 + static_cast<int64_t>(16) * T;
 
-  f32x4 acc[8][2];
+  f32x4 acc[CW][2];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < CW; ++c) {
     acc[c][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  u32x4 rows[2][8], yv[2][2];
+  RowT rows[2][8];
+  u32x4 yv[2][2];
   auto load = [&](int buf, int t) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rows[buf][e] = ld16(xbase + static_cast<int64_t>(t + e) * W);
+    for (int e = 0; e < 8; ++e)
+      rows[buf][e] = *reinterpret_cast<const RowT*>(xbase + static_cast<int64_t>(t + e) * W);
     yv[buf][0] = ld16(yb0 + t);
     yv[buf][1] = ld16(yb1 + t);
   };
   auto compute = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < CW; ++c) {
       const u32x4 a = transpose_col(rows[buf], c);
       acc[c][0] = mfma16(a, yv[buf][0], acc[c][0]);
       acc[c][1] = mfma16(a, yv[buf][1], acc[c][1]);
@@ -218,26 +255,41 @@ __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__
     }
   }
 
+  // D[row][col] of block (c, nb) sits in lane (col, g), register i, row 4 g + i:
+  // probe j = 16 nb + col, column q0 + CW (4 g + i) + c.
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
+  for (int c = 0; c < CW; ++c)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][nb * 16 + m][8 * (4 * g + i) + c] = acc[c][nb][i];
+      for (int i = 0; i < 4; ++i) red[wave][nb * 16 + m][CW * (4 * g + i) + c] = acc[c][nb][i];
   __syncthreads();
 
-  // 32 x 128 outputs: thread -> row j = tid / 8, 16 consecutive q.
+  // 32 x kQ outputs: thread -> row j = tid / 8, kQ / 8 consecutive q.
+  constexpr int PER = kQ / 8;
   const int j = threadIdx.x >> 3;
-  const int qc = (threadIdx.x & 7) * 16;
-  float* dst = Zp + ((static_cast<int64_t>(b) * nsplit + split) * kMfmaProbeCols + j) * W + q0 + qc;
+  const int qc = (threadIdx.x & 7) * PER;
+  if constexpr (SQ) {
+    const float w = j < n0 ? w0 : (j < n0 + n1 ? w1 : 0.f);
+    double sq = 0.0;
 #pragma unroll
-  for (int u = 0; u < 16; u += 4) {
-    float4 v;
-    v.x = red[0][j][qc + u + 0] + red[1][j][qc + u + 0] + red[2][j][qc + u + 0] + red[3][j][qc + u + 0];
-    v.y = red[0][j][qc + u + 1] + red[1][j][qc + u + 1] + red[2][j][qc + u + 1] + red[3][j][qc + u + 1];
-    v.z = red[0][j][qc + u + 2] + red[1][j][qc + u + 2] + red[2][j][qc + u + 2] + red[3][j][qc + u + 2];
-    v.w = red[0][j][qc + u + 3] + red[1][j][qc + u + 3] + red[2][j][qc + u + 3] + red[3][j][qc + u + 3];
-    *reinterpret_cast<float4*>(dst + u) = v;
+    for (int u = 0; u < PER; ++u) {
+      const float z = red[0][j][qc + u] + red[1][j][qc + u] + red[2][j][qc + u] + red[3][j][qc + u];
+      sq += static_cast<double>(z) * z;
+    }
+    const double tot = block_sum_d(static_cast<double>(w) * sq, dred);
+    if (threadIdx.x == 0) part[static_cast<int64_t>(b) * gridDim.x + blockIdx.x] = tot;
+  } else {
+    float* dst = Zp + ((static_cast<int64_t>(b) * nsplit + split) * kMfmaProbeCols + j) * W + q0 + qc;
+#pragma unroll
+    for (int u = 0; u < PER; u += 4) {
+      float4 v;
+      v.x = red[0][j][qc + u + 0] + red[1][j][qc + u + 0] + red[2][j][qc + u + 0] + red[3][j][qc + u + 0];
+      v.y = red[0][j][qc + u + 1] + red[1][j][qc + u + 1] + red[2][j][qc + u + 1] + red[3][j][qc + u + 1];
+      v.z = red[0][j][qc + u + 2] + red[1][j][qc + u + 2] + red[2][j][qc + u + 2] + red[3][j][qc + u + 2];
+      v.w = red[0][j][qc + u + 3] + red[1][j][qc + u + 3] + red[2][j][qc + u + 3] + red[3][j][qc + u + 3];
+      *reinterpret_cast<float4*>(dst + u) = v;
+    }
   }
 }
 
@@ -311,13 +363,13 @@ hipError_t launch_frob_finish(const float* Zp, int B, int nsplit, int W, int n0,
   return hipGetLastError();
 }
 
-bool mfma_project_ok(int T, int W) { return T > 0 && T % (4 * kProjK) == 0 && W % kProjQ == 0; }
+bool mfma_project_ok(int T, int W) { return T > 0 && T % (4 * kProjK) == 0 && W % 128 == 0; }
 
-// Token splits: about 256 workgroups in all (fewer splits mean fewer fp32
-// partials to write and re-read; measured best), each split a multiple of 128
-// tokens dividing T.
+// Token splits of the 128-column projection: about 256 workgroups in all
+// (fewer splits mean fewer fp32 partials to write and re-read; measured
+// best), each split a multiple of 128 tokens dividing T.
 int mfma_project_splits(int B, int T, int W) {
-  const int64_t base = static_cast<int64_t>(B) * (W / kProjQ);
+  const int64_t base = static_cast<int64_t>(B) * (W / 128);
   int want = static_cast<int>((256 + base - 1) / (base > 0 ? base : 1));
   const int maxs = T / (4 * kProjK);
   if (want > maxs) want = maxs;
@@ -332,8 +384,33 @@ hipError_t launch_project_mfma(const bf16_t* X, int B, int T, int W, const bf16_
   if (B <= 0) return hipSuccess;
   if (!mfma_project_ok(T, W) || nsplit < 1 || T % (nsplit * 4 * kProjK) != 0)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_project_mfma, dim3(W / kProjQ, nsplit, B), dim3(256), 0, s, X, T, W, Y,
-                     T / nsplit, nsplit, Zp);
+  hipLaunchKernelGGL((k_project_mfma<8, false>), dim3(W / 128, nsplit, B), dim3(256), 0, s, X, T,
+                     W, Y, T / nsplit, nsplit, Zp, 0, 0.f, 0, 0.f, nullptr);
+  return hipGetLastError();
+}
+
+// Column block of the fused projection-and-square: 128 columns when that
+// alone gives at least 256 workgroups, else 64 when that does; 0 when neither
+// does (the caller then takes the split projection and the finish).
+int mfma_project_sq_cols(int B, int T, int W) {
+  if (B <= 0 || !mfma_project_ok(T, W)) return 0;
+  const int64_t b = B;
+  if (b * (W / 128) >= 256) return 128;
+  if (b * (W / 64) >= 256) return 64;
+  return 0;
+}
+
+hipError_t launch_project_sq_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* Y, int cols,
+                                  int n0, float w0, int n1, float w1, double* part, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  if (!mfma_project_ok(T, W) || (cols != 64 && cols != 128)) return hipErrorInvalidValue;
+  if (cols == 128) {
+    hipLaunchKernelGGL((k_project_mfma<8, true>), dim3(W / 128, 1, B), dim3(256), 0, s, X, T, W, Y,
+                       T, 1, nullptr, n0, w0, n1, w1, part);
+  } else {
+    hipLaunchKernelGGL((k_project_mfma<4, true>), dim3(W / 64, 1, B), dim3(256), 0, s, X, T, W, Y,
+                       T, 1, nullptr, n0, w0, n1, w1, part);
+  }
   return hipGetLastError();
 }
 
