@@ -183,7 +183,7 @@ template <> struct ProjRow<4> { typedef u32x2 type; };
 // Column c of eight rows of 16-bit values (rows[e] holds 2 per dword), as the
 // MFMA's 8 contraction values (4 dwords, row e in slot e).
 template <typename R>
-__device__ __forceinline__ u32x4 transpose_col(const R (&rows)[8], int c) {
+__device__ __forceinline__ u32x4 transpose_col(const R* rows, int c) {
   u32x4 a;
   const int w = c >> 1;
   if ((c & 1) == 0) {
@@ -226,31 +226,41 @@ __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__
     acc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  RowT rows[2][8];
-  u32x4 yv[2][2];
+  // An iteration covers U = 8 / CW sub-steps of 32 tokens (sub-step u: tokens
+  // t + 32 u + 8 g + e), so that a lane has 128 bytes of X in flight per buffer
+  // whatever the column block.
+  constexpr int U = 8 / CW;
+  RowT rows[2][8 * U];
+  u32x4 yv[2][U][2];
   auto load = [&](int buf, int t) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      rows[buf][e] = *reinterpret_cast<const RowT*>(xbase + static_cast<int64_t>(t + e) * W);
-    yv[buf][0] = ld16(yb0 + t);
-    yv[buf][1] = ld16(yb1 + t);
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        rows[buf][8 * u + e] =
+            *reinterpret_cast<const RowT*>(xbase + static_cast<int64_t>(t + kProjK * u + e) * W);
+      yv[buf][u][0] = ld16(yb0 + t + kProjK * u);
+      yv[buf][u][1] = ld16(yb1 + t + kProjK * u);
+    }
   };
   auto compute = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < CW; ++c) {
-      const u32x4 a = transpose_col(rows[buf], c);
-      acc[c][0] = mfma16(a, yv[buf][0], acc[c][0]);
-      acc[c][1] = mfma16(a, yv[buf][1], acc[c][1]);
-    }
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < CW; ++c) {
+        const u32x4 a = transpose_col(&rows[buf][8 * u], c);
+        acc[c][0] = mfma16(a, yv[buf][u][0], acc[c][0]);
+        acc[c][1] = mfma16(a, yv[buf][u][1], acc[c][1]);
+      }
   };
 
-  const int niter = tw / kProjK;
+  const int niter = tw / (kProjK * U);
   load(0, 0);
   for (int it = 0; it < niter; it += 2) {
-    if (it + 1 < niter) load(1, (it + 1) * kProjK);
+    if (it + 1 < niter) load(1, (it + 1) * kProjK * U);
     compute(0);
     if (it + 1 < niter) {
-      if (it + 2 < niter) load(0, (it + 2) * kProjK);
+      if (it + 2 < niter) load(0, (it + 2) * kProjK * U);
       compute(1);
     }
   }
@@ -396,14 +406,15 @@ int mfma_project_sq_cols(int B, int T, int W) {
   if (B <= 0 || !mfma_project_ok(T, W)) return 0;
   const int64_t b = B;
   if (b * (W / 128) >= 256) return 128;
-  if (b * (W / 64) >= 256) return 64;
+  if (b * (W / 64) >= 256 && T % (4 * 2 * kProjK) == 0) return 64;
   return 0;
 }
 
 hipError_t launch_project_sq_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* Y, int cols,
                                   int n0, float w0, int n1, float w1, double* part, hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  if (!mfma_project_ok(T, W) || (cols != 64 && cols != 128)) return hipErrorInvalidValue;
+  if (!mfma_project_ok(T, W) || (cols != 64 && cols != 128) || (cols == 64 && T % 256 != 0))
+    return hipErrorInvalidValue;
   if (cols == 128) {
     hipLaunchKernelGGL((k_project_mfma<8, true>), dim3(W / 128, 1, B), dim3(256), 0, s, X, T, W, Y,
                        T, 1, nullptr, n0, w0, n1, w1, part);

@@ -93,7 +93,7 @@ NORM_CASES = [
     ("k3_bf16_mfma", "bf16", 2, 256, 256, 512, 3),    # Hutch++ s = r = 1 with T > s, MFMA
     # MFMA projection with the weighted square taken in the same kernel (at least 256
     # column blocks): 64-column blocks (B d / 64 = 256), 128-column blocks (B d / 128 = 256)
-    ("fused_sq64_bf16", "bf16", 8, 128, 2048, 256, 32),
+    ("fused_sq64_bf16", "bf16", 8, 256, 2048, 256, 32),
     ("fused_sq128_bf16", "bf16", 4, 128, 8192, 256, 32),
 ]
 
