@@ -46,7 +46,10 @@ def parse():
     ap.add_argument("--rademacher", action="store_true",
                     help="sign (+-1) probes instead of Gaussian ones for Hutch / Hutch++")
     ap.add_argument("--unfused", action="store_true",
-                    help="aggregate and update with two calls (S materialised) instead of one")
+                    help="aggregate and update with two calls per layer (S materialised)")
+    ap.add_argument("--per-layer", action="store_true",
+                    help="one norm call and one update call per layer instead of the batched "
+                         "calls over all layers")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -662,10 +665,16 @@ def main():
     S = ([torch.empty(l.p, l.d, dtype=torch.float32, device=dev) for l in wl.layers]
          if args.unfused else None)
     theta = [torch.zeros(l.p, l.d, dtype=torch.float32, device=dev) for l in wl.layers]
+    # the batched calls over the step's layers (one descriptor list per input copy)
+    lay_n = [[(A, G, l.layer_id) for (A, G), l in zip(cp, wl.layers)] for cp in inputs]
+    lay_u = [[(A, G, l.layer_id, th) for (A, G), l, th in zip(cp, wl.layers, theta)]
+             for cp in inputs]
     ws_n = max(dp.dp_norm_est_workspace(method, wl.dtype, wl.B, wl.T, l.d, l.p, wl.k)
                for l in wl.layers)
+    ws_n = max(ws_n, dp.dp_norm_est_layers_workspace(method, wl.dtype, wl.B, wl.T, wl.k, lay_n[0]))
     ws_a = max(dp.dp_clip_aggregate_update_workspace(wl.dtype, wl.B, wl.T, l.d, l.p)
                for l in wl.layers)
+    ws_a = max(ws_a, dp.dp_clip_aggregate_update_layers_workspace(wl.dtype, wl.B, wl.T, lay_u[0]))
     ws_norm = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
     ws_agg = dp.clip_workspace(ws_a, dev)
 
@@ -680,30 +689,46 @@ def main():
 
     def step(it, evs, only=None):
         """One step.  evs: per layer the six events (norm_est, aggregate, noise_update
-        pairs), or None; with ``only`` set, just that kernel's pair is recorded."""
+        pairs), or None; with ``only`` set, just that kernel's pair is recorded.  The
+        batched norm call records its pair once, in layer 0's slot, around all layers'
+        streaming passes."""
         def pair(li, name):
             if evs is None or (only is not None and only != name):
                 return None
             j = {"norm_est": 0, "aggregate": 2, "noise_update": 4}[name]
             return (evs[li][j], evs[li][j + 1])
-        cp = inputs[it % copies]
-        for li, l in enumerate(wl.layers):
-            A, G = cp[li]
-            flags = (dp.DP_ACCUMULATE if li else 0) | (
-                dp.DP_PROBE_RADEMACHER if args.rademacher else 0)
-            dp.dp_norm_est(method, A, G, wl.k, wl.method_seed + it, l.layer_id, n,
-                           flags=flags, ws=ws_norm, events=pair(li, "norm_est"))
-        for li, l in enumerate(wl.layers):
-            A, G = cp[li]
-            if args.unfused:  # clipped sum to S, then noise + update: two calls
+        ci = it % copies
+        cp = inputs[ci]
+        probe = dp.DP_PROBE_RADEMACHER if args.rademacher else 0
+        if args.per_layer:  # one call per layer
+            for li, l in enumerate(wl.layers):
+                A, G = cp[li]
+                dp.dp_norm_est(method, A, G, wl.k, wl.method_seed + it, l.layer_id, n,
+                               flags=(dp.DP_ACCUMULATE if li else 0) | probe, ws=ws_norm,
+                               events=pair(li, "norm_est"))
+        else:  # all layers in one call
+            dp.dp_norm_est_layers(method, lay_n[ci], wl.k, wl.method_seed + it, n, flags=probe,
+                                  ws=ws_norm, events=pair(0, "norm_est"))
+        if args.unfused:  # clipped sum to S, then noise + update: two calls per layer
+            for li, l in enumerate(wl.layers):
+                A, G = cp[li]
                 dp.dp_clip_aggregate(A, G, n, wl.C, S[li], ws=ws_agg, events=pair(li, "aggregate"))
                 dp.dp_noise_update(theta[li], S[li], wl.sigma, wl.C, wl.eta, wl.B,
                                    wl.noise_seed + it, l.layer_id, events=pair(li, "noise_update"))
-            else:  # one call: clip, clipped sum, noise, update (S not stored)
+        elif args.per_layer:  # one fused call per layer: clip, clipped sum, noise, update
+            for li, l in enumerate(wl.layers):
+                A, G = cp[li]
                 ea, eu = pair(li, "aggregate"), pair(li, "noise_update")
                 dp.dp_clip_aggregate_update(
                     A, G, n, wl.C, wl.sigma, wl.eta, wl.noise_seed + it, l.layer_id, theta[li],
                     ws=ws_agg, events=None if ea is None and eu is None else (ea, eu))
+        else:  # all layers in one call: the clip factors once, then per layer the rest
+            ea = [pair(li, "aggregate") for li in range(L)]
+            eu = [pair(li, "noise_update") for li in range(L)]
+            dp.dp_clip_aggregate_update_layers(
+                lay_u[ci], n, wl.C, wl.sigma, wl.eta, wl.noise_seed + it, ws=ws_agg,
+                agg_events=None if all(e is None for e in ea) else ea,
+                upd_events=None if all(e is None for e in eu) else eu)
 
     for it in range(W):
         step(it, None)
@@ -722,7 +747,8 @@ def main():
     for it in range(KI):
         for li in range(L):
             e = ev_i[it][li]
-            t_inst["norm_est"] += e[0].elapsed_time(e[1]) / KI
+            if args.per_layer or li == 0:
+                t_inst["norm_est"] += e[0].elapsed_time(e[1]) / KI
             t_inst["aggregate"] += e[2].elapsed_time(e[3]) / KI
             t_inst["noise_update"] += e[4].elapsed_time(e[5]) / KI
     dom_name = max(t_inst, key=t_inst.get)
@@ -752,7 +778,8 @@ def main():
     t_step = dict(t_inst)
     j = {"norm_est": 0, "aggregate": 2, "noise_update": 4}[dom_name]
     t_step[dom_name] = sum(ev[it][li][j].elapsed_time(ev[it][li][j + 1])
-                           for it in timed_ev for li in range(L)) / len(timed_ev)
+                           for it in timed_ev for li in range(L)
+                           if dom_name != "norm_est" or args.per_layer or li == 0) / len(timed_ev)
     t_norm, t_agg, t_noise = (t_step["norm_est"] * K, t_step["aggregate"] * K,
                               t_step["noise_update"] * K)
     launches = K * L
@@ -774,7 +801,9 @@ def main():
     # per step: algorithmic work of all layers / summed kernel time of one step
     s_norm, s_agg, s_noise = t_norm / K / 1e3, t_agg / K / 1e3, t_noise / K / 1e3
     kernels = {
-        "norm_est": {"name": f"{method} passes (per layer: sketch+projection)" if method == "hutch"
+        "norm_est": {"name": f"{method} passes (per layer: sketch+projection"
+                     + ("" if args.per_layer else "; all layers timed in one call, per-layer mean")
+                     + ")" if method == "hutch"
                      else f"{method} main kernels", "ms_per_launch": t_norm / launches,
                      "bound": "hbm" if method in ("hutch", "hutchpp") else "mfma",
                      "GBps": b_norm / s_norm / 1e9, "TFLOPs": f_norm / s_norm / 1e12},
@@ -850,7 +879,9 @@ def main():
                    "shapes_dp": sorted({(l.d, l.p) for l in wl.layers}), "method": method,
                    "k": wl.k, "probes": "rademacher" if args.rademacher else "gaussian",
                    "C": wl.C, "sigma": wl.sigma, "eta": wl.eta,
-                   "input_copies": copies, "global_batch": wl.B, "seq_len": wl.T},
+                   "input_copies": copies, "global_batch": wl.B, "seq_len": wl.T,
+                   "calls": ("one per layer" if args.per_layer or args.unfused
+                             else "batched over the layers")},
         "roofline": roof,
         "kernels": kernels,
         "estimator_accuracy": accuracy,

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define DPRC_ABI_VERSION 2
+#define DPRC_ABI_VERSION 3
 
 typedef void *dp_stream_t; /* a hipStream_t */
 
@@ -76,8 +76,8 @@ typedef enum {
 
 /*
  * Device status flags.  Every call that forms clip factors (dp_clip_aggregate,
- * dp_clip_aggregate_update, dp_rmsnorm_clip_aggregate_update,
- * dp_embedding_clip_aggregate_update) ORs them into a sticky status word kept
+ * dp_clip_aggregate_update, dp_clip_aggregate_update_layers,
+ * dp_rmsnorm_clip_aggregate_update, dp_embedding_clip_aggregate_update) ORs them into a sticky status word kept
  * in the first 8 bytes of its workspace; the word stays set over any number of
  * calls that reuse the workspace until dp_read_device_status reads and clears
  * it.  A newly allocated workspace must start with that word at zero: allocate
@@ -226,6 +226,65 @@ dp_status_t dp_clip_aggregate_update(int dtype, int B, int T, int d, int p, cons
  */
 dp_status_t dp_read_device_status(void *ws, uint32_t *flags_out, dp_stream_t stream);
 
+/* ---- batched calls over the linear layers of one step ----
+ * One training step applies the method to every linear layer of the model:
+ * the per-sample norm is summed over all layers before anything is clipped
+ * (glossary page, section DP-SGDのアルゴリズム, steps 2-3: one clip factor per
+ * sample from the whole gradient's norm), and each layer then gets its clipped
+ * sum, noise and update (steps 4-5; summary, section アルゴリズム的フロー,
+ * steps 3-6).  These two calls take all layers at once and compute exactly
+ * what the per-layer calls compute, with fewer launches: the norm call draws
+ * the probes of all layers in one launch (per 64 layers) and adds the layers'
+ * estimates into n_sq in one pass; the update call forms the clip factors once.
+ */
+typedef struct dp_linear_layer {
+  int d;              /* input width (columns of A) */
+  int p;              /* output width (columns of G) */
+  uint32_t layer;     /* layer id: keys the probe and noise streams, as `layer` above */
+  const void *A;      /* [B][T][d] layer inputs, row-major, dtype of the call */
+  const void *G;      /* [B][T][p] output gradients, row-major */
+  float *theta;       /* [p][d] fp32 parameters (updated in place; unused by the norm call) */
+} dp_linear_layer_t;
+
+/* Bytes of workspace dp_norm_est_layers needs, or (size_t)-1 if invalid. */
+size_t dp_norm_est_layers_workspace(int method, int dtype, int B, int T, int k, int nlayers,
+                                    const dp_linear_layer_t *layers);
+
+/*
+ * n_sq[i] (= or, with DP_ACCUMULATE, +=) sum over the layers of the estimate
+ * dp_norm_est gives for each (same method, k, seed, layer ids and flags).
+ *  layers   host array of nlayers >= 1 descriptors (read during the call only;
+ *           theta is not used); every layer's A and G as in dp_norm_est.
+ * Hutch on bf16 inputs whose layers all take the MFMA path with at least 256
+ * column blocks of the projection (e.g. B 8, T 4096, d >= 2048) runs batched:
+ * one probe launch, sketch and projection per layer, one per-sample sum in
+ * fp64 (the sum over layers is rounded to fp32 once, not once per layer).
+ * Anything else runs the per-layer calls in order on the same workspace.
+ * Errors: as dp_norm_est, for any layer.
+ */
+dp_status_t dp_norm_est_layers(int method, int dtype, int B, int T, int k, int nlayers,
+                               const dp_linear_layer_t *layers, uint64_t seed, uint32_t flags,
+                               float *n_sq, void *ws, size_t ws_bytes, dp_stream_t stream);
+
+/* Bytes of workspace dp_clip_aggregate_update_layers needs, or (size_t)-1 if invalid. */
+size_t dp_clip_aggregate_update_layers_workspace(int dtype, int B, int T, int nlayers,
+                                                 const dp_linear_layer_t *layers);
+
+/*
+ * dp_clip_aggregate_update for every layer in order (same n_sq, C, sigma, eta
+ * and seed; each layer's own id and theta), with the clip factors formed once.
+ * theta of each layer is bit-identical to the per-layer call's.  S is not
+ * stored.  c_out (may be NULL) and the status word as in dp_clip_aggregate.
+ *  layers   host array of nlayers >= 1 descriptors (read during the call only);
+ *           the thetas must not overlap each other or the workspace.
+ * Errors: as dp_clip_aggregate_update, for any layer.
+ */
+dp_status_t dp_clip_aggregate_update_layers(int dtype, int B, int T, int nlayers,
+                                            const dp_linear_layer_t *layers, const float *n_sq,
+                                            float C, float sigma, float eta, uint64_t seed,
+                                            float *c_out, void *ws, size_t ws_bytes,
+                                            dp_stream_t stream);
+
 /* ---- timed variants: the same calls, plus live kernel timing ----
  * Identical to the call without "_timed", and additionally record the two
  * hipEvent_t handles ev_begin / ev_end (either may be NULL) on `stream`
@@ -256,6 +315,22 @@ dp_status_t dp_clip_aggregate_update_timed(int dtype, int B, int T, int d, int p
                                            size_t ws_bytes, dp_stream_t stream,
                                            void *ev_agg_begin, void *ev_agg_end,
                                            void *ev_upd_begin, void *ev_upd_end);
+/* dp_norm_est_layers, with ev_begin / ev_end around all layers' streaming
+ * passes (after the probe launch, before the per-sample sum). */
+dp_status_t dp_norm_est_layers_timed(int method, int dtype, int B, int T, int k, int nlayers,
+                                     const dp_linear_layer_t *layers, uint64_t seed,
+                                     uint32_t flags, float *n_sq, void *ws, size_t ws_bytes,
+                                     dp_stream_t stream, void *ev_begin, void *ev_end);
+/* dp_clip_aggregate_update_layers, with agg_begin[l] / agg_end[l] around layer
+ * l's clipped-sum contraction and upd_begin[l] / upd_end[l] around its noise +
+ * update kernel (arrays of nlayers hipEvent_t, any of them NULL). */
+dp_status_t dp_clip_aggregate_update_layers_timed(int dtype, int B, int T, int nlayers,
+                                                  const dp_linear_layer_t *layers,
+                                                  const float *n_sq, float C, float sigma,
+                                                  float eta, uint64_t seed, float *c_out,
+                                                  void *ws, size_t ws_bytes, dp_stream_t stream,
+                                                  void *const *agg_begin, void *const *agg_end,
+                                                  void *const *upd_begin, void *const *upd_end);
 
 /* ---- RMSNorm gains (a parameter that is not a linear layer) ----
  *

@@ -38,6 +38,27 @@ def lib_path():
     return os.environ.get("DPRC_LIB", os.path.join(_PKG, "libdprc.so"))
 
 
+class DpLinearLayer(ctypes.Structure):
+    """dp_linear_layer_t: one linear layer of a batched call."""
+    _fields_ = [("d", ctypes.c_int), ("p", ctypes.c_int), ("layer", ctypes.c_uint32),
+                ("A", ctypes.c_void_p), ("G", ctypes.c_void_p), ("theta", ctypes.c_void_p)]
+
+
+def _layer_array(layers):
+    """ctypes array of dp_linear_layer_t from (A, G, layer_id[, theta]) tuples."""
+    arr = (DpLinearLayer * len(layers))()
+    for i, ly in enumerate(layers):
+        A, G, lid = ly[0], ly[1], ly[2]
+        theta = ly[3] if len(ly) > 3 else None
+        arr[i].d = A.shape[2]
+        arr[i].p = G.shape[2]
+        arr[i].layer = int(lid)
+        arr[i].A = A.data_ptr()
+        arr[i].G = G.data_ptr()
+        arr[i].theta = None if theta is None else theta.data_ptr()
+    return arr
+
+
 def load_library():
     """Load libdprc.so once and declare the C signatures."""
     global _lib
@@ -80,6 +101,21 @@ def load_library():
     L.dp_read_device_status.restype = c_int
     L.dp_clip_aggregate_update_timed.argtypes = L.dp_clip_aggregate_update.argtypes + [c_p] * 4
     L.dp_clip_aggregate_update_timed.restype = c_int
+    LP = ctypes.POINTER(DpLinearLayer)
+    L.dp_norm_est_layers_workspace.argtypes = [c_int] * 6 + [LP]
+    L.dp_norm_est_layers_workspace.restype = c_sz
+    L.dp_norm_est_layers.argtypes = [c_int] * 6 + [LP, c_u64, c_u32, c_p, c_p, c_sz, c_p]
+    L.dp_norm_est_layers.restype = c_int
+    L.dp_norm_est_layers_timed.argtypes = L.dp_norm_est_layers.argtypes + [c_p, c_p]
+    L.dp_norm_est_layers_timed.restype = c_int
+    L.dp_clip_aggregate_update_layers_workspace.argtypes = [c_int] * 4 + [LP]
+    L.dp_clip_aggregate_update_layers_workspace.restype = c_sz
+    L.dp_clip_aggregate_update_layers.argtypes = ([c_int] * 4 + [LP, c_p, c_f, c_f, c_f, c_u64, c_p,
+                                                                 c_p, c_sz, c_p])
+    L.dp_clip_aggregate_update_layers.restype = c_int
+    L.dp_clip_aggregate_update_layers_timed.argtypes = (L.dp_clip_aggregate_update_layers.argtypes
+                                                        + [ctypes.POINTER(c_p)] * 4)
+    L.dp_clip_aggregate_update_layers_timed.restype = c_int
     L.dp_philox_u32.argtypes = [c_u64, c_p, c_p, c_sz, c_p]
     L.dp_philox_u32.restype = c_int
     L.dp_probe_fill.argtypes = [c_u64, c_u32, c_u32, c_int, c_int, c_p, c_p]
@@ -328,6 +364,81 @@ def dp_noise_update(theta, S, sigma, C, eta, B, seed, layer, stream=None, events
         st = L.dp_noise_update_timed(*args, _event(events[0]), _event(events[1]))
     _check(st, "dp_noise_update")
     return theta
+
+
+def dp_norm_est_layers_workspace(method, dtype, B, T, k, layers):
+    """Workspace bytes of dp_norm_est_layers for (A, G, layer_id) tuples, or None."""
+    code = dtype if isinstance(dtype, int) else {"f32": DP_F32, "bf16": DP_BF16}[dtype]
+    n = load_library().dp_norm_est_layers_workspace(_method_code(method), code, B, T, int(k or 0),
+                                                    len(layers), _layer_array(layers))
+    return None if n == _SIZE_INVALID else n
+
+
+def dp_norm_est_layers(method, layers, k, seed, n_sq, flags=0, ws=None, stream=None,
+                       events=None):
+    """n_sq[i] (= or += with DP_ACCUMULATE) the estimate summed over ``layers``, a list
+    of (A, G, layer_id) with A [B][T][d_l] and G [B][T][p_l] of one dtype.
+    ``events``: optional (begin, end) pair -> dp_norm_est_layers_timed."""
+    L = load_library()
+    A0 = layers[0][0]
+    B, T = A0.shape[0], A0.shape[1]
+    dt = _dtype_code(A0)
+    m = _method_code(method)
+    k = int(k or 0)
+    arr = _layer_array(layers)
+    nbytes = L.dp_norm_est_layers_workspace(m, dt, B, T, k, len(layers), arr)
+    ws_t = _workspace(nbytes, A0.device, ws)
+    args = [m, dt, B, T, k, len(layers), arr, int(seed) & (2**64 - 1), int(flags), _ptr(n_sq),
+            _ptr(ws_t), 0 if ws_t is None else ws_t.numel(), _stream(stream)]
+    if events is None:
+        st = L.dp_norm_est_layers(*args)
+    else:
+        st = L.dp_norm_est_layers_timed(*args, _event(events[0]), _event(events[1]))
+    _check(st, "dp_norm_est_layers")
+    return n_sq
+
+
+def dp_clip_aggregate_update_layers_workspace(dtype, B, T, layers):
+    """Workspace bytes of dp_clip_aggregate_update_layers, or None."""
+    code = dtype if isinstance(dtype, int) else {"f32": DP_F32, "bf16": DP_BF16}[dtype]
+    n = load_library().dp_clip_aggregate_update_layers_workspace(code, B, T, len(layers),
+                                                                 _layer_array(layers))
+    return None if n == _SIZE_INVALID else n
+
+
+def dp_clip_aggregate_update_layers(layers, n_sq, C, sigma, eta, seed, c_out=None, ws=None,
+                                    stream=None, agg_events=None, upd_events=None):
+    """dp_clip_aggregate_update over ``layers``, a list of (A, G, layer_id, theta), with
+    the clip factors formed once.  ``agg_events`` / ``upd_events``: optional lists of
+    (begin, end) pairs, one per layer (or None), around each layer's contraction /
+    noise + update."""
+    L = load_library()
+    A0 = layers[0][0]
+    B, T = A0.shape[0], A0.shape[1]
+    dt = _dtype_code(A0)
+    arr = _layer_array(layers)
+    nbytes = L.dp_clip_aggregate_update_layers_workspace(dt, B, T, len(layers), arr)
+    ws_t = _workspace(nbytes, A0.device, ws, zeroed=True)
+    args = [dt, B, T, len(layers), arr, _ptr(n_sq), float(C), float(sigma), float(eta),
+            int(seed) & (2**64 - 1), _ptr(c_out), _ptr(ws_t), 0 if ws_t is None else ws_t.numel(),
+            _stream(stream)]
+    if agg_events is None and upd_events is None:
+        st = L.dp_clip_aggregate_update_layers(*args)
+    else:
+        n = len(layers)
+
+        def arrays(evs):
+            if evs is None:
+                return None, None
+            b = (ctypes.c_void_p * n)(*[_event(e[0]).value if e is not None else None for e in evs])
+            f = (ctypes.c_void_p * n)(*[_event(e[1]).value if e is not None else None for e in evs])
+            return b, f
+
+        ab, ae = arrays(agg_events)
+        ub, ue = arrays(upd_events)
+        st = L.dp_clip_aggregate_update_layers_timed(*args, ab, ae, ub, ue)
+    _check(st, "dp_clip_aggregate_update_layers")
+    return n_sq
 
 
 def dp_philox_u32(seed, ctr, out, stream=None):

@@ -8,6 +8,7 @@
 #include <cstring>
 #include <initializer_list>
 #include <mutex>
+#include <vector>
 
 #include "dprc.h"
 #include "internal.h"
@@ -194,7 +195,7 @@ dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, i
   DP_TRY(launch_sketch_mfma(G, B, T, p, Pb, pbs, Yb, s));
   if (P.sq_cols > 0) {
     double* part = at<double>(ws, P.part);
-    DP_TRY(launch_project_sq_mfma(A, B, T, d, Yb, P.sq_cols, k, 1.0f / k, 0, 0.f, part, s));
+    DP_TRY(launch_project_sq_mfma(A, B, T, d, Yb, P.sq_cols, k, 1.0f / k, 0, 0.f, part, d / P.sq_cols, s));
     DP_TRY(mk.close(s));
     DP_TRY(launch_sum_parts(part, B, d / P.sq_cols, n_sq, accum ? 1 : 0, s));
     return DP_OK;
@@ -274,7 +275,7 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
   DP_TRY(launch_sketch_mfma(G, B, T, p, P3b, pad_p, Yb, s));
   if (P.sq_cols > 0) {
     double* part = at<double>(ws, P.part);
-    DP_TRY(launch_project_sq_mfma(A, B, T, d, Yb, P.sq_cols, S_, 1.0f, R_, 1.0f / R_, part, s));
+    DP_TRY(launch_project_sq_mfma(A, B, T, d, Yb, P.sq_cols, S_, 1.0f, R_, 1.0f / R_, part, d / P.sq_cols, s));
     DP_TRY(mk.close(s));
     DP_TRY(launch_sum_parts(part, B, d / P.sq_cols, n_sq, accum ? 1 : 0, s));
     return DP_OK;
@@ -491,11 +492,12 @@ bool agg_ptrs_ok(int B, int T, const void* A, const void* G, const float* n_sq, 
 dp_status_t clip_and_sum(const AggPlan& P, int dtype, int B, int T, int d, int p, const void* A,
                          const void* G, const float* n_sq, float C, float* c_out, float* S,
                          void* ws, hipStream_t s, const Marks& mk, const float** planes,
-                         int* nplanes) {
+                         int* nplanes, bool run_clip = true) {
   float* c = at<float>(ws, P.c);
   int* order = at<int>(ws, P.order);
   int* count = at<int>(ws, P.count);
-  DP_TRY(launch_clip(n_sq, B, C, c, c_out, at<uint32_t>(ws, P.status), order, count, s));
+  if (run_clip)  // else c, order and count are already in the workspace (batched call)
+    DP_TRY(launch_clip(n_sq, B, C, c, c_out, at<uint32_t>(ws, P.status), order, count, s));
   *planes = S;
   *nplanes = 1;
   if (P.mfma) {
@@ -552,6 +554,33 @@ bool update_args_ok(int d, int p, int B, float sigma, float C, float eta) {
   return sigma >= 0.f && std::isfinite(sigma) && C > 0.f && std::isfinite(C) && std::isfinite(eta);
 }
 
+// One layer's clipped sum, noise and update on a validated plan.  run_clip =
+// false: the clip factors are already in the workspace (batched call).
+static dp_status_t aggregate_update_layer(const AggPlan& P, int dtype, int B, int T, int d, int p,
+                                          const void* A, const void* G, const float* n_sq,
+                                          float C, float sigma, float eta, uint64_t seed,
+                                          uint32_t layer, float* theta, float* S, float* c_out,
+                                          void* ws, hipStream_t s, const Marks& mk_agg,
+                                          const Marks& mk_upd, bool run_clip) {
+  float* sum = S != nullptr ? S : at<float>(ws, P.sbuf);
+  const float* planes = nullptr;
+  int nplanes = 1;
+  const dp_status_t st = clip_and_sum(P, dtype, B, T, d, p, A, G, n_sq, C, c_out, sum, ws, s,
+                                      mk_agg, &planes, &nplanes, run_clip);
+  if (st != DP_OK) return st;
+  const float sigmaC = sigma * C;
+  const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
+  const int64_t n = static_cast<int64_t>(p) * d;
+  DP_TRY(mk_upd.open(s));
+  if (planes == sum)
+    DP_TRY(launch_noise_update(theta, sum, n, sigmaC, eta_over_B, seed, layer, s));
+  else
+    DP_TRY(launch_noise_update_splits(theta, planes, nplanes, n, S, sigmaC, eta_over_B, seed,
+                                      layer, s));
+  DP_TRY(mk_upd.close(s));
+  return DP_OK;
+}
+
 static dp_status_t clip_aggregate_update_impl(int dtype, int B, int T, int d, int p,
                                               const void* A, const void* G, const float* n_sq,
                                               float C, float sigma, float eta, uint64_t seed,
@@ -571,24 +600,9 @@ static dp_status_t clip_aggregate_update_impl(int dtype, int B, int T, int d, in
   if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
   if (overlaps(theta, bytes, ws, P.total) || (S != nullptr && overlaps(S, bytes, ws, P.total)))
     return DP_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float* sum = S != nullptr ? S : at<float>(ws, P.sbuf);
-  const float* planes = nullptr;
-  int nplanes = 1;
-  const dp_status_t st = clip_and_sum(P, dtype, B, T, d, p, A, G, n_sq, C, c_out, sum, ws, s,
-                                      mk_agg, &planes, &nplanes);
-  if (st != DP_OK) return st;
-  const float sigmaC = sigma * C;
-  const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
-  const int64_t n = static_cast<int64_t>(p) * d;
-  DP_TRY(mk_upd.open(s));
-  if (planes == sum)
-    DP_TRY(launch_noise_update(theta, sum, n, sigmaC, eta_over_B, seed, layer, s));
-  else
-    DP_TRY(launch_noise_update_splits(theta, planes, nplanes, n, S, sigmaC, eta_over_B, seed,
-                                      layer, s));
-  DP_TRY(mk_upd.close(s));
-  return DP_OK;
+  return aggregate_update_layer(P, dtype, B, T, d, p, A, G, n_sq, C, sigma, eta, seed, layer,
+                                theta, S, c_out, ws, static_cast<hipStream_t>(stream), mk_agg,
+                                mk_upd, true);
 }
 
 dp_status_t dp_clip_aggregate(int dtype, int B, int T, int d, int p, const void* A, const void* G,
@@ -1257,6 +1271,233 @@ dp_status_t dp_attn_backward(int B, int T, int d, int H, int KV, double rope_bas
   DP_TRY(launch_rmsnorm_bwd(static_cast<const bf16_t*>(x), rstd, gamma,
                             static_cast<const bf16_t*>(dy), db, M, d, static_cast<bf16_t*>(dx), s));
   return DP_OK;
+}
+
+
+// ---- batched calls over the linear layers of one step ----
+// The norm pass over all layers: with Hutch on bf16 inputs and every layer on
+// the fused MFMA projection, one probe launch per kProbeLayersMax layers, the
+// sketch and fused projection per layer into one row of partials per sample,
+// and one per-sample sum; otherwise the per-layer calls one after another.
+namespace {
+
+struct LayersNormPlan {
+  bool fused = false;
+  size_t pb = 0, yb = 0, part = 0, total = 0;
+  std::vector<int64_t> poff;   // per layer: first element of its probe block in pb
+  std::vector<int> cols;       // per layer: column block of the fused projection
+  std::vector<int64_t> pbase;  // per layer: first partial of its column blocks
+  int64_t nparts = 0;          // partials per sample, all layers
+};
+
+bool layers_norm_ok(int method, int dtype, int B, int T, int k, int n, const dp_linear_layer_t* L) {
+  if (n < 1 || L == nullptr) return false;
+  for (int l = 0; l < n; ++l)
+    if (!norm_args_ok(method, dtype, B, T, L[l].d, L[l].p, k)) return false;
+  return true;
+}
+
+LayersNormPlan plan_norm_layers(int method, int dtype, int B, int T, int k, int n,
+                                const dp_linear_layer_t* L) {
+  LayersNormPlan P;
+  bool fused = method == DP_NORM_HUTCH && dtype == DP_BF16 && k <= kMfmaProbeCols && B > 0 && T > 0;
+  for (int l = 0; l < n && fused; ++l)
+    fused = mfma_sketch_ok(T, L[l].p) && mfma_project_sq_cols(B, T, L[l].d) > 0;
+  if (!fused) {
+    for (int l = 0; l < n; ++l) {
+      const size_t t = plan_norm(method, dtype, B, T, L[l].d, L[l].p, k).total;
+      if (t > P.total) P.total = t;
+    }
+    return P;
+  }
+  P.fused = true;
+  const size_t Bz = static_cast<size_t>(B);
+  Carver pc;  // the probe blocks, one after another
+  P.poff.resize(n);
+  P.cols.resize(n);
+  P.pbase.resize(n);
+  for (int l = 0; l < n; ++l) {
+    P.poff[l] = static_cast<int64_t>(pc.take(Bz * kMfmaProbeCols * L[l].p * 2) / 2);
+    P.cols[l] = mfma_project_sq_cols(B, T, L[l].d);
+    P.pbase[l] = P.nparts;
+    P.nparts += L[l].d / P.cols[l];
+  }
+  Carver cv;
+  P.pb = cv.take(pc.off);
+  P.yb = cv.take(Bz * kMfmaProbeCols * T * 2);
+  P.part = cv.take(Bz * static_cast<size_t>(P.nparts) * sizeof(double));
+  P.total = cv.off;
+  return P;
+}
+
+size_t plan_update_layers(int dtype, int B, int T, int n, const dp_linear_layer_t* L) {
+  size_t t = 0;
+  for (int l = 0; l < n; ++l) {
+    const size_t x = plan_agg(dtype, B, T, L[l].d, L[l].p, true).total;
+    if (x > t) t = x;
+  }
+  return t;
+}
+
+}  // namespace
+
+size_t dp_norm_est_layers_workspace(int method, int dtype, int B, int T, int k, int nlayers,
+                                    const dp_linear_layer_t* layers) {
+  if (!layers_norm_ok(method, dtype, B, T, k, nlayers, layers)) return kInvalid;
+  return plan_norm_layers(method, dtype, B, T, k, nlayers, layers).total;
+}
+
+static dp_status_t norm_est_layers_impl(int method, int dtype, int B, int T, int k, int n,
+                                        const dp_linear_layer_t* L, uint64_t seed,
+                                        uint32_t flags, float* n_sq, void* ws, size_t ws_bytes,
+                                        dp_stream_t stream, const Marks& mk) {
+  if (!layers_norm_ok(method, dtype, B, T, k, n, L)) return DP_ERR_INVALID_ARG;
+  if ((flags & ~(DP_ACCUMULATE | DP_PROBE_SHARED | DP_PROBE_RADEMACHER)) != 0)
+    return DP_ERR_INVALID_ARG;
+  if (B == 0) return DP_OK;
+  if (n_sq == nullptr || !aligned(n_sq, 4)) return DP_ERR_INVALID_ARG;
+  for (int l = 0; l < n; ++l)
+    if (T > 0 && (L[l].A == nullptr || L[l].G == nullptr || !aligned(L[l].A, 16) ||
+                  !aligned(L[l].G, 16)))
+      return DP_ERR_INVALID_ARG;
+  const LayersNormPlan P = plan_norm_layers(method, dtype, B, T, k, n, L);
+  if (ws_bytes < P.total) return DP_ERR_WORKSPACE;
+  if (P.total > 0 && (ws == nullptr || !aligned(ws, 16))) return DP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!P.fused) {  // the per-layer calls, accumulating after the first
+    DP_TRY(mk.open(s));
+    for (int l = 0; l < n; ++l) {
+      const uint32_t f = l > 0 ? (flags | DP_ACCUMULATE) : flags;
+      const dp_status_t st = norm_est_impl(method, dtype, B, T, L[l].d, L[l].p, k, L[l].A, L[l].G,
+                                           seed, L[l].layer, f, n_sq, ws, ws_bytes, stream, Marks{});
+      if (st != DP_OK) return st;
+    }
+    DP_TRY(mk.close(s));
+    return DP_OK;
+  }
+  const bool shared = (flags & DP_PROBE_SHARED) != 0;
+  const bool signs = (flags & DP_PROBE_RADEMACHER) != 0;
+  const int nS = shared ? 1 : B;
+  bf16_t* Pb = at<bf16_t>(ws, P.pb);
+  bf16_t* Yb = at<bf16_t>(ws, P.yb);
+  double* part = at<double>(ws, P.part);
+  for (int c0 = 0; c0 < n; c0 += kProbeLayersMax) {
+    ProbeLayerTable<kProbeLayersMax> tab{};
+    tab.n = n - c0 < kProbeLayersMax ? n - c0 : kProbeLayersMax;
+    int nb = 0;
+    for (int t = 0; t < tab.n; ++t) {
+      const dp_linear_layer_t& ly = L[c0 + t];
+      tab.layer[t] = ly.layer;
+      tab.p[t] = ly.p;
+      tab.off[t] = P.poff[c0 + t];
+      tab.bstart[t] = nb;
+      nb += ((ly.p + 3) / 4 + 255) / 256;
+    }
+    tab.bstart[tab.n] = nb;
+    DP_TRY(launch_probe_fill_layers_bf16(seed, tab, nS, k, kMfmaProbeCols, Pb, s, signs));
+  }
+  DP_TRY(mk.open(s));
+  for (int l = 0; l < n; ++l) {
+    const dp_linear_layer_t& ly = L[l];
+    const int64_t pbs = shared ? 0 : static_cast<int64_t>(kMfmaProbeCols) * ly.p;
+    DP_TRY(launch_sketch_mfma(static_cast<const bf16_t*>(ly.G), B, T, ly.p, Pb + P.poff[l], pbs, Yb,
+                              s));
+    DP_TRY(launch_project_sq_mfma(static_cast<const bf16_t*>(ly.A), B, T, ly.d, Yb, P.cols[l], k,
+                                  1.0f / k, 0, 0.f, part + P.pbase[l], P.nparts, s));
+  }
+  DP_TRY(mk.close(s));
+  DP_TRY(launch_sum_parts(part, B, static_cast<int>(P.nparts), n_sq,
+                          (flags & DP_ACCUMULATE) ? 1 : 0, s));
+  return DP_OK;
+}
+
+dp_status_t dp_norm_est_layers(int method, int dtype, int B, int T, int k, int nlayers,
+                               const dp_linear_layer_t* layers, uint64_t seed, uint32_t flags,
+                               float* n_sq, void* ws, size_t ws_bytes, dp_stream_t stream) {
+  return norm_est_layers_impl(method, dtype, B, T, k, nlayers, layers, seed, flags, n_sq, ws,
+                              ws_bytes, stream, Marks{});
+}
+
+dp_status_t dp_norm_est_layers_timed(int method, int dtype, int B, int T, int k, int nlayers,
+                                     const dp_linear_layer_t* layers, uint64_t seed,
+                                     uint32_t flags, float* n_sq, void* ws, size_t ws_bytes,
+                                     dp_stream_t stream, void* ev_begin, void* ev_end) {
+  return norm_est_layers_impl(method, dtype, B, T, k, nlayers, layers, seed, flags, n_sq, ws,
+                              ws_bytes, stream,
+                              Marks{static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)});
+}
+
+size_t dp_clip_aggregate_update_layers_workspace(int dtype, int B, int T, int nlayers,
+                                                 const dp_linear_layer_t* layers) {
+  if (nlayers < 1 || layers == nullptr) return kInvalid;
+  for (int l = 0; l < nlayers; ++l)
+    if (!agg_args_ok(dtype, B, T, layers[l].d, layers[l].p)) return kInvalid;
+  return plan_update_layers(dtype, B, T, nlayers, layers);
+}
+
+static dp_status_t update_layers_impl(int dtype, int B, int T, int n, const dp_linear_layer_t* L,
+                                      const float* n_sq, float C, float sigma, float eta,
+                                      uint64_t seed, float* c_out, void* ws, size_t ws_bytes,
+                                      dp_stream_t stream, void* const* agg_begin,
+                                      void* const* agg_end, void* const* upd_begin,
+                                      void* const* upd_end) {
+  if (n < 1 || L == nullptr) return DP_ERR_INVALID_ARG;
+  for (int l = 0; l < n; ++l) {
+    const dp_linear_layer_t& ly = L[l];
+    if (!agg_args_ok(dtype, B, T, ly.d, ly.p)) return DP_ERR_INVALID_ARG;
+    if (!update_args_ok(ly.d, ly.p, B, sigma, C, eta)) return DP_ERR_INVALID_ARG;
+    if (!agg_ptrs_ok(B, T, ly.A, ly.G, n_sq, C, c_out)) return DP_ERR_INVALID_ARG;
+    if (ly.theta == nullptr || !aligned(ly.theta, 16)) return DP_ERR_INVALID_ARG;
+  }
+  const size_t need = plan_update_layers(dtype, B, T, n, L);
+  if (ws_bytes < need) return DP_ERR_WORKSPACE;
+  if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
+  for (int l = 0; l < n; ++l) {
+    const size_t bytes = static_cast<size_t>(L[l].p) * L[l].d * 4;
+    if (overlaps(L[l].theta, bytes, ws, need)) return DP_ERR_INVALID_ARG;
+    for (int m = 0; m < l; ++m)
+      if (overlaps(L[l].theta, bytes, L[m].theta, static_cast<size_t>(L[m].p) * L[m].d * 4))
+        return DP_ERR_INVALID_ARG;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the clip factors once: the same n for every layer (the plans share the
+  // status / c / order / count prefix, which depends on B only)
+  const AggPlan P0 = plan_agg(dtype, B, T, L[0].d, L[0].p, true);
+  DP_TRY(launch_clip(n_sq, B, C, at<float>(ws, P0.c), c_out, at<uint32_t>(ws, P0.status),
+                     at<int>(ws, P0.order), at<int>(ws, P0.count), s));
+  for (int l = 0; l < n; ++l) {
+    const dp_linear_layer_t& ly = L[l];
+    const AggPlan P = plan_agg(dtype, B, T, ly.d, ly.p, true);
+    const Marks mk{agg_begin ? static_cast<hipEvent_t>(agg_begin[l]) : nullptr,
+                   agg_end ? static_cast<hipEvent_t>(agg_end[l]) : nullptr};
+    const Marks mu{upd_begin ? static_cast<hipEvent_t>(upd_begin[l]) : nullptr,
+                   upd_end ? static_cast<hipEvent_t>(upd_end[l]) : nullptr};
+    const dp_status_t st =
+        aggregate_update_layer(P, dtype, B, T, ly.d, ly.p, ly.A, ly.G, n_sq, C, sigma, eta, seed,
+                               ly.layer, ly.theta, nullptr, c_out, ws, s, mk, mu, false);
+    if (st != DP_OK) return st;
+  }
+  return DP_OK;
+}
+
+dp_status_t dp_clip_aggregate_update_layers(int dtype, int B, int T, int nlayers,
+                                            const dp_linear_layer_t* layers, const float* n_sq,
+                                            float C, float sigma, float eta, uint64_t seed,
+                                            float* c_out, void* ws, size_t ws_bytes,
+                                            dp_stream_t stream) {
+  return update_layers_impl(dtype, B, T, nlayers, layers, n_sq, C, sigma, eta, seed, c_out, ws,
+                            ws_bytes, stream, nullptr, nullptr, nullptr, nullptr);
+}
+
+dp_status_t dp_clip_aggregate_update_layers_timed(int dtype, int B, int T, int nlayers,
+                                                  const dp_linear_layer_t* layers,
+                                                  const float* n_sq, float C, float sigma,
+                                                  float eta, uint64_t seed, float* c_out,
+                                                  void* ws, size_t ws_bytes, dp_stream_t stream,
+                                                  void* const* agg_begin, void* const* agg_end,
+                                                  void* const* upd_begin, void* const* upd_end) {
+  return update_layers_impl(dtype, B, T, nlayers, layers, n_sq, C, sigma, eta, seed, c_out, ws,
+                            ws_bytes, stream, agg_begin, agg_end, upd_begin, upd_end);
 }
 
 

@@ -27,6 +27,21 @@ hipError_t launch_probe_fill_f32(uint64_t seed, uint32_t layer, uint32_t sample0
 hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample0, int nsamp,
                                   int p, int kfill, int kpad, bf16_t* out, hipStream_t s,
                                   bool signs = false);
+// Probes of several layers in one launch (bf16, kpad columns): layer t's block
+// [nsamp][kpad][p[t]] starts at element off[t] of out; bstart[t] = first
+// workgroup of layer t (256 row groups of 4 per workgroup), bstart[n] = total.
+constexpr int kProbeLayersMax = 64;
+template <int N>
+struct ProbeLayerTable {
+  int n;
+  uint32_t layer[N];
+  int p[N];
+  int64_t off[N];
+  int bstart[N + 1];
+};
+hipError_t launch_probe_fill_layers_bf16(uint64_t seed, const ProbeLayerTable<kProbeLayersMax>& tab,
+                                         int nsamp, int kfill, int kpad, bf16_t* out,
+                                         hipStream_t s, bool signs);
 hipError_t launch_noise_fill(uint64_t seed, uint32_t layer, uint64_t offset, size_t n, float* xi,
                              hipStream_t s);
 hipError_t launch_noise_update(float* theta, const float* S, int64_t n, float sigmaC,
@@ -147,10 +162,12 @@ hipError_t launch_project_mfma(const bf16_t* X, int B, int T, int W, const bf16_
 // Column block (128 or 64) of the fused projection-and-square, 0 if it would
 // give fewer than 256 workgroups.
 int mfma_project_sq_cols(int B, int T, int W);
-// part[b][W / cols] (fp64) = sum_j w_j sum_{q in block} (sum_t X[b][t][q] Y[b][j][t])^2,
-// w_j as in launch_frob_finish; whole token range in one workgroup per block.
+// part[b * part_stride + blk] (fp64, blk < W / cols) = sum_j w_j sum_{q in block}
+// (sum_t X[b][t][q] Y[b][j][t])^2, w_j as in launch_frob_finish; whole token
+// range in one workgroup per block.
 hipError_t launch_project_sq_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* Y, int cols,
-                                  int n0, float w0, int n1, float w1, double* part, hipStream_t s);
+                                  int n0, float w0, int n1, float w1, double* part,
+                                  int64_t part_stride, hipStream_t s);
 // n_sq[b] (= or +=) sum_j w_j ||sum_split Zp[b][split][j][:]||^2 with w_j = w0
 // for j < n0, w1 for n0 <= j < n0 + n1, else 0 (W % 4 == 0).  One block per
 // sample, fixed-order fp64 sums.

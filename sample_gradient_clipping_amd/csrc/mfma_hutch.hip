@@ -202,7 +202,8 @@ __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__
                                                       int split_tokens, int nsplit,
                                                       float* __restrict__ Zp, int n0, float w0,
                                                       int n1, float w1,
-                                                      double* __restrict__ part) {
+                                                      double* __restrict__ part,
+                                                      int64_t part_stride) {
   constexpr int kQ = 16 * CW;
   typedef typename ProjRow<CW>::type RowT;
   __shared__ float red[4][32][kQ + 4];
@@ -288,7 +289,7 @@ __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__
       sq += static_cast<double>(z) * z;
     }
     const double tot = block_sum_d(static_cast<double>(w) * sq, dred);
-    if (threadIdx.x == 0) part[static_cast<int64_t>(b) * gridDim.x + blockIdx.x] = tot;
+    if (threadIdx.x == 0) part[static_cast<int64_t>(b) * part_stride + blockIdx.x] = tot;
   } else {
     float* dst = Zp + ((static_cast<int64_t>(b) * nsplit + split) * kMfmaProbeCols + j) * W + q0 + qc;
 #pragma unroll
@@ -395,7 +396,7 @@ hipError_t launch_project_mfma(const bf16_t* X, int B, int T, int W, const bf16_
   if (!mfma_project_ok(T, W) || nsplit < 1 || T % (nsplit * 4 * kProjK) != 0)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_project_mfma<8, false>), dim3(W / 128, nsplit, B), dim3(256), 0, s, X, T,
-                     W, Y, T / nsplit, nsplit, Zp, 0, 0.f, 0, 0.f, nullptr);
+                     W, Y, T / nsplit, nsplit, Zp, 0, 0.f, 0, 0.f, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -411,16 +412,17 @@ int mfma_project_sq_cols(int B, int T, int W) {
 }
 
 hipError_t launch_project_sq_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* Y, int cols,
-                                  int n0, float w0, int n1, float w1, double* part, hipStream_t s) {
+                                  int n0, float w0, int n1, float w1, double* part,
+                                  int64_t part_stride, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (!mfma_project_ok(T, W) || (cols != 64 && cols != 128) || (cols == 64 && T % 256 != 0))
     return hipErrorInvalidValue;
   if (cols == 128) {
     hipLaunchKernelGGL((k_project_mfma<8, true>), dim3(W / 128, 1, B), dim3(256), 0, s, X, T, W, Y,
-                       T, 1, nullptr, n0, w0, n1, w1, part);
+                       T, 1, nullptr, n0, w0, n1, w1, part, part_stride);
   } else {
     hipLaunchKernelGGL((k_project_mfma<4, true>), dim3(W / 64, 1, B), dim3(256), 0, s, X, T, W, Y,
-                       T, 1, nullptr, n0, w0, n1, w1, part);
+                       T, 1, nullptr, n0, w0, n1, w1, part, part_stride);
   }
   return hipGetLastError();
 }

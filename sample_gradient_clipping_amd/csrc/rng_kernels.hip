@@ -100,6 +100,57 @@ hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample
   return probe_fill<bf16_t>(seed, layer, sample0, nsamp, p, kfill, kpad, out, s, signs);
 }
 
+// Probes of up to kProbeLayersMax layers in one launch, bf16, padded to kpad
+// columns: the same entries as k_probe_fill for each layer.  Workgroup x walks
+// the layers' row-group blocks in order (layer t owns blocks bstart[t] ..
+// bstart[t + 1] - 1), y is the column, z the sample.
+template <int N>
+__global__ void k_probe_fill_layers(uint32_t k0, uint32_t k1, ProbeLayerTable<N> tab, int kfill,
+                                    int kpad, bf16_t* __restrict__ out, int signs) {
+  int t = 0;
+  while (t + 1 < tab.n && static_cast<int>(blockIdx.x) >= tab.bstart[t + 1]) ++t;
+  const int p = tab.p[t];
+  const int ngroups = (p + 3) >> 2;
+  const int g = (static_cast<int>(blockIdx.x) - tab.bstart[t]) * blockDim.x + threadIdx.x;
+  const int j = blockIdx.y;
+  const int i = blockIdx.z;
+  if (g >= ngroups) return;
+  float z[4] = {0.f, 0.f, 0.f, 0.f};
+  if (j < kfill) {
+    u32x4 c;
+    c.x = static_cast<uint32_t>(g);
+    c.y = static_cast<uint32_t>(j);
+    c.z = static_cast<uint32_t>(i);
+    c.w = tab.layer[t];
+    if (signs) {
+      const u32x4 w = philox4x32_10(c, k0, k1);
+#pragma unroll
+      for (int l = 0; l < 4; ++l) z[l] = (w[l] >> 31) ? -1.f : 1.f;
+    } else {
+      normals4(c, k0, k1, z);
+    }
+  }
+  bf16_t* row = out + tab.off[t] + (static_cast<int64_t>(i) * kpad + j) * p;
+#pragma unroll
+  for (int l = 0; l < 4; ++l) {
+    const int r = 4 * g + l;
+    if (r < p) row[r] = f32_to_bf16(z[l]);
+  }
+}
+
+hipError_t launch_probe_fill_layers_bf16(uint64_t seed, const ProbeLayerTable<kProbeLayersMax>& tab,
+                                         int nsamp, int kfill, int kpad, bf16_t* out,
+                                         hipStream_t s, bool signs) {
+  if (nsamp <= 0 || kpad <= 0 || tab.n <= 0) return hipSuccess;
+  if (tab.n > kProbeLayersMax) return hipErrorInvalidValue;
+  const int nblocks = tab.bstart[tab.n];
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_probe_fill_layers<kProbeLayersMax>, dim3(nblocks, kpad, nsamp), dim3(256),
+                     0, s, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), tab,
+                     kfill, kpad, out, signs ? 1 : 0);
+  return hipGetLastError();
+}
+
 // xi[e - offset] for e in [offset, offset + n); one thread per counter group.
 __global__ void k_noise_fill(uint32_t k0, uint32_t k1, uint32_t layer, uint64_t offset, size_t n,
                              float* __restrict__ xi) {

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dp.dp_abi_version() == 2
+    assert dp.dp_abi_version() == 3
     for s in range(5):
         assert dp.dp_status_string(s).startswith("DP_")
     assert "unknown" in dp.dp_status_string(99)
@@ -162,6 +162,62 @@ def test_clip_aggregate_update_rejects_bad_arguments(lib):
     need = dp.dp_clip_aggregate_update_workspace("f32", 2, 8, 8, 8)
     assert need >= dp.dp_clip_aggregate_workspace("f32", 2, 8, 8, 8) + 8 * 8 * 4
     assert dp.dp_clip_aggregate_update_workspace("f32", 2, 8, 0, 8) is None
+
+
+def _layers(specs):
+    """ctypes dp_linear_layer_t array from (d, p, layer, A, G, theta) with raw addresses."""
+    arr = (dp.DpLinearLayer * len(specs))()
+    for i, (d, p, lid, A, G, th) in enumerate(specs):
+        arr[i].d, arr[i].p, arr[i].layer = d, p, lid
+        arr[i].A, arr[i].G, arr[i].theta = A, G, th
+    return arr
+
+
+def test_batched_workspace_queries(lib):
+    SZ = ctypes.c_size_t(-1).value
+    two = _layers([(2048, 2048, 0, 0x100000, 0x100000, None), (2048, 512, 1, 0x100000, 0x100000, None)])
+    # fused Hutch: the probes of both layers, one Y buffer, the partial row per sample
+    n = lib.dp_norm_est_layers_workspace(0, 1, 8, 4096, 32, 2, two)
+    assert n >= 8 * 32 * (2048 + 512) * 2 + 8 * 32 * 4096 * 2
+    # the per-layer fallback needs the largest per-layer workspace
+    n = lib.dp_norm_est_layers_workspace(0, 0, 4, 64, 8, 2, two)
+    assert n == max(dp.dp_norm_est_workspace("hutch", "f32", 4, 64, 2048, 2048, 8),
+                    dp.dp_norm_est_workspace("hutch", "f32", 4, 64, 2048, 512, 8))
+    assert lib.dp_norm_est_layers_workspace(0, 1, 8, 4096, 32, 0, two) == SZ    # no layers
+    assert lib.dp_norm_est_layers_workspace(0, 1, 8, 4096, 32, 2, None) == SZ
+    assert lib.dp_norm_est_layers_workspace(0, 1, 8, 4096, 600, 2, two) == SZ  # k > p of layer 1
+    bad = _layers([(2048, 2048, 0, 0x100000, 0x100000, None), (0, 512, 1, 0x100000, 0x100000, None)])
+    assert lib.dp_norm_est_layers_workspace(0, 1, 8, 4096, 32, 2, bad) == SZ
+    u = lib.dp_clip_aggregate_update_layers_workspace(1, 8, 4096, 2, two)
+    assert u == max(dp.dp_clip_aggregate_update_workspace("bf16", 8, 4096, 2048, 2048),
+                    dp.dp_clip_aggregate_update_workspace("bf16", 8, 4096, 2048, 512))
+    assert lib.dp_clip_aggregate_update_layers_workspace(1, 8, 4096, 0, two) == SZ
+    assert lib.dp_clip_aggregate_update_layers_workspace(1, 8, 4096, 2, bad) == SZ
+
+
+def test_batched_calls_reject_bad_arguments(lib):
+    E, W = dp.DP_ERR_INVALID_ARG, dp.DP_ERR_WORKSPACE
+    ok = [(8, 8, 0, 0x100000, 0x100000, 0x400000), (8, 8, 1, 0x100000, 0x100000, 0x500000)]
+    norm = lambda specs, n=FAKE, flags=0, ws=FAKE, ws_bytes=1 << 30, k=4, nl=None: \
+        lib.dp_norm_est_layers(0, 0, 2, 8, k, len(specs) if nl is None else nl, _layers(specs),
+                               1, flags, n, ws, ws_bytes, NULL)
+    assert norm(ok, nl=0) == E
+    assert norm(ok, k=9) == E                                   # k > p
+    assert norm(ok, flags=8) == E
+    assert norm(ok, n=NULL) == E
+    assert norm([ok[0], (8, 8, 1, 0, 0x100000, None)]) == E     # layer 1 has no A
+    assert norm([ok[0], (8, 8, 1, 0x100004, 0x100000, None)]) == E  # misaligned A
+    assert norm(ok, ws_bytes=16) == W
+    upd = lambda specs, n=FAKE, C=1.0, sigma=1.0, ws=ctypes.c_void_p(0x800000), ws_bytes=1 << 20: \
+        lib.dp_clip_aggregate_update_layers(0, 2, 8, len(specs), _layers(specs), n, C, sigma, 0.1,
+                                            1, NULL, ws, ws_bytes, NULL)
+    assert upd(ok, C=0.0) == E
+    assert upd(ok, sigma=-1.0) == E
+    assert upd(ok, n=NULL) == E
+    assert upd([ok[0], (8, 8, 1, 0x100000, 0x100000, None)]) == E        # no theta
+    assert upd([ok[0], (8, 8, 1, 0x100000, 0x100000, 0x400000 + 64)]) == E  # thetas overlap
+    assert upd(ok, ws=ctypes.c_void_p(0x500000)) == E                     # ws overlaps a theta
+    assert upd(ok, ws_bytes=0) == W
 
 
 def test_read_device_status_rejects_bad_arguments(lib):
