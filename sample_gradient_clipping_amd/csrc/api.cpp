@@ -1324,7 +1324,9 @@ LayersNormPlan plan_norm_layers(int method, int dtype, int B, int T, int k, int 
   }
   Carver cv;
   P.pb = cv.take(pc.off);
-  P.yb = cv.take(Bz * kMfmaProbeCols * T * 2);
+  // one Y slab per layer of a launch group (kNormLayersMax layers per group)
+  P.yb = cv.take(static_cast<size_t>(n < kNormLayersMax ? n : kNormLayersMax) * Bz * kMfmaProbeCols *
+                 T * 2);
   P.part = cv.take(Bz * static_cast<size_t>(P.nparts) * sizeof(double));
   P.total = cv.off;
   return P;
@@ -1396,14 +1398,41 @@ static dp_status_t norm_est_layers_impl(int method, int dtype, int B, int T, int
     tab.bstart[tab.n] = nb;
     DP_TRY(launch_probe_fill_layers_bf16(seed, tab, nS, k, kMfmaProbeCols, Pb, s, signs));
   }
+  // Groups of up to kNormLayersMax layers: the sketches of a group, one launch per
+  // sketch shape, then its projections, one launch per column block.
+  const int64_t yslab = static_cast<int64_t>(B) * kMfmaProbeCols * T;  // elements
   DP_TRY(mk.open(s));
-  for (int l = 0; l < n; ++l) {
-    const dp_linear_layer_t& ly = L[l];
-    const int64_t pbs = shared ? 0 : static_cast<int64_t>(kMfmaProbeCols) * ly.p;
-    DP_TRY(launch_sketch_mfma(static_cast<const bf16_t*>(ly.G), B, T, ly.p, Pb + P.poff[l], pbs, Yb,
-                              s));
-    DP_TRY(launch_project_sq_mfma(static_cast<const bf16_t*>(ly.A), B, T, ly.d, Yb, P.cols[l], k,
-                                  1.0f / k, 0, 0.f, part + P.pbase[l], P.nparts, s));
+  for (int c0 = 0; c0 < n; c0 += kNormLayersMax) {
+    const int cn = n - c0 < kNormLayersMax ? n - c0 : kNormLayersMax;
+    for (int v = 0; v < 3; ++v) {
+      SketchLayers tab{};
+      for (int t = 0; t < cn; ++t) {
+        const dp_linear_layer_t& ly = L[c0 + t];
+        if (mfma_sketch_variant(B, T, ly.p) != v) continue;
+        tab.X[tab.n] = static_cast<const bf16_t*>(ly.G);
+        tab.P[tab.n] = Pb + P.poff[c0 + t];
+        tab.Y[tab.n] = Yb + t * yslab;
+        tab.W[tab.n] = ly.p;
+        tab.pbs[tab.n] = shared ? 0 : static_cast<int64_t>(kMfmaProbeCols) * ly.p;
+        ++tab.n;
+      }
+      if (tab.n > 0) DP_TRY(launch_sketch_mfma_layers(v, B, T, tab, s));
+    }
+    for (const int cols : {64, 128}) {
+      ProjectLayers tab{};
+      for (int t = 0; t < cn; ++t) {
+        const dp_linear_layer_t& ly = L[c0 + t];
+        if (P.cols[c0 + t] != cols) continue;
+        tab.X[tab.n] = static_cast<const bf16_t*>(ly.A);
+        tab.Y[tab.n] = Yb + t * yslab;
+        tab.W[tab.n] = ly.d;
+        tab.pbase[tab.n] = P.pbase[c0 + t];
+        ++tab.n;
+      }
+      if (tab.n > 0)
+        DP_TRY(launch_project_sq_mfma_layers(B, T, cols, tab, k, 1.0f / k, 0, 0.f, part, P.nparts,
+                                             s));
+    }
   }
   DP_TRY(mk.close(s));
   DP_TRY(launch_sum_parts(part, B, static_cast<int>(P.nparts), n_sq,

@@ -151,6 +151,34 @@ hipError_t launch_emb_zero_norm(int B, float* n_sq, int accumulate, hipStream_t 
 // ---- MFMA kernels for bf16 inputs (mfma_hutch.hip, mfma_gemm.hip) ----
 constexpr int kMfmaProbeCols = 32;  // padded probe width of the MFMA Hutch path
 bool mfma_sketch_ok(int T, int W);
+// Several layers per launch of the Hutch passes (layer tables in the kernel
+// arguments, kNormLayersMax per launch).
+constexpr int kNormLayersMax = 40;
+struct SketchLayers {
+  int n;
+  const bf16_t* X[kNormLayersMax];
+  const bf16_t* P[kNormLayersMax];
+  bf16_t* Y[kNormLayersMax];
+  int W[kNormLayersMax];
+  int64_t pbs[kNormLayersMax];
+};
+struct ProjectLayers {
+  int n;
+  const bf16_t* X[kNormLayersMax];
+  const bf16_t* Y[kNormLayersMax];
+  int W[kNormLayersMax];
+  int64_t pbase[kNormLayersMax];
+};
+// 2: 128-token workgroups of 8 waves, 1: 64 tokens, 4 waves, 0: 32 tokens, 4 waves.
+int mfma_sketch_variant(int B, int T, int W);
+// The sketch of every layer of the table (all of shape class `variant`).
+hipError_t launch_sketch_mfma_layers(int variant, int B, int T, const SketchLayers& tab,
+                                     hipStream_t s);
+// The fused projection-and-square of every layer of the table (all with column
+// block `cols`); layer l's partials at part + pbase[l], row stride part_stride.
+hipError_t launch_project_sq_mfma_layers(int B, int T, int cols, const ProjectLayers& tab, int n0,
+                                         float w0, int n1, float w1, double* part,
+                                         int64_t part_stride, hipStream_t s);
 bool mfma_project_ok(int T, int W);
 int mfma_project_splits(int B, int T, int W);
 // Y[b][j][t] (bf16, [B][32][T]) = sum_r X[b][t][r] P[b or 0][j][r], P bf16 [.][32][W].

@@ -39,16 +39,16 @@ __device__ __forceinline__ u32x4 ld16(const bf16_t* p) {
 // ---------------------------------------------------------------------------
 constexpr int kSketchK = 64;
 
+// The workgroup of token block tb of sample b.
 template <int MB, int NW>
-__global__ void __launch_bounds__(64 * NW) k_sketch_mfma(const bf16_t* __restrict__ X, int T, int W,
-                                                     const bf16_t* __restrict__ P,
-                                                     int64_t p_bstride, bf16_t* __restrict__ Y) {
+__device__ __forceinline__ void sketch_body(const bf16_t* __restrict__ X, int T, int W,
+                                            const bf16_t* __restrict__ P, int64_t p_bstride,
+                                            bf16_t* __restrict__ Y, int tb, int b) {
   constexpr int TM = 16 * MB;
   __shared__ float red[NW][32][TM + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, g = lane >> 4;
-  const int b = blockIdx.y;
-  const int t0 = blockIdx.x * TM;
+  const int t0 = tb * TM;
   const int Wq = W / NW;
   const int rbeg = wave * Wq + 16 * g;
 
@@ -135,22 +135,72 @@ __global__ void __launch_bounds__(64 * NW) k_sketch_mfma(const bf16_t* __restric
   }
 }
 
+template <int MB, int NW>
+__global__ void __launch_bounds__(64 * NW) k_sketch_mfma(const bf16_t* __restrict__ X, int T, int W,
+                                                     const bf16_t* __restrict__ P,
+                                                     int64_t p_bstride, bf16_t* __restrict__ Y) {
+  sketch_body<MB, NW>(X, T, W, P, p_bstride, Y, blockIdx.x, blockIdx.y);
+}
+
+// Several layers of one shape class in one launch: layer blockIdx.z of the table.
+template <int MB, int NW>
+__global__ void __launch_bounds__(64 * NW) k_sketch_mfma_layers(int T, SketchLayers tab) {
+  const int l = blockIdx.z;
+  sketch_body<MB, NW>(tab.X[l], T, tab.W[l], tab.P[l], tab.pbs[l], tab.Y[l], blockIdx.x,
+                      blockIdx.y);
+}
+
 bool mfma_sketch_ok(int T, int W) { return T > 0 && T % 32 == 0 && W % (4 * kSketchK) == 0; }
+
+// Sketch shape: 2 = 128-token workgroups of 8 waves (rows of 4096+ features),
+// 1 = 64 tokens and 4 waves, 0 = 32 tokens and 4 waves (few token blocks).
+int mfma_sketch_variant(int B, int T, int W) {
+  if (T % 128 == 0 && W >= 4096 && W % (8 * kSketchK) == 0 &&
+      static_cast<int64_t>(B) * (T / 128) >= 256)
+    return 2;
+  if (T % 64 == 0 && static_cast<int64_t>(B) * (T / 64) >= 512) return 1;
+  return 0;
+}
 
 hipError_t launch_sketch_mfma(const bf16_t* X, int B, int T, int W, const bf16_t* P,
                               int64_t p_bstride, bf16_t* Y, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (!mfma_sketch_ok(T, W)) return hipErrorInvalidValue;
-  if (T % 128 == 0 && W >= 4096 && W % (8 * kSketchK) == 0 &&
-      static_cast<int64_t>(B) * (T / 128) >= 256) {
-    hipLaunchKernelGGL((k_sketch_mfma<8, 8>), dim3(T / 128, B), dim3(512), 0, s, X, T, W, P,
-                       p_bstride, Y);
-  } else if (T % 64 == 0 && static_cast<int64_t>(B) * (T / 64) >= 512) {
-    hipLaunchKernelGGL((k_sketch_mfma<4, 4>), dim3(T / 64, B), dim3(256), 0, s, X, T, W, P,
-                       p_bstride, Y);
-  } else {
-    hipLaunchKernelGGL((k_sketch_mfma<2, 4>), dim3(T / 32, B), dim3(256), 0, s, X, T, W, P,
-                       p_bstride, Y);
+  switch (mfma_sketch_variant(B, T, W)) {
+    case 2:
+      hipLaunchKernelGGL((k_sketch_mfma<8, 8>), dim3(T / 128, B), dim3(512), 0, s, X, T, W, P,
+                         p_bstride, Y);
+      break;
+    case 1:
+      hipLaunchKernelGGL((k_sketch_mfma<4, 4>), dim3(T / 64, B), dim3(256), 0, s, X, T, W, P,
+                         p_bstride, Y);
+      break;
+    default:
+      hipLaunchKernelGGL((k_sketch_mfma<2, 4>), dim3(T / 32, B), dim3(256), 0, s, X, T, W, P,
+                         p_bstride, Y);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sketch_mfma_layers(int variant, int B, int T, const SketchLayers& tab,
+                                     hipStream_t s) {
+  if (B <= 0 || tab.n <= 0) return hipSuccess;
+  if (tab.n > kNormLayersMax) return hipErrorInvalidValue;
+  for (int l = 0; l < tab.n; ++l)
+    if (!mfma_sketch_ok(T, tab.W[l]) || mfma_sketch_variant(B, T, tab.W[l]) != variant)
+      return hipErrorInvalidValue;
+  switch (variant) {
+    case 2:
+      hipLaunchKernelGGL((k_sketch_mfma_layers<8, 8>), dim3(T / 128, B, tab.n), dim3(512), 0, s, T,
+                         tab);
+      break;
+    case 1:
+      hipLaunchKernelGGL((k_sketch_mfma_layers<4, 4>), dim3(T / 64, B, tab.n), dim3(256), 0, s, T,
+                         tab);
+      break;
+    default:
+      hipLaunchKernelGGL((k_sketch_mfma_layers<2, 4>), dim3(T / 32, B, tab.n), dim3(256), 0, s, T,
+                         tab);
   }
   return hipGetLastError();
 }
@@ -196,23 +246,20 @@ __device__ __forceinline__ u32x4 transpose_col(const R* rows, int c) {
   return a;
 }
 
+// The workgroup of column block qb, token split `split`, sample b.
 template <int CW, bool SQ>
-__global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__ X, int T, int W,
-                                                      const bf16_t* __restrict__ Y,
-                                                      int split_tokens, int nsplit,
-                                                      float* __restrict__ Zp, int n0, float w0,
-                                                      int n1, float w1,
-                                                      double* __restrict__ part,
-                                                      int64_t part_stride) {
+__device__ __forceinline__ void project_body(const bf16_t* __restrict__ X, int T, int W,
+                                             const bf16_t* __restrict__ Y, int split_tokens,
+                                             int nsplit, float* __restrict__ Zp, int n0, float w0,
+                                             int n1, float w1, double* __restrict__ part,
+                                             int64_t part_stride, int qb, int split, int b) {
   constexpr int kQ = 16 * CW;
   typedef typename ProjRow<CW>::type RowT;
   __shared__ float red[4][32][kQ + 4];
   __shared__ double dred[16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int m = lane & 15, g = lane >> 4;
-  const int q0 = blockIdx.x * kQ;
-  const int split = blockIdx.y;
-  const int b = blockIdx.z;
+  const int q0 = qb * kQ;
   const int tw = split_tokens >> 2;
   const int tbeg = split * split_tokens + wave * tw;
 
@@ -289,7 +336,7 @@ __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__
       sq += static_cast<double>(z) * z;
     }
     const double tot = block_sum_d(static_cast<double>(w) * sq, dred);
-    if (threadIdx.x == 0) part[static_cast<int64_t>(b) * part_stride + blockIdx.x] = tot;
+    if (threadIdx.x == 0) part[static_cast<int64_t>(b) * part_stride + qb] = tot;
   } else {
     float* dst = Zp + ((static_cast<int64_t>(b) * nsplit + split) * kMfmaProbeCols + j) * W + q0 + qc;
 #pragma unroll
@@ -302,6 +349,32 @@ __global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__
       *reinterpret_cast<float4*>(dst + u) = v;
     }
   }
+}
+
+template <int CW, bool SQ>
+__global__ void __launch_bounds__(256) k_project_mfma(const bf16_t* __restrict__ X, int T, int W,
+                                                      const bf16_t* __restrict__ Y,
+                                                      int split_tokens, int nsplit,
+                                                      float* __restrict__ Zp, int n0, float w0,
+                                                      int n1, float w1,
+                                                      double* __restrict__ part,
+                                                      int64_t part_stride) {
+  project_body<CW, SQ>(X, T, W, Y, split_tokens, nsplit, Zp, n0, w0, n1, w1, part, part_stride,
+                       blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// The fused projection-and-square of several layers in one launch: layer
+// blockIdx.y of the table, its column blocks blockIdx.x < W / (16 CW).
+template <int CW>
+__global__ void __launch_bounds__(256) k_project_sq_layers(int T, ProjectLayers tab, int n0,
+                                                           float w0, int n1, float w1,
+                                                           double* __restrict__ part,
+                                                           int64_t part_stride) {
+  const int l = blockIdx.y;
+  const int W = tab.W[l];
+  if (static_cast<int>(blockIdx.x) >= W / (16 * CW)) return;
+  project_body<CW, true>(tab.X[l], T, W, tab.Y[l], T, 1, nullptr, n0, w0, n1, w1,
+                         part + tab.pbase[l], part_stride, blockIdx.x, 0, blockIdx.z);
 }
 
 // ---------------------------------------------------------------------------
@@ -371,6 +444,26 @@ hipError_t launch_frob_finish(const float* Zp, int B, int nsplit, int W, int n0,
   if (W % 4 != 0 || nsplit < 1) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_frob_finish, dim3(B), dim3(kFrobThreads), 0, s, Zp, nsplit, W, n0, w0, n1,
                      w1, n_sq, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_sq_mfma_layers(int B, int T, int cols, const ProjectLayers& tab, int n0,
+                                         float w0, int n1, float w1, double* part,
+                                         int64_t part_stride, hipStream_t s) {
+  if (B <= 0 || tab.n <= 0) return hipSuccess;
+  if (tab.n > kNormLayersMax || (cols != 64 && cols != 128)) return hipErrorInvalidValue;
+  int maxblk = 0;
+  for (int l = 0; l < tab.n; ++l) {
+    if (mfma_project_sq_cols(B, T, tab.W[l]) != cols) return hipErrorInvalidValue;
+    maxblk = tab.W[l] / cols > maxblk ? tab.W[l] / cols : maxblk;
+  }
+  if (cols == 128) {
+    hipLaunchKernelGGL((k_project_sq_layers<8>), dim3(maxblk, tab.n, B), dim3(256), 0, s, T, tab, n0,
+                       w0, n1, w1, part, part_stride);
+  } else {
+    hipLaunchKernelGGL((k_project_sq_layers<4>), dim3(maxblk, tab.n, B), dim3(256), 0, s, T, tab, n0,
+                       w0, n1, w1, part, part_stride);
+  }
   return hipGetLastError();
 }
 
