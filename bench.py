@@ -309,6 +309,31 @@ def estimator_costs(dp, dev, reps=5):
     return out
 
 
+def read_ceiling(dp, dev, nbytes=512 << 20, reps=10):
+    """The practical HBM read ceiling of this GPU: dp_stream_read (a plain streaming
+    read with 16-byte loads) over a 512 MiB buffer (twice the MALL), the best of
+    two grid sizes, HIP events over ``reps`` back-to-back reads."""
+    import torch
+    from sample_gradient_clipping_amd import roofline as rf
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    best = 0.0
+    for nblocks in (1024, 2048):
+        out = torch.zeros(nblocks, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            dp.dp_stream_read(buf, out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            dp.dp_stream_read(buf, out)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del buf
+    return {"GBps": best, "bytes": nbytes, "frac_of_spec": best / rf.PEAK_HBM_GBPS,
+            "kernel": "dp_stream_read: 16-byte loads, 8 in flight per thread, 1024 or 2048 "
+                      "workgroups of 256"}
+
+
 def poisson_timing(dp, dev, reps=20):
     """Time the Poisson subsampling call (step 1 of DP-SGD) for two training-set
     sizes, with q chosen so that the expected minibatch is 8 sequences.
@@ -836,10 +861,20 @@ def main():
         {"bytes": b_noise / L} if dom_name == "noise_update" else
         {"flops": (f_agg if dom_name == "aggregate" else f_norm) / L,
          "bytes": (b_agg if dom_name == "aggregate" else b_norm) / L})
+    ceiling = None
+    if not args.only_step:
+        # the practical HBM read ceiling, measured in the same run, beside the spec fraction
+        ceiling = read_ceiling(dp, dev)
+        log(f"[bench] HBM read ceiling {ceiling['GBps']:.1f} GB/s ({ceiling['frac_of_spec']:.3f} of spec)")
+        for kv in kernels.values():
+            if kv["bound"] == "hbm":
+                kv["frac_of_read_ceiling"] = kv["GBps"] / ceiling["GBps"]
     for kname, kv in kernels.items():
         log(f"[bench] {kname:13s} {kv['ms_per_launch'] * 1e3:9.2f} us/launch  "
             f"{kv['GBps']:8.1f} GB/s  {kv.get('TFLOPs', 0):8.1f} TF/s  frac {kv['frac']:.3f}  "
-            f"share {kv['share_of_step']:.2f}")
+            f"share {kv['share_of_step']:.2f}"
+            + (f"  of read ceiling {kv['frac_of_read_ceiling']:.3f}" if "frac_of_read_ceiling" in kv
+               else ""))
 
     accuracy = sampler = rms = emb = mlp = attn = layer = costs = None
     if not args.only_step:
@@ -884,6 +919,7 @@ def main():
                              else "batched over the layers")},
         "roofline": roof,
         "kernels": kernels,
+        "hbm_read_ceiling": ceiling,
         "estimator_accuracy": accuracy,
         "estimator_costs": costs,
         "poisson_sampler": sampler,

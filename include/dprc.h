@@ -526,6 +526,18 @@ dp_status_t dp_attn_backward(int B, int T, int d, int H, int KV, double rope_bas
 
 /* ---- test hooks: expose the random streams for bit-level parity checks ---- */
 
+/*
+ * Measurement hook (not part of the method): a plain streaming read of `bytes`
+ * (a multiple of 16) at `buf` (16-byte aligned device memory) with nblocks
+ * workgroups (1 .. 65536) of 256 threads, 16-byte loads, eight in flight per
+ * thread; out[x] (device, nblocks uint32) receives the XOR of every 32-bit word
+ * workgroup x read.  It gives the practical HBM read ceiling that the
+ * bandwidth-bound kernels are compared with.  DP_ERR_INVALID_ARG for bad
+ * pointers or sizes.
+ */
+dp_status_t dp_stream_read(const void *buf, size_t bytes, uint32_t *out, int nblocks,
+                           dp_stream_t stream);
+
 /* out[4 n] = Philox4x32-10 words of the n counters ctr[4 n] (device arrays). */
 dp_status_t dp_philox_u32(uint64_t seed, const uint32_t *ctr, uint32_t *out, size_t n,
                           dp_stream_t stream);

@@ -116,6 +116,8 @@ def load_library():
     L.dp_clip_aggregate_update_layers_timed.argtypes = (L.dp_clip_aggregate_update_layers.argtypes
                                                         + [ctypes.POINTER(c_p)] * 4)
     L.dp_clip_aggregate_update_layers_timed.restype = c_int
+    L.dp_stream_read.argtypes = [c_p, c_sz, c_p, c_int, c_p]
+    L.dp_stream_read.restype = c_int
     L.dp_philox_u32.argtypes = [c_u64, c_p, c_p, c_sz, c_p]
     L.dp_philox_u32.restype = c_int
     L.dp_probe_fill.argtypes = [c_u64, c_u32, c_u32, c_int, c_int, c_p, c_p]
@@ -439,6 +441,15 @@ def dp_clip_aggregate_update_layers(layers, n_sq, C, sigma, eta, seed, c_out=Non
         st = L.dp_clip_aggregate_update_layers_timed(*args, ab, ae, ub, ue)
     _check(st, "dp_clip_aggregate_update_layers")
     return n_sq
+
+
+def dp_stream_read(buf, out, stream=None):
+    """Measurement hook: stream every byte of the device tensor ``buf`` (size a
+    multiple of 16); out (int32 [nblocks]) receives each workgroup's XOR."""
+    st = load_library().dp_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out),
+                                       out.numel(), _stream(stream))
+    _check(st, "dp_stream_read")
+    return out
 
 
 def dp_philox_u32(seed, ctr, out, stream=None):

@@ -690,6 +690,17 @@ dp_status_t dp_read_device_status(void* ws, uint32_t* flags_out, dp_stream_t str
   return DP_OK;
 }
 
+dp_status_t dp_stream_read(const void* buf, size_t bytes, uint32_t* out, int nblocks,
+                           dp_stream_t stream) {
+  if (bytes == 0) return DP_OK;
+  if (buf == nullptr || out == nullptr || !aligned(buf, 16) || !aligned(out, 4) || bytes % 16 != 0 ||
+      nblocks < 1 || nblocks > 65536)
+    return DP_ERR_INVALID_ARG;
+  DP_TRY(launch_stream_read(buf, static_cast<int64_t>(bytes / 16), out, nblocks,
+                            static_cast<hipStream_t>(stream)));
+  return DP_OK;
+}
+
 dp_status_t dp_philox_u32(uint64_t seed, const uint32_t* ctr, uint32_t* out, size_t n,
                           dp_stream_t stream) {
   if (n == 0) return DP_OK;

@@ -284,6 +284,47 @@ hipError_t launch_clip(const float* n, int B, float C, float* c, float* c_out, u
   return hipGetLastError();
 }
 
+// Measurement hook: a plain streaming read of n16 16-byte words, the
+// practical HBM read ceiling the bandwidth-bound kernels are compared with.
+// Workgroup x reads words x * 256 * kReadUnroll + ... grid-stride, eight 16-byte
+// loads per thread in flight, and writes the XOR of everything it read to
+// out[x] (so that no load can be dropped, and the result can be checked).
+constexpr int kReadUnroll = 8;
+
+__global__ void __launch_bounds__(256) k_stream_read(const u32x4* __restrict__ in, int64_t n16,
+                                                     uint32_t* __restrict__ out) {
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const int64_t step = static_cast<int64_t>(gridDim.x) * 256 * kReadUnroll;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * 256 * kReadUnroll + threadIdx.x; base < n16;
+       base += step) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) {
+      const int64_t i = base + u * 256;
+      v[u] = in[i < n16 ? i : n16 - 1];  // clamped: no load under a branch
+    }
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u)
+      if (base + u * 256 < n16) acc ^= v[u];
+  }
+  __shared__ uint32_t red[256];
+  red[threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] ^= red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0];
+}
+
+hipError_t launch_stream_read(const void* in, int64_t n16, uint32_t* out, int nblocks,
+                              hipStream_t s) {
+  if (n16 <= 0 || nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_stream_read, dim3(nblocks), dim3(256), 0, s,
+                     static_cast<const u32x4*>(in), n16, out);
+  return hipGetLastError();
+}
+
 // Sticky status word: w[1] receives w[0], and w[0] is cleared, in one atomic
 // exchange (stream-ordered after every clip kernel that ORed into w[0]).
 __global__ void k_take_status(uint32_t* w) {

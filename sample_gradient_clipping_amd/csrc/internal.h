@@ -86,6 +86,9 @@ hipError_t launch_aggregate_generic(const TIn* A, const TIn* G, int B, int T, in
 hipError_t launch_clip(const float* n, int B, float C, float* c, float* c_out, uint32_t* status,
                        int* order, int* count, hipStream_t s);
 // w[1] = w[0], w[0] = 0 (one atomic exchange).
+// out[x] (x < nblocks) = XOR of the 16-byte words workgroup x read of in[0 .. n16).
+hipError_t launch_stream_read(const void* in, int64_t n16, uint32_t* out, int nblocks,
+                              hipStream_t s);
 hipError_t launch_take_status(uint32_t* w, hipStream_t s);
 // out[e] = sum_{sp < nsplit} part[sp][e].
 hipError_t launch_reduce_splits(const float* part, int nsplit, int64_t n, float* out, hipStream_t s);

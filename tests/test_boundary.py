@@ -220,6 +220,18 @@ def test_batched_calls_reject_bad_arguments(lib):
     assert upd(ok, ws_bytes=0) == W
 
 
+def test_stream_read_rejects_bad_arguments(lib):
+    E = dp.DP_ERR_INVALID_ARG
+    f = lambda buf=FAKE, nbytes=1024, out=FAKE, nblocks=4: lib.dp_stream_read(buf, nbytes, out, nblocks, NULL)
+    assert f(nbytes=0) == dp.DP_OK
+    assert f(buf=NULL) == E
+    assert f(buf=FAKE_MIS) == E
+    assert f(out=NULL) == E
+    assert f(nbytes=1000) == E       # not a multiple of 16
+    assert f(nblocks=0) == E
+    assert f(nblocks=65537) == E
+
+
 def test_read_device_status_rejects_bad_arguments(lib):
     E = dp.DP_ERR_INVALID_ARG
     flags = ctypes.c_uint32(77)

@@ -513,3 +513,17 @@ def test_whole_step(dev, dtype):
         assert max_rel_normwise(f64(S), S_r) <= (TOL_F32 if dtype == "f32" else 1e-4)
         t_r = oracle.noise_update(th0, S_r, sigma, C, eta, B, 60, lid)
         assert max_rel_normwise(f64(th), t_r) <= TOL_F32
+
+
+@pytest.mark.parametrize("nbytes,nblocks", [(16, 1), (4096 * 16 + 48, 7), (3 << 20, 2048)])
+def test_stream_read_reads_every_word(dev, nbytes, nblocks):
+    # the measurement hook touches every 32-bit word once: the XOR of its
+    # workgroups' results is the XOR of the whole buffer (ragged last round)
+    g = torch.Generator().manual_seed(nbytes)
+    host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g)
+    out = torch.zeros(nblocks, dtype=torch.int32, device=dev)
+    dp.dp_stream_read(host.to(dev), out)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert int(got) == int(want)
