@@ -28,7 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "DP-SGD-RC step tokens/sec (norm-est+clip+noisy agg); % HBM / MFMA peak"
-EV_STRIDE = 5  # timed steps between two that bracket the dominant kernel with events
+EV_STRIDE = 10  # timed steps between two that bracket the dominant kernel with events
 
 
 def parse():
