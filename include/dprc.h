@@ -271,12 +271,21 @@ size_t dp_clip_aggregate_update_layers_workspace(int dtype, int B, int T, int nl
                                                  const dp_linear_layer_t *layers);
 
 /*
- * dp_clip_aggregate_update for every layer in order (same n_sq, C, sigma, eta
- * and seed; each layer's own id and theta), with the clip factors formed once.
- * theta of each layer is bit-identical to the per-layer call's.  S is not
+ * dp_clip_aggregate_update for every layer (same n_sq, C, sigma, eta and seed;
+ * each layer's own id and theta), with the clip factors formed once.  S is not
  * stored.  c_out (may be NULL) and the status word as in dp_clip_aggregate.
  *  layers   host array of nlayers >= 1 descriptors (read during the call only);
  *           the thetas must not overlap each other or the workspace.
+ * Launches.  A bf16 layer on the MFMA contraction whose count of 256 x 256
+ * output tiles, (p / 256) (d / 256), is below 256 and divides 256 shares one
+ * contraction launch with the next layers of the same tile count in the
+ * array, 256 / tiles of them (at most 16) per launch: a full group fills the
+ * chip without splitting the tokens, so each sum is written once instead of
+ * as token-split partials that the update adds.  Such a layer's sum then adds
+ * the tokens in fewer, longer runs than the per-layer call's, and its theta
+ * agrees with the per-layer call's to fp32 rounding (still the same result
+ * from run to run).  Every other layer, including one that finds no partner,
+ * runs exactly the per-layer call's kernels: its theta is bit-identical.
  * Errors: as dp_clip_aggregate_update, for any layer.
  */
 dp_status_t dp_clip_aggregate_update_layers(int dtype, int B, int T, int nlayers,
@@ -315,6 +324,11 @@ dp_status_t dp_clip_aggregate_update_timed(int dtype, int B, int T, int d, int p
                                            size_t ws_bytes, dp_stream_t stream,
                                            void *ev_agg_begin, void *ev_agg_end,
                                            void *ev_upd_begin, void *ev_upd_end);
+/* Number of clipped-sum contraction launches dp_clip_aggregate_update_layers
+ * makes for these layers (layers sharing a launch count once), or -1 if the
+ * arguments are invalid; for timing and per-launch accounting. */
+int dp_clip_aggregate_update_layers_launches(int dtype, int B, int T, int nlayers,
+                                             const dp_linear_layer_t *layers);
 /* dp_norm_est_layers, with ev_begin / ev_end around all layers' streaming
  * passes (after the probe launch, before the per-sample sum). */
 dp_status_t dp_norm_est_layers_timed(int method, int dtype, int B, int T, int k, int nlayers,
@@ -323,7 +337,10 @@ dp_status_t dp_norm_est_layers_timed(int method, int dtype, int B, int T, int k,
                                      dp_stream_t stream, void *ev_begin, void *ev_end);
 /* dp_clip_aggregate_update_layers, with agg_begin[l] / agg_end[l] around layer
  * l's clipped-sum contraction and upd_begin[l] / upd_end[l] around its noise +
- * update kernel (arrays of nlayers hipEvent_t, any of them NULL). */
+ * update kernel (arrays of nlayers hipEvent_t, any of them NULL).  A
+ * contraction launch shared by several layers is bracketed by the pair of the
+ * first of them; the others' pairs are both recorded right after it (zero
+ * duration), so the pairs still add up to the contraction time of the call. */
 dp_status_t dp_clip_aggregate_update_layers_timed(int dtype, int B, int T, int nlayers,
                                                   const dp_linear_layer_t *layers,
                                                   const float *n_sq, float C, float sigma,

@@ -110,6 +110,8 @@ def load_library():
     L.dp_norm_est_layers_timed.restype = c_int
     L.dp_clip_aggregate_update_layers_workspace.argtypes = [c_int] * 4 + [LP]
     L.dp_clip_aggregate_update_layers_workspace.restype = c_sz
+    L.dp_clip_aggregate_update_layers_launches.argtypes = [c_int] * 4 + [LP]
+    L.dp_clip_aggregate_update_layers_launches.restype = c_int
     L.dp_clip_aggregate_update_layers.argtypes = ([c_int] * 4 + [LP, c_p, c_f, c_f, c_f, c_u64, c_p,
                                                                  c_p, c_sz, c_p])
     L.dp_clip_aggregate_update_layers.restype = c_int
@@ -408,12 +410,21 @@ def dp_clip_aggregate_update_layers_workspace(dtype, B, T, layers):
     return None if n == _SIZE_INVALID else n
 
 
+def dp_clip_aggregate_update_layers_launches(dtype, B, T, layers):
+    """Contraction launches the batched update makes for ``layers`` (None if invalid)."""
+    code = dtype if isinstance(dtype, int) else {"f32": DP_F32, "bf16": DP_BF16}[dtype]
+    n = load_library().dp_clip_aggregate_update_layers_launches(code, B, T, len(layers),
+                                                                _layer_array(layers))
+    return None if n < 0 else n
+
+
 def dp_clip_aggregate_update_layers(layers, n_sq, C, sigma, eta, seed, c_out=None, ws=None,
                                     stream=None, agg_events=None, upd_events=None):
     """dp_clip_aggregate_update over ``layers``, a list of (A, G, layer_id, theta), with
     the clip factors formed once.  ``agg_events`` / ``upd_events``: optional lists of
     (begin, end) pairs, one per layer (or None), around each layer's contraction /
-    noise + update."""
+    noise + update; a contraction launch shared by several layers is timed in the
+    first one's pair, the others' pairs are empty."""
     L = load_library()
     A0 = layers[0][0]
     B, T = A0.shape[0], A0.shape[1]

@@ -335,14 +335,19 @@ struct AggPlan {
 
 // with_sbuf: also a [p][d] buffer for the clipped sum when the caller of the
 // fused update passes no S.
-AggPlan plan_agg(int dtype, int B, int T, int d, int p, bool with_sbuf = false) {
-  AggPlan P;
-  Carver cv;
+// The workspace prefix every clipped-sum plan starts with (it depends on B only).
+void carve_agg_prefix(Carver& cv, AggPlan& P, int B) {
   const size_t Bz = static_cast<size_t>(B > 0 ? B : 1);
   P.status = cv.take(kStatusBytes);
   P.c = cv.take(Bz * 4);
   P.order = cv.take(Bz * 4);
   P.count = cv.take(4);
+}
+
+AggPlan plan_agg(int dtype, int B, int T, int d, int p, bool with_sbuf = false) {
+  AggPlan P;
+  Carver cv;
+  carve_agg_prefix(cv, P, B);
   P.mfma = dtype == DP_BF16 && B > 0 && mfma_gemm_ok(T, d, p);
   if (P.mfma) {
     P.nsplit = mfma_gemm_splits(B, T, d, p);
@@ -1343,13 +1348,70 @@ LayersNormPlan plan_norm_layers(int method, int dtype, int B, int T, int k, int 
   return P;
 }
 
-size_t plan_update_layers(int dtype, int B, int T, int n, const dp_linear_layer_t* L) {
-  size_t t = 0;
+// The batched update's contraction launches.  A layer on the MFMA contraction
+// whose count of 256 x 256 output tiles is below 256 and divides it shares a
+// launch with other layers of the same tile count, 256 / tiles of them (at
+// most kGemmLayersMax), in the order of the call: a full group fills the chip
+// without token splits, so its sums are written once, not as split planes that
+// the update must add.  A layer left alone, and every other layer, takes the
+// per-layer path.  Each unit's workspace is the clip prefix, then the unit's
+// buffers (a group: every layer's planes, or its sum when unsplit).
+struct UpdateUnit {
+  int n = 0;
+  bool grouped = false;
+  int idx[kGemmLayersMax] = {};
+  int tiles = 0;   // per layer (grouped units)
+  int nsplit = 1;  // grouped units
+  size_t buf[kGemmLayersMax] = {};
+  size_t total = 0;
+};
+struct UpdateLayersPlan {
+  std::vector<UpdateUnit> units;  // in the order of their first layer
+  size_t total = 0;
+};
+
+UpdateLayersPlan plan_update_layers(int dtype, int B, int T, int n, const dp_linear_layer_t* L) {
+  UpdateLayersPlan U;
+  std::vector<int> open_unit(257, -1);  // the open group of each tile count
   for (int l = 0; l < n; ++l) {
-    const size_t x = plan_agg(dtype, B, T, L[l].d, L[l].p, true).total;
-    if (x > t) t = x;
+    const AggPlan P = plan_agg(dtype, B, T, L[l].d, L[l].p, true);
+    const int tiles = P.mfma ? mfma_gemm_tiles(L[l].d, L[l].p) : 0;
+    if (tiles > 0 && tiles < 256 && 256 % tiles == 0) {
+      const int cap = 256 / tiles < kGemmLayersMax ? 256 / tiles : kGemmLayersMax;
+      int& u = open_unit[tiles];
+      if (u < 0 || U.units[u].n == cap) {
+        U.units.emplace_back();
+        u = static_cast<int>(U.units.size()) - 1;
+        U.units[u].grouped = true;
+        U.units[u].tiles = tiles;
+      }
+      U.units[u].idx[U.units[u].n++] = l;
+    } else {
+      UpdateUnit one;
+      one.n = 1;
+      one.idx[0] = l;
+      U.units.push_back(one);
+    }
   }
-  return t;
+  for (UpdateUnit& un : U.units) {
+    if (un.grouped && un.n == 1) un.grouped = false;  // alone: the per-layer path
+    if (!un.grouped) {
+      const dp_linear_layer_t& ly = L[un.idx[0]];
+      un.total = plan_agg(dtype, B, T, ly.d, ly.p, true).total;
+    } else {
+      un.nsplit = mfma_gemm_splits_tiles(B, T, static_cast<int64_t>(un.tiles) * un.n);
+      Carver cv;
+      AggPlan P;
+      carve_agg_prefix(cv, P, B);
+      for (int i = 0; i < un.n; ++i) {
+        const dp_linear_layer_t& ly = L[un.idx[i]];
+        un.buf[i] = cv.take(static_cast<size_t>(un.nsplit) * ly.p * ly.d * 4);
+      }
+      un.total = cv.off;
+    }
+    if (un.total > U.total) U.total = un.total;
+  }
+  return U;
 }
 
 }  // namespace
@@ -1472,7 +1534,15 @@ size_t dp_clip_aggregate_update_layers_workspace(int dtype, int B, int T, int nl
   if (nlayers < 1 || layers == nullptr) return kInvalid;
   for (int l = 0; l < nlayers; ++l)
     if (!agg_args_ok(dtype, B, T, layers[l].d, layers[l].p)) return kInvalid;
-  return plan_update_layers(dtype, B, T, nlayers, layers);
+  return plan_update_layers(dtype, B, T, nlayers, layers).total;
+}
+
+int dp_clip_aggregate_update_layers_launches(int dtype, int B, int T, int nlayers,
+                                             const dp_linear_layer_t* layers) {
+  if (nlayers < 1 || layers == nullptr) return -1;
+  for (int l = 0; l < nlayers; ++l)
+    if (!agg_args_ok(dtype, B, T, layers[l].d, layers[l].p)) return -1;
+  return static_cast<int>(plan_update_layers(dtype, B, T, nlayers, layers).units.size());
 }
 
 static dp_status_t update_layers_impl(int dtype, int B, int T, int n, const dp_linear_layer_t* L,
@@ -1489,7 +1559,8 @@ static dp_status_t update_layers_impl(int dtype, int B, int T, int n, const dp_l
     if (!agg_ptrs_ok(B, T, ly.A, ly.G, n_sq, C, c_out)) return DP_ERR_INVALID_ARG;
     if (ly.theta == nullptr || !aligned(ly.theta, 16)) return DP_ERR_INVALID_ARG;
   }
-  const size_t need = plan_update_layers(dtype, B, T, n, L);
+  const UpdateLayersPlan U = plan_update_layers(dtype, B, T, n, L);
+  const size_t need = U.total;
   if (ws_bytes < need) return DP_ERR_WORKSPACE;
   if (ws == nullptr || !aligned(ws, 16)) return DP_ERR_INVALID_ARG;
   for (int l = 0; l < n; ++l) {
@@ -1505,17 +1576,66 @@ static dp_status_t update_layers_impl(int dtype, int B, int T, int n, const dp_l
   const AggPlan P0 = plan_agg(dtype, B, T, L[0].d, L[0].p, true);
   DP_TRY(launch_clip(n_sq, B, C, at<float>(ws, P0.c), c_out, at<uint32_t>(ws, P0.status),
                      at<int>(ws, P0.order), at<int>(ws, P0.count), s));
-  for (int l = 0; l < n; ++l) {
-    const dp_linear_layer_t& ly = L[l];
-    const AggPlan P = plan_agg(dtype, B, T, ly.d, ly.p, true);
-    const Marks mk{agg_begin ? static_cast<hipEvent_t>(agg_begin[l]) : nullptr,
-                   agg_end ? static_cast<hipEvent_t>(agg_end[l]) : nullptr};
-    const Marks mu{upd_begin ? static_cast<hipEvent_t>(upd_begin[l]) : nullptr,
-                   upd_end ? static_cast<hipEvent_t>(upd_end[l]) : nullptr};
-    const dp_status_t st =
-        aggregate_update_layer(P, dtype, B, T, ly.d, ly.p, ly.A, ly.G, n_sq, C, sigma, eta, seed,
-                               ly.layer, ly.theta, nullptr, c_out, ws, s, mk, mu, false);
-    if (st != DP_OK) return st;
+  auto agg_marks = [&](int l) {
+    return Marks{agg_begin ? static_cast<hipEvent_t>(agg_begin[l]) : nullptr,
+                 agg_end ? static_cast<hipEvent_t>(agg_end[l]) : nullptr};
+  };
+  auto upd_marks = [&](int l) {
+    return Marks{upd_begin ? static_cast<hipEvent_t>(upd_begin[l]) : nullptr,
+                 upd_end ? static_cast<hipEvent_t>(upd_end[l]) : nullptr};
+  };
+  const float sigmaC = sigma * C;
+  const float eta_over_B = static_cast<float>(static_cast<double>(eta) / B);
+  for (const UpdateUnit& un : U.units) {
+    if (!un.grouped) {
+      const int l = un.idx[0];
+      const dp_linear_layer_t& ly = L[l];
+      const AggPlan P = plan_agg(dtype, B, T, ly.d, ly.p, true);
+      const dp_status_t st = aggregate_update_layer(P, dtype, B, T, ly.d, ly.p, ly.A, ly.G, n_sq,
+                                                    C, sigma, eta, seed, ly.layer, ly.theta,
+                                                    nullptr, c_out, ws, s, agg_marks(l),
+                                                    upd_marks(l), false);
+      if (st != DP_OK) return st;
+      continue;
+    }
+    GemmLayers tab;
+    tab.n = un.n;
+    int tiles = 0;
+    for (int i = 0; i < un.n; ++i) {
+      const dp_linear_layer_t& ly = L[un.idx[i]];
+      tab.tile0[i] = tiles;
+      tab.d[i] = ly.d;
+      tab.p[i] = ly.p;
+      tab.A[i] = static_cast<const bf16_t*>(ly.A);
+      tab.G[i] = static_cast<const bf16_t*>(ly.G);
+      tab.out[i] = at<float>(ws, un.buf[i]);
+      tiles += un.tiles;
+    }
+    tab.tile0[un.n] = tiles;
+    // the shared launch is timed in its first layer's pair; the others get an
+    // empty pair right after it
+    const Marks mk = agg_marks(un.idx[0]);
+    DP_TRY(mk.open(s));
+    DP_TRY(launch_aggregate_mfma_layers(B, T, tab, at<float>(ws, P0.c), at<int>(ws, P0.order),
+                                        at<int>(ws, P0.count), un.nsplit, s));
+    DP_TRY(mk.close(s));
+    for (int i = 1; i < un.n; ++i) {
+      const Marks mo = agg_marks(un.idx[i]);
+      DP_TRY(mo.open(s));
+      DP_TRY(mo.close(s));
+    }
+    for (int i = 0; i < un.n; ++i) {
+      const dp_linear_layer_t& ly = L[un.idx[i]];
+      const int64_t np = static_cast<int64_t>(ly.p) * ly.d;
+      const Marks mu = upd_marks(un.idx[i]);
+      DP_TRY(mu.open(s));
+      if (un.nsplit == 1)
+        DP_TRY(launch_noise_update(ly.theta, tab.out[i], np, sigmaC, eta_over_B, seed, ly.layer, s));
+      else
+        DP_TRY(launch_noise_update_splits(ly.theta, tab.out[i], un.nsplit, np, nullptr, sigmaC,
+                                          eta_over_B, seed, ly.layer, s));
+      DP_TRY(mu.close(s));
+    }
   }
   return DP_OK;
 }

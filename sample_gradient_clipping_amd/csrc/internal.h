@@ -213,6 +213,26 @@ hipError_t launch_ghost_mfma(const bf16_t* A, const bf16_t* G, int B, int T, int
 
 bool mfma_gemm_ok(int T, int d, int p);
 int mfma_gemm_splits(int B, int T, int d, int p);
+// Token splits for `tiles` 256 x 256 output tiles: about 256 workgroups.
+int mfma_gemm_splits_tiles(int B, int T, int64_t tiles);
+// 256 x 256 output tiles of a p x d clipped sum.
+int mfma_gemm_tiles(int d, int p);
+// Several layers' clipped sums in one launch (layer table in the kernel
+// arguments): layer i owns the flattened tiles tile0[i] .. tile0[i + 1] - 1,
+// tile0[0] = 0, and its token-split planes out[i][split][o][q].
+constexpr int kGemmLayersMax = 16;
+struct GemmLayers {
+  int n;
+  int tile0[kGemmLayersMax + 1];
+  int d[kGemmLayersMax];
+  int p[kGemmLayersMax];
+  const bf16_t* A[kGemmLayersMax];
+  const bf16_t* G[kGemmLayersMax];
+  float* out[kGemmLayersMax];
+};
+hipError_t launch_aggregate_mfma_layers(int B, int T, const GemmLayers& tab, const float* c,
+                                        const int* order, const int* count, int nsplit,
+                                        hipStream_t s);
 // Clipped sum over the active samples order[0..*count) (ascending c):
 // part[split][o][q] = sum over the split's tokens of c G[t][o] A[t][q].
 hipError_t launch_aggregate_mfma(const bf16_t* A, const bf16_t* G, int B, int T, int d, int p,

@@ -118,12 +118,14 @@ __device__ __forceinline__ f32x4 mfma_tr(v4i16 a0, v4i16 a1, v4i16 b0, v4i16 b1,
 // groups of four o tiles (q outer, o inner), so that a run of 32 workgroups
 // covers a 4 x 8 block of tiles of one split: 12 distinct operand panels per
 // XCD instead of up to 33 with the plain row-major order.
-__device__ __forceinline__ void tile_of(int w, int to, int tq, int n, int& ot, int& qt, int& z) {
-  constexpr int kXcd = 8, kGroupM = 4;
-  const int l = (n % kXcd == 0) ? (w % kXcd) * (n / kXcd) + w / kXcd : w;
-  const int tiles = to * tq;
-  z = l / tiles;
-  const int t = l - z * tiles;
+__device__ __forceinline__ int xcd_dealt(int w, int n) {
+  constexpr int kXcd = 8;
+  return (n % kXcd == 0) ? (w % kXcd) * (n / kXcd) + w / kXcd : w;
+}
+
+// Tile t of a to x tq grid in groups of four o tiles (q outer, o inner).
+__device__ __forceinline__ void tile_in_grid(int t, int to, int tq, int& ot, int& qt) {
+  constexpr int kGroupM = 4;
   const int grp = t / (kGroupM * tq);
   const int r = t - grp * kGroupM * tq;
   const int gm = to - grp * kGroupM < kGroupM ? to - grp * kGroupM : kGroupM;
@@ -131,18 +133,26 @@ __device__ __forceinline__ void tile_of(int w, int to, int tq, int n, int& ot, i
   ot = grp * kGroupM + (r - qt * gm);
 }
 
+__device__ __forceinline__ void tile_of(int w, int to, int tq, int n, int& ot, int& qt, int& z) {
+  const int l = xcd_dealt(w, n);
+  const int tiles = to * tq;
+  z = l / tiles;
+  tile_in_grid(l - z * tiles, to, tq, ot, qt);
+}
+
+// One workgroup's tile (o tile ot, q tile qt, token split or sample z).
 // MODE 0: clipped aggregation, split-K over the active samples in ascending c.
 // MODE 1: FGC, z = sample, whole sample, no scaling.
 template <int MODE>
-__global__ void __launch_bounds__(512, 1) k_gemm_tokens(
-    const bf16_t* __restrict__ A, const bf16_t* __restrict__ G, int T, int d, int p,
-    const float* __restrict__ cvec, const int* __restrict__ order, const int* __restrict__ count,
-    int64_t split_tokens, float* __restrict__ out) {
+__device__ __forceinline__ void gemm_tile(const bf16_t* __restrict__ A,
+                                          const bf16_t* __restrict__ G, int T, int d, int p,
+                                          const float* __restrict__ cvec,
+                                          const int* __restrict__ order,
+                                          const int* __restrict__ count, int64_t split_tokens,
+                                          int ot, int qt, int z, float* __restrict__ out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  int ot, qt, z;
-  tile_of(blockIdx.x, p / kGM, d / kGN, gridDim.x, ot, qt, z);
   const int o0 = ot * kGM;
   const int q0 = qt * kGN;
 
@@ -324,6 +334,37 @@ __global__ void __launch_bounds__(512, 1) k_gemm_tokens(
     }
 }
 
+template <int MODE>
+__global__ void __launch_bounds__(512, 1) k_gemm_tokens(
+    const bf16_t* __restrict__ A, const bf16_t* __restrict__ G, int T, int d, int p,
+    const float* __restrict__ cvec, const int* __restrict__ order, const int* __restrict__ count,
+    int64_t split_tokens, float* __restrict__ out) {
+  int ot, qt, z;
+  tile_of(blockIdx.x, p / kGM, d / kGN, gridDim.x, ot, qt, z);
+  gemm_tile<MODE>(A, G, T, d, p, cvec, order, count, split_tokens, ot, qt, z, out);
+}
+
+// The clipped sums of several layers in one launch: the flattened tile list is
+// layer 0's tiles, then layer 1's, ..., repeated once per token split; the
+// workgroup -> tile mapping deals contiguous runs of it to the XCDs as above,
+// so that an XCD works on one or two layers at a time.
+__global__ void __launch_bounds__(512, 1) k_gemm_tokens_layers(
+    int T, const float* __restrict__ cvec, const int* __restrict__ order,
+    const int* __restrict__ count, int64_t split_tokens, GemmLayers tab) {
+  const int l = xcd_dealt(blockIdx.x, gridDim.x);
+  const int tiles = tab.tile0[tab.n];
+  const int z = l / tiles;
+  int t = l - z * tiles;
+  int i = 0;
+  while (i + 1 < tab.n && t >= tab.tile0[i + 1]) ++i;
+  t -= tab.tile0[i];
+  const int d = tab.d[i], p = tab.p[i];
+  int ot, qt;
+  tile_in_grid(t, p / kGM, d / kGN, ot, qt);
+  gemm_tile<0>(tab.A[i], tab.G[i], T, d, p, cvec, order, count, split_tokens, ot, qt, z,
+               tab.out[i]);
+}
+
 bool mfma_gemm_ok(int T, int d, int p) {
   return T > 0 && T % kGroup == 0 && d % kGN == 0 && p % kGM == 0;
 }
@@ -331,7 +372,10 @@ bool mfma_gemm_ok(int T, int d, int p) {
 // Split the token range so that there are about 256 workgroups; each split is
 // a whole number of 128-token groups.
 int mfma_gemm_splits(int B, int T, int d, int p) {
-  const int64_t tiles = static_cast<int64_t>(p / kGM) * (d / kGN);
+  return mfma_gemm_splits_tiles(B, T, static_cast<int64_t>(p / kGM) * (d / kGN));
+}
+
+int mfma_gemm_splits_tiles(int B, int T, int64_t tiles) {
   int64_t want = (256 + tiles - 1) / (tiles > 0 ? tiles : 1);
   const int64_t groups = static_cast<int64_t>(B) * T / kGroup;
   if (want > groups) want = groups;
@@ -348,6 +392,26 @@ hipError_t launch_aggregate_mfma(const bf16_t* A, const bf16_t* G, int B, int T,
   per = (per + kGroup - 1) / kGroup * kGroup;
   hipLaunchKernelGGL(k_gemm_tokens<0>, dim3((p / kGM) * (d / kGN) * nsplit), dim3(64 * kWaves), 0, s,
                      A, G, T, d, p, c, order, count, per, part);
+  return hipGetLastError();
+}
+
+int mfma_gemm_tiles(int d, int p) { return (p / kGM) * (d / kGN); }
+
+hipError_t launch_aggregate_mfma_layers(int B, int T, const GemmLayers& tab, const float* c,
+                                        const int* order, const int* count, int nsplit,
+                                        hipStream_t s) {
+  if (tab.n < 1 || tab.n > kGemmLayersMax || nsplit < 1) return hipErrorInvalidValue;
+  int tiles = 0;
+  for (int i = 0; i < tab.n; ++i) {
+    if (!mfma_gemm_ok(T, tab.d[i], tab.p[i]) || tab.tile0[i] != tiles) return hipErrorInvalidValue;
+    tiles += mfma_gemm_tiles(tab.d[i], tab.p[i]);
+  }
+  if (tab.tile0[tab.n] != tiles) return hipErrorInvalidValue;
+  const int64_t total = static_cast<int64_t>(B) * T;
+  int64_t per = (total + nsplit - 1) / nsplit;
+  per = (per + kGroup - 1) / kGroup * kGroup;
+  hipLaunchKernelGGL(k_gemm_tokens_layers, dim3(tiles * nsplit), dim3(64 * kWaves), 0, s, T, c,
+                     order, count, per, tab);
   return hipGetLastError();
 }
 

@@ -193,6 +193,38 @@ def test_batched_workspace_queries(lib):
                     dp.dp_clip_aggregate_update_workspace("bf16", 8, 4096, 2048, 512))
     assert lib.dp_clip_aggregate_update_layers_workspace(1, 8, 4096, 0, two) == SZ
     assert lib.dp_clip_aggregate_update_layers_workspace(1, 8, 4096, 2, bad) == SZ
+    # 64- and 16-tile layers with no partner of their tile count: two launches
+    assert lib.dp_clip_aggregate_update_layers_launches(1, 8, 4096, 2, two) == 2
+    assert lib.dp_clip_aggregate_update_layers_launches(1, 8, 4096, 0, two) == -1
+    assert lib.dp_clip_aggregate_update_layers_launches(1, 8, 4096, 2, bad) == -1
+
+
+def test_batched_update_groups_small_contractions(lib):
+    # layers whose 256 x 256 tile count divides 256 share launches, 256 / tiles per
+    # launch: a full group is unsplit and needs one p x d fp32 sum per layer
+    F = 0x100000
+    qo = [(2048, 2048, i, F, F, None) for i in range(4)]      # 64 tiles each
+    kv = [(2048, 512, 10 + i, F, F, None) for i in range(16)]  # 16 tiles each
+    per_q = dp.dp_clip_aggregate_update_workspace("bf16", 8, 4096, 2048, 2048)
+    for specs, one in ((qo, 2048 * 2048 * 4), (kv, 2048 * 512 * 4)):
+        arr = _layers(specs)
+        assert lib.dp_clip_aggregate_update_layers_launches(1, 8, 4096, len(specs), arr) == 1
+        u = lib.dp_clip_aggregate_update_layers_workspace(1, 8, 4096, len(specs), arr)
+        assert len(specs) * one <= u < len(specs) * one + 4096
+    assert lib.dp_clip_aggregate_update_layers_workspace(1, 8, 4096, 4, _layers(qo)) < per_q
+    # the stack's order: q k v o per block, then gate up down (256 tiles, never grouped)
+    block = lambda b: [(2048, 2048, 0, F, F, None), (2048, 512, 1, F, F, None),
+                       (2048, 512, 2, F, F, None), (2048, 2048, 3, F, F, None),
+                       (2048, 8192, 4, F, F, None), (2048, 8192, 5, F, F, None),
+                       (8192, 2048, 6, F, F, None)]
+    stack = [ly for b in range(16) for ly in block(b)]
+    assert lib.dp_clip_aggregate_update_layers_launches(1, 8, 4096, 112, _layers(stack)) == 8 + 2 + 48
+    # a fifth 64-tile layer has no partner: the per-layer path and its workspace
+    five = qo + [(2048, 2048, 9, F, F, None)]
+    assert lib.dp_clip_aggregate_update_layers_launches(1, 8, 4096, 5, _layers(five)) == 2
+    assert lib.dp_clip_aggregate_update_layers_workspace(1, 8, 4096, 5, _layers(five)) == per_q
+    # fp32 layers never share a launch
+    assert lib.dp_clip_aggregate_update_layers_launches(0, 8, 4096, 4, _layers(qo)) == 4
 
 
 def test_batched_calls_reject_bad_arguments(lib):

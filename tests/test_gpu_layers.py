@@ -21,7 +21,7 @@ import torch
 import oracle
 from sample_gradient_clipping_amd import binding as dp
 from sample_gradient_clipping_amd.inputs import linear_inputs
-from tests.gpu_util import device, f64, max_rel_elementwise, report
+from tests.gpu_util import device, f64, max_rel_elementwise, max_rel_normwise, report
 
 pytestmark = pytest.mark.gpu
 
@@ -138,7 +138,9 @@ def test_norm_layers_fallback_matches_per_layer(dev, method, dtype, shapes):
 
 
 @pytest.mark.parametrize("dtype,B,T,shapes", [
-    ("bf16", 8, 256, FUSED_SHAPES),                   # MFMA contractions, split and whole
+    # MFMA contractions with token splits, each alone in its tile count (16 and
+    # 64 tiles of 256 x 256), and one of 256 tiles (no splits)
+    ("bf16", 8, 256, [(2048, 512, 4), (2048, 2048, 3), (4096, 4096, 5)]),
     ("f32", 3, 40, [(24, 20, 1), (16, 12, 2)]),        # generic kernels
 ])
 def test_update_layers_bit_identical_to_per_layer(dev, dtype, B, T, shapes):
@@ -174,3 +176,72 @@ def test_update_layers_status_word(dev):
     dp.dp_clip_aggregate_update_layers(layers, bad, 1.0, 1.0, 1e-4, 5, ws=ws)
     assert dp.dp_read_device_status(ws) == dp.DP_STATUS_NONFINITE_NORM
     assert dp.dp_read_device_status(ws) == 0
+
+
+def _tiles(d, p):
+    return (p // 256) * (d // 256)
+
+
+@pytest.mark.parametrize("B,T,shapes,alone", [
+    # two 64-tile layers of different shapes: one launch of 128 tiles, 2 token splits
+    (8, 256, [(2048, 2048, 3), (4096, 1024, 9)], []),
+    # four 64-tile layers: 256 tiles, no splits
+    (4, 256, [(2048, 2048, 20 + i) for i in range(4)], []),
+    # sixteen 16-tile layers: 256 tiles, no splits
+    (4, 128, [(2048, 512, 40 + i) for i in range(16)], []),
+    # two 16-tile layers sharing a launch (with token splits), four 64-tile layers
+    # in a full group, and a fifth 64-tile layer alone (the per-layer path)
+    (4, 128, [(2048, 512, 70), (2048, 2048, 71), (2048, 2048, 72), (2048, 2048, 73),
+              (2048, 512, 74), (2048, 2048, 75), (2048, 2048, 76)], [6]),
+])
+def test_update_layers_grouped_contraction(dev, B, T, shapes, alone):
+    """Layers whose tile counts divide 256 share contraction launches: theta matches
+    the per-layer calls to fp32 rounding (bit for bit for a layer left alone) and
+    the oracle on sampled rows."""
+    host, devl = _make(B, T, shapes, "bf16", 12)
+    n = torch.linspace(0.5, 40.0, B, dtype=torch.float32, device=dev)
+    C, sigma, eta, seed = 2.0, 2e-3, 50.0, 123
+    th0 = [torch.randn(G.shape[2], A.shape[2], device=dev) * 1e-2 for A, G, _ in devl]
+    th_b = [t.clone() for t in th0]
+    th_p = [t.clone() for t in th0]
+    c_b = torch.empty(B, dtype=torch.float32, device=dev)
+    dp.dp_clip_aggregate_update_layers([(A, G, lid, th) for (A, G, lid), th in zip(devl, th_b)],
+                                       n, C, sigma, eta, seed, c_out=c_b)
+    for (A, G, lid), th in zip(devl, th_p):
+        dp.dp_clip_aggregate_update(A, G, n, C, sigma, eta, seed, lid, th)
+    torch.cuda.synchronize()
+    c_ref, _ = oracle.clip_factors(f64(n), C)
+    assert max_rel_elementwise(f64(c_b), c_ref) <= 1e-6
+    worst_p = worst_o = 0.0
+    for i, ((A, G, lid), t0, tb, tp) in enumerate(zip(host, th0, th_b, th_p)):
+        if i in alone:
+            assert torch.equal(tb, tp)
+        e_p = max_rel_normwise(f64(tb) - f64(t0), f64(tp) - f64(t0))
+        rows = np.sort(np.random.default_rng(i).choice(tb.shape[0], size=8, replace=False))
+        S_rows = oracle.aggregate_rows(A, G, c_ref, rows)
+        t_ref = oracle.noise_update(f64(t0)[rows], S_rows, sigma, C, eta, B, seed, lid, rows=rows)
+        e_o = max_rel_normwise(f64(tb)[rows] - f64(t0)[rows], t_ref - f64(t0)[rows])
+        worst_p, worst_o = max(worst_p, e_p), max(worst_o, e_o)
+    report(f"update layers grouped x{len(shapes)}", per_layer=worst_p, oracle=worst_o)
+    assert worst_p <= 1e-5
+    assert worst_o <= 1e-4
+
+
+def test_update_layers_grouped_timed_pairs_add_up(dev):
+    # a shared launch is timed in its first layer's pair; the others' pairs are empty
+    B, T = 4, 1024  # 137 GFLOP in the shared launch: far longer than an empty pair
+    _, devl = _make(B, T, [(2048, 2048, 80 + i) for i in range(4)], "bf16", 13)
+    thetas = [torch.zeros(G.shape[2], A.shape[2], device=dev) for A, G, _ in devl]
+    layers = [(A, G, lid, th) for (A, G, lid), th in zip(devl, thetas)]
+    n = torch.full((B,), 4.0, dtype=torch.float32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in layers]
+    eu = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in layers]
+    dp.dp_clip_aggregate_update_layers(layers, n, 1.0, 1.0, 1e-3, 5, agg_events=ev, upd_events=eu)
+    torch.cuda.synchronize()
+    t = [a.elapsed_time(b) for a, b in ev]
+    report("update layers grouped timed pairs", first_ms=t[0], others_max_ms=max(t[1:]))
+    assert t[0] > 0.0
+    assert all(abs(x) < 0.2 * t[0] for x in t[1:])
+    assert all(a.elapsed_time(b) > 0.0 for a, b in eu)
