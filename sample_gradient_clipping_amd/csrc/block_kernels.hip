@@ -62,6 +62,12 @@ __device__ __forceinline__ void nt_wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt lgkmcnt(0): the wave's LDS reads (and scalar loads) have returned;
+// vmcnt and expcnt unconstrained.
+__device__ __forceinline__ void nt_wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((0x3 << 14) | 0xF | (0x7 << 4));
+}
+
 __device__ __forceinline__ uint32_t nt_lds_addr(const unsigned char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((nt_lds_void*)(p)));
 }
@@ -151,23 +157,27 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
   const int side = wave >> 2;
   const int rbase = (wave & 3) * 64;
   const int dst_off = side * kNtSideBytes + rbase * kNtRowBytes;
-  int64_t goff1[4], goff2[4], goff3[4];  // element offsets of this lane's chunk, per instruction
+  // This lane's global row of instruction i is row_of(i) below, from one row
+  // kept in a register (rows 16 i further, clamped to M - 1 on the A side; on
+  // the interleaved gate/up side 16 (i / 2) further); its 16-byte chunk
+  // depends on the parity of i only.  The element offsets are formed at issue
+  // time, so that few registers stay live across the loop.
+  const int r0 = rbase + (lane >> 2);
+  int grow0;
+  if (side == 0)
+    grow0 = m0 + r0;
+  else if (EPI == kEpiSwiglu)
+    grow0 = n0 / 2 + (r0 >> 5) * 16 + (r0 & 15);  // block r / 16: gate if even, up if odd
+  else
+    grow0 = n0 + r0;
+  int gcol[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = rbase + i * 16 + (lane >> 2);
-    const int gchunk = (lane & 3) ^ nt_swz(r);
-    int grow;
-    if (side == 0) {
-      grow = m0 + r < M ? m0 + r : M - 1;
-    } else if (EPI == kEpiSwiglu) {
-      grow = n0 / 2 + (r >> 5) * 16 + (r & 15);  // block r / 16: gate if even, up if odd
-    } else {
-      grow = n0 + r;
-    }
-    goff1[i] = static_cast<int64_t>(grow) * K1 + gchunk * 8;
-    goff2[i] = static_cast<int64_t>(grow) * K2 + gchunk * 8;
-    goff3[i] = static_cast<int64_t>(grow) * K3 + gchunk * 8;
-  }
+  for (int par = 0; par < 2; ++par) gcol[par] = ((lane & 3) ^ nt_swz(r0 + 16 * par)) * 8;
+  auto row_of = [&](int i) -> int64_t {
+    if (side == 0) return grow0 + 16 * i < M ? grow0 + 16 * i : M - 1;
+    if (EPI == kEpiSwiglu) return grow0 + (i >> 1) * 16;
+    return grow0 + 16 * i;
+  };
   // Instruction i covers rows 16 i + rbase / 16 ..; rbase / 16 is even, so the
   // 16-row block of instruction i is a gate block for even i, an up block for odd.
   const bf16_t* src1[2] = {side == 0 ? A1 : a.B1,
@@ -180,18 +190,21 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
     if (s < ns1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        nt_dma(reinterpret_cast<const unsigned char*>(src1[i & 1] + s * kNtK + goff1[i]),
+        nt_dma(reinterpret_cast<const unsigned char*>(src1[i & 1] + row_of(i) * K1 + s * kNtK +
+                                                      gcol[i & 1]),
                base + i * 1024);
     } else if (s < ns12) {
       const bf16_t* p = src2 + (s - ns1) * kNtK;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        nt_dma(reinterpret_cast<const unsigned char*>(p + goff2[i]), base + i * 1024);
+        nt_dma(reinterpret_cast<const unsigned char*>(p + row_of(i) * K2 + gcol[i & 1]),
+               base + i * 1024);
     } else {
       const bf16_t* p = src3 + (s - ns12) * kNtK;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        nt_dma(reinterpret_cast<const unsigned char*>(p + goff3[i]), base + i * 1024);
+        nt_dma(reinterpret_cast<const unsigned char*>(p + row_of(i) * K3 + gcol[i & 1]),
+               base + i * 1024);
     }
   };
 
@@ -200,16 +213,16 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
   // 8 g .. 8 g + 7 for both operands).
   const int wm = wave >> 2, wn = wave & 3;
   const int li = lane & 15, g = lane >> 4;
-  int rd_a[8], rd_b[4];
+  // The swizzle of row r = base + 16 mb + li (base a multiple of 128) depends
+  // on li and on the parity of mb only: two base addresses per operand, the
+  // blocks at constant offsets from them.
+  int rd_a[2], rd_b[2];
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) {
-    const int r = wm * 128 + mb * 16 + li;
-    rd_a[mb] = r * kNtRowBytes + ((g ^ nt_swz(r)) << 4);
-  }
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int r = wn * 64 + nb * 16 + li;
-    rd_b[nb] = kNtSideBytes + r * kNtRowBytes + ((g ^ nt_swz(r)) << 4);
+  for (int par = 0; par < 2; ++par) {
+    const int ra = wm * 128 + par * 16 + li;
+    rd_a[par] = ra * kNtRowBytes + ((g ^ nt_swz(ra)) << 4);
+    const int rb = wn * 64 + par * 16 + li;
+    rd_b[par] = kNtSideBytes + rb * kNtRowBytes + ((g ^ nt_swz(rb)) << 4);
   }
 
   f32x4 acc[8][4];
@@ -218,49 +231,88 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const unsigned char* st) {
+  // A stage's MFMA operands, read from LDS into registers one stage ahead of
+  // the products that use them.
+  struct Frag {
     u32x4 xa[8], wb[4];
+  };
+  auto read_frags = [&](const unsigned char* st, Frag& f) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) wb[nb] = nt_read16(st + rd_b[nb]);
+    for (int nb = 0; nb < 4; ++nb)
+      f.wb[nb] = nt_read16(st + rd_b[nb & 1] + (nb & ~1) * 16 * kNtRowBytes);
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) xa[mb] = nt_read16(st + rd_a[mb]);
+    for (int mb = 0; mb < 8; ++mb)
+      f.xa[mb] = nt_read16(st + rd_a[mb & 1] + (mb & ~1) * 16 * kNtRowBytes);
+  };
+  auto mma = [&](const Frag& f) {
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = nt_mfma(wb[nb], xa[mb], acc[mb][nb]);
+      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = nt_mfma(f.wb[nb], f.xa[mb], acc[mb][nb]);
   };
 
   unsigned char* L0 = nt_lds0;
   unsigned char* L1 = nt_lds1;
   unsigned char* L2 = nt_lds2;
   unsigned char* L3 = nt_lds3;
+  Frag F0, F1;
 
+  // Prologue: stages 0..2 in flight; once stage 0 has landed everywhere, its
+  // operands go to registers and stage 3 fills the fourth slot.
   if (nstage > 0) issue(0, L0);
   if (nstage > 1) issue(1, L1);
   if (nstage > 2) issue(2, L2);
+  if (nstage > 2)
+    nt_wait_vm<8>();
+  else if (nstage > 1)
+    nt_wait_vm<4>();
+  else
+    nt_wait_vm<0>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (nstage > 0) read_frags(L0, F0);
+  if (nstage > 3) issue(3, L3);
 
-  // Stage s: wait for this wave's loads of s (those of s + 1, s + 2 may stay in
-  // flight), barrier, refill the slot of stage s - 1 with s + 3, compute.
-  auto stage = [&](int s, const unsigned char* cur, unsigned char* refill) {
-    const int ahead = nstage - 1 - s;
+  // Step s (stage s's operands are in `cur`): wait for this wave's loads of
+  // stage s + 1 (those of s + 2 and s + 3 may stay in flight) and for its LDS
+  // reads of stage s; the barrier then certifies that stage s + 1 has landed
+  // for every wave and that no wave still reads stage s's slot, which is
+  // refilled with stage s + 4.  Stage s + 1's operands are read while stage
+  // s's products run, one 16-byte read after every second of the first 24
+  // products, so that the reads issue under the matrix pipe instead of ahead
+  // of it.
+  auto step = [&](int s, const Frag& cur, Frag& next, const unsigned char* next_lds,
+                  unsigned char* refill) {
+    const int ahead = nstage - 2 - s;  // stages issued beyond s + 1
     if (ahead >= 2)
       nt_wait_vm<8>();
     else if (ahead == 1)
       nt_wait_vm<4>();
     else
       nt_wait_vm<0>();
+    nt_wait_lgkm0();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (s + 3 < nstage) issue(s + 3, refill);
-    compute(cur);
+    if (s + 4 < nstage) issue(s + 4, refill);
+    // unconditional, so that the reads and the products share one basic block:
+    // after the last stage this reads a slot no later stage fills, unused
+    read_frags(next_lds, next);
+    mma(cur);
+#pragma unroll
+    for (int k = 0; k < 12; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   for (int s = 0; s < nstage; s += 4) {
-    stage(s, L0, L3);
-    if (s + 1 < nstage) stage(s + 1, L1, L0);
-    if (s + 2 < nstage) stage(s + 2, L2, L1);
-    if (s + 3 < nstage) stage(s + 3, L3, L2);
+    step(s, F0, F1, L1, L0);
+    if (s + 1 < nstage) step(s + 1, F1, F0, L2, L1);
+    if (s + 2 < nstage) step(s + 2, F0, F1, L3, L2);
+    if (s + 3 < nstage) step(s + 3, F1, F0, L0, L3);
   }
 
   // Epilogue: lane (li, g) holds acc[m][n .. n + 3] of block (mb, nb), m = row
