@@ -31,7 +31,9 @@
 // Synchronisation is an explicit vmcnt wait for this wave's loads plus a bare
 // s_barrier (no fence that would drain the loads of later stages).  Inside a
 // step the 24 transposing reads are interleaved one by one with the first 24
-// of its 32 MFMAs.
+// of its 32 MFMAs, and the refill's DMA is issued after the first eight of
+// them: every wave leaves the barrier at the same moment, and whatever a wave
+// issues before its first MFMA leaves the matrix pipe of its SIMD idle.
 //
 // Per-sample clip factors without a second accumulator: the active samples are
 // visited in ascending c, and the accumulator holds sum_{seen} (c_seg / c_cur)
@@ -83,22 +85,31 @@ __device__ __forceinline__ v4i16 tr_read(const unsigned char* p) {
 // LDS.  Issued as inline asm so that the compiler does not treat the DMA as an
 // LDS write it must drain before every later LDS read: the kernel counts these
 // loads itself (wait_vm) and orders the stages with s_barrier.  lds_addr is
-// the wave-uniform LDS byte address of the first pair (goes to m0).
-__device__ __forceinline__ void dma_pairs(const unsigned char* gsrc, uint32_t pair_step,
+// the wave-uniform LDS byte address of the first pair (goes to m0); off[i] is
+// this lane's byte offset of pair i from the wave-uniform gbase, so that the
+// issue is four m0 writes and four loads, with no 64-bit address arithmetic
+// per load (that arithmetic, on the scalar unit after every stage barrier,
+// cost 3% of the contraction).
+__device__ __forceinline__ void dma_pairs(const unsigned char* gbase, const uint32_t off[4],
                                           uint32_t lds_addr) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const unsigned char* gp = gsrc + i * pair_step;
-    // m0 carries the LDS address; it is saved and restored around the load
-    // (the compiler reserves m0 and must find it unchanged).
-    uint32_t m0_saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(m0_saved)
-        : "v"(gp), "s"(__builtin_amdgcn_readfirstlane(lds_addr + i * kPairBytes))
-        : "memory");
-  }
+  // m0 carries the LDS address; it is saved and restored around the loads
+  // (the compiler reserves m0 and must find it unchanged).  The global address
+  // is the wave-uniform base (SGPRs) plus this lane's 32-bit offset.
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\tglobal_load_lds_dwordx4 %1, %5\n\t"
+      "s_mov_b32 m0, %7\n\tglobal_load_lds_dwordx4 %2, %5\n\t"
+      "s_mov_b32 m0, %8\n\tglobal_load_lds_dwordx4 %3, %5\n\t"
+      "s_mov_b32 m0, %9\n\tglobal_load_lds_dwordx4 %4, %5\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(gbase),
+        "s"(__builtin_amdgcn_readfirstlane(lds_addr)),
+        "s"(__builtin_amdgcn_readfirstlane(lds_addr + kPairBytes)),
+        "s"(__builtin_amdgcn_readfirstlane(lds_addr + 2 * kPairBytes)),
+        "s"(__builtin_amdgcn_readfirstlane(lds_addr + 3 * kPairBytes))
+      : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr_of(const unsigned char* p) {
@@ -179,7 +190,10 @@ __device__ __forceinline__ void gemm_tile(const bf16_t* __restrict__ A,
   const uint32_t lane_src =
       static_cast<uint32_t>(((2 * pair0 + (lane >> 5)) * ld + col0 + (lane & 31) * 8) * 2);
   const uint32_t pair_step = static_cast<uint32_t>(2 * ld * 2);
+  const uint32_t dma_off[4] = {lane_src, lane_src + pair_step, lane_src + 2 * pair_step,
+                                lane_src + 3 * pair_step};
   const int dst_off = side * kSideBytes + pair0 * kPairBytes;
+  const int64_t stage_bytes_g = static_cast<int64_t>(kGK) * ld * 2;
 
   // The sample being loaded is looked up once per sample (its entry of the
   // visiting order is read when the previous sample's last tile is issued), so
@@ -189,15 +203,21 @@ __device__ __forceinline__ void gemm_tile(const bf16_t* __restrict__ A,
   const int64_t nseg = MODE == 0 ? static_cast<int64_t>(*count) : 1;
   int64_t ld_sample = MODE == 0 ? (nstage > 0 ? static_cast<int64_t>(order[ld_seg]) : 0)
                                 : static_cast<int64_t>(z);
+  // wave-uniform global base of the next stage to load, advanced by one stage
+  // per issue and re-formed when the visiting order moves to the next sample
+  const unsigned char* gbase =
+      reinterpret_cast<const unsigned char*>(src + (ld_sample * T + ld_off) * ld);
   auto issue = [&](unsigned char* stage_lds) {
-    const unsigned char* base =
-        reinterpret_cast<const unsigned char*>(src + (ld_sample * T + ld_off) * ld) + lane_src;
-    dma_pairs(base, pair_step, lds_addr_of(stage_lds) + dst_off);
+    dma_pairs(gbase, dma_off, lds_addr_of(stage_lds) + dst_off);
+    gbase += stage_bytes_g;
     ld_off += kGK;
     if (ld_off == T) {
       ld_off = 0;
       ++ld_seg;
-      if (MODE == 0 && ld_seg < nseg) ld_sample = order[ld_seg];
+      if (MODE == 0 && ld_seg < nseg) {
+        ld_sample = order[ld_seg];
+        gbase = reinterpret_cast<const unsigned char*>(src + ld_sample * T * ld);
+      }
     }
   };
 
@@ -221,22 +241,25 @@ __device__ __forceinline__ void gemm_tile(const bf16_t* __restrict__ A,
   struct Frag {
     v4i16 a[8][2], b[4][2];
   };
-  auto read_frags = [&](const unsigned char* st, Frag& f) {
+  // reads r0 .. r1 - 1 of the 24 (16 of the 128-wide operand, then 8)
+  auto read_frags = [&](const unsigned char* st, Frag& f, int r0, int r1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) f.a[i][h] = tr_read(st + rd_a + h * kRowBytes + i * 32);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) f.b[j][h] = tr_read(st + rd_b + h * kRowBytes + j * 32);
+    for (int r = 0; r < 24; ++r) {
+      if (r < r0 || r >= r1) continue;
+      if (r < 16)
+        f.a[r >> 1][r & 1] = tr_read(st + rd_a + (r & 1) * kRowBytes + (r >> 1) * 32);
+      else
+        f.b[(r - 16) >> 1][r & 1] = tr_read(st + rd_b + (r & 1) * kRowBytes + ((r - 16) >> 1) * 32);
+    }
   };
-  auto mma = [&](const Frag& f) {
+  // products m0 .. m1 - 1 of the 32 (column block j = m / 8, row block i = m % 8)
+  auto mma = [&](const Frag& f, int m0, int m1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        acc[i][j] = mfma_tr(f.a[i][0], f.a[i][1], f.b[j][0], f.b[j][1], acc[i][j]);
+    for (int m = 0; m < 32; ++m) {
+      if (m < m0 || m >= m1) continue;
+      const int j = m >> 3, i = m & 7;
+      acc[i][j] = mfma_tr(f.a[i][0], f.a[i][1], f.b[j][0], f.b[j][1], acc[i][j]);
+    }
   };
 
   unsigned char* L0 = g_lds0;
@@ -257,7 +280,7 @@ __device__ __forceinline__ void gemm_tile(const bf16_t* __restrict__ A,
   else
     wait_vm<0>();
   __builtin_amdgcn_s_barrier();
-  if (nstage > 0) read_frags(L0, F0);
+  if (nstage > 0) read_frags(L0, F0, 0, 24);
   if (nstage > 3) issue(L3);
 
   // Step s (stage s's operands are in `cur`): wait for this wave's loads of
@@ -276,40 +299,52 @@ __device__ __forceinline__ void gemm_tile(const bf16_t* __restrict__ A,
       wait_vm<0>();
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();
-    if (s + 4 < nstage) issue(refill);
     // Unconditional, so that the reads and the products share one basic block
     // and can be interleaved: after the last stage this reads a slot that no
-    // later stage fills, and those operands are never used.
-    read_frags(next_lds, next);
-    mma(cur);
-    // One transposing read after each of the first 24 products: the LDS reads
-    // then issue under the MFMA pipe instead of ahead of it.
+    // later stage fills, and those operands are never used.  The first eight
+    // products go ahead of the refill's DMA, so that the matrix pipe restarts
+    // right after the barrier.
+    read_frags(next_lds, next, 0, 8);
+    mma(cur, 0, 8);
 #pragma unroll
-    for (int k = 0; k < 24; ++k) {
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    if (s + 4 < nstage) issue(refill);
+    read_frags(next_lds, next, 8, 24);
+    mma(cur, 8, 32);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
+  // The visiting order's sample of the stage group starting at stage s: the
+  // group never straddles two samples (T % 128 == 0), so the sample changes
+  // exactly at next_bd, every T / 32 stages after the first change (kept as a
+  // counter: a 64-bit division per group cost as much as the group's barrier).
   float cur_c = 1.f;
   int64_t cur_seg = -1;
+  int next_bd = 0;
+  if (MODE == 0 && nstage > 0) {
+    cur_seg = kv0 / T;
+    cur_c = cvec[order[cur_seg]];
+    next_bd = static_cast<int>(((cur_seg + 1) * T - kv0) / kGK);
+  }
   for (int s = 0; s < nstage; s += kNStage) {
-    if (MODE == 0) {
-      // A group of four stages never straddles two samples (T % 128 == 0).
-      const int64_t seg = (kv0 + static_cast<int64_t>(s) * kGK) / T;
-      if (seg != cur_seg) {
-        const float c_new = cvec[order[seg]];
-        if (cur_seg >= 0) {
-          const float ratio = cur_c / c_new;
+    if (MODE == 0 && s == next_bd) {
+      ++cur_seg;
+      next_bd += T / kGK;
+      const float c_new = cvec[order[cur_seg]];
+      const float ratio = cur_c / c_new;
 #pragma unroll
-          for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] *= ratio;
-        }
-        cur_c = c_new;
-        cur_seg = seg;
-      }
+        for (int j = 0; j < 4; ++j) acc[i][j] *= ratio;
+      cur_c = c_new;
     }
     step(s, F0, F1, L1, L0);
     if (s + 1 < nstage) step(s + 1, F1, F0, L2, L1);
