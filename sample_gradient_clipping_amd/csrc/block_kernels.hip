@@ -89,6 +89,28 @@ __device__ __forceinline__ void nt_dma(const unsigned char* gp, uint32_t lds_add
       : "memory");
 }
 
+// Four 1 KB DMA instructions of one stage: instruction i reads from the
+// wave-uniform base b[i] (SGPRs) plus this lane's 32-bit offset off[i], into
+// LDS m0 = lds_addr + 1 KB i.  No per-load address arithmetic.
+__device__ __forceinline__ void nt_dma4(const unsigned char* const b[4], const uint32_t off[4],
+                                        uint32_t lds_addr) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %9\n\tglobal_load_lds_dwordx4 %1, %5\n\t"
+      "s_mov_b32 m0, %10\n\tglobal_load_lds_dwordx4 %2, %6\n\t"
+      "s_mov_b32 m0, %11\n\tglobal_load_lds_dwordx4 %3, %7\n\t"
+      "s_mov_b32 m0, %12\n\tglobal_load_lds_dwordx4 %4, %8\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(b[0]), "s"(b[1]), "s"(b[2]),
+        "s"(b[3]), "s"(__builtin_amdgcn_readfirstlane(lds_addr)),
+        "s"(__builtin_amdgcn_readfirstlane(lds_addr + 1024)),
+        "s"(__builtin_amdgcn_readfirstlane(lds_addr + 2048)),
+        "s"(__builtin_amdgcn_readfirstlane(lds_addr + 3072))
+      : "memory");
+}
+
 __device__ __forceinline__ f32x4 nt_mfma(u32x4 w, u32x4 x, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
                                                  __builtin_bit_cast(bf16x8, x), c, 0, 0, 0);
@@ -157,27 +179,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
   const int side = wave >> 2;
   const int rbase = (wave & 3) * 64;
   const int dst_off = side * kNtSideBytes + rbase * kNtRowBytes;
-  // This lane's global row of instruction i is row_of(i) below, from one row
-  // kept in a register (rows 16 i further, clamped to M - 1 on the A side; on
-  // the interleaved gate/up side 16 (i / 2) further); its 16-byte chunk
-  // depends on the parity of i only.  The element offsets are formed at issue
-  // time, so that few registers stay live across the loop.
   const int r0 = rbase + (lane >> 2);
-  int grow0;
-  if (side == 0)
-    grow0 = m0 + r0;
-  else if (EPI == kEpiSwiglu)
-    grow0 = n0 / 2 + (r0 >> 5) * 16 + (r0 & 15);  // block r / 16: gate if even, up if odd
-  else
-    grow0 = n0 + r0;
-  int gcol[2];
-#pragma unroll
-  for (int par = 0; par < 2; ++par) gcol[par] = ((lane & 3) ^ nt_swz(r0 + 16 * par)) * 8;
-  auto row_of = [&](int i) -> int64_t {
-    if (side == 0) return grow0 + 16 * i < M ? grow0 + 16 * i : M - 1;
-    if (EPI == kEpiSwiglu) return grow0 + (i >> 1) * 16;
-    return grow0 + 16 * i;
-  };
   // Instruction i covers rows 16 i + rbase / 16 ..; rbase / 16 is even, so the
   // 16-row block of instruction i is a gate block for even i, an up block for odd.
   const bf16_t* src1[2] = {side == 0 ? A1 : a.B1,
@@ -185,27 +187,42 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
   const bf16_t* src2 = side == 0 ? A2 : a.B2;
   const bf16_t* src3 = side == 0 ? a.A3 : a.B3;
 
-  auto issue = [&](int s, unsigned char* stage_lds) {
-    const uint32_t base = nt_lds_addr(stage_lds) + dst_off;
-    if (s < ns1) {
+  // Instruction i loads a 16-row block through a wave-uniform base that
+  // advances 64 bytes per stage; each lane adds its row and chunk offset (both
+  // re-formed when the k range moves to the next operand pair).  On the A side
+  // rows past M read row M - 1: the block's base row is clamped to M - 1 and
+  // each lane's row to M - 1, so the lane offset is never negative.  On the
+  // interleaved gate/up side, block i is block (rbase / 32 + i / 2) of the gate
+  // rows for even i and of the up rows for odd i.
+  const unsigned char* gb[4];
+  uint32_t goff[4];
+  auto phase = [&](const bf16_t* sa, const bf16_t* sb, int K) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        nt_dma(reinterpret_cast<const unsigned char*>(src1[i & 1] + row_of(i) * K1 + s * kNtK +
-                                                      gcol[i & 1]),
-               base + i * 1024);
-    } else if (s < ns12) {
-      const bf16_t* p = src2 + (s - ns1) * kNtK;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        nt_dma(reinterpret_cast<const unsigned char*>(p + row_of(i) * K2 + gcol[i & 1]),
-               base + i * 1024);
-    } else {
-      const bf16_t* p = src3 + (s - ns12) * kNtK;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        nt_dma(reinterpret_cast<const unsigned char*>(p + row_of(i) * K3 + gcol[i & 1]),
-               base + i * 1024);
+    for (int i = 0; i < 4; ++i) {
+      int br, lrow;
+      if (side == 0) {
+        const int b0 = m0 + rbase + 16 * i;
+        br = b0 < M ? b0 : M - 1;
+        lrow = (b0 + (lane >> 2) < M ? b0 + (lane >> 2) : M - 1) - br;
+      } else {
+        br = EPI == kEpiSwiglu ? n0 / 2 + ((rbase >> 5) + (i >> 1)) * 16 : n0 + rbase + 16 * i;
+        lrow = lane >> 2;
+      }
+      gb[i] = reinterpret_cast<const unsigned char*>((i & 1 ? sb : sa) + static_cast<int64_t>(br) * K);
+      const int gcol = ((lane & 3) ^ nt_swz(r0 + 16 * (i & 1))) * 8;
+      goff[i] = static_cast<uint32_t>((lrow * K + gcol) * 2);
     }
+  };
+  auto issue = [&](int s, unsigned char* stage_lds) {
+    if (s == 0)
+      phase(src1[0], src1[1], K1);
+    else if (s == ns1)
+      phase(src2, src2, K2);
+    else if (s == ns12)
+      phase(src3, src3, K3);
+    nt_dma4(gb, goff, nt_lds_addr(stage_lds) + dst_off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gb[i] += kNtK * 2;
   };
 
   // Operand reads: wave tile rows wm * 128 + mb * 16 + (lane % 16) of A and
@@ -236,19 +253,24 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
   struct Frag {
     u32x4 xa[8], wb[4];
   };
-  auto read_frags = [&](const unsigned char* st, Frag& f) {
+  // reads r0 .. r1 - 1 of the 12 (the 4 weight fragments, then the 8 of A)
+  auto read_frags = [&](const unsigned char* st, Frag& f, int r0, int r1) {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      f.wb[nb] = nt_read16(st + rd_b[nb & 1] + (nb & ~1) * 16 * kNtRowBytes);
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-      f.xa[mb] = nt_read16(st + rd_a[mb & 1] + (mb & ~1) * 16 * kNtRowBytes);
+    for (int r = 0; r < 12; ++r) {
+      if (r < r0 || r >= r1) continue;
+      if (r < 4)
+        f.wb[r] = nt_read16(st + rd_b[r & 1] + (r & ~1) * 16 * kNtRowBytes);
+      else
+        f.xa[r - 4] = nt_read16(st + rd_a[r & 1] + ((r - 4) & ~1) * 16 * kNtRowBytes);
+    }
   };
-  auto mma = [&](const Frag& f) {
+  // products m0 .. m1 - 1 of the 32 (row block mb = m / 4, column block nb = m % 4)
+  auto mma = [&](const Frag& f, int m0_, int m1_) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = nt_mfma(f.wb[nb], f.xa[mb], acc[mb][nb]);
+    for (int m = 0; m < 32; ++m) {
+      if (m < m0_ || m >= m1_) continue;
+      acc[m >> 2][m & 3] = nt_mfma(f.wb[m & 3], f.xa[m >> 2], acc[m >> 2][m & 3]);
+    }
   };
 
   unsigned char* L0 = nt_lds0;
@@ -271,7 +293,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  if (nstage > 0) read_frags(L0, F0);
+  if (nstage > 0) read_frags(L0, F0, 0, 12);
   if (nstage > 3) issue(3, L3);
 
   // Step s (stage s's operands are in `cur`): wait for this wave's loads of
@@ -295,13 +317,23 @@ __global__ void __launch_bounds__(512, 1) k_gemm_nt(const NtArgs a) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (s + 4 < nstage) issue(s + 4, refill);
     // unconditional, so that the reads and the products share one basic block:
-    // after the last stage this reads a slot no later stage fills, unused
-    read_frags(next_lds, next);
-    mma(cur);
+    // after the last stage this reads a slot no later stage fills, unused.  The
+    // refill's DMA follows the first eight products: every wave leaves the
+    // barrier at once, and what a wave issues before its first MFMA leaves
+    // the matrix pipe idle.
+    read_frags(next_lds, next, 0, 4);
+    mma(cur, 0, 8);
 #pragma unroll
-    for (int k = 0; k < 12; ++k) {
+    for (int k = 0; k < 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    if (s + 4 < nstage) issue(s + 4, refill);
+    read_frags(next_lds, next, 4, 12);
+    mma(cur, 8, 32);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
@@ -507,6 +539,10 @@ int elementwise_blocks(int64_t n8) {
 }  // namespace
 
 bool gemm_nt_ok(int64_t M, int N, int K1, int K2, int K3) {
+  // K < 2^26: a lane's byte offset inside its 16-row block, 2 (15 K + 24), fits
+  // 32 bits
+  constexpr int kKMax = 1 << 26;
+  if (K1 >= kKMax || K2 >= kKMax || K3 >= kKMax) return false;
   return M >= 1 && M <= (int64_t{1} << 30) && N > 0 && N % kNtN == 0 && K1 > 0 &&
          K1 % kNtK == 0 && K2 >= 0 && K2 % kNtK == 0 && K3 >= 0 && K3 % kNtK == 0 &&
          (K3 == 0 || K2 > 0);
