@@ -262,13 +262,13 @@ __global__ void __launch_bounds__(512, 1) k_ghost_mfma(const bf16_t* __restrict_
     asm volatile("" ::: "memory");
     // unconditional, so that reads and products share one basic block: after the
     // last slab this reads a slot no later slab fills, unused
-    read_frags(s + 1, 0, F0, 0, 2);
-    mma(F1, acc, 0, 4);
-    interleave(2);
+    read_frags(s + 1, 0, F0, 0, 4);
+    mma(F1, acc, 0, 8);
+    interleave(4);
     if (s + kGStages < n) issue(s + kGStages);
-    read_frags(s + 1, 0, F0, 2, 8);
-    mma(F1, acc, 4, 16);
-    interleave(6);
+    read_frags(s + 1, 0, F0, 4, 8);
+    mma(F1, acc, 8, 16);
+    interleave(4);
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
   for (int s = 0; s < nA; ++s) slab(s, ga);
