@@ -103,7 +103,10 @@ hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample
 // Probes of up to kProbeLayersMax layers in one launch, bf16, padded to kpad
 // columns: the same entries as k_probe_fill for each layer.  Workgroup x walks
 // the layers' row-group blocks in order (layer t owns blocks bstart[t] ..
-// bstart[t + 1] - 1), y is the column, z the sample.
+// bstart[t + 1] - 1), z is the sample, and each thread fills its four rows in
+// every column in turn: one workgroup per 1024 rows and sample instead of one
+// per column as well, since workgroups that each write only 2 KB are limited
+// by how fast they can be dispatched.
 template <int N>
 __global__ void k_probe_fill_layers(uint32_t k0, uint32_t k1, ProbeLayerTable<N> tab, int kfill,
                                     int kpad, bf16_t* __restrict__ out, int signs) {
@@ -112,29 +115,31 @@ __global__ void k_probe_fill_layers(uint32_t k0, uint32_t k1, ProbeLayerTable<N>
   const int p = tab.p[t];
   const int ngroups = (p + 3) >> 2;
   const int g = (static_cast<int>(blockIdx.x) - tab.bstart[t]) * blockDim.x + threadIdx.x;
-  const int j = blockIdx.y;
   const int i = blockIdx.z;
   if (g >= ngroups) return;
-  float z[4] = {0.f, 0.f, 0.f, 0.f};
-  if (j < kfill) {
-    u32x4 c;
-    c.x = static_cast<uint32_t>(g);
-    c.y = static_cast<uint32_t>(j);
-    c.z = static_cast<uint32_t>(i);
-    c.w = tab.layer[t];
-    if (signs) {
-      const u32x4 w = philox4x32_10(c, k0, k1);
+  bf16_t* base = out + tab.off[t] + static_cast<int64_t>(i) * kpad * p;
+  for (int j = 0; j < kpad; ++j) {
+    float z[4] = {0.f, 0.f, 0.f, 0.f};
+    if (j < kfill) {
+      u32x4 c;
+      c.x = static_cast<uint32_t>(g);
+      c.y = static_cast<uint32_t>(j);
+      c.z = static_cast<uint32_t>(i);
+      c.w = tab.layer[t];
+      if (signs) {
+        const u32x4 w = philox4x32_10(c, k0, k1);
 #pragma unroll
-      for (int l = 0; l < 4; ++l) z[l] = (w[l] >> 31) ? -1.f : 1.f;
-    } else {
-      normals4(c, k0, k1, z);
+        for (int l = 0; l < 4; ++l) z[l] = (w[l] >> 31) ? -1.f : 1.f;
+      } else {
+        normals4(c, k0, k1, z);
+      }
     }
-  }
-  bf16_t* row = out + tab.off[t] + (static_cast<int64_t>(i) * kpad + j) * p;
+    bf16_t* row = base + static_cast<int64_t>(j) * p;
 #pragma unroll
-  for (int l = 0; l < 4; ++l) {
-    const int r = 4 * g + l;
-    if (r < p) row[r] = f32_to_bf16(z[l]);
+    for (int l = 0; l < 4; ++l) {
+      const int r = 4 * g + l;
+      if (r < p) row[r] = f32_to_bf16(z[l]);
+    }
   }
 }
 
@@ -145,9 +150,9 @@ hipError_t launch_probe_fill_layers_bf16(uint64_t seed, const ProbeLayerTable<kP
   if (tab.n > kProbeLayersMax) return hipErrorInvalidValue;
   const int nblocks = tab.bstart[tab.n];
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_probe_fill_layers<kProbeLayersMax>, dim3(nblocks, kpad, nsamp), dim3(256),
-                     0, s, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), tab,
-                     kfill, kpad, out, signs ? 1 : 0);
+  hipLaunchKernelGGL(k_probe_fill_layers<kProbeLayersMax>, dim3(nblocks, 1, nsamp), dim3(256), 0, s,
+                     static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), tab, kfill,
+                     kpad, out, signs ? 1 : 0);
   return hipGetLastError();
 }
 
