@@ -115,6 +115,33 @@ def test_norm_parity(dev, method, case):
     assert err <= (TOL_F32 if dtype == "f32" else TOL_BF16)
 
 
+GHOST_CASES = [
+    # (name, B, T, d, p): the MFMA ghost kernel deals super-tiles of 4 x 8 blocks
+    # (256-token S blocks by 128-token t blocks) to the XCDs, one per XCD per round.
+    # Several super-tile rows with 9 super-tiles in all (the second round almost
+    # empty), and a last S block that T cuts in half in every sample.
+    ("ghost_rows_b3_t2048", 3, 2048, 64, 128),
+    ("ghost_ragged_b2_t1152", 2, 1152, 128, 64),
+]
+
+
+@pytest.mark.parametrize("case", GHOST_CASES, ids=[c[0] for c in GHOST_CASES])
+def test_ghost_tile_dealing(dev, case):
+    """The exact ghost norm on bf16 inputs against the oracle's fp64 Grams of the
+    same inputs: only the fp32 accumulation of each Gram entry (d + p <= 192
+    products) differs, so the bound is 1e-4 relative, tighter than the 2e-2 of
+    the estimators."""
+    name, B, T, d, p = case
+    A, G = linear_inputs(B, T, d, p, "bf16", "llama_logu", seed=23 + T)
+    n = torch.full((B,), -1.0, dtype=torch.float32, device=dev)
+    dp.dp_norm_est("ghost", A.to(dev), G.to(dev), 0, 0, 0, n)
+    torch.cuda.synchronize()
+    ref = oracle.norm_est("ghost", A, G)
+    err = max_rel_elementwise(f64(n), ref)
+    report(f"ghost dealing {name}", max_rel=err)
+    assert err <= 1e-4
+
+
 LOWRANK_CASES = [
     # (name, dtype, B, T, d, p, k): rank-8 signal plus noise (decaying spectrum)
     ("lowrank_f32", "f32", 3, 96, 64, 80, 12),
