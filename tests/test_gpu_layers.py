@@ -70,6 +70,26 @@ def test_norm_layers_batched_hutch(dev):
     assert e_pl <= 1e-5
 
 
+def test_norm_layers_batched_full_width(dev):
+    """The batched norm call at the stack's width and token count (B 8, T 4096,
+    a q and a k projection of Llama 3.2 1B): the 64-token sketch workgroups and
+    the fused projection-and-square of the grouped launches that the step over
+    the stack runs, every per-sample norm against the oracle and against the
+    per-layer calls."""
+    B, T, k, seed = 8, 4096, 32, 515
+    host, devl = _make(B, T, [(2048, 2048, 0), (2048, 512, 1)], "bf16", 14)
+    n = torch.zeros(B, dtype=torch.float32, device=dev)
+    dp.dp_norm_est_layers("hutch", devl, k, seed, n)
+    torch.cuda.synchronize()
+    ref = sum(oracle.norm_est("hutch", A, G, k=k, seed=seed, layer=lid) for A, G, lid in host)
+    e_or = max_rel_elementwise(f64(n), ref)
+    e_pl = max_rel_elementwise(f64(n), _per_layer("hutch", devl, k, seed, B, dev))
+    report("norm layers batched full width", oracle=e_or, per_layer=e_pl)
+    assert e_or <= 2e-2
+    # same kernels per layer: only the order of the sums over layers differs
+    assert e_pl <= 1e-5
+
+
 @pytest.mark.parametrize("flags", [dp.DP_PROBE_SHARED, dp.DP_PROBE_RADEMACHER,
                                    dp.DP_PROBE_SHARED | dp.DP_PROBE_RADEMACHER])
 def test_norm_layers_probe_flags(dev, flags):
