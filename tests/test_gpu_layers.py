@@ -70,14 +70,17 @@ def test_norm_layers_batched_hutch(dev):
     assert e_pl <= 1e-5
 
 
-def test_norm_layers_batched_full_width(dev):
+@pytest.mark.parametrize("shapes", [
+    [(2048, 2048, 0), (2048, 512, 1)],   # q, k: 64-token sketches, 64-column projections
+    [(2048, 8192, 5), (8192, 2048, 6)],  # up, down: 128-token sketch, 128-column projection
+], ids=["q_k", "up_down"])
+def test_norm_layers_batched_full_width(dev, shapes):
     """The batched norm call at the stack's width and token count (B 8, T 4096,
-    a q and a k projection of Llama 3.2 1B): the 64-token sketch workgroups and
-    the fused projection-and-square of the grouped launches that the step over
-    the stack runs, every per-sample norm against the oracle and against the
-    per-layer calls."""
+    Llama 3.2 1B projections): the grouped sketch and fused projection-and-square
+    launches that the step over the stack runs, every per-sample norm against
+    the oracle and against the per-layer calls."""
     B, T, k, seed = 8, 4096, 32, 515
-    host, devl = _make(B, T, [(2048, 2048, 0), (2048, 512, 1)], "bf16", 14)
+    host, devl = _make(B, T, shapes, "bf16", 14)
     n = torch.zeros(B, dtype=torch.float32, device=dev)
     dp.dp_norm_est_layers("hutch", devl, k, seed, n)
     torch.cuda.synchronize()
