@@ -104,12 +104,14 @@ hipError_t launch_probe_fill_bf16(uint64_t seed, uint32_t layer, uint32_t sample
 // columns: the same entries as k_probe_fill for each layer.  Workgroup x walks
 // the layers' row-group blocks in order (layer t owns blocks bstart[t] ..
 // bstart[t + 1] - 1), z is the sample, and each thread fills its four rows in
-// every column in turn: one workgroup per 1024 rows and sample instead of one
+// the columns of range y (jper columns) in turn: with many layers one range
+// covers every column, one workgroup per 1024 rows and sample instead of one
 // per column as well, since workgroups that each write only 2 KB are limited
-// by how fast they can be dispatched.
+// by how fast they can be dispatched; a launch of few layers splits the
+// columns so that the chip still gets about a thousand workgroups.
 template <int N>
 __global__ void k_probe_fill_layers(uint32_t k0, uint32_t k1, ProbeLayerTable<N> tab, int kfill,
-                                    int kpad, bf16_t* __restrict__ out, int signs) {
+                                    int kpad, int jper, bf16_t* __restrict__ out, int signs) {
   int t = 0;
   while (t + 1 < tab.n && static_cast<int>(blockIdx.x) >= tab.bstart[t + 1]) ++t;
   const int p = tab.p[t];
@@ -118,7 +120,9 @@ __global__ void k_probe_fill_layers(uint32_t k0, uint32_t k1, ProbeLayerTable<N>
   const int i = blockIdx.z;
   if (g >= ngroups) return;
   bf16_t* base = out + tab.off[t] + static_cast<int64_t>(i) * kpad * p;
-  for (int j = 0; j < kpad; ++j) {
+  const int j0 = static_cast<int>(blockIdx.y) * jper;
+  const int j1 = j0 + jper < kpad ? j0 + jper : kpad;
+  for (int j = j0; j < j1; ++j) {
     float z[4] = {0.f, 0.f, 0.f, 0.f};
     if (j < kfill) {
       u32x4 c;
@@ -150,9 +154,15 @@ hipError_t launch_probe_fill_layers_bf16(uint64_t seed, const ProbeLayerTable<kP
   if (tab.n > kProbeLayersMax) return hipErrorInvalidValue;
   const int nblocks = tab.bstart[tab.n];
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_probe_fill_layers<kProbeLayersMax>, dim3(nblocks, 1, nsamp), dim3(256), 0, s,
-                     static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), tab, kfill,
-                     kpad, out, signs ? 1 : 0);
+  // column ranges: enough for about 1024 workgroups, at most one column each
+  const int64_t wgs = static_cast<int64_t>(nblocks) * nsamp;
+  int64_t want = (1024 + wgs - 1) / wgs;
+  if (want > kpad) want = kpad;
+  const int jper = static_cast<int>((kpad + want - 1) / want);
+  const int nrange = (kpad + jper - 1) / jper;
+  hipLaunchKernelGGL(k_probe_fill_layers<kProbeLayersMax>, dim3(nblocks, nrange, nsamp), dim3(256), 0,
+                     s, static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32), tab, kfill,
+                     kpad, jper, out, signs ? 1 : 0);
   return hipGetLastError();
 }
 
