@@ -216,6 +216,10 @@ def _tiles(d, p):
     # in a full group, and a fifth 64-tile layer alone (the per-layer path)
     (4, 128, [(2048, 512, 70), (2048, 2048, 71), (2048, 2048, 72), (2048, 2048, 73),
               (2048, 512, 74), (2048, 2048, 75), (2048, 2048, 76)], [6]),
+    # the stack's two grouped launches at full width (B 8, T 4096: 1024 stages a
+    # workgroup): four q/o-shaped layers, and sixteen k/v-shaped ones
+    (8, 4096, [(2048, 2048, 100 + i) for i in range(4)], []),
+    (8, 4096, [(2048, 512, 120 + i) for i in range(16)], []),
 ])
 def test_update_layers_grouped_contraction(dev, B, T, shapes, alone):
     """Layers whose tile counts divide 256 share contraction launches: theta matches
