@@ -92,6 +92,7 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
       } else {
         P.nsplit_d = mfma_project_splits(B, T, d);
         P.zp = cv.take(Bz * P.nsplit_d * kMfmaProbeCols * d * f4);
+        P.part = cv.take(Bz * mfma_frob_chunks(d) * sizeof(double));
       }
     } else {
       P.pf = cv.take(Bz * k * p * f4);
@@ -118,7 +119,7 @@ NormPlan plan_norm(int method, int dtype, int B, int T, int d, int p, int k) {
       P.xp = cv.take(Bz * P.nsplit_p * kMfmaProbeCols * p * f4);
       P.p3b = cv.take(Bz * kMfmaProbeCols * p * h2);
       P.sq_cols = mfma_project_sq_cols(B, T, d);
-      if (P.sq_cols > 0) P.part = cv.take(Bz * (d / P.sq_cols) * sizeof(double));
+      P.part = cv.take(Bz * (P.sq_cols > 0 ? d / P.sq_cols : mfma_frob_chunks(d)) * sizeof(double));
     } else {
       P.y = cv.take(Bz * P.k3 * (T > 0 ? T : 1) * f4);
       P.z = cv.take(Bz * P.k3 * d * f4);
@@ -202,7 +203,8 @@ dp_status_t run_norm_mfma_hutch(const NormPlan& P, int B, int T, int d, int p, i
   }
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
   DP_TRY(mk.close(s));
-  DP_TRY(launch_frob_finish(Zp, B, P.nsplit_d, d, k, 1.0f / k, 0, 0.f, n_sq, accum ? 1 : 0, s));
+  DP_TRY(launch_frob_finish(Zp, B, P.nsplit_d, d, k, 1.0f / k, 0, 0.f, at<double>(ws, P.part), n_sq,
+                            accum ? 1 : 0, s));
   return DP_OK;
 }
 
@@ -282,8 +284,8 @@ dp_status_t run_norm_mfma_hpp(const NormPlan& P, int B, int T, int d, int p, con
   }
   DP_TRY(launch_project_mfma(A, B, T, d, Yb, P.nsplit_d, Zp, s));
   DP_TRY(mk.close(s));
-  DP_TRY(launch_frob_finish(Zp, B, P.nsplit_d, d, S_, 1.0f, R_, 1.0f / R_, n_sq, accum ? 1 : 0,
-                            s));
+  DP_TRY(launch_frob_finish(Zp, B, P.nsplit_d, d, S_, 1.0f, R_, 1.0f / R_, at<double>(ws, P.part),
+                            n_sq, accum ? 1 : 0, s));
   return DP_OK;
 }
 

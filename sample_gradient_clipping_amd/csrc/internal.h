@@ -200,10 +200,11 @@ hipError_t launch_project_sq_mfma(const bf16_t* X, int B, int T, int W, const bf
                                   int n0, float w0, int n1, float w1, double* part,
                                   int64_t part_stride, hipStream_t s);
 // n_sq[b] (= or +=) sum_j w_j ||sum_split Zp[b][split][j][:]||^2 with w_j = w0
-// for j < n0, w1 for n0 <= j < n0 + n1, else 0 (W % 4 == 0).  One block per
-// sample, fixed-order fp64 sums.
+// for j < n0, w1 for n0 <= j < n0 + n1, else 0 (W % 4 == 0).  Fixed-order fp64
+// sums through part [B][mfma_frob_chunks(W)] (workspace), then k_sum_parts.
+int mfma_frob_chunks(int W);
 hipError_t launch_frob_finish(const float* Zp, int B, int nsplit, int W, int n0, float w0, int n1,
-                              float w1, float* n_sq, int accumulate, hipStream_t s);
+                              float w1, double* part, float* n_sq, int accumulate, hipStream_t s);
 
 // Ghost norm per sample from 128 x 128 Gram tile pairs: part[b][pair] (fp64).
 bool mfma_ghost_ok(int T, int d, int p);

@@ -380,71 +380,79 @@ __global__ void __launch_bounds__(256) k_project_sq_layers(int T, ProjectLayers 
 // ---------------------------------------------------------------------------
 // Finish (randomized-clipping summary, section 中核メカニズム, item 1: the
 // estimate is the weighted squared Frobenius norm of Z = sum of the token
-// splits).  One block of 1024 threads per sample: each thread takes float4
-// positions u = tid + 1024 m of the sample's [32][W] rows, kFrobU of them with
-// every split's loads in flight together, sums the splits in order, and adds
-// the weighted squares in fp64; a block reduction in a fixed shape gives n_i.
+// splits), in two fixed-order passes.  Block (c, b) takes the float4
+// positions 512 c .. 512 c + 511 of sample b's [32][W] rows, two per thread
+// with every split's loads in flight, sums the splits in order and the
+// weighted squares in fp64, and writes one partial; k_sum_parts then adds the
+// sample's W / 64 partials in block order.  There are enough blocks to stream
+// the splits at any B (one block per sample left two CUs at work at B = 2).
 // Positions past the end load the last element (in bounds) and count zero, so
-// no load sits under a branch (the compiler would wait for it before the join).
-// No block communicates with another, so no atomics or fences are needed and
-// the result is deterministic.
+// no load sits under a branch.  No block communicates with another, so no
+// atomics or fences are needed and the result is deterministic.
 // ---------------------------------------------------------------------------
-constexpr int kFrobThreads = 1024, kFrobU = 8;
+constexpr int kFrobThreads = 256, kFrobU = 2;
 
-__global__ void __launch_bounds__(kFrobThreads) k_frob_finish(const float* __restrict__ Zp,
+int mfma_frob_chunks(int W) {
+  const int E4 = kMfmaProbeCols * W / 4;
+  return (E4 + kFrobThreads * kFrobU - 1) / (kFrobThreads * kFrobU);
+}
+
+__global__ void __launch_bounds__(kFrobThreads) k_frob_chunks(const float* __restrict__ Zp,
                                                               int nsplit, int W, int n0, float w0,
                                                               int n1, float w1,
-                                                              float* __restrict__ n_sq,
-                                                              int accumulate) {
+                                                              double* __restrict__ part,
+                                                              int nchunk) {
   __shared__ double red[16];
-  const int b = blockIdx.x;
+  const int c = blockIdx.x, b = blockIdx.y;
   const int E4 = kMfmaProbeCols * W / 4;
   const float4* zb = reinterpret_cast<const float4*>(Zp) + static_cast<int64_t>(b) * nsplit * E4;
-  double acc = 0.0;
-  for (int u0 = 0; u0 < E4; u0 += kFrobThreads * kFrobU) {
-    int uc[kFrobU];
-    float4 z[kFrobU];
+  const int u0 = c * kFrobThreads * kFrobU + threadIdx.x;
+  int uc[kFrobU];
+  float4 z[kFrobU];
+#pragma unroll
+  for (int q = 0; q < kFrobU; ++q) {
+    const int u = u0 + kFrobThreads * q;
+    uc[q] = u < E4 ? u : E4 - 1;
+    z[q] = zb[uc[q]];
+  }
+#pragma unroll 4
+  for (int sp = 1; sp < nsplit; ++sp) {
+    float4 v[kFrobU];
+#pragma unroll
+    for (int q = 0; q < kFrobU; ++q) v[q] = zb[static_cast<int64_t>(sp) * E4 + uc[q]];
 #pragma unroll
     for (int q = 0; q < kFrobU; ++q) {
-      const int u = u0 + threadIdx.x + kFrobThreads * q;
-      uc[q] = u < E4 ? u : E4 - 1;
-      z[q] = zb[uc[q]];
-    }
-    for (int sp = 1; sp < nsplit; ++sp) {
-      float4 v[kFrobU];
-#pragma unroll
-      for (int q = 0; q < kFrobU; ++q) v[q] = zb[static_cast<int64_t>(sp) * E4 + uc[q]];
-#pragma unroll
-      for (int q = 0; q < kFrobU; ++q) {
-        z[q].x += v[q].x;
-        z[q].y += v[q].y;
-        z[q].z += v[q].z;
-        z[q].w += v[q].w;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kFrobU; ++q) {
-      const int u = u0 + threadIdx.x + kFrobThreads * q;
-      const int j = (4 * u) / W;  // probe column of this float4 (W % 4 == 0)
-      const float w = j < n0 ? w0 : (j < n0 + n1 ? w1 : 0.f);
-      if (u < E4 && w != 0.f)
-        acc += static_cast<double>(w) *
-               (static_cast<double>(z[q].x) * z[q].x + static_cast<double>(z[q].y) * z[q].y +
-                static_cast<double>(z[q].z) * z[q].z + static_cast<double>(z[q].w) * z[q].w);
+      z[q].x += v[q].x;
+      z[q].y += v[q].y;
+      z[q].z += v[q].z;
+      z[q].w += v[q].w;
     }
   }
+  double acc = 0.0;
+#pragma unroll
+  for (int q = 0; q < kFrobU; ++q) {
+    const int u = u0 + kFrobThreads * q;
+    const int j = (4 * u) / W;  // probe column of this float4 (W % 4 == 0)
+    const float w = j < n0 ? w0 : (j < n0 + n1 ? w1 : 0.f);
+    if (u < E4 && w != 0.f)
+      acc += static_cast<double>(w) *
+             (static_cast<double>(z[q].x) * z[q].x + static_cast<double>(z[q].y) * z[q].y +
+              static_cast<double>(z[q].z) * z[q].z + static_cast<double>(z[q].w) * z[q].w);
+  }
   acc = block_sum_d(acc, red);
-  if (threadIdx.x == 0)
-    n_sq[b] = static_cast<float>(accumulate ? static_cast<double>(n_sq[b]) + acc : acc);
+  if (threadIdx.x == 0) part[static_cast<int64_t>(b) * nchunk + c] = acc;
 }
 
 hipError_t launch_frob_finish(const float* Zp, int B, int nsplit, int W, int n0, float w0, int n1,
-                              float w1, float* n_sq, int accumulate, hipStream_t s) {
+                              float w1, double* part, float* n_sq, int accumulate, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (W % 4 != 0 || nsplit < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_frob_finish, dim3(B), dim3(kFrobThreads), 0, s, Zp, nsplit, W, n0, w0, n1,
-                     w1, n_sq, accumulate);
-  return hipGetLastError();
+  const int nchunk = mfma_frob_chunks(W);
+  hipLaunchKernelGGL(k_frob_chunks, dim3(nchunk, B), dim3(kFrobThreads), 0, s, Zp, nsplit, W, n0,
+                     w0, n1, w1, part, nchunk);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_sum_parts(part, B, nchunk, n_sq, accumulate, s);
 }
 
 hipError_t launch_project_sq_mfma_layers(int B, int T, int cols, const ProjectLayers& tab, int n0,
