@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define DPRC_ABI_VERSION 3
+#define DPRC_ABI_VERSION 4
 
 typedef void *dp_stream_t; /* a hipStream_t */
 
@@ -151,6 +151,22 @@ dp_status_t dp_norm_est_noalloc(int method, int dtype, int B, int T, int d, int 
 
 /* Bytes of workspace dp_clip_aggregate needs, or (size_t)-1 if invalid. */
 size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p);
+
+/*
+ * Which kernels serve a call: 1 if the MFMA kernels do (bf16 inputs on their
+ * tiles), 0 if the generic kernels do (one thread per output element with
+ * plain loads: correct, and covered by the same tests, but one to three orders
+ * of magnitude slower), -1 if the arguments are invalid.  Host-only; nothing
+ * is enqueued.  The MFMA conditions: the Hutchinson sketch and projection need
+ * T % 128 == 0, p % 256 == 0, d % 128 == 0 and k <= 32 (Hutch++: s + r <= 32
+ * and the same conditions on both widths); ghost needs T % 128 == 0 and d, p
+ * multiples of 64; FGC and the clipped sum need T % 128 == 0 and d, p
+ * multiples of 256.  Arguments as for the calls they describe (for these
+ * queries B, T, d, p follow the call's validation; k is ignored for ghost and
+ * FGC).  The pages fix no kernel; these only report this library's choice.
+ */
+int dp_norm_est_uses_mfma(int method, int dtype, int B, int T, int d, int p, int k);
+int dp_clip_aggregate_uses_mfma(int dtype, int B, int T, int d, int p);
 
 /*
  * Clip factors and the clipped sum of per-sample gradients of one layer.

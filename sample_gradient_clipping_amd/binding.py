@@ -72,6 +72,10 @@ def load_library():
     c_int, c_u32, c_u64, c_sz, c_f, c_p = (ctypes.c_int, ctypes.c_uint32, ctypes.c_uint64,
                                            ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p)
     L.dp_abi_version.restype = c_int
+    L.dp_norm_est_uses_mfma.argtypes = [c_int] * 7
+    L.dp_norm_est_uses_mfma.restype = c_int
+    L.dp_clip_aggregate_uses_mfma.argtypes = [c_int] * 5
+    L.dp_clip_aggregate_uses_mfma.restype = c_int
     L.dp_status_string.argtypes = [c_int]
     L.dp_status_string.restype = ctypes.c_char_p
     L.dp_norm_est_workspace.argtypes = [c_int] * 7
@@ -182,6 +186,17 @@ def dp_abi_version():
     return load_library().dp_abi_version()
 
 
+def dp_norm_est_uses_mfma(method, dtype, B, T, d, p, k):
+    """1 if the MFMA kernels serve this dp_norm_est call, 0 if the generic ones, -1 if invalid."""
+    return load_library().dp_norm_est_uses_mfma(_method_code(method), _dtype_name_code(dtype), B, T,
+                                                d, p, k)
+
+
+def dp_clip_aggregate_uses_mfma(dtype, B, T, d, p):
+    """1 if the MFMA contraction serves this dp_clip_aggregate call, 0 if the generic one, -1 if invalid."""
+    return load_library().dp_clip_aggregate_uses_mfma(_dtype_name_code(dtype), B, T, d, p)
+
+
 def dp_status_string(status):
     return load_library().dp_status_string(int(status)).decode()
 
@@ -222,6 +237,10 @@ def _dtype_code(t):
 
 def _method_code(method):
     return METHODS[method] if isinstance(method, str) else int(method)
+
+
+def _dtype_name_code(dtype):
+    return dtype if isinstance(dtype, int) else {"f32": DP_F32, "bf16": DP_BF16}[dtype]
 
 
 def _workspace(nbytes, device, ws, zeroed=False):

@@ -483,6 +483,16 @@ size_t dp_clip_aggregate_workspace(int dtype, int B, int T, int d, int p) {
   return plan_agg(dtype, B, T, d, p).total;
 }
 
+int dp_norm_est_uses_mfma(int method, int dtype, int B, int T, int d, int p, int k) {
+  if (!norm_args_ok(method, dtype, B, T, d, p, k)) return -1;
+  return plan_norm(method, dtype, B, T, d, p, k).mfma ? 1 : 0;
+}
+
+int dp_clip_aggregate_uses_mfma(int dtype, int B, int T, int d, int p) {
+  if (!agg_args_ok(dtype, B, T, d, p)) return -1;
+  return plan_agg(dtype, B, T, d, p).mfma ? 1 : 0;
+}
+
 bool agg_ptrs_ok(int B, int T, const void* A, const void* G, const float* n_sq, float C,
                  float* c_out) {
   if (!(C > 0.f) || !std::isfinite(C)) return false;

@@ -39,7 +39,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dp.dp_abi_version() == 3
+    assert dp.dp_abi_version() == 4
     for s in range(5):
         assert dp.dp_status_string(s).startswith("DP_")
     assert "unknown" in dp.dp_status_string(99)
@@ -419,3 +419,25 @@ def test_mlp_block_entry_points_reject_bad_arguments(lib):
     assert bwd(dx=_addr(8)) == E                          # dx overlaps dout
     assert bwd(G=FAKE_MIS) == E
     assert bwd(T=0) == dp.DP_OK
+
+
+def test_kernel_path_queries(lib):
+    """Which kernels serve a call, decided on the host: the MFMA kernels for bf16
+    on their tiles, the generic ones otherwise, -1 for invalid arguments."""
+    # the stack's shapes and the long-context layer take the MFMA kernels
+    for method, k in (("hutch", 32), ("hutchpp", 32), ("ghost", 0), ("fgc", 0)):
+        assert dp.dp_norm_est_uses_mfma(method, "bf16", 8, 4096, 2048, 8192, k) == 1
+        assert dp.dp_norm_est_uses_mfma(method, "bf16", 2, 16384, 2048, 8192, k) == 1
+    assert dp.dp_clip_aggregate_uses_mfma("bf16", 8, 4096, 8192, 2048) == 1
+    # fp32, more than 32 probes, off-tile widths and token counts: generic
+    assert dp.dp_norm_est_uses_mfma("hutch", "f32", 8, 4096, 2048, 2048, 32) == 0
+    assert dp.dp_norm_est_uses_mfma("hutch", "bf16", 8, 4096, 2048, 2048, 48) == 0
+    assert dp.dp_norm_est_uses_mfma("hutch", "bf16", 8, 4096, 2048, 2000, 32) == 0
+    assert dp.dp_norm_est_uses_mfma("fgc", "bf16", 8, 4000, 2048, 2048, 0) == 0
+    assert dp.dp_norm_est_uses_mfma("ghost", "bf16", 4, 64, 64, 64, 0) == 0
+    assert dp.dp_clip_aggregate_uses_mfma("f32", 4, 64, 64, 64) == 0
+    assert dp.dp_clip_aggregate_uses_mfma("bf16", 8, 4096, 2048, 2000) == 0
+    # invalid arguments
+    assert dp.dp_norm_est_uses_mfma("hutch", "bf16", 8, 4096, 2048, 2048, 0) == -1
+    assert dp.dp_norm_est_uses_mfma("hutchpp", "bf16", 8, 4096, 2048, 2048, 2) == -1
+    assert dp.dp_clip_aggregate_uses_mfma("bf16", -1, 4096, 2048, 2048) == -1
