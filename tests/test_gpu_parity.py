@@ -95,6 +95,8 @@ NORM_CASES = [
     # column blocks): 64-column blocks (B d / 64 = 256), 128-column blocks (B d / 128 = 256)
     ("fused_sq64_bf16", "bf16", 8, 256, 2048, 256, 32),
     ("fused_sq128_bf16", "bf16", 4, 128, 8192, 256, 32),
+    # one sample: token splits of the projection and the chunked finish at B = 1
+    ("single_sample_bf16", "bf16", 1, 512, 1024, 512, 32),
 ]
 
 
